@@ -1,0 +1,162 @@
+"""CPU oracle for the FP8 scaled GEMM and the block-scaled GEMM + amax.
+
+TEST INFRASTRUCTURE: only the test suite, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package. The product path
+(``block_scaled_gemm_amd``) never imports it and shares no code with it.
+
+All arithmetic lives in ``oracle.cpp`` (plain C++, float64); this module only
+marshals numpy arrays through ctypes. Its format numbers are its own:
+E4M3FN = 0, E5M2 = 1, F32 = 2, BF16 = 3, F16 = 4; scale modes TENSOR = 0,
+1x128 = 1, 128x128 = 2; accumulation EXACT = 0, F32_CHUNKS = 1.
+
+Parity status of each function (what pins it is in tests/test_oracle_*.py):
+decode_fp8, round_to, scaled_gemm (exact and f32-chunk modes),
+blockscaled_gemm_amax: pinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+E4M3FN, E5M2, F32, BF16, F16 = 0, 1, 2, 3, 4
+SCALE_TENSOR, SCALE_1x128, SCALE_128x128 = 0, 1, 2
+ACC_EXACT, ACC_F32_CHUNKS = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# The mutation tests point this at a deliberately broken copy of the oracle.
+_LIB_OVERRIDE = os.environ.get("ORACLE_LIB_PATH")
+_lib = None
+
+_BITS_DTYPE = {E4M3FN: np.uint8, E5M2: np.uint8, F32: np.uint32, BF16: np.uint16, F16: np.uint16}
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.cpp into liboracle.so with g++ (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-pthread",
+               "-ffp-contract=off", "-fno-fast-math", "-o", _LIB + ".tmp", _SRC]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = _LIB_OVERRIDE or _LIB
+        if not os.path.exists(path):
+            build()
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        lib.orc_decode_fp8.argtypes = [P, I64, I, P]
+        lib.orc_round.argtypes = [P, I64, I, P]
+        lib.orc_scaled_gemm.argtypes = [I64, I64, I64, P, I, I64, P, I, I64, P, I, P, I, P, I, I,
+                                        P, I64, P, P, P, I]
+        lib.orc_blockscaled_gemm_amax.argtypes = [I64, I64, I64, I64, P, P, I, P, P, I, I, P, I64,
+                                                  P, P, P, P, P, I]
+        for f in (lib.orc_decode_fp8, lib.orc_round, lib.orc_scaled_gemm,
+                  lib.orc_blockscaled_gemm_amax):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc):
+    if rc == 2:
+        raise RuntimeError("oracle refuses to run: the host FP environment flushes subnormals (FTZ/DAZ)")
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+
+
+def _threads(threads):
+    return int(threads) if threads else (os.cpu_count() or 1)
+
+
+def bits_dtype(fmt: int):
+    return _BITS_DTYPE[fmt]
+
+
+def decode_fp8(codes: np.ndarray, fmt: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape, dtype=np.float64)
+    _check(_load().orc_decode_fp8(_ptr(codes), codes.size, fmt, _ptr(out)))
+    return out
+
+
+def round_to(x: np.ndarray, dtype: int) -> np.ndarray:
+    """Round float64 values to dtype with the oracle's output rules; returns bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=_BITS_DTYPE[dtype])
+    _check(_load().orc_round(_ptr(x), x.size, dtype, _ptr(out)))
+    return out
+
+
+def scaled_gemm(a, a_fmt, b, b_fmt, scale_a, sa_mode, scale_b, sb_mode, d_type,
+                scale_result=None, accum=ACC_EXACT, rows=None, threads=None):
+    """d = (a*s_a) @ (b*s_b)^T for a [M, lda>=K] and b [N, ldb>=K] uint8 codes.
+
+    ``a`` and ``b`` are 2-D uint8 arrays whose first K columns are used (pass K
+    via ``a.shape[1]`` unless the arrays are wider, see ``K`` below). Returns
+    (value float64 [R,N], sum_abs float64 [R,N], d_bits [R,N]) for the R rows in
+    ``rows`` (all rows when None).
+    """
+    return scaled_gemm_k(a, a_fmt, b, b_fmt, a.shape[1], scale_a, sa_mode, scale_b, sb_mode,
+                         d_type, scale_result, accum, rows, threads)
+
+
+def scaled_gemm_k(a, a_fmt, b, b_fmt, K, scale_a, sa_mode, scale_b, sb_mode, d_type,
+                  scale_result=None, accum=ACC_EXACT, rows=None, threads=None):
+    """As scaled_gemm, with an explicit K <= row pitch of a and b."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    M, lda = a.shape
+    N, ldb = b.shape
+    sa = np.ascontiguousarray(scale_a, dtype=np.float32).reshape(-1)
+    sb = np.ascontiguousarray(scale_b, dtype=np.float32).reshape(-1)
+    sr = None if scale_result is None else np.asarray([scale_result], dtype=np.float32).reshape(-1)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    R = M if r is None else r.size
+    value = np.empty((R, N), dtype=np.float64)
+    sabs = np.empty((R, N), dtype=np.float64)
+    bits = np.empty((R, N), dtype=_BITS_DTYPE[d_type])
+    _check(_load().orc_scaled_gemm(M, N, K, _ptr(a), a_fmt, lda, _ptr(b), b_fmt, ldb,
+                                   _ptr(sa), sa_mode, _ptr(sb), sb_mode, _ptr(sr), d_type, accum,
+                                   _ptr(r), R, _ptr(value), _ptr(sabs), _ptr(bits),
+                                   _threads(threads)))
+    return value, sabs, bits
+
+
+def blockscaled_gemm_amax(a, b, ab_fmt, sfa, sfb, sf_vec, c_type, rows=None, threads=None):
+    """C[l,m,n] = sum_k A^ B^ with A^ = A*SFA[l,m,k//sf]; a [L,M,K], b [L,N,K] uint8.
+
+    Returns (value [L,R,N], sum_abs [L,R,N], c_bits [L,R,N], amax float32, amax_index int).
+    """
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    L, M, K = a.shape
+    N = b.shape[1]
+    sfa = np.ascontiguousarray(sfa, dtype=np.float32)
+    sfb = np.ascontiguousarray(sfb, dtype=np.float32)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    R = M if r is None else r.size
+    value = np.empty((L, R, N), dtype=np.float64)
+    sabs = np.empty((L, R, N), dtype=np.float64)
+    bits = np.empty((L, R, N), dtype=_BITS_DTYPE[c_type])
+    amax = np.zeros(1, dtype=np.float32)
+    idx = np.zeros(1, dtype=np.int64)
+    _check(_load().orc_blockscaled_gemm_amax(M, N, K, L, _ptr(a), _ptr(b), ab_fmt, _ptr(sfa),
+                                             _ptr(sfb), sf_vec, c_type, _ptr(r), R, _ptr(value),
+                                             _ptr(sabs), _ptr(bits), _ptr(amax), _ptr(idx),
+                                             _threads(threads)))
+    return value, sabs, bits, float(amax[0]), int(idx[0])

@@ -1,0 +1,191 @@
+"""Seeded synthetic inputs for the FP8 scaled GEMM workloads.
+
+This module is shared by the oracle tests, the GPU parity tests and the
+benchmark. It holds none of the GEMM's arithmetic: it draws random numbers
+(numpy PCG64, seed = 1000 * workload + stream, stream 0 = A, 1 = B,
+2 = scales, 3 = adversarial codes) and turns synthetic real values into FP8
+codes with torch's CPU float8 casts after clamping to the format's range.
+
+Workloads (the shapes and value recipes of the pages' LLM-layer GEMMs; where
+the pages leave a value open, the recipe below is this repository's choice):
+
+ 1. 256^3, E4M3 from N(0,1)*64 clamped to +-448, per-tensor scales 0.5 / 0.25,
+    fast accumulation, fp32 output.
+ 2. per-tensor E4M3, N = K = 4096, M in {16, 64, 256, 1024, 2048, 8192},
+    slow accumulation, bf16 output. Gaussian set: z ~ N(0,1) per tensor,
+    x = z * 240 / max|z|, scale = max|z| / 240. Adversarial set: i.i.d. codes
+    (25% +-448, 25% random-sign subnormals, 10% +-0, 40% uniform finite codes)
+    with structured rows, scales 1.
+ 3. M = 4096, N = 14336, K = 4096, E4M3 from N(0,1)*64, scale_a per 1x128
+    [M, K/128], scale_b per 128x128 [N/128, K/128], fp32 values 2^u with
+    u ~ U(-8, 4) (log-uniform in [2^-8, 2^4]), bf16 output.
+ 4. L = 8, M = N = 2048, K = 8192, E4M3 from N(0,1)*64, power-of-two scale
+    factors 2^e, e ~ U{-8..4}, per 32 K elements per row; fp32 C and amax.
+ 5. M = 8192, N = 28672, K = 8200; (a) E4M3 from N(0,1)*32 with 1% outliers at
+    +-448, scales 2^-3, scale_result 1/16, E4M3 output, slow accumulation;
+    (b) E5M2 from N(0,1)*32 with 1% outliers at +-57344, scales 2^-10, f16
+    output, slow accumulation.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+E4M3FN, E5M2 = 0, 1
+FMT_MAX = {E4M3FN: 448.0, E5M2: 57344.0}
+_TORCH_FP8 = {E4M3FN: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
+
+GEMM2_MS = (16, 64, 256, 1024, 2048, 8192)
+
+
+def rng(workload: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(1000 * workload + stream))
+
+
+def to_codes(x: np.ndarray, fmt: int) -> np.ndarray:
+    """FP8 codes of float values already inside the format's finite range."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(_TORCH_FP8[fmt]).view(torch.uint8).numpy()
+
+
+def gauss_codes(g: np.random.Generator, shape, sigma: float, fmt: int = E4M3FN,
+                outlier_frac: float = 0.0) -> np.ndarray:
+    """clip(N(0,1)*sigma, +-max) as FP8 codes, with a fraction of entries set to +-max."""
+    mx = FMT_MAX[fmt]
+    x = g.standard_normal(size=shape, dtype=np.float32)
+    x *= np.float32(sigma)
+    np.clip(x, -mx, mx, out=x)
+    if outlier_frac > 0:
+        mask = g.random(size=shape, dtype=np.float32) < outlier_frac
+        sign = np.where(g.random(size=shape, dtype=np.float32) < 0.5, -mx, mx).astype(np.float32)
+        x[mask] = sign[mask]
+    return to_codes(x, fmt)
+
+
+def normalized_codes(g: np.random.Generator, shape, target: float = 240.0, fmt: int = E4M3FN):
+    """x = z * target / max|z| as FP8 codes; returns (codes, scale = max|z| / target)."""
+    z = g.standard_normal(size=shape, dtype=np.float32)
+    zmax = float(np.max(np.abs(z))) if z.size else 1.0
+    x = z * np.float32(target / zmax)
+    return to_codes(x, fmt), np.float32(zmax / target)
+
+
+def finite_codes(fmt: int) -> np.ndarray:
+    """Every code of the format that encodes a finite value."""
+    c = np.arange(256, dtype=np.uint8)
+    if fmt == E4M3FN:
+        return c[(c & 0x7F) != 0x7F]
+    return c[((c >> 2) & 31) != 31]
+
+
+def adversarial_codes(g: np.random.Generator, shape, fmt: int = E4M3FN) -> np.ndarray:
+    """i.i.d. codes: 25% +-max, 25% random-sign subnormals, 10% +-0, 40% uniform finite."""
+    n = int(np.prod(shape))
+    u = g.random(n)
+    sign = (g.random(n) < 0.5).astype(np.uint8) << 7
+    maxcode = 0x7E if fmt == E4M3FN else 0x7B
+    sub_hi = 7 if fmt == E4M3FN else 3
+    sub = g.integers(1, sub_hi + 1, size=n).astype(np.uint8)
+    fin = finite_codes(fmt)
+    uni = fin[g.integers(0, fin.size, size=n)]
+    out = np.where(u < 0.25, maxcode | sign,
+          np.where(u < 0.50, sub | sign,
+          np.where(u < 0.60, sign, uni))).astype(np.uint8)
+    return out.reshape(shape)
+
+
+def adversarial_pair(M: int, N: int, K: int, workload: int = 2, fmt: int = E4M3FN):
+    """Adversarial A [M,K], B [N,K] with structured rows.
+
+    Row 0 of A and of B is all +max; row 1 of A alternates +max / -max against
+    B row 1 all +max (the sum cancels to 0); row 2 of A and B is all the
+    smallest subnormal; row 3 of A is all -0.
+    """
+    g = rng(workload, 3)
+    a = adversarial_codes(g, (M, K), fmt)
+    b = adversarial_codes(g, (N, K), fmt)
+    maxcode = 0x7E if fmt == E4M3FN else 0x7B
+    if M > 0 and N > 0:
+        a[0, :] = maxcode
+        b[0, :] = maxcode
+    if M > 1 and N > 1:
+        a[1, :] = maxcode
+        a[1, 1::2] = maxcode | 0x80
+        b[1, :] = maxcode
+    if M > 2 and N > 2:
+        a[2, :] = 0x01
+        b[2, :] = 0x01
+    if M > 3:
+        a[3, :] = 0x80
+    return a, b
+
+
+def log_uniform_scales(g: np.random.Generator, shape, lo: float = -8.0, hi: float = 4.0):
+    """fp32 values 2^u with u ~ U(lo, hi)."""
+    u = g.uniform(lo, hi, size=shape)
+    return np.exp2(u).astype(np.float32)
+
+
+def pow2_scales(g: np.random.Generator, shape, lo: int = -8, hi: int = 4):
+    """fp32 powers of two 2^e with e ~ U{lo..hi}."""
+    e = g.integers(lo, hi + 1, size=shape)
+    return np.ldexp(np.ones(shape, dtype=np.float32), e).astype(np.float32)
+
+
+# ----------------------------------------------------------------- workloads
+
+def workload1(M=256, N=256, K=256):
+    a = gauss_codes(rng(1, 0), (M, K), 64.0)
+    b = gauss_codes(rng(1, 1), (N, K), 64.0)
+    return dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN,
+                scale_a=np.float32(0.5), scale_b=np.float32(0.25))
+
+
+def workload2_gauss(M: int, N: int = 4096, K: int = 4096, seed_offset: int = 0):
+    """Gaussian set of workload 2; seed_offset selects an independent copy."""
+    ga = rng(2, 0 + 10 * seed_offset)
+    gb = rng(2, 1 + 10 * seed_offset)
+    a, sa = normalized_codes(ga, (M, K))
+    b, sb = normalized_codes(gb, (N, K))
+    return dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN, scale_a=sa, scale_b=sb)
+
+
+def workload2_adversarial(M: int, N: int = 4096, K: int = 4096):
+    a, b = adversarial_pair(M, N, K, 2)
+    return dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN,
+                scale_a=np.float32(1.0), scale_b=np.float32(1.0))
+
+
+def workload3(M=4096, N=14336, K=4096):
+    a = gauss_codes(rng(3, 0), (M, K), 64.0)
+    b = gauss_codes(rng(3, 1), (N, K), 64.0)
+    kb = -(-K // 128)
+    g = rng(3, 2)
+    sa = log_uniform_scales(g, (M, kb))
+    sb = log_uniform_scales(g, (-(-N // 128), kb))
+    return dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN, scale_a=sa, scale_b=sb)
+
+
+def workload4(L=8, M=2048, N=2048, K=8192, sf=32):
+    a = gauss_codes(rng(4, 0), (L, M, K), 64.0)
+    b = gauss_codes(rng(4, 1), (L, N, K), 64.0)
+    ks = -(-K // sf)
+    g = rng(4, 2)
+    sfa = pow2_scales(g, (L, M, ks))
+    sfb = pow2_scales(g, (L, N, ks))
+    return dict(a=a, b=b, ab_fmt=E4M3FN, sfa=sfa, sfb=sfb, sf_vec=sf)
+
+
+def workload5a(M=8192, N=28672, K=8200):
+    a = gauss_codes(rng(5, 0), (M, K), 32.0, E4M3FN, 0.01)
+    b = gauss_codes(rng(5, 1), (N, K), 32.0, E4M3FN, 0.01)
+    return dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN,
+                scale_a=np.float32(2.0 ** -3), scale_b=np.float32(2.0 ** -3),
+                scale_result=np.float32(1.0 / 16))
+
+
+def workload5b(M=8192, N=28672, K=8200):
+    a = gauss_codes(rng(6, 0), (M, K), 32.0, E5M2, 0.01)
+    b = gauss_codes(rng(6, 1), (N, K), 32.0, E5M2, 0.01)
+    return dict(a=a, b=b, K=K, a_fmt=E5M2, b_fmt=E5M2,
+                scale_a=np.float32(2.0 ** -10), scale_b=np.float32(2.0 ** -10))
