@@ -1,0 +1,205 @@
+"""Benchmark: FP8 scaled-GEMM TFLOP/s on one MI355X.
+
+Workload: per-tensor E4M3 x E4M3 scaled GEMM d = (a * s_a) @ (b * s_b)^T with
+N = K = 4096 and M in {16, 64, 256, 1024, 2048, 8192}, slow accumulation
+(128-element chunks promoted into fp32), bf16 output, seeded synthetic
+Gaussian inputs (x = z * 240 / max|z| per tensor). One step = one GEMM at each
+of the six M values. Inputs stay resident in HBM; every M cycles through
+enough distinct buffer sets (row rotations of the seeded data, at least
+512 MB per M) that the 256 MB Infinity Cache cannot hold them, so the small-M
+runs are measured against HBM rather than cache.
+
+Prints one JSON line. `value` = the step's total flops / the step's time.
+`roofline` describes the dominant kernel (the M = 8192 GEMM), timed with HIP
+events on the stream it runs on. `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+MS = (16, 64, 256, 1024, 2048, 8192)
+N = K = 4096
+PEAK_FP8_TFLOPS = 5033.0      # MI355X dense FP8 MFMA: 256 CUs x 8192 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+ROTATION_BYTES = 512 << 20    # 2x the Infinity Cache
+METRIC = "FP8 scaled-GEMM TFLOP/s and % of MI355X FP8 MFMA peak, M=16..8192"
+
+
+def gemm_bytes(M):
+    # algorithmic bytes: A + B read once, D (bf16) written once, two fp32 scales
+    return M * K + N * K + 2 * M * N + 8
+
+
+def gemm_flops(M):
+    return 2.0 * M * N * K
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_sets(M, torch, dev, datagen):
+    d = datagen.workload2_gauss(M, N, K)
+    a0 = torch.from_numpy(d["a"]).to(dev)
+    b0 = torch.from_numpy(d["b"]).to(dev)
+    sa = torch.tensor([d["scale_a"]], dtype=torch.float32, device=dev)
+    sb = torch.tensor([d["scale_b"]], dtype=torch.float32, device=dev)
+    n = max(2, math.ceil(ROTATION_BYTES / gemm_bytes(M)))
+    sets = []
+    for i in range(n):
+        a = torch.roll(a0, shifts=(i * 7) % max(M, 1), dims=0).contiguous()
+        b = torch.roll(b0, shifts=i * 131, dims=0).contiguous()
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        sets.append((a, b, out))
+    return dict(sets=sets, sa=sa, sb=sb)
+
+
+def launch(mm, M, s, S, stream):
+    a, b, out = s
+    st = mm.mm_scaled_gemm(M, N, K, a.data_ptr(), mm.MM_F8_E4M3FN, K, b.data_ptr(), mm.MM_F8_E4M3FN, K,
+                           S["sa"].data_ptr(), mm.MM_SCALE_TENSOR, S["sb"].data_ptr(), mm.MM_SCALE_TENSOR, 0,
+                           out.data_ptr(), mm.MM_BF16, N, 0, stream)
+    if st != mm.MM_OK:
+        raise RuntimeError(f"mm_scaled_gemm failed: {mm.mm_last_error()}")
+
+
+def cpu_baseline(seconds_target=15.0):
+    """The oracle, untuned, on the host cores: the first R rows of the M = 8192
+    problem (R x 4096 x 4096, exact float64 sums), R sized to ~10-30 s."""
+    import numpy as np
+    import datagen
+    import oracle
+    threads = os.cpu_count() or 1
+    d = datagen.workload2_gauss(8192, N, K)
+    # calibrate on a few rows, then run the bounded sample
+    r0 = max(threads, 16)
+    t = time.perf_counter()
+    oracle.scaled_gemm(d["a"], 0, d["b"], 0, d["scale_a"], 0, d["scale_b"], 0, oracle.BF16,
+                       accum=oracle.ACC_EXACT, rows=np.arange(r0), threads=threads)
+    per_row = (time.perf_counter() - t) / r0
+    R = int(min(8192, max(r0, seconds_target / max(per_row, 1e-9))))
+    R = max(threads, (R // threads) * threads)
+    t = time.perf_counter()
+    oracle.scaled_gemm(d["a"], 0, d["b"], 0, d["scale_a"], 0, d["scale_b"], 0, oracle.BF16,
+                       accum=oracle.ACC_EXACT, rows=np.arange(R), threads=threads)
+    dt = time.perf_counter() - t
+    return {"value": 2.0 * R * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{R - 1} of the M=8192, N=K=4096 problem ({R}x4096x4096, float64), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only-m", type=int, default=0, help="run only this M (for profiler runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_gemm_amd as mm
+    import datagen
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ms = (args.only_m,) if args.only_m else MS
+    t0 = time.time()
+    data = {M: make_sets(M, torch, dev, datagen) for M in ms}
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s: " + ", ".join(f"M={M}: {len(data[M]['sets'])} sets" for M in ms))
+    stream = torch.cuda.current_stream().cuda_stream
+    dominant = max(ms)
+    flops_step = sum(gemm_flops(M) for M in ms)
+
+    def step(i, ev=None):
+        for M in ms:
+            S = data[M]
+            s = S["sets"][i % len(S["sets"])]
+            if ev is not None and M == dominant:
+                ev[0].record()
+                launch(mm, M, s, S, stream)
+                ev[1].record()
+            else:
+                launch(mm, M, s, S, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    dom_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step; M={dominant} kernel {dom_us:.2f} us")
+
+    # per-M breakdown (each M alone, same rotation)
+    per_m = {}
+    for M in ms:
+        S = data[M]
+        reps = max(50, min(2000, int(2e5 / max(gemm_flops(M) / 4e12 * 1e6, 1))))
+        for i in range(10):
+            launch(mm, M, S["sets"][i % len(S["sets"])], S, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(reps):
+            launch(mm, M, S["sets"][i % len(S["sets"])], S, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        tf = gemm_flops(M) / us / 1e6
+        gbs = gemm_bytes(M) / us / 1e3
+        per_m[str(M)] = {"us": round(us, 3), "tflops": round(tf, 1), "frac_mfma": round(tf / PEAK_FP8_TFLOPS, 4),
+                         "hbm_gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"M={M}: {us:.2f} us, {tf:.1f} TFLOP/s ({100 * tf / PEAK_FP8_TFLOPS:.1f}% MFMA), "
+            f"{gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% HBM)")
+
+    achieved = gemm_flops(dominant) / dom_us / 1e6
+    result = {
+        "metric": METRIC,
+        "value": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": "per-tensor E4M3 x E4M3 scaled GEMM, N=K=4096, M in {16,64,256,1024,2048,8192}, "
+                               "slow accumulation, bf16 out", "M": list(ms), "N": N, "K": K,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "kernel": f"gemm_tile M={dominant} N=K=4096", "kernel_us": round(dom_us, 3)},
+        "per_m": per_m,
+    }
+    if not args.no_cpu_baseline and not args.only_m:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

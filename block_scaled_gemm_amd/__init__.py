@@ -1,0 +1,184 @@
+"""Python binding of libmmfp8 (FP8 scaled GEMM and block-scaled GEMM + amax on MI355X).
+
+Argument marshalling only: every step of the computation runs in the gfx950
+kernels behind the C ABI declared in include/mm.h. torch is used for device
+memory and the current stream. Importing the package loads libmmfp8.so from
+this directory and raises if it is missing: there is no fallback path.
+
+Raw C-ABI wrappers (same names as the C functions, integer pointers):
+``mm_scaled_gemm``, ``mm_blockscaled_gemm_amax``, ``mm_debug_convert``,
+``mm_last_error``, ``mm_version``. Tensor-level helpers: ``scaled_gemm`` and
+``blockscaled_gemm_amax``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmmfp8.so")
+
+MM_OK, MM_ERR_INVALID_ARGUMENT, MM_ERR_UNSUPPORTED, MM_ERR_MISALIGNED, MM_ERR_DEVICE = 0, 1, 2, 3, 4
+MM_F8_E4M3FN, MM_F8_E5M2, MM_F32, MM_BF16, MM_F16 = 0, 1, 2, 3, 4
+MM_SCALE_TENSOR, MM_SCALE_1x128, MM_SCALE_128x128 = 0, 1, 2
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_scaled_gemm_amd.build` "
+                      "(or __graft_entry__.build()); there is no CPU fallback")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+_lib.mm_scaled_gemm.argtypes = [_I64, _I64, _I64, _P, _I, _I64, _P, _I, _I64, _P, _I, _P, _I, _P, _P, _I, _I64, _I, _P]
+_lib.mm_scaled_gemm.restype = _I
+_lib.mm_blockscaled_gemm_amax.argtypes = [_I64, _I64, _I64, _I64, _P, _P, _I, _P, _P, _I, _P, _I, _P, _P, _P]
+_lib.mm_blockscaled_gemm_amax.restype = _I
+_lib.mm_debug_convert.argtypes = [_P, _P, _I, _I64, _P]
+_lib.mm_debug_convert.restype = _I
+_lib.mm_last_error.restype = ctypes.c_char_p
+_lib.mm_version.restype = ctypes.c_char_p
+
+EXPORTED = ("mm_scaled_gemm", "mm_blockscaled_gemm_amax", "mm_last_error", "mm_version", "mm_debug_convert")
+
+
+class MMError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+def mm_last_error() -> str:
+    return _lib.mm_last_error().decode()
+
+
+def mm_version() -> str:
+    return _lib.mm_version().decode()
+
+
+def mm_scaled_gemm(M, N, K, a, a_type, lda, b, b_type, ldb, scale_a, sa_mode, scale_b, sb_mode,
+                   scale_result, d, d_type, ldd, use_fast_accum, stream) -> int:
+    """Raw call of the C function; pointers and the stream are integers (0 = NULL). Returns the status."""
+    return _lib.mm_scaled_gemm(M, N, K, a or None, a_type, lda, b or None, b_type, ldb, scale_a or None, sa_mode,
+                               scale_b or None, sb_mode, scale_result or None, d or None, d_type, ldd,
+                               int(use_fast_accum), stream or None)
+
+
+def mm_blockscaled_gemm_amax(M, N, K, L, a, b, ab_type, sfa, sfb, sf_vec_size, c, c_type, amax, amax_index,
+                             stream) -> int:
+    """Raw call of the C function; pointers and the stream are integers (0 = NULL). Returns the status."""
+    return _lib.mm_blockscaled_gemm_amax(M, N, K, L, a or None, b or None, ab_type, sfa or None, sfb or None,
+                                         sf_vec_size, c or None, c_type, amax or None, amax_index or None,
+                                         stream or None)
+
+
+def mm_debug_convert(x, y, dtype, n, stream) -> int:
+    return _lib.mm_debug_convert(x or None, y or None, dtype, n, stream or None)
+
+
+def _check(status: int):
+    if status != MM_OK:
+        raise MMError(status, mm_last_error())
+
+
+# ------------------------------------------------------------------ tensor helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(dt) -> int:
+    torch = _torch()
+    table = {torch.float8_e4m3fn: MM_F8_E4M3FN, torch.float8_e5m2: MM_F8_E5M2, torch.float32: MM_F32,
+             torch.bfloat16: MM_BF16, torch.float16: MM_F16}
+    if dt not in table:
+        raise TypeError(f"unsupported dtype {dt}")
+    return table[dt]
+
+
+def _fp8_code(t, fmt):
+    torch = _torch()
+    if t.dtype == torch.uint8:
+        if fmt is None:
+            raise TypeError("uint8 operands need an explicit format (MM_F8_E4M3FN or MM_F8_E5M2)")
+        return fmt
+    return dtype_code(t.dtype)
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _rows(t):
+    """(row pitch in elements) of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D tensor with contiguous rows")
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def scaled_gemm(a, b, scale_a, scale_b, out_dtype, scale_result=None, use_fast_accum=False, out=None,
+                a_format=None, b_format=None):
+    """d = (a * scale_a) @ (b * scale_b)^T on the current stream.
+
+    a: [M, K] FP8 (or uint8 codes with a_format) with contiguous rows.
+    b: [N, K] FP8 with contiguous rows, or torch._scaled_mm's column-major
+       mat2 [K, N] (detected by its strides and read as its [N, K] transpose).
+    scale_a / scale_b: fp32 tensors, per-tensor (one element), 1x128 [M, ceil(K/128)],
+       or for b 1x128 [N, ceil(K/128)] / 128x128 [ceil(N/128), ceil(K/128)].
+    """
+    torch = _torch()
+    if b.dim() == 2 and a.dim() == 2 and b.shape[0] == a.shape[1] and b.stride(0) == 1 and b.shape[1] != a.shape[1]:
+        b = b.t()  # scaled_mm's column-major mat2 [K, N] -> its [N, K] rows
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}")
+    kb = -(-K // 128)
+
+    def mode_of(s, rows):
+        if s.numel() == 1:
+            return MM_SCALE_TENSOR
+        if tuple(s.shape) == (rows, kb):
+            return MM_SCALE_1x128
+        if tuple(s.shape) == (-(-rows // 128), kb):
+            return MM_SCALE_128x128
+        raise ValueError(f"scale of shape {tuple(s.shape)} fits no scale mode")
+
+    sa_mode = mode_of(scale_a, M)
+    sb_mode = mode_of(scale_b, N)
+    for s in (scale_a, scale_b):
+        if s.dtype != torch.float32 or not s.is_contiguous():
+            raise TypeError("scales must be contiguous float32 tensors")
+    d_type = dtype_code(out_dtype)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    sr = 0 if scale_result is None else scale_result.data_ptr()
+    st = mm_scaled_gemm(M, N, K, a.data_ptr(), _fp8_code(a, a_format), _rows(a) if M else K,
+                        b.data_ptr(), _fp8_code(b, b_format), _rows(b) if N else K,
+                        scale_a.data_ptr(), sa_mode, scale_b.data_ptr(), sb_mode, sr,
+                        out.data_ptr(), d_type, _rows(out) if M else N, use_fast_accum, _stream())
+    _check(st)
+    return out
+
+
+def blockscaled_gemm_amax(a, b, sfa, sfb, c_dtype=None, sf_vec_size=32, with_index=False, ab_format=None):
+    """C[l] = (A[l] * SFA[l]) @ (B[l] * SFB[l])^T and the global amax of C.
+
+    a: [L, M, K] FP8, b: [L, N, K] FP8 (same format), sfa: [L, M, ceil(K/32)],
+    sfb: [L, N, ceil(K/32)] float32 powers of two. Returns (c [L, M, N], amax [1])
+    or (c, amax, amax_index [1]) with with_index.
+    """
+    torch = _torch()
+    c_dtype = c_dtype or torch.float32
+    L, M, K = a.shape
+    N = b.shape[1]
+    for t in (a, b, sfa, sfb):
+        if not t.is_contiguous():
+            raise ValueError("operands must be contiguous")
+    c = torch.empty((L, M, N), dtype=c_dtype, device=a.device)
+    amax = torch.empty((1,), dtype=torch.float32, device=a.device)
+    idx = torch.empty((1,), dtype=torch.int64, device=a.device) if with_index else None
+    st = mm_blockscaled_gemm_amax(M, N, K, L, a.data_ptr(), b.data_ptr(), _fp8_code(a, ab_format),
+                                  sfa.data_ptr(), sfb.data_ptr(), sf_vec_size, c.data_ptr(), dtype_code(c_dtype),
+                                  amax.data_ptr(), idx.data_ptr() if with_index else 0, _stream())
+    _check(st)
+    return (c, amax, idx) if with_index else (c, amax)

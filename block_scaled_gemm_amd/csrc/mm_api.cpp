@@ -1,0 +1,258 @@
+// mm_api.cpp -- the C ABI of libmmfp8 (declared in include/mm.h): argument
+// validation (complete before any HIP call), kernel choice and launch.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "mm.h"
+#include "mm_launch.hpp"
+
+namespace {
+
+thread_local std::string g_error;
+
+mm_status fail(mm_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+mm_status fail(mm_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return st;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool is_fp8(int t) { return t == MM_F8_E4M3FN || t == MM_F8_E5M2; }
+bool is_dtype(int t) { return t >= MM_F8_E4M3FN && t <= MM_F16; }
+int elem_size(int t) { return t == MM_F32 ? 4 : (t == MM_BF16 || t == MM_F16) ? 2 : 1; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // M, N, K, L < 2^31
+constexpr int64_t kMaxPitch = (int64_t)1 << 22; // row pitch in bytes (buffer offsets stay below 2^31)
+
+// Test hook: MM_TEST_FORCE_FAIL=launch makes a valid call return MM_ERR_DEVICE
+// right after validation, before any HIP call, so the device-error path can be
+// exercised without a GPU.
+bool forced_launch_failure() {
+    const char* e = std::getenv("MM_TEST_FORCE_FAIL");
+    return e && std::strstr(e, "launch") != nullptr;
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Largest workgroup tile that still gives every compute unit a tile.
+int choose_cfg(int64_t M, int64_t N, int64_t L, int cus) {
+    for (int c = 0; c < mmfp8::CFG_COUNT - 1; ++c) {
+        const int64_t tiles = cdiv(M, mmfp8::kCfgBM[c]) * cdiv(N, mmfp8::kCfgBN[c]) * L;
+        if (tiles >= cus) return c;
+    }
+    return mmfp8::CFG_64x64;
+}
+
+mm_status device_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return MM_OK;
+    return fail(MM_ERR_DEVICE, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mm_last_error(void) { return g_error.c_str(); }
+
+const char* mm_version(void) { return "mmfp8 0.1.0 gfx950"; }
+
+mm_status mm_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, int a_type, int64_t lda, const void* b,
+                         int b_type, int64_t ldb, const float* scale_a, int sa_mode, const float* scale_b,
+                         int sb_mode, const float* scale_result, void* d, int d_type, int64_t ldd,
+                         int use_fast_accum, void* stream) {
+    g_error.clear();
+    if (M < 0 || N < 0 || K < 0) return fail(MM_ERR_INVALID_ARGUMENT, "M, N and K must be >= 0 (got %lld, %lld, %lld)",
+                                             (long long)M, (long long)N, (long long)K);
+    if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+        return fail(MM_ERR_UNSUPPORTED, "M, N and K must be below 2^31");
+    if (!is_fp8(a_type) || !is_fp8(b_type))
+        return fail(MM_ERR_INVALID_ARGUMENT, "a_type and b_type must be MM_F8_E4M3FN or MM_F8_E5M2 (got %d, %d)",
+                    a_type, b_type);
+    if (!is_dtype(d_type)) return fail(MM_ERR_INVALID_ARGUMENT, "unknown d_type %d", d_type);
+    if (sa_mode < MM_SCALE_TENSOR || sa_mode > MM_SCALE_128x128 || sb_mode < MM_SCALE_TENSOR ||
+        sb_mode > MM_SCALE_128x128)
+        return fail(MM_ERR_INVALID_ARGUMENT, "unknown scale mode (%d, %d)", sa_mode, sb_mode);
+    const bool per_tensor = sa_mode == MM_SCALE_TENSOR && sb_mode == MM_SCALE_TENSOR;
+    const bool block = sa_mode == MM_SCALE_1x128 && (sb_mode == MM_SCALE_1x128 || sb_mode == MM_SCALE_128x128);
+    if (!per_tensor && !block)
+        return fail(MM_ERR_UNSUPPORTED,
+                    "scale pair (%d, %d) not supported: use (TENSOR, TENSOR), (1x128, 1x128) or (1x128, 128x128)",
+                    sa_mode, sb_mode);
+    if (lda < K || ldb < K) return fail(MM_ERR_INVALID_ARGUMENT, "lda and ldb must be >= K");
+    if (ldd < N) return fail(MM_ERR_INVALID_ARGUMENT, "ldd must be >= N");
+    if (lda > kMaxPitch || ldb > kMaxPitch) return fail(MM_ERR_UNSUPPORTED, "lda and ldb must be at most 2^22 bytes");
+    if (M == 0 || N == 0) return MM_OK;
+    if (!d) return fail(MM_ERR_INVALID_ARGUMENT, "d is NULL");
+    if (K > 0 && (!a || !b)) return fail(MM_ERR_INVALID_ARGUMENT, "a or b is NULL");
+    if ((per_tensor || K > 0) && (!scale_a || !scale_b)) return fail(MM_ERR_INVALID_ARGUMENT, "scale_a or scale_b is NULL");
+    if (!aligned(a, 16) || !aligned(b, 16)) return fail(MM_ERR_MISALIGNED, "a and b must be 16-byte aligned");
+    if (lda % 8 || ldb % 8) return fail(MM_ERR_MISALIGNED, "lda and ldb must be multiples of 8 bytes");
+    if (!aligned(d, elem_size(d_type))) return fail(MM_ERR_MISALIGNED, "d must be aligned to its element size");
+    if (!aligned(scale_a, 4) || !aligned(scale_b, 4) || !aligned(scale_result, 4))
+        return fail(MM_ERR_MISALIGNED, "scale pointers must be 4-byte aligned");
+    if (forced_launch_failure()) return fail(MM_ERR_DEVICE, "launch failure forced by MM_TEST_FORCE_FAIL");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    mmfp8::GemmArgs p{};
+    p.a = static_cast<const uint8_t*>(a);
+    p.b = static_cast<const uint8_t*>(b);
+    p.lda = lda;
+    p.ldb = ldb;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.L = 1;
+    p.sa = scale_a;
+    p.sb = scale_b;
+    const int64_t kb = cdiv(K, 128);
+    p.sa_ld = kb;
+    p.sb_ld = kb;
+    p.scale_result = scale_result;
+    p.d = d;
+    p.ldd = ldd;
+    p.d_type = d_type;
+    const int es = elem_size(d_type);
+    p.vec_store = (ldd % 4 == 0) && aligned(d, 4 * es);
+
+    const int fa = a_type == MM_F8_E5M2 ? 1 : 0;
+    const int fb = b_type == MM_F8_E5M2 ? 1 : 0;
+    hipError_t e;
+    if (per_tensor && M <= 64) {
+        const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+        const int grid = (int)cdiv(N, 16);
+        e = mmfp8::launch_skinny(mt, use_fast_accum ? mmfp8::MODE_FAST : mmfp8::MODE_SLOW, fa, fb, p, grid, s);
+        return device_status(e, "mm_scaled_gemm (skinny) launch");
+    }
+    const int cfg = choose_cfg(M, N, 1, cu_count());
+    p.tiles_m = (int)cdiv(M, mmfp8::kCfgBM[cfg]);
+    p.tiles_n = (int)cdiv(N, mmfp8::kCfgBN[cfg]);
+    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+    if (per_tensor) {
+        e = use_fast_accum ? mmfp8::launch_tile_fast(cfg, fa, fb, p, (int)grid, s)
+                           : mmfp8::launch_tile_slow(cfg, fa, fb, p, (int)grid, s);
+    } else {
+        const int sbm = sb_mode == MM_SCALE_128x128 ? mmfp8::SB_128x128 : mmfp8::SB_1x128;
+        e = mmfp8::launch_tile_block(cfg, sbm, fa, fb, p, (int)grid, s);
+    }
+    return device_status(e, "mm_scaled_gemm launch");
+}
+
+mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L, const void* a, const void* b,
+                                   int ab_type, const float* sfa, const float* sfb, int sf_vec_size, void* c,
+                                   int c_type, float* amax, int64_t* amax_index, void* stream) {
+    g_error.clear();
+    if (M < 0 || N < 0 || K < 0 || L < 0)
+        return fail(MM_ERR_INVALID_ARGUMENT, "M, N, K and L must be >= 0");
+    if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim || L >= kMaxDim)
+        return fail(MM_ERR_UNSUPPORTED, "M, N, K and L must be below 2^31");
+    const int64_t lim = (int64_t)1 << 48;
+    if ((K && L * M > lim / K) || (K && L * N > lim / K) || (N && L * M > lim / N))
+        return fail(MM_ERR_UNSUPPORTED, "L*M*K, L*N*K and L*M*N must be below 2^48");
+    if (!is_fp8(ab_type)) return fail(MM_ERR_INVALID_ARGUMENT, "ab_type must be MM_F8_E4M3FN or MM_F8_E5M2");
+    if (sf_vec_size == 16)
+        return fail(MM_ERR_UNSUPPORTED, "sf_vec_size 16 is not supported with FP8 operands; use 32");
+    if (sf_vec_size != 32) return fail(MM_ERR_INVALID_ARGUMENT, "sf_vec_size must be 32 (got %d)", sf_vec_size);
+    if (is_fp8(c_type)) return fail(MM_ERR_UNSUPPORTED, "FP8 C with FP8 operands is not supported");
+    if (!is_dtype(c_type)) return fail(MM_ERR_INVALID_ARGUMENT, "unknown c_type %d", c_type);
+    if (K > kMaxPitch) return fail(MM_ERR_UNSUPPORTED, "K must be at most 2^22");
+    const int64_t outs = L * M * N;
+    if (amax_index && outs >= ((int64_t)1 << 33))
+        return fail(MM_ERR_UNSUPPORTED, "amax_index needs L*M*N < 2^33");
+    if (outs > 0 && !c) return fail(MM_ERR_INVALID_ARGUMENT, "c is NULL");
+    if (outs > 0 && K > 0 && (!a || !b || !sfa || !sfb))
+        return fail(MM_ERR_INVALID_ARGUMENT, "a, b, sfa or sfb is NULL");
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16))
+        return fail(MM_ERR_MISALIGNED, "a, b and c must be 16-byte aligned");
+    if (K % 16) return fail(MM_ERR_MISALIGNED, "K must be a multiple of 16 (16-byte aligned rows)");
+    if (!aligned(sfa, 4) || !aligned(sfb, 4) || !aligned(amax, 4))
+        return fail(MM_ERR_MISALIGNED, "sfa, sfb and amax must be 4-byte aligned");
+    if (!aligned(amax_index, 8)) return fail(MM_ERR_MISALIGNED, "amax_index must be 8-byte aligned");
+    if (outs == 0 && !amax && !amax_index) return MM_OK;
+    if (forced_launch_failure()) return fail(MM_ERR_DEVICE, "launch failure forced by MM_TEST_FORCE_FAIL");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t* amax_bits = amax_index ? nullptr : reinterpret_cast<uint32_t*>(amax);
+    unsigned long long* key = reinterpret_cast<unsigned long long*>(amax_index);
+    if (amax || amax_index) {
+        mm_status st = device_status(mmfp8::launch_amax_init(amax_bits, key, s), "amax init launch");
+        if (st != MM_OK) return st;
+    }
+    if (outs > 0) {
+        mmfp8::GemmArgs p{};
+        p.a = static_cast<const uint8_t*>(a);
+        p.b = static_cast<const uint8_t*>(b);
+        p.lda = K;
+        p.ldb = K;
+        p.a_batch = M * K;
+        p.b_batch = N * K;
+        p.M = (int)M;
+        p.N = (int)N;
+        p.K = (int)K;
+        p.L = (int)L;
+        const int64_t ks = cdiv(K, 32);
+        p.sa = sfa;
+        p.sb = sfb;
+        p.sa_ld = ks;
+        p.sb_ld = ks;
+        p.sa_batch = M * ks;
+        p.sb_batch = N * ks;
+        p.d = c;
+        p.ldd = N;
+        p.d_batch = M * N;
+        p.d_type = c_type;
+        p.vec_store = (N % 4 == 0);
+        p.amax_bits = amax_bits;
+        p.amax_key = key;
+        const int cfg = choose_cfg(M, N, L, cu_count());
+        p.tiles_m = (int)cdiv(M, mmfp8::kCfgBM[cfg]);
+        p.tiles_n = (int)cdiv(N, mmfp8::kCfgBN[cfg]);
+        const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * L;
+        if (grid >= kMaxDim) return fail(MM_ERR_UNSUPPORTED, "too many output tiles");
+        mm_status st = device_status(mmfp8::launch_tile_sf32(cfg, ab_type == MM_F8_E5M2 ? 1 : 0, p, (int)grid, s),
+                                     "mm_blockscaled_gemm_amax launch");
+        if (st != MM_OK) return st;
+    }
+    if (amax_index) return device_status(mmfp8::launch_amax_finalize(amax, key, s), "amax finalize launch");
+    return MM_OK;
+}
+
+mm_status mm_debug_convert(const float* x, void* y, int dtype, int64_t n, void* stream) {
+    g_error.clear();
+    if (n < 0) return fail(MM_ERR_INVALID_ARGUMENT, "n must be >= 0");
+    if (!is_dtype(dtype)) return fail(MM_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    if (n >= ((int64_t)1 << 40)) return fail(MM_ERR_UNSUPPORTED, "n too large");
+    if (n == 0) return MM_OK;
+    if (!x || !y) return fail(MM_ERR_INVALID_ARGUMENT, "x or y is NULL");
+    if (!aligned(x, 4) || !aligned(y, elem_size(dtype))) return fail(MM_ERR_MISALIGNED, "x or y misaligned");
+    if (forced_launch_failure()) return fail(MM_ERR_DEVICE, "launch failure forced by MM_TEST_FORCE_FAIL");
+    return device_status(mmfp8::launch_debug_convert(x, y, dtype, n, static_cast<hipStream_t>(stream)),
+                         "mm_debug_convert launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,576 @@
+// mm_kernels.hpp -- gfx950 kernels of libmmfp8: FP8 scaled GEMM (per-tensor,
+// 1x128 / 128x128 block scales, 32-element MX scale factors), fused epilogue
+// cast and amax.
+//
+// The computation is the FP8 NT GEMM d = (a * s_a) @ (b * s_b)^T of "TileOPs:
+// Linear Algebra Operators" (tileops.gemm.GemmFP8FwdOp), with the fast / slow
+// accumulation and scale_result of "mmaemu API reference (v0.1)"
+// (mmaemu.scaled_mm) and the batched block-scaled GEMM + amax of "cuDNN
+// frontend: GEMM + Amax (SM100)" (Equations).
+//
+// Hardware facts this file relies on (measured on MI355X with in-bounds
+// probes, see the design notes):
+//  * v_mfma_scale_f32_16x16x128_f8f6f4: lane l = r + 16 g (r = l & 15,
+//    g = l >> 4) supplies row r of each operand. Bytes 0..15 of its 8 VGPRs are
+//    k = 16g .. 16g+15 and bytes 16..31 are k = 64+16g .. 64+16g+15; the E8M0
+//    scale of 32-element block b (k = 32b .. 32b+31) is taken from lane group
+//    b. The result D[i][j] (i from the first operand, j from the second) is in
+//    lane j + 16 (i / 4), register i % 4.
+//  * The MFMA adds C to the product sum with one round-to-nearest-even; C is
+//    not scaled; fp32 subnormal results are kept.
+//  * Buffer loads check the range per dword: a dword past num_records reads 0.
+//  * buffer_load ... lds writes lane l's 16 bytes to LDS base + 16 l.
+//  * v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 round to nearest even but do not
+//    saturate; v_cvt_pk_bf16_f32 and v_cvt_f16_f32 are IEEE RNE. NaN payloads
+//    are not canonical, so the epilogue rewrites NaN itself.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mmfp8 {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Element types (the values of mm_dtype).
+enum : int { T_E4M3 = 0, T_E5M2 = 1, T_F32 = 2, T_BF16 = 3, T_F16 = 4 };
+// Accumulation / scaling modes of the main loop.
+enum : int { MODE_FAST = 0, MODE_SLOW = 1, MODE_BLOCK = 2, MODE_SF32 = 3 };
+// Granularity of scale_b in MODE_BLOCK.
+enum : int { SB_1x128 = 0, SB_128x128 = 1 };
+
+constexpr int kBK = 128;                 // K per main-loop step = one MFMA = one 128-element chunk
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 buffer descriptor dword 3 (raw, 32-bit format)
+constexpr uint32_t kOOB = 0x80000000u;   // a voffset beyond any extent: loads return 0
+constexpr int kNeutralE8M0 = 127;        // E8M0 code of 1.0
+
+struct GemmArgs {
+    const uint8_t* a;   // [L][M] rows of lda bytes
+    const uint8_t* b;   // [L][N] rows of ldb bytes
+    int64_t lda, ldb;   // bytes
+    int64_t a_batch, b_batch;  // bytes between batch items
+    int M, N, K, L;
+    const float* sa;    // TENSOR: [1]; BLOCK: [M][sa_ld]; SF32: [L][M][sa_ld]
+    const float* sb;    // TENSOR: [1]; BLOCK: [N or ceil(N/128)][sb_ld]; SF32: [L][N][sb_ld]
+    int64_t sa_ld, sb_ld;
+    int64_t sa_batch, sb_batch;   // elements between batch items (SF32)
+    const float* scale_result;    // FP8 outputs only; may be null
+    void* d;            // [L][M] rows of ldd elements
+    int64_t ldd, d_batch;         // elements
+    int d_type;
+    int vec_store;      // 4-element vector stores are aligned
+    uint32_t* amax_bits;          // amax without index (atomic max of |x| bits) or null
+    unsigned long long* amax_key; // (|x| bits << 33) | (2^33 - 1 - index), or null
+    int tiles_m, tiles_n;
+};
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, (int)kRsrcWord3);
+}
+
+// Extent in bytes of `rows` rows of pitch ld of which the last has K valid
+// bytes, rounded up to a dword: the per-dword range check then never drops a
+// valid byte, and bytes past it read as zero.
+__device__ __forceinline__ uint32_t operand_extent(int rows, int64_t ld, int K) {
+    if (rows <= 0) return 0;
+    const int64_t e = (int64_t)(rows - 1) * ld + K;
+    return (uint32_t)((e + 3) & ~(int64_t)3);
+}
+
+// The format codes of the f8f6f4 MFMA are immediates, so they are template
+// arguments: 0 = E4M3 (fp8), 1 = E5M2 (bf8).
+template <int F1, int F2>
+__device__ __forceinline__ f32x4 mfma(const i32x8& first, const i32x8& second, const f32x4& c,
+                                      int scale_first, int scale_second) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 0, scale_first, 0,
+                                                            scale_second);
+}
+
+__device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// E8M0 code of a power-of-two fp32 scale factor: its exponent field.
+__device__ __forceinline__ int e8m0_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFFu); }
+
+// ------------------------------------------------------------------ output conversions
+
+__device__ __forceinline__ uint32_t cvt_f32(float v) {
+    return __builtin_isnan(v) ? 0x7FFFFFFFu : __float_as_uint(v);
+}
+__device__ __forceinline__ uint32_t cvt_bf16(float v) {
+    __bf16 h = (__bf16)v;  // v_cvt_pk_bf16_f32: RNE, overflow to Inf
+    return __builtin_isnan(v) ? 0x7FFFu : (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t cvt_f16(float v) {
+    _Float16 h = (_Float16)v;  // v_cvt_f16_f32: RNE, overflow to Inf
+    return __builtin_isnan(v) ? 0x7FFFu : (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+// FP8 outputs saturate: clamp to +-max first (the converter itself would give
+// NaN / Inf), then round; NaN becomes the canonical 0x7F.
+__device__ __forceinline__ uint32_t cvt_e4m3(float v) {
+    const float c = __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
+    const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+    return __builtin_isnan(v) ? 0x7Fu : code;
+}
+__device__ __forceinline__ uint32_t cvt_e5m2(float v) {
+    const float c = __builtin_fminf(__builtin_fmaxf(v, -57344.0f), 57344.0f);
+    const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, c, 0, false) & 0xFFu;
+    return __builtin_isnan(v) ? 0x7Fu : code;
+}
+
+__device__ __forceinline__ uint32_t convert(float v, int t) {
+    switch (t) {
+        case T_F32: return cvt_f32(v);
+        case T_BF16: return cvt_bf16(v);
+        case T_F16: return cvt_f16(v);
+        case T_E4M3: return cvt_e4m3(v);
+        default: return cvt_e5m2(v);
+    }
+}
+
+__device__ __forceinline__ int elem_bytes(int t) { return t == T_F32 ? 4 : (t == T_E4M3 || t == T_E5M2) ? 1 : 2; }
+
+// Store 4 consecutive converted outputs starting at element e (row-major
+// index); `valid` of them (0..4) exist. Vector store when aligned and whole.
+__device__ __forceinline__ void store4(void* d, int t, int64_t e, const uint32_t v[4], int valid, bool vec) {
+    if (t == T_F32) {
+        uint32_t* p = (uint32_t*)d + e;
+        if (vec && valid == 4) { *(i32x4*)p = i32x4{(int)v[0], (int)v[1], (int)v[2], (int)v[3]}; return; }
+        for (int r = 0; r < valid; ++r) p[r] = v[r];
+    } else if (t == T_BF16 || t == T_F16) {
+        uint16_t* p = (uint16_t*)d + e;
+        if (vec && valid == 4) {
+            *(i32x2*)p = i32x2{(int)(v[0] | (v[1] << 16)), (int)(v[2] | (v[3] << 16))};
+            return;
+        }
+        for (int r = 0; r < valid; ++r) p[r] = (uint16_t)v[r];
+    } else {
+        uint8_t* p = (uint8_t*)d + e;
+        if (vec && valid == 4) { *(uint32_t*)p = v[0] | (v[1] << 8) | (v[2] << 16) | (v[3] << 24); return; }
+        for (int r = 0; r < valid; ++r) p[r] = (uint8_t)v[r];
+    }
+}
+
+// Amax keys. |x| as fp32 bits orders like |x|; canonical NaN (0x7FFFFFFF)
+// beats +Inf. With an index the key also prefers the smallest index on ties.
+__device__ __forceinline__ uint32_t abs_bits(float v) {
+    return __builtin_isnan(v) ? 0x7FFFFFFFu : (__float_as_uint(v) & 0x7FFFFFFFu);
+}
+__device__ __forceinline__ unsigned long long amax_key(float v, int64_t idx) {
+    return ((unsigned long long)abs_bits(v) << 33) | ((1ull << 33) - 1ull - (unsigned long long)idx);
+}
+
+template <class T>
+__device__ __forceinline__ T wave_max(T x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const T y = __shfl_xor(x, off, 64);
+        x = y > x ? y : x;
+    }
+    return x;
+}
+
+// Block-wide max of per-thread keys, then one atomic per workgroup.
+template <int NT>
+__device__ __forceinline__ void amax_commit(const GemmArgs& p, uint32_t kb, unsigned long long kk) {
+    __shared__ unsigned long long red[NT / 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (p.amax_key) {
+        kk = wave_max(kk);
+        if (lane == 0) red[wave] = kk;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            unsigned long long m = red[0];
+            for (int w = 1; w < NT / 64; ++w) m = red[w] > m ? red[w] : m;
+            if (m) atomicMax(p.amax_key, m);
+        }
+    } else if (p.amax_bits) {
+        kb = wave_max(kb);
+        if (lane == 0) red[wave] = kb;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            unsigned long long m = red[0];
+            for (int w = 1; w < NT / 64; ++w) m = red[w] > m ? red[w] : m;
+            atomicMax(p.amax_bits, (uint32_t)m);
+        }
+    }
+}
+
+// Map the linear workgroup id to a tile. Workgroups are dispatched round-robin
+// over the 8 XCDs (each with its own L2); this gives every XCD a contiguous run
+// of tiles, walked in groups of `group_m` tile rows so that the tiles live on
+// one XCD at the same time share A rows and B columns.
+__device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int group_m, int& l,
+                                        int& tm, int& tn) {
+    const int per = nblocks / 8, rem = nblocks % 8;
+    const int x = bid % 8, i = bid / 8;
+    const int t = (x < rem) ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+    const int tiles = tiles_m * tiles_n;
+    l = t / tiles;
+    const int u = t - l * tiles;
+    const int width = group_m * tiles_n;
+    const int grp = u / width;
+    const int first = grp * group_m;
+    const int gsz = min(tiles_m - first, group_m);
+    const int v = u - grp * width;
+    tm = first + v % gsz;
+    tn = v / gsz;
+}
+
+// ------------------------------------------------------------------ tiled kernel
+//
+// Workgroup tile BM x BN, 4 waves in a 2 x 2 grid, each wave (BM/2) x (BN/2)
+// made of 16 x 16 MFMA tiles. The MFMA's first operand is b (rows n) and its
+// second is a (rows m), so every lane's results share one m and hold 4
+// consecutive n: one scale_a value per lane, vector stores along N.
+//
+// K is walked in steps of 128 (= one MFMA, = one "slow" chunk, = one 1x128
+// scale block, = four 32-element MX groups). Each step's A and B tiles go from
+// HBM straight to LDS with buffer_load ... lds (two stages), rows 128 bytes,
+// the 16-byte chunk c of row r stored at chunk c ^ (r & 7) so that the
+// fragment reads are free of bank conflicts.
+template <int BM, int BN, int MODE, int FA, int FB, int SBM>
+__global__ void __launch_bounds__(256, 1) gemm_tile(GemmArgs p) {
+    constexpr int NT = 256;
+    constexpr int WTM = BM / 2, WTN = BN / 2;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int A_INS = BM / 32, B_INS = BN / 32;  // 1 KB LDS writes per wave per step (tile rows / 8 / 4 waves)
+    constexpr int STAGE = (BM + BN) * kBK;
+    // Two distinct LDS objects (not one array indexed by stage) so that the
+    // compiler can tell a fragment read of one stage from the in-flight LDS-DMA
+    // writes into the other and does not wait for those loads.
+    __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    int l, tm, tn;
+    tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, 8, l, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int K = p.K;
+    const int KT = (K + kBK - 1) / kBK;
+
+    const uint8_t* abase = p.a + (int64_t)l * p.a_batch + (int64_t)m0 * p.lda;
+    const uint8_t* bbase = p.b + (int64_t)l * p.b_batch + (int64_t)n0 * p.ldb;
+    const rsrc_t ra = make_rsrc(abase, operand_extent(min(BM, p.M - m0), p.lda, K));
+    const rsrc_t rb = make_rsrc(bbase, operand_extent(min(BN, p.N - n0), p.ldb, K));
+
+    // Loader: wave-instruction q of a tile writes LDS bytes [1024 q, 1024 q + 1024),
+    // i.e. rows 8q .. 8q+7; lane l fills row 8q + l/8, stored chunk l%8, which
+    // holds logical chunk (l%8) ^ (row & 7) = (l%8) ^ (l/8).
+    const int ld_row = lane >> 3;
+    const int ld_chunk = (lane & 7) ^ ld_row;
+    const bool k_tail = (K % kBK) != 0;
+
+    auto issue = [&](int kt, uint8_t* sbase) {
+        const int k0 = kt * kBK + ld_chunk * 16;
+        const bool last = k_tail && kt == KT - 1;
+#pragma unroll
+        for (int q = 0; q < A_INS; ++q) {
+            const int ins = wave * A_INS + q;
+            const int row = ins * 8 + ld_row;
+            uint32_t off = (uint32_t)(row * p.lda + k0);
+            if (last && k0 >= K) off = kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sbase + ins * 1024), 16, off, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < B_INS; ++q) {
+            const int ins = wave * B_INS + q;
+            const int row = ins * 8 + ld_row;
+            uint32_t off = (uint32_t)(row * p.ldb + k0);
+            if (last && k0 >= K) off = kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sbase + BM * kBK + ins * 1024), 16, off, 0, 0,
+                                                     0);
+        }
+    };
+    // In the last step of a K that is not a multiple of 16, a chunk straddling K
+    // holds bytes of the next row (or padding): zero them in this lane's own
+    // LDS slots once its loads have landed.
+    auto mask_straddle = [&](int kt, uint8_t* sbase) {
+        const int k0 = kt * kBK + ld_chunk * 16;
+        if (!(k0 < K && K < k0 + 16)) return;
+        const int valid = K - k0;
+        auto fix = [&](uint8_t* slot) {
+            i32x4 v = *(i32x4*)slot;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int nb = valid - 4 * d;  // valid bytes in dword d
+                const uint32_t m = nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : ((1u << (8 * nb)) - 1u));
+                v[d] = (int)((uint32_t)v[d] & m);
+            }
+            *(i32x4*)slot = v;
+        };
+#pragma unroll
+        for (int q = 0; q < A_INS; ++q) fix(sbase + (wave * A_INS + q) * 1024 + lane * 16);
+#pragma unroll
+        for (int q = 0; q < B_INS; ++q) fix(sbase + BM * kBK + (wave * B_INS + q) * 1024 + lane * 16);
+    };
+
+    // Fragment reads: lane (r, g) takes chunks g and 4 + g of row r.
+    const int fr = lane & 15, fg = lane >> 4;
+    const int foff0 = fr * kBK + ((fg ^ (fr & 7)) << 4);
+    const int foff1 = fr * kBK + (((4 + fg) ^ (fr & 7)) << 4);
+
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Per-lane scale rows (clamped to the matrix: results of clamped rows are discarded).
+    int srow_a[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) srow_a[i] = min(m0 + wm * WTM + i * 16 + fr, p.M - 1);
+    int srow_b[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        if (MODE == MODE_SF32) srow_b[j] = min(n0 + wn * WTN + j * 16 + fr, p.N - 1);
+        else if (SBM == SB_128x128) srow_b[j] = min((n0 + wn * WTN + j * 16) / 128, (p.N - 1) / 128);
+        else srow_b[j] = n0 + wn * WTN + j * 16 + 4 * fg;  // first of 4 rows, clamped at use
+    }
+    const float* sa_l = p.sa + (int64_t)l * p.sa_batch;
+    const float* sb_l = p.sb + (int64_t)l * p.sb_batch;
+
+    // One main-loop step: wait for this step's tiles, release the other stage
+    // to the next step's loads, then run the MFMAs on this stage.
+    auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
+        __builtin_amdgcn_s_waitcnt(0);
+        if (k_tail && kt == KT - 1 && (K & 15)) mask_straddle(kt, cur);
+        __syncthreads();
+        if (kt + 1 < KT) issue(kt + 1, nxt);
+
+        // scales of this step
+        float s_a[FM];
+        float s_b[FN][4];
+        int e_a[FM], e_b[FN];
+        if (MODE == MODE_BLOCK) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) s_a[i] = sa_l[(int64_t)srow_a[i] * p.sa_ld + kt];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                if (SBM == SB_128x128) {
+                    const float v = sb_l[(int64_t)srow_b[j] * p.sb_ld + kt];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) s_b[j][r] = v;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) s_b[j][r] = sb_l[(int64_t)min(srow_b[j] + r, p.N - 1) * p.sb_ld + kt];
+                }
+            }
+        } else if (MODE == MODE_SF32) {
+            const int grp = kt * 4 + fg;
+            const bool gv = grp < p.sa_ld;  // groups past ceil(K/32) hold zero data
+#pragma unroll
+            for (int i = 0; i < FM; ++i) e_a[i] = gv ? e8m0_of(sa_l[(int64_t)srow_a[i] * p.sa_ld + grp]) : kNeutralE8M0;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) e_b[j] = gv ? e8m0_of(sb_l[(int64_t)srow_b[j] * p.sb_ld + grp]) : kNeutralE8M0;
+        }
+
+        const uint8_t* As = cur;
+        const uint8_t* Bs = cur + BM * kBK;
+        i32x8 af[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const uint8_t* base = As + (wm * WTM + i * 16) * kBK;
+            af[i] = cat(*(const i32x4*)(base + foff0), *(const i32x4*)(base + foff1));
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const uint8_t* base = Bs + (wn * WTN + j * 16) * kBK;
+            const i32x8 bf = cat(*(const i32x4*)(base + foff0), *(const i32x4*)(base + foff1));
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                if (MODE == MODE_FAST) {
+                    acc[j][i] = mfma<FB, FA>(bf, af[i], acc[j][i], kNeutralE8M0, kNeutralE8M0);
+                } else if (MODE == MODE_SF32) {
+                    acc[j][i] = mfma<FB, FA>(bf, af[i], acc[j][i], e_b[j], e_a[i]);
+                } else {
+                    const f32x4 part = mfma<FB, FA>(bf, af[i], f32x4{0.f, 0.f, 0.f, 0.f}, kNeutralE8M0, kNeutralE8M0);
+                    if (MODE == MODE_SLOW) {
+                        acc[j][i] += part;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[j][i][r] = __builtin_fmaf(part[r], s_a[i] * s_b[j][r], acc[j][i][r]);
+                    }
+                }
+            }
+        }
+    };
+    if (KT > 0) issue(0, smem0);
+    for (int kt = 0; kt < KT; kt += 2) {
+        step(kt, smem0, smem1);
+        if (kt + 1 < KT) step(kt + 1, smem1, smem0);
+    }
+
+    // ---------------------------------------------------------- epilogue
+    float alpha = 1.0f;
+    if (MODE == MODE_FAST || MODE == MODE_SLOW) alpha = p.sa[0] * p.sb[0];
+    const bool fp8_out = p.d_type == T_E4M3 || p.d_type == T_E5M2;
+    const float sr = (fp8_out && p.scale_result) ? p.scale_result[0] : 1.0f;
+    const int64_t dbase = (int64_t)l * p.d_batch;
+    const bool want_amax = p.amax_bits || p.amax_key;
+    uint32_t kb = 0;
+    unsigned long long kk = 0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * WTM + i * 16 + fr;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn * WTN + j * 16 + 4 * fg;
+            const int valid = (m < p.M) ? max(0, min(4, p.N - n)) : 0;
+            uint32_t out[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // +0.0f turns a -0 sum into +0: a sum of products starts from +0
+                float v = (acc[j][i][r] + 0.0f) * alpha;
+                if (want_amax && r < valid) {
+                    if (p.amax_key) {
+                        const unsigned long long key = amax_key(v, (int64_t)l * p.M * p.N + (int64_t)m * p.N + n + r);
+                        kk = key > kk ? key : kk;
+                    } else {
+                        const uint32_t a = abs_bits(v);
+                        kb = a > kb ? a : kb;
+                    }
+                }
+                if (fp8_out) v *= sr;
+                out[r] = convert(v, p.d_type);
+            }
+            if (valid > 0) store4(p.d, p.d_type, dbase + (int64_t)m * p.ldd + n, out, valid, p.vec_store != 0);
+        }
+    }
+    if (want_amax) amax_commit<NT>(p, kb, kk);
+}
+
+// ------------------------------------------------------------------ skinny kernel
+//
+// For M <= 16 * MT (MT <= 4) with per-tensor scales: the run is bound by
+// streaming B once from HBM. A workgroup owns 16 columns of the output; its 4
+// waves split the K steps round-robin (wave w takes steps w, w+4, ...), load
+// their B and A fragments straight from memory into registers (A is small and
+// stays in L2), keep kU steps in flight, and add their partial tiles in LDS in
+// a fixed order at the end.
+template <int MT, int MODE, int FA, int FB>
+__global__ void __launch_bounds__(256) gemm_skinny(GemmArgs p) {
+    constexpr int kU = MT <= 2 ? 4 : 2;  // K steps in flight per wave
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * 16;
+    const int K = p.K, KT = (K + kBK - 1) / kBK;
+    const int fr = lane & 15, fg = lane >> 4;
+    const rsrc_t rb = make_rsrc(p.b + (int64_t)n0 * p.ldb, operand_extent(min(16, p.N - n0), p.ldb, K));
+    const rsrc_t ra = make_rsrc(p.a, operand_extent(p.M, p.lda, K));
+    const uint32_t boff = (uint32_t)(fr * p.ldb + 16 * fg);
+    uint32_t aoff[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) aoff[i] = (uint32_t)((i * 16 + fr) * p.lda + 16 * fg);
+
+    struct Frag {
+        i32x8 b;
+        i32x8 a[MT];
+    };
+    // Load step kt: chunk k = 128 kt + 16 fg and 128 kt + 64 + 16 fg of each row.
+    auto load = [&](int kt, Frag& f) {
+        const int k0 = kt * kBK + 16 * fg;
+        const int k1 = k0 + 64;
+        const bool tail = kt * kBK + kBK > K;
+        uint32_t o0 = (uint32_t)(kt * kBK), o1 = (uint32_t)(kt * kBK + 64);
+        // chunks starting at or past K read zero; a straddling chunk is masked below
+        const bool z0 = tail && k0 >= K, z1 = tail && k1 >= K;
+        i32x4 b0 = __builtin_amdgcn_raw_buffer_load_b128(rb, z0 ? kOOB : boff + o0, 0, 0);
+        i32x4 b1 = __builtin_amdgcn_raw_buffer_load_b128(rb, z1 ? kOOB : boff + o1, 0, 0);
+        f.b = cat(b0, b1);
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            i32x4 a0 = __builtin_amdgcn_raw_buffer_load_b128(ra, z0 ? kOOB : aoff[i] + o0, 0, 0);
+            i32x4 a1 = __builtin_amdgcn_raw_buffer_load_b128(ra, z1 ? kOOB : aoff[i] + o1, 0, 0);
+            f.a[i] = cat(a0, a1);
+        }
+    };
+    auto mask = [&](int kt, Frag& f) {
+        // zero bytes at k >= K in a chunk straddling K (only in the last step)
+        const int k0 = kt * kBK + 16 * fg;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int ks = k0 + 64 * h;
+            if (ks < K && K < ks + 16) {
+                const int valid = K - ks;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const int nb = valid - 4 * d;
+                    const uint32_t m = nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : ((1u << (8 * nb)) - 1u));
+                    f.b[4 * h + d] = (int)((uint32_t)f.b[4 * h + d] & m);
+#pragma unroll
+                    for (int i = 0; i < MT; ++i) f.a[i][4 * h + d] = (int)((uint32_t)f.a[i][4 * h + d] & m);
+                }
+            }
+        }
+    };
+
+    f32x4 acc[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nsteps = (KT - wave + 3) / 4;  // steps of this wave: wave, wave+4, ...
+    Frag buf[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+        if (u < nsteps) load(wave + 4 * u, buf[u]);
+    for (int s0 = 0; s0 < nsteps; s0 += kU) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int s = s0 + u;
+            if (s < nsteps) {
+                Frag cur = buf[u];
+                const int kt = wave + 4 * s;
+                if (s + kU < nsteps) load(wave + 4 * (s + kU), buf[u]);
+                if (kt * kBK + kBK > K && (K & 15)) mask(kt, cur);
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+                    if (MODE == MODE_FAST) {
+                        acc[i] = mfma<FB, FA>(cur.b, cur.a[i], acc[i], kNeutralE8M0, kNeutralE8M0);
+                    } else {
+                        acc[i] += mfma<FB, FA>(cur.b, cur.a[i], f32x4{0.f, 0.f, 0.f, 0.f}, kNeutralE8M0, kNeutralE8M0);
+                    }
+                }
+            }
+        }
+    }
+
+    // Fixed-order reduction of the 4 waves' partial tiles.
+    __shared__ f32x4 red[3][MT][64];
+    if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) red[wave - 1][i][lane] = acc[i];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[i] = ((acc[i] + red[0][i][lane]) + red[1][i][lane]) + red[2][i][lane];
+
+    const float alpha = p.sa[0] * p.sb[0];
+    const bool fp8_out = p.d_type == T_E4M3 || p.d_type == T_E5M2;
+    const float sr = (fp8_out && p.scale_result) ? p.scale_result[0] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int m = i * 16 + fr;
+        const int n = n0 + 4 * fg;
+        const int valid = (m < p.M) ? max(0, min(4, p.N - n)) : 0;
+        uint32_t out[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float v = (acc[i][r] + 0.0f) * alpha;
+            if (fp8_out) v *= sr;
+            out[r] = convert(v, p.d_type);
+        }
+        if (valid > 0) store4(p.d, p.d_type, (int64_t)m * p.ldd + n, out, valid, p.vec_store != 0);
+    }
+}
+
+}  // namespace mmfp8

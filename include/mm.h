@@ -1,0 +1,185 @@
+/*
+ * mm.h -- C ABI of libmmfp8.so: FP8 scaled GEMM and batched block-scaled
+ * GEMM + global amax on AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor arguments are DEVICE pointers owned by the caller. The library
+ *    never allocates, frees or keeps them.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
+ *    enqueued on it and the call returns without waiting for the GPU, so the
+ *    calls can be captured into a HIP graph (the library records no memset
+ *    nodes: outputs it must clear are cleared by its own kernels).
+ *  - Arguments are validated completely before any HIP call. On any status
+ *    other than MM_OK nothing has been enqueued or written, and
+ *    mm_last_error() describes the problem. No C++ exception crosses the ABI.
+ *  - The library uses the calling thread's current HIP device.
+ *  - The kernels never fault whatever the byte values of the operands are:
+ *    NaN and Inf codes, padding bytes and partial tiles are all handled.
+ *  - Integer arguments are int64_t; enumerations are passed as int.
+ */
+#ifndef MMFP8_MM_H
+#define MMFP8_MM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. The error classes of the "mmaemu API reference (v0.1)",
+ * Errors and warnings table map onto them: a call the reference platform
+ * rejects (ReferenceRejectsError / ValueError) -> MM_ERR_INVALID_ARGUMENT;
+ * a feature not provided (UnsupportedFeatureError) -> MM_ERR_UNSUPPORTED. */
+typedef enum mm_status {
+    MM_OK = 0,
+    MM_ERR_INVALID_ARGUMENT = 1, /* malformed call: negative size, bad enum, null pointer, ld < K ... */
+    MM_ERR_UNSUPPORTED = 2,      /* well-formed but not provided (scale pairing, sf_vec_size, FP8 C ...) */
+    MM_ERR_MISALIGNED = 3,       /* pointer or row pitch alignment violated */
+    MM_ERR_DEVICE = 4            /* the HIP runtime reported an error while enqueueing */
+} mm_status;
+
+/* Element types. FP8 codes follow the OCP 8-bit formats E4M3FN (largest
+ * finite 448, no infinities, NaN = 0x7F / 0xFF) and E5M2 (largest finite
+ * 57344, IEEE-like infinities and NaNs): the float8_e4m3fn / float8_e5m2
+ * dtypes of the "mmaemu API reference (v0.1)", scaled_mm argument table. */
+typedef enum mm_dtype {
+    MM_F8_E4M3FN = 0,
+    MM_F8_E5M2 = 1,
+    MM_F32 = 2,
+    MM_BF16 = 3,
+    MM_F16 = 4
+} mm_dtype;
+
+/* Scale granularities ("TileOPs: Linear Algebra Operators",
+ * tileops.gemm.GemmFP8FwdOp): one fp32 per tensor, one per 1x128 block along
+ * K, or one per 128x128 block. */
+typedef enum mm_scale_mode {
+    MM_SCALE_TENSOR = 0,  /* [1]                                 */
+    MM_SCALE_1x128 = 1,   /* [rows, ceil(K/128)], row-major      */
+    MM_SCALE_128x128 = 2  /* [ceil(rows/128), ceil(K/128)]       */
+} mm_scale_mode;
+
+/*
+ * mm_scaled_gemm -- d = (a * s_a) @ (b * s_b)^T, cast to d_type.
+ *
+ * Defined by "TileOPs: Linear Algebra Operators", tileops.gemm.GemmFP8FwdOp
+ * (the FP8 NT GEMM with per-tensor, 1x128 or 128x128 scales) and
+ * "mmaemu API reference (v0.1)", mmaemu.scaled_mm (torch._scaled_mm's
+ * arguments: per-tensor scales multiply the result, scale_result for FP8
+ * outputs, fast or slow accumulation, output dtypes).
+ *
+ *  a        [M, K] FP8 codes of a_type, row-major with row pitch lda bytes
+ *           (lda >= K). The caller guarantees (M-1)*lda + K readable bytes.
+ *  b        [N, K] FP8 codes of b_type, row pitch ldb bytes (ldb >= K): the
+ *           [N, K] weight, i.e. scaled_mm's column-major mat2 [K, N] read as
+ *           its transpose. a_type and b_type may differ (E4M3 x E5M2 mixes).
+ *  scale_a  fp32, by sa_mode: [1] or [M, ceil(K/128)] (1x128).
+ *  scale_b  fp32, by sb_mode: [1], [N, ceil(K/128)] (1x128) or
+ *           [ceil(N/128), ceil(K/128)] (128x128).
+ *           Accepted pairs: (TENSOR, TENSOR), (1x128, 1x128), (1x128, 128x128);
+ *           any other pair -> MM_ERR_UNSUPPORTED.
+ *  scale_result  fp32 [1] or NULL (= 1). Read only when d_type is an FP8
+ *           type; the value is multiplied into the result before the cast.
+ *  d        [M, N] of d_type (F32, BF16, F16, F8_E4M3FN or F8_E5M2), row pitch
+ *           ldd ELEMENTS (ldd >= N). Previous contents never matter.
+ *  use_fast_accum  nonzero: one fp32 accumulation chain over all of K;
+ *           zero: each 128-element K chunk is summed into a fresh fp32
+ *           partial that is then added to the fp32 accumulator ("slow").
+ *           Block-scaled modes always promote per 128-chunk (the scale changes
+ *           per chunk), so the flag does not change them.
+ *
+ * Result, per output element: the sum over k of the products is formed in
+ * fp32 by the MFMA units (every product of two FP8 values is exact in fp32);
+ * per-tensor scales multiply it as fp32(s_a * s_b); block scales multiply each
+ * 128-chunk partial as fp32(sa[m,kb] * sb[n,kb]) in a fused multiply-add; an
+ * FP8 output is then multiplied by scale_result. The cast rounds to nearest
+ * even: bf16 / f16 / f32 overflow to +-Inf, FP8 outputs saturate to +-max
+ * (+-Inf included); NaN is stored as the canonical pattern of its type (f32
+ * 0x7FFFFFFF, bf16 / f16 0x7FFF, FP8 0x7F), the encodings of "mmaemu
+ * testing", Bitwise policy. An exactly-zero sum is +0 before the scales.
+ *
+ * Sizes and alignment: M, N, K in [0, 2^31); M == 0 or N == 0 returns MM_OK
+ * with nothing enqueued; K == 0 gives the empty sum (+0) times the scales.
+ * a and b must be 16-byte aligned, lda and ldb multiples of 8 and at most
+ * 2^22 bytes; d aligned to its element size; scale pointers 4-byte aligned.
+ * Violations -> MM_ERR_MISALIGNED.
+ */
+mm_status mm_scaled_gemm(int64_t M, int64_t N, int64_t K,
+                         const void* a, int a_type, int64_t lda,
+                         const void* b, int b_type, int64_t ldb,
+                         const float* scale_a, int sa_mode,
+                         const float* scale_b, int sb_mode,
+                         const float* scale_result,
+                         void* d, int d_type, int64_t ldd,
+                         int use_fast_accum,
+                         void* stream);
+
+/*
+ * mm_blockscaled_gemm_amax -- batched block-scaled GEMM with a global amax.
+ *
+ * Defined by "cuDNN frontend: GEMM + Amax (SM100)", Overview, Shapes and
+ * Equations: A^[m,k,l] = A[m,k,l] * SFA(m, k / sf_vec_size, l),
+ * B^[n,k,l] = B[n,k,l] * SFB(n, k / sf_vec_size, l),
+ * C[m,n,l] = sum_k A^[m,k,l] B^[n,k,l], Amax = max over m,n,l of |C[m,n,l]|.
+ *
+ *  a        [L][M][K] FP8 codes (k-major), b [L][N][K], both of ab_type (the
+ *           two operands must have the same type, as the page requires).
+ *  sfa      [L][M][ceil(K/sf_vec_size)] fp32 scale factors, sfb
+ *           [L][N][ceil(K/sf_vec_size)]. Each value must be a power of two
+ *           2^e with -127 <= e <= 127 (an E8M0 value carried in fp32; 2^-127
+ *           is the fp32 subnormal 0x00400000). Only the exponent field is
+ *           read: any other value x acts as 2^floor(log2|x|), zero as 2^-127,
+ *           Inf / NaN as the E8M0 NaN.
+ *  sf_vec_size  32. The page's other value, 16, is not supported with FP8
+ *           operands there either -> MM_ERR_UNSUPPORTED; anything else ->
+ *           MM_ERR_INVALID_ARGUMENT.
+ *  c        [L][M][N] of c_type (F32, BF16 or F16), i.e. the page's (M, N, L)
+ *           tensor in n-major order. FP8 C with FP8 operands is disabled on
+ *           the page as well -> MM_ERR_UNSUPPORTED.
+ *  amax     fp32 [1] or NULL: max over all outputs of |C| taken on the fp32
+ *           value before the cast to c_type. NaN if any output is NaN; +0 when
+ *           M*N*L == 0.
+ *  amax_index  int64 [1] or NULL: linear index l*M*N + m*N + n of the
+ *           maximum, the smallest such index on ties; -1 when M*N*L == 0.
+ *           Requires M*N*L < 2^33.
+ *
+ * The sum of each 32-element group is scaled in the MFMA units by the product
+ * of its two scale factors (exact for powers of two) and accumulated over K in
+ * one fp32 chain. The cast to c_type and NaN encodings follow mm_scaled_gemm.
+ * The library clears amax / amax_index itself, with its own kernels on
+ * `stream`; the outputs are final when the stream reaches the end of the call.
+ *
+ * Sizes and alignment: M, N, K, L in [0, 2^31) with L*M*K, L*N*K and L*M*N
+ * below 2^48. a, b and c 16-byte aligned and K a multiple of 16 (the page
+ * asks for 16-byte alignment along the contiguous dimension); sfa, sfb, amax
+ * 4-byte and amax_index 8-byte aligned -> else MM_ERR_MISALIGNED.
+ * M, N or L == 0: no GEMM is launched; amax / amax_index are still written.
+ */
+mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L,
+                                   const void* a, const void* b, int ab_type,
+                                   const float* sfa, const float* sfb, int sf_vec_size,
+                                   void* c, int c_type,
+                                   float* amax, int64_t* amax_index,
+                                   void* stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if
+ * none). The pointer stays valid until the thread's next mm_* call. */
+const char* mm_last_error(void);
+
+/* Library name, version and target, e.g. "mmfp8 0.1.0 gfx950". */
+const char* mm_version(void);
+
+/*
+ * mm_debug_convert -- test hook, not part of the GEMM contract: rounds n fp32
+ * values x (device) to dtype with exactly the conversion the GEMM epilogues
+ * use (round to nearest even, FP8 saturating, canonical NaN) and writes the
+ * bit patterns to y (device; 1, 2 or 4 bytes per element). x and y must be
+ * aligned to their element sizes.
+ */
+mm_status mm_debug_convert(const float* x, void* y, int dtype, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MMFP8_MM_H */

@@ -257,10 +257,15 @@ int orc_scaled_gemm(int64_t M, int64_t N, int64_t K,
     const double sr = (fp8_out && scale_result) ? (double)scale_result[0] : 1.0;
     const Format out_f = format_of(d_type);
 
-    /* Decode once: the decoded operands as float64. */
-    std::vector<double> A((size_t)M * K), B((size_t)N * K);
-    for (int64_t m = 0; m < M; ++m)
-        for (int64_t k = 0; k < K; ++k) A[(size_t)m * K + k] = decode(a[m * lda + k], a_fmt);
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows && (rows[i] < 0 || rows[i] >= M)) return ORC_ERR_ARG;
+
+    /* Decode once: the decoded operands as float64 (only the requested rows of a). */
+    std::vector<double> A((size_t)n_rows * K), B((size_t)N * K);
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const int64_t m = rows ? rows[i] : i;
+        for (int64_t k = 0; k < K; ++k) A[(size_t)i * K + k] = decode(a[m * lda + k], a_fmt);
+    }
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k) B[(size_t)n * K + k] = decode(b[n * ldb + k], b_fmt);
 
@@ -269,12 +274,9 @@ int orc_scaled_gemm(int64_t M, int64_t N, int64_t K,
         return sb_mode == ORC_SCALE_1x128 ? scale_b[n * KB + kb] : scale_b[(n / 128) * KB + kb];
     };
 
-    for (int64_t i = 0; i < n_rows; ++i)
-        if (rows && (rows[i] < 0 || rows[i] >= M)) return ORC_ERR_ARG;
-
     parallel_rows(n_rows, threads, [&](int64_t i) {
         const int64_t m = rows ? rows[i] : i;
-        const double* Am = &A[(size_t)m * K];
+        const double* Am = &A[(size_t)i * K];
         for (int64_t n = 0; n < N; ++n) {
             const double* Bn = &B[(size_t)n * K];
             double v, sabs = 0.0;
@@ -366,18 +368,19 @@ int orc_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L,
     std::vector<double> vals((size_t)L * n_rows * N);
     for (int64_t l = 0; l < L; ++l) {
         /* Dequantized operands of this batch item: A^ = A * SFA, B^ = B * SFB. */
-        std::vector<double> Ah((size_t)M * K), Bh((size_t)N * K);
-        for (int64_t m = 0; m < M; ++m)
+        std::vector<double> Ah((size_t)n_rows * K), Bh((size_t)N * K);
+        for (int64_t i = 0; i < n_rows; ++i) {
+            const int64_t m = rows ? rows[i] : i;
             for (int64_t k = 0; k < K; ++k)
-                Ah[(size_t)m * K + k] = decode(a[(l * M + m) * K + k], ab_fmt) *
+                Ah[(size_t)i * K + k] = decode(a[(l * M + m) * K + k], ab_fmt) *
                                         (double)sfa[(l * M + m) * KS + k / sf_vec];
+        }
         for (int64_t n = 0; n < N; ++n)
             for (int64_t k = 0; k < K; ++k)
                 Bh[(size_t)n * K + k] = decode(b[(l * N + n) * K + k], ab_fmt) *
                                         (double)sfb[(l * N + n) * KS + k / sf_vec];
         parallel_rows(n_rows, threads, [&](int64_t i) {
-            const int64_t m = rows ? rows[i] : i;
-            const double* Am = &Ah[(size_t)m * K];
+            const double* Am = &Ah[(size_t)i * K];
             for (int64_t n = 0; n < N; ++n) {
                 const double* Bn = &Bh[(size_t)n * K];
                 double S = +0.0, T = 0.0;

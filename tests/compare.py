@@ -7,8 +7,9 @@ Tolerances (one floating-point rule per output type):
    |gpu - exact| <= 2^-20 * sum|t| + ulp_out(exact) / 2 (the second form covers
    heavy cancellation, where the fp32 accumulator's own error already exceeds
    an output ulp of a tiny result).
- - NaN must be NaN in both and carry the canonical encoding; infinities must
-   match exactly; +0 and -0 are at distance 0 in the ulp rule.
+ - NaN must be NaN in both and carry the canonical encoding; +0 and -0 are at
+   distance 0 and +-Inf one step past the largest finite value in the ulp rule;
+   fp32 infinities must match exactly.
 """
 from __future__ import annotations
 
@@ -88,10 +89,11 @@ def check(gpu_bits: np.ndarray, value: np.ndarray, sum_abs: np.ndarray, oracle_b
             err = np.abs(g - v)
             ok |= fin & np.isfinite(g) & np.isfinite(v) & (err <= TOL * sa)
     else:
+        # +-Inf sits one step past the largest finite value in the ordered-integer map
         dist = np.abs(ordered_int(gb, fmt) - ordered_int(ob, fmt))
+        ok |= fin & (dist <= 1)
         o_val = bits_to_float(ob, fmt)
         both_finite = fin & np.isfinite(g) & np.isfinite(o_val)
-        ok |= both_finite & (dist <= 1)
         with np.errstate(invalid="ignore"):
             err = np.abs(g - v)
             ok |= both_finite & np.isfinite(v) & (err <= TOL * sa + 0.5 * ulp_of(v, fmt))

@@ -1,0 +1,73 @@
+"""Helpers for the GPU parity tests: run the C ABI on device buffers, fetch bits."""
+import numpy as np
+import torch
+
+import block_scaled_gemm_amd as mm
+
+DEV = torch.device("cuda:0")
+BITS_TORCH = {0: torch.uint8, 1: torch.uint8, 2: torch.int32, 3: torch.int16, 4: torch.int16}
+BITS_NP = {0: np.uint8, 1: np.uint8, 2: np.uint32, 3: np.uint16, 4: np.uint16}
+
+
+def dev_u8(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(DEV)
+
+
+def dev_f32(x) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(np.atleast_1d(np.asarray(x, dtype=np.float32)))).to(DEV)
+
+
+def stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def scaled_gemm(a, a_fmt, b, b_fmt, K, sa, sa_mode, sb, sb_mode, d_type, scale_result=None, fast=False,
+                ldd=None, d_fill=0x5A):
+    """a [M, lda], b [N, ldb] uint8 codes (numpy); returns the output bits [M, N] (numpy)."""
+    M, lda = a.shape
+    N, ldb = b.shape
+    ldd = ldd or N
+    ta, tb = dev_u8(a), dev_u8(b)
+    tsa, tsb = dev_f32(sa), dev_f32(sb)
+    tsr = dev_f32(scale_result) if scale_result is not None else None
+    es = np.dtype(BITS_NP[d_type]).itemsize
+    # output buffer prefilled with junk: previous contents must never matter
+    td = torch.full((max(M, 1) * ldd * es,), d_fill, dtype=torch.uint8, device=DEV)
+    st = mm.mm_scaled_gemm(M, N, K, ta.data_ptr(), a_fmt, lda, tb.data_ptr(), b_fmt, ldb, tsa.data_ptr(), sa_mode,
+                           tsb.data_ptr(), sb_mode, tsr.data_ptr() if tsr is not None else 0, td.data_ptr(), d_type,
+                           ldd, int(fast), stream())
+    assert st == mm.MM_OK, (st, mm.mm_last_error())
+    torch.cuda.synchronize()
+    out = td.cpu().numpy().view(BITS_NP[d_type])[: M * ldd].reshape(M, ldd)[:, :N]
+    return np.ascontiguousarray(out)
+
+
+def blockscaled_gemm_amax(a, b, fmt, sfa, sfb, c_type, with_amax=True, with_index=True):
+    """a [L, M, K], b [L, N, K] uint8 codes; returns (c bits [L, M, N], amax float or None, index or None)."""
+    L, M, K = a.shape
+    N = b.shape[1]
+    ta, tb = dev_u8(a), dev_u8(b)
+    tsa = torch.from_numpy(np.ascontiguousarray(sfa, dtype=np.float32)).to(DEV)
+    tsb = torch.from_numpy(np.ascontiguousarray(sfb, dtype=np.float32)).to(DEV)
+    es = np.dtype(BITS_NP[c_type]).itemsize
+    tc = torch.full((max(L * M * N, 1) * es,), 0x5A, dtype=torch.uint8, device=DEV)
+    tam = torch.full((1,), 123.0, dtype=torch.float32, device=DEV)
+    tix = torch.full((1,), 777, dtype=torch.int64, device=DEV)
+    st = mm.mm_blockscaled_gemm_amax(M, N, K, L, ta.data_ptr(), tb.data_ptr(), fmt, tsa.data_ptr(), tsb.data_ptr(),
+                                     32, tc.data_ptr(), c_type, tam.data_ptr() if with_amax else 0,
+                                     tix.data_ptr() if with_index else 0, stream())
+    assert st == mm.MM_OK, (st, mm.mm_last_error())
+    torch.cuda.synchronize()
+    c = tc.cpu().numpy().view(BITS_NP[c_type])[: L * M * N].reshape(L, M, N)
+    return (np.ascontiguousarray(c), float(tam.item()) if with_amax else None,
+            int(tix.item()) if with_index else None)
+
+
+def debug_convert(x: np.ndarray, dtype: int) -> np.ndarray:
+    tx = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+    es = np.dtype(BITS_NP[dtype]).itemsize
+    ty = torch.empty((x.size * es,), dtype=torch.uint8, device=DEV)
+    st = mm.mm_debug_convert(tx.data_ptr(), ty.data_ptr(), dtype, x.size, stream())
+    assert st == mm.MM_OK, (st, mm.mm_last_error())
+    torch.cuda.synchronize()
+    return ty.cpu().numpy().view(BITS_NP[dtype])

@@ -1,0 +1,134 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol include/mm.h
+declares, and validates arguments completely before any HIP call.
+
+Every call here is either invalid (validation returns before touching HIP), of
+zero size (nothing is launched), or made with MM_TEST_FORCE_FAIL=launch (the
+library returns MM_ERR_DEVICE right after validation): none launches a kernel,
+so the fake device pointers are never dereferenced, here or on a GPU machine.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_gemm_amd as mm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mm.h")
+P = 0x10000          # a fake, 64 KiB-aligned device address
+P8 = P + 8           # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mm_status|const char\*)\s+(mm_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == {"mm_scaled_gemm", "mm_blockscaled_gemm_amax", "mm_last_error", "mm_version",
+                          "mm_debug_convert"}
+    lib = ctypes.CDLL(mm.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(mm.EXPORTED) == set(names)
+
+
+def test_version():
+    assert mm.mm_version().startswith("mmfp8 ") and "gfx950" in mm.mm_version()
+
+
+def gemm(**kw):
+    args = dict(M=64, N=64, K=128, a=P, a_type=0, lda=128, b=P, b_type=0, ldb=128, scale_a=P, sa_mode=0,
+                scale_b=P, sb_mode=0, scale_result=0, d=P, d_type=2, ldd=64, use_fast_accum=0, stream=0)
+    args.update(kw)
+    return mm.mm_scaled_gemm(**args)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(M=-1), mm.MM_ERR_INVALID_ARGUMENT, "must be >= 0"),
+    (dict(K=-5), mm.MM_ERR_INVALID_ARGUMENT, "must be >= 0"),
+    (dict(N=1 << 31), mm.MM_ERR_UNSUPPORTED, "below 2^31"),
+    (dict(a_type=2), mm.MM_ERR_INVALID_ARGUMENT, "a_type and b_type"),
+    (dict(b_type=7), mm.MM_ERR_INVALID_ARGUMENT, "a_type and b_type"),
+    (dict(d_type=5), mm.MM_ERR_INVALID_ARGUMENT, "unknown d_type"),
+    (dict(sa_mode=3), mm.MM_ERR_INVALID_ARGUMENT, "unknown scale mode"),
+    (dict(sa_mode=0, sb_mode=1), mm.MM_ERR_UNSUPPORTED, "scale pair"),
+    (dict(sa_mode=2, sb_mode=2), mm.MM_ERR_UNSUPPORTED, "scale pair"),
+    (dict(sa_mode=1, sb_mode=0), mm.MM_ERR_UNSUPPORTED, "scale pair"),
+    (dict(lda=64), mm.MM_ERR_INVALID_ARGUMENT, "lda and ldb"),
+    (dict(ldd=63), mm.MM_ERR_INVALID_ARGUMENT, "ldd"),
+    (dict(lda=(1 << 22) + 8, ldb=(1 << 22) + 8), mm.MM_ERR_UNSUPPORTED, "2^22"),
+    (dict(d=0), mm.MM_ERR_INVALID_ARGUMENT, "d is NULL"),
+    (dict(a=0), mm.MM_ERR_INVALID_ARGUMENT, "a or b is NULL"),
+    (dict(scale_b=0), mm.MM_ERR_INVALID_ARGUMENT, "scale_a or scale_b"),
+    (dict(a=P8), mm.MM_ERR_MISALIGNED, "16-byte"),
+    (dict(lda=132, ldb=132), mm.MM_ERR_MISALIGNED, "multiples of 8"),
+    (dict(d=P + 2), mm.MM_ERR_MISALIGNED, "element size"),
+    (dict(d=P + 1, d_type=3), mm.MM_ERR_MISALIGNED, "element size"),
+    (dict(scale_a=P + 2), mm.MM_ERR_MISALIGNED, "4-byte"),
+])
+def test_scaled_gemm_validation(kw, status, msg):
+    assert gemm(**kw) == status
+    assert msg in mm.mm_last_error()
+
+
+def test_scaled_gemm_zero_sizes_launch_nothing():
+    assert gemm(M=0, d=0, a=0) == mm.MM_OK
+    assert gemm(N=0, d=0, b=0) == mm.MM_OK
+    assert mm.mm_last_error() == ""
+
+
+def amax_call(**kw):
+    args = dict(M=64, N=64, K=256, L=2, a=P, b=P, ab_type=0, sfa=P, sfb=P, sf_vec_size=32, c=P, c_type=2,
+                amax=P, amax_index=P, stream=0)
+    args.update(kw)
+    return mm.mm_blockscaled_gemm_amax(**args)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(L=-1), mm.MM_ERR_INVALID_ARGUMENT, "must be >= 0"),
+    (dict(ab_type=3), mm.MM_ERR_INVALID_ARGUMENT, "ab_type"),
+    (dict(sf_vec_size=16), mm.MM_ERR_UNSUPPORTED, "sf_vec_size 16"),
+    (dict(sf_vec_size=64), mm.MM_ERR_INVALID_ARGUMENT, "sf_vec_size must be 32"),
+    (dict(c_type=0), mm.MM_ERR_UNSUPPORTED, "FP8 C"),
+    (dict(c_type=9), mm.MM_ERR_INVALID_ARGUMENT, "unknown c_type"),
+    (dict(K=1 << 23), mm.MM_ERR_UNSUPPORTED, "2^22"),
+    (dict(M=1 << 17, N=1 << 17, L=1), mm.MM_ERR_UNSUPPORTED, "2^33"),
+    (dict(c=0), mm.MM_ERR_INVALID_ARGUMENT, "c is NULL"),
+    (dict(sfb=0), mm.MM_ERR_INVALID_ARGUMENT, "NULL"),
+    (dict(a=P8), mm.MM_ERR_MISALIGNED, "16-byte"),
+    (dict(K=264), mm.MM_ERR_MISALIGNED, "multiple of 16"),
+    (dict(amax=P + 2), mm.MM_ERR_MISALIGNED, "4-byte"),
+    (dict(amax_index=P + 4), mm.MM_ERR_MISALIGNED, "8-byte"),
+])
+def test_amax_validation(kw, status, msg):
+    assert amax_call(**kw) == status
+    assert msg in mm.mm_last_error()
+
+
+def test_amax_zero_size_without_outputs_launches_nothing():
+    assert amax_call(M=0, amax=0, amax_index=0, c=0) == mm.MM_OK
+
+
+def test_forced_launch_failure(monkeypatch):
+    monkeypatch.setenv("MM_TEST_FORCE_FAIL", "launch")
+    assert gemm() == mm.MM_ERR_DEVICE
+    assert "forced" in mm.mm_last_error()
+    assert amax_call() == mm.MM_ERR_DEVICE
+    assert mm.mm_debug_convert(P, P, 2, 16, 0) == mm.MM_ERR_DEVICE
+
+
+def test_debug_convert_validation():
+    assert mm.mm_debug_convert(P, P, 9, 16, 0) == mm.MM_ERR_INVALID_ARGUMENT
+    assert mm.mm_debug_convert(P, P, 2, -1, 0) == mm.MM_ERR_INVALID_ARGUMENT
+    assert mm.mm_debug_convert(P + 1, P, 2, 16, 0) == mm.MM_ERR_MISALIGNED
+    assert mm.mm_debug_convert(0, 0, 2, 0, 0) == mm.MM_OK
+
+
+def test_error_message_is_thread_local_and_cleared():
+    assert gemm(M=-1) == mm.MM_ERR_INVALID_ARGUMENT
+    assert mm.mm_last_error() != ""
+    assert gemm(M=0, d=0) == mm.MM_OK
+    assert mm.mm_last_error() == ""

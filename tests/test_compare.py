@@ -46,8 +46,13 @@ def test_ulp_rule_across_zero_and_inf():
     sa = np.array([0.0, 0.0, 1.0])
     ob = np.array([0x0000, 0x0000, 0x7C00], np.uint16)
     compare.check(np.array([0x8000, 0x0001, 0x7C00], np.uint16), v, sa, ob, F16)
-    with pytest.raises(AssertionError):   # infinities must match exactly
-        compare.check(np.array([0x0000, 0x0000, 0x7BFF], np.uint16), v, sa, ob, F16)
+    # the largest finite value is one step from +Inf; two steps is out
+    compare.check(np.array([0x0000, 0x0000, 0x7BFF], np.uint16), v, sa, ob, F16)
+    with pytest.raises(AssertionError):
+        compare.check(np.array([0x0000, 0x0000, 0x7BFE], np.uint16), v, sa, ob, F16)
+    with pytest.raises(AssertionError):   # fp32 infinities must match exactly
+        compare.check(np.array([0x7F7FFFFF], np.uint32), np.array([np.inf]), np.array([1.0]),
+                      np.array([0x7F800000], np.uint32), F32)
 
 
 def test_cancellation_branch_fp8():

@@ -1,0 +1,285 @@
+"""GPU parity: the C ABI on an MI355X against the CPU oracle, element by element.
+
+Bars: bit-exact where the result is exact by construction (single products,
+conversions, closed forms, amax against the GPU's own C, batch vs separate
+calls); otherwise the tolerances of tests/compare.py (fp32 out: 2^-20 * sum|t|;
+bf16 / f16 / FP8 out: 1 ulp after rounding).
+"""
+import numpy as np
+import pytest
+
+import compare
+import datagen
+import oracle
+from oracle import E4M3FN, E5M2, F32, BF16, F16
+
+pytestmark = pytest.mark.gpu
+
+gu = pytest.importorskip("gpu_util")
+DTYPES = (F32, BF16, F16, E4M3FN, E5M2)
+DT_NAME = {F32: "f32", BF16: "bf16", F16: "f16", E4M3FN: "e4m3", E5M2: "e5m2"}
+
+
+def sample_rows(M, n_each=16, seed=0):
+    if M <= 3 * n_each:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(n_each, M - n_each), size=n_each, replace=False)
+    return np.unique(np.concatenate([np.arange(n_each), mid, np.arange(M - n_each, M)]))
+
+
+def check_gemm(d, sa_mode, sb_mode, d_type, fast, rows=None, scale_result=None, what="", ldd=None):
+    a, b, K = d["a"], d["b"], d["K"]
+    gpu = gu.scaled_gemm(a, d["a_fmt"], b, d["b_fmt"], K, d["scale_a"], sa_mode, d["scale_b"], sb_mode, d_type,
+                         scale_result=scale_result, fast=fast, ldd=ldd)
+    value, sabs, bits = oracle.scaled_gemm_k(a, d["a_fmt"], b, d["b_fmt"], K, d["scale_a"], sa_mode, d["scale_b"],
+                                             sb_mode, d_type, scale_result=scale_result, rows=rows)
+    g = gpu if rows is None else gpu[rows]
+    return compare.check(g, value, sabs, bits, d_type, what), gpu, value, bits
+
+
+# ------------------------------------------------------------------ exact cases
+
+@pytest.mark.parametrize("fa,fb", [(E4M3FN, E4M3FN), (E5M2, E5M2), (E4M3FN, E5M2), (E5M2, E4M3FN)])
+@pytest.mark.parametrize("fast", [True, False])
+def test_product_table_bit_exact(fa, fb, fast):
+    """All 256 x 256 code pairs as single products (K = 128, codes in column 0):
+    every output is one exact product, NaN / Inf included."""
+    a = np.zeros((256, 128), np.uint8); a[:, 0] = np.arange(256)
+    b = np.zeros((256, 128), np.uint8); b[:, 0] = np.arange(256)
+    gpu = gu.scaled_gemm(a, fa, b, fb, 128, 1.0, 0, 1.0, 0, F32, fast=fast)
+    _, _, bits = oracle.scaled_gemm(a, fa, b, fb, np.float32(1), 0, np.float32(1), 0, F32)
+    compare.assert_bitwise_equal(gpu, bits, f"product table {fa}x{fb}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=[DT_NAME[t] for t in DTYPES])
+def test_epilogue_conversion_bit_exact(dtype):
+    """The epilogue cast alone (test hook) on 2^24 sampled fp32 patterns plus
+    dense sweeps of every binade near the output ranges."""
+    rng = np.random.default_rng(1)
+    bits = (np.arange(1 << 24, dtype=np.uint64) * 256 + rng.integers(0, 256, 1 << 24)).astype(np.uint32)
+    dense = [np.float32(2.0 ** e).view(np.uint32) + (np.arange(8192, dtype=np.uint32) << 10) for e in range(-30, 20)]
+    bits = np.concatenate([bits] + dense + [np.array([0x7FC00000, 0x7F800001, 0xFFFFFFFF, 0x7F800000, 0, 0x80000000],
+                                                     np.uint32)])
+    x = bits.view(np.float32)
+    gpu = gu.debug_convert(x, dtype)
+    want = oracle.round_to(x.astype(np.float64), dtype)
+    compare.assert_bitwise_equal(gpu, want, f"convert to {DT_NAME[dtype]}")
+
+
+def test_adversarial_structured_rows_bit_exact():
+    d = datagen.workload2_adversarial(64, 4096, 4096)
+    gpu = gu.scaled_gemm(d["a"], 0, d["b"], 0, 4096, 1.0, 0, 1.0, 0, BF16, fast=False)
+    _, _, bits = oracle.scaled_gemm(d["a"], 0, d["b"], 0, np.float32(1), 0, np.float32(1), 0, BF16, rows=[0, 1, 2, 3])
+    assert gpu[0, 0] == bits[0, 0] and gpu[0, 0] != 0          # K * 448^2, exact in bf16
+    assert gpu[1, 1] == 0x0000                                 # alternating +-448 against +448: +0
+    assert gpu[2, 2] == bits[2, 2]                             # K * 2^-18
+    assert np.all(gpu[3] == 0x0000)                            # all -0 codes: +0 everywhere
+
+
+# ------------------------------------------------------------------ workload 1
+
+@pytest.mark.parametrize("fast", [True, False])
+def test_workload1_256_cubed(fast):
+    d = datagen.workload1()
+    check_gemm(d, 0, 0, F32, fast, what="256^3")
+
+
+# ------------------------------------------------------------------ workload 2 (the benchmark shapes)
+
+@pytest.mark.parametrize("M", datagen.GEMM2_MS)
+def test_workload2_gauss_full_size(M):
+    d = datagen.workload2_gauss(M)
+    rows = None if M <= 64 else sample_rows(M)
+    check_gemm(d, 0, 0, BF16, fast=False, rows=rows, what=f"workload2 gauss M={M}")
+
+
+@pytest.mark.parametrize("M", [16, 64, 256, 2048])
+def test_workload2_adversarial_full_size(M):
+    d = datagen.workload2_adversarial(M)
+    rows = None if M <= 64 else sample_rows(M)
+    check_gemm(d, 0, 0, BF16, fast=False, rows=rows, what=f"workload2 adversarial M={M}")
+
+
+@pytest.mark.parametrize("M", [16, 2048])
+def test_workload2_fast_accumulation(M):
+    d = datagen.workload2_gauss(M)
+    check_gemm(d, 0, 0, BF16, fast=True, rows=None if M <= 64 else sample_rows(M), what=f"fast M={M}")
+
+
+# ------------------------------------------------------------------ ragged shapes, padding, all output types
+
+RAGGED = [(300, 520, 1000), (17, 33, 132), (1, 1, 1), (5, 7, 3), (257, 129, 4104), (65, 100, 200),
+          (40, 4096, 520), (130, 260, 136), (33, 48, 8200)]
+
+
+@pytest.mark.parametrize("M,N,K", RAGGED)
+@pytest.mark.parametrize("fast", [True, False])
+def test_ragged_shapes_with_padding(M, N, K, fast):
+    """Row pitches padded past K with NaN codes (never read as data), output
+    rows padded (scalar stores), every output type."""
+    g = np.random.default_rng(M * 7 + N * 3 + K)
+    lda = (K + 7) // 8 * 8 + 8
+    ldb = (K + 7) // 8 * 8 + 16
+    a = np.full((M, lda), 0x7F, np.uint8); a[:, :K] = datagen.gauss_codes(g, (M, K), 64.0)
+    b = np.full((N, ldb), 0x7F, np.uint8); b[:, :K] = datagen.gauss_codes(g, (N, K), 64.0)
+    d = dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN, scale_a=np.float32(0.75), scale_b=np.float32(-0.375))
+    for i, dt in enumerate(DTYPES):
+        ldd = N + (3 if i % 2 else 0)
+        check_gemm(d, 0, 0, dt, fast, scale_result=np.float32(1 / 64) if dt in (E4M3FN, E5M2) else None,
+                   what=f"{M}x{N}x{K} {DT_NAME[dt]}", ldd=ldd)
+
+
+def test_zero_k_gives_scaled_zero():
+    a = np.zeros((20, 8), np.uint8); b = np.zeros((30, 8), np.uint8)
+    gpu = gu.scaled_gemm(a, 0, b, 0, 0, 2.0, 0, -1.0, 0, F32)
+    assert np.all(gpu == 0x80000000)        # (+0) * 2 * (-1) = -0
+    gpu = gu.scaled_gemm(a, 0, b, 0, 0, 2.0, 0, 1.0, 0, BF16)
+    assert np.all(gpu == 0)
+
+
+def test_nan_and_inf_inputs():
+    d = datagen.workload1(64, 80, 384)
+    a = d["a"].copy(); b = d["b"].copy()
+    a[5, 17] = 0x7F                          # E4M3 NaN code: row 5 is NaN everywhere
+    b_e5 = datagen.gauss_codes(np.random.default_rng(3), (80, 384), 4.0, E5M2)
+    b_e5[7, 100] = 0x7C                      # +Inf in column 7
+    dd = dict(a=a, b=b_e5, K=384, a_fmt=E4M3FN, b_fmt=E5M2, scale_a=np.float32(1), scale_b=np.float32(1))
+    for dt in (F32, BF16, E4M3FN):
+        _, gpu, value, _ = check_gemm(dd, 0, 0, dt, False, what=f"nan/inf {DT_NAME[dt]}")
+        assert np.all(gpu[5] == compare.CANON_NAN[dt])
+
+
+@pytest.mark.parametrize("fa,fb", [(E4M3FN, E5M2), (E5M2, E4M3FN), (E5M2, E5M2)])
+def test_mixed_and_e5m2_formats(fa, fb):
+    g = np.random.default_rng(fa * 2 + fb)
+    a = datagen.gauss_codes(g, (150, 640), 8.0, fa)
+    b = datagen.gauss_codes(g, (270, 640), 8.0, fb)
+    d = dict(a=a, b=b, K=640, a_fmt=fa, b_fmt=fb, scale_a=np.float32(0.5), scale_b=np.float32(0.125))
+    for dt in (F32, F16):
+        check_gemm(d, 0, 0, dt, False, what=f"mixed {fa}x{fb} {DT_NAME[dt]}")
+
+
+# ------------------------------------------------------------------ workload 3: block scales
+
+@pytest.mark.parametrize("sb_mode", [1, 2], ids=["1x128", "128x128"])
+@pytest.mark.parametrize("M,N,K", [(300, 400, 1000), (64, 256, 512), (260, 130, 4096)])
+def test_block_scales_small(M, N, K, sb_mode):
+    g = oracle  # noqa
+    rng = np.random.default_rng(M + N + K + sb_mode)
+    a = datagen.gauss_codes(rng, (M, K), 64.0)
+    b = datagen.gauss_codes(rng, (N, K), 64.0)
+    kb = -(-K // 128)
+    sa = datagen.log_uniform_scales(rng, (M, kb))
+    sb = datagen.log_uniform_scales(rng, (N if sb_mode == 1 else -(-N // 128), kb))
+    d = dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN, scale_a=sa, scale_b=sb)
+    for dt in (F32, BF16):
+        check_gemm(d, 1, sb_mode, dt, False, what=f"block {M}x{N}x{K} sb={sb_mode} {DT_NAME[dt]}")
+
+
+def test_workload3_full_size():
+    d = datagen.workload3()
+    check_gemm(d, 1, 2, BF16, False, rows=sample_rows(4096, 8), what="workload3 4096x14336x4096")
+
+
+# ------------------------------------------------------------------ workload 4: sf32 + amax
+
+def check_amax_case(w, c_type, rows=None):
+    c, amax, idx = gu.blockscaled_gemm_amax(w["a"], w["b"], w["ab_fmt"], w["sfa"], w["sfb"], c_type)
+    value, sabs, bits, _, _ = oracle.blockscaled_gemm_amax(w["a"], w["b"], w["ab_fmt"], w["sfa"], w["sfb"], 32,
+                                                           c_type, rows=rows)
+    cg = c if rows is None else c[:, rows]
+    compare.check(cg, value, sabs, bits, c_type, "sf32 gemm")
+    return c, amax, idx, value, sabs
+
+
+def test_sf32_amax_small_with_oracle():
+    w = datagen.workload4(3, 200, 136, 1024)
+    c, amax, idx, value, sabs = check_amax_case(w, F32)
+    cf = c.view(np.float32).astype(np.float64).reshape(-1)
+    # amax and its index are bit-exact against the GPU's own C
+    assert amax == float(np.max(np.abs(cf))) and idx == int(np.argmax(np.abs(cf)))
+    # and within the bound of the oracle's amax
+    v = np.abs(value.reshape(-1))
+    assert abs(amax - v.max()) <= 2.0 ** -20 * sabs.reshape(-1)[np.argmax(v)]
+
+
+@pytest.mark.parametrize("c_type", [BF16, F16])
+def test_sf32_low_precision_outputs(c_type):
+    w = datagen.workload4(2, 96, 200, 512)
+    c, amax, idx, value, sabs = check_amax_case(w, c_type)
+    # amax is taken before the cast: within the fp32 bound of the oracle's max |C|
+    v = np.abs(value.reshape(-1))
+    assert abs(amax - v.max()) <= 2.0 ** -20 * sabs.reshape(-1)[np.argmax(v)] + 0.0
+
+
+def test_sf32_batch_equals_separate_calls():
+    w = datagen.workload4(3, 72, 80, 256)
+    c, amax, idx = gu.blockscaled_gemm_amax(w["a"], w["b"], 0, w["sfa"], w["sfb"], F32)
+    best = None
+    for l in range(3):
+        cl, al, il = gu.blockscaled_gemm_amax(w["a"][l:l + 1], w["b"][l:l + 1], 0, w["sfa"][l:l + 1],
+                                              w["sfb"][l:l + 1], F32)
+        compare.assert_bitwise_equal(cl[0], c[l], f"batch item {l}")
+        cand = (al, -(l * 72 * 80 + il))
+        best = cand if best is None or cand > best else best
+    assert amax == best[0] and idx == -best[1]
+
+
+def test_sf32_nan_and_empty():
+    w = datagen.workload4(2, 40, 48, 128)
+    a = w["a"].copy(); a[1, 7, 3] = 0x7F
+    c, amax, idx = gu.blockscaled_gemm_amax(a, w["b"], 0, w["sfa"], w["sfb"], F32)
+    assert np.isnan(amax) and idx == 1 * 40 * 48 + 7 * 48 + 0
+    z = np.zeros((0, 40, 128), np.uint8)
+    c, amax, idx = gu.blockscaled_gemm_amax(z, np.zeros((0, 48, 128), np.uint8), 0, np.ones((0, 40, 4), np.float32),
+                                            np.ones((0, 48, 4), np.float32), F32)
+    assert amax == 0.0 and idx == -1
+
+
+def test_sf32_amax_without_index():
+    w = datagen.workload4(2, 100, 60, 256)
+    c, amax, _ = gu.blockscaled_gemm_amax(w["a"], w["b"], 0, w["sfa"], w["sfb"], F32, with_index=False)
+    assert amax == float(np.max(np.abs(c.view(np.float32))))
+
+
+def test_sf32_e5m2_unit_scales_is_plain_gemm():
+    """The cuDNN example shape (m, n, k = 512, 256, 256, sf 32, E5M2, all-ones scales)."""
+    g = np.random.default_rng(0)
+    a = datagen.gauss_codes(g, (1, 512, 256), 1.0, E5M2)
+    b = datagen.gauss_codes(g, (1, 256, 256), 1.0, E5M2)
+    w = dict(a=a, b=b, ab_fmt=E5M2, sfa=np.ones((1, 512, 8), np.float32), sfb=np.ones((1, 256, 8), np.float32))
+    check_amax_case(w, F32)
+
+
+def test_workload4_full_size():
+    w = datagen.workload4()
+    rows = sample_rows(2048, 4)
+    c, amax, idx, value, sabs = check_amax_case(w, F32, rows=rows)
+    cf = np.abs(c.view(np.float32).reshape(-1))
+    assert amax == float(cf.max()) and idx == int(np.argmax(cf))
+
+
+# ------------------------------------------------------------------ workload 5: K tail, FP8 / f16 out
+
+def test_workload5_small():
+    for d, dt, sr in ((datagen.workload5a(200, 300, 8200), E4M3FN, np.float32(1 / 16)),
+                      (datagen.workload5b(200, 300, 8200), F16, None)):
+        check_gemm(d, 0, 0, dt, False, scale_result=sr, what=f"workload5 small {DT_NAME[dt]}")
+
+
+def test_workload5a_saturation_edge():
+    d = datagen.workload5a(96, 160, 8200)
+    d["scale_a"] = np.float32(1.0); d["scale_b"] = np.float32(1.0)
+    _, gpu, value, _ = check_gemm(d, 0, 0, E4M3FN, False, scale_result=np.float32(1 / 16), what="saturation")
+    assert np.mean((gpu & 0x7F) == 0x7E) > 0.9       # almost every output saturates
+
+
+@pytest.mark.parametrize("which", ["5a", "5b"])
+def test_workload5_full_size(which):
+    if which == "5a":
+        d, dt, sr = datagen.workload5a(), E4M3FN, np.float32(1 / 16)
+    else:
+        d, dt, sr = datagen.workload5b(), F16, None
+    rows = np.array([0, 1, 2, 4095, 8190, 8191])
+    check_gemm(d, 0, 0, dt, False, rows=rows, scale_result=sr, what=f"workload5{which} full size")
