@@ -60,9 +60,10 @@ int cu_count() {
     return cache[dev];
 }
 
-// Largest workgroup tile that still gives every compute unit a tile.
-int choose_cfg(int64_t M, int64_t N, int64_t L, int cus) {
-    for (int c = 0; c < mmfp8::CFG_COUNT - 1; ++c) {
+// Largest workgroup tile (not larger than `first`) that still gives every
+// compute unit a tile.
+int choose_cfg(int64_t M, int64_t N, int64_t L, int cus, int first) {
+    for (int c = first; c < mmfp8::CFG_COUNT - 1; ++c) {
         const int64_t tiles = cdiv(M, mmfp8::kCfgBM[c]) * cdiv(N, mmfp8::kCfgBN[c]) * L;
         if (tiles >= cus) return c;
     }
@@ -149,7 +150,9 @@ mm_status mm_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, int a_t
         e = mmfp8::launch_skinny(mt, use_fast_accum ? mmfp8::MODE_FAST : mmfp8::MODE_SLOW, fa, fb, p, grid, s);
         return device_status(e, "mm_scaled_gemm (skinny) launch");
     }
-    const int cfg = choose_cfg(M, N, 1, cu_count());
+    const int mode = per_tensor ? (use_fast_accum ? mmfp8::MODE_FAST : mmfp8::MODE_SLOW) : mmfp8::MODE_BLOCK;
+    const int sbm = sb_mode == MM_SCALE_128x128 ? mmfp8::SB_128x128 : mmfp8::SB_1x128;
+    const int cfg = choose_cfg(M, N, 1, cu_count(), mmfp8::min_cfg(mode, sbm));
     p.tiles_m = (int)cdiv(M, mmfp8::kCfgBM[cfg]);
     p.tiles_n = (int)cdiv(N, mmfp8::kCfgBN[cfg]);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
@@ -157,7 +160,6 @@ mm_status mm_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, int a_t
         e = use_fast_accum ? mmfp8::launch_tile_fast(cfg, fa, fb, p, (int)grid, s)
                            : mmfp8::launch_tile_slow(cfg, fa, fb, p, (int)grid, s);
     } else {
-        const int sbm = sb_mode == MM_SCALE_128x128 ? mmfp8::SB_128x128 : mmfp8::SB_1x128;
         e = mmfp8::launch_tile_block(cfg, sbm, fa, fb, p, (int)grid, s);
     }
     return device_status(e, "mm_scaled_gemm launch");
@@ -229,7 +231,7 @@ mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L, c
         p.vec_store = (N % 4 == 0);
         p.amax_bits = amax_bits;
         p.amax_key = key;
-        const int cfg = choose_cfg(M, N, L, cu_count());
+        const int cfg = choose_cfg(M, N, L, cu_count(), mmfp8::min_cfg(mmfp8::MODE_SF32, 0));
         p.tiles_m = (int)cdiv(M, mmfp8::kCfgBM[cfg]);
         p.tiles_n = (int)cdiv(N, mmfp8::kCfgBN[cfg]);
         const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * L;

@@ -10,14 +10,21 @@
 //
 // Hardware facts this file relies on (measured on MI355X with in-bounds
 // probes, see the design notes):
-//  * v_mfma_scale_f32_16x16x128_f8f6f4: lane l = r + 16 g (r = l & 15,
-//    g = l >> 4) supplies row r of each operand. Bytes 0..15 of its 8 VGPRs are
-//    k = 16g .. 16g+15 and bytes 16..31 are k = 64+16g .. 64+16g+15; the E8M0
-//    scale of 32-element block b (k = 32b .. 32b+31) is taken from lane group
-//    b. The result D[i][j] (i from the first operand, j from the second) is in
-//    lane j + 16 (i / 4), register i % 4.
-//  * The MFMA adds C to the product sum with one round-to-nearest-even; C is
-//    not scaled; fp32 subnormal results are kept.
+//  * The FP8 MFMAs of gfx950 (v_mfma_scale_f32_16x16x128_f8f6f4 and the older
+//    fp8 ones) do not sum their products exactly: small products that share an
+//    adder group with large ones lose low bits, up to ~2^-16.5 * sum|t| per
+//    128 products on Gaussian data, which is outside the 2^-20 * sum|t| bound
+//    this library guarantees. v_mfma_f32_16x16x32_bf16 forms exact products and
+//    accumulates to ~2^-26 * sum|t|. Every FP8 value (E4M3 and E5M2) is exactly
+//    a bf16 value, so the kernels convert FP8 to bf16 in registers
+//    (v_cvt_scalef32_pk_bf16_fp8 / _bf8, with a power-of-two scale that is
+//    exact) and contract with the bf16 MFMA.
+//  * 16x16 MFMA results: D[i][j] (i from the first operand, j from the
+//    second) is in lane j + 16 (i / 4), register i % 4. Both operands use the
+//    same lane layout, so any assignment of k to (lane group, element) that is
+//    the same for A and B gives the same sum.
+//  * The MFMA adds C to the product sum with one round-to-nearest-even; fp32
+//    subnormal results are kept.
 //  * Buffer loads check the range per dword: a dword past num_records reads 0.
 //  * buffer_load ... lds writes lane l's 16 bytes to LDS base + 16 l.
 //  * v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 round to nearest even but do not
@@ -34,6 +41,8 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -47,7 +56,6 @@ enum : int { SB_1x128 = 0, SB_128x128 = 1 };
 constexpr int kBK = 128;                 // K per main-loop step = one MFMA = one 128-element chunk
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 buffer descriptor dword 3 (raw, 32-bit format)
 constexpr uint32_t kOOB = 0x80000000u;   // a voffset beyond any extent: loads return 0
-constexpr int kNeutralE8M0 = 127;        // E8M0 code of 1.0
 
 struct GemmArgs {
     const uint8_t* a;   // [L][M] rows of lda bytes
@@ -84,21 +92,43 @@ __device__ __forceinline__ uint32_t operand_extent(int rows, int64_t ld, int K) 
     return (uint32_t)((e + 3) & ~(int64_t)3);
 }
 
-// The format codes of the f8f6f4 MFMA are immediates, so they are template
-// arguments: 0 = E4M3 (fp8), 1 = E5M2 (bf8).
-template <int F1, int F2>
-__device__ __forceinline__ f32x4 mfma(const i32x8& first, const i32x8& second, const f32x4& c,
-                                      int scale_first, int scale_second) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, c, F1, F2, 0, scale_first, 0,
-                                                            scale_second);
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& first, const bf16x8& second, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(first, second, c, 0, 0, 0);
+}
+
+// Two FP8 codes (bytes 2 hi, 2 hi + 1 of w) to two bf16 values times `scale`.
+// F = 0: E4M3, F = 1: E5M2. Exact: every FP8 value is a bf16 value and the
+// scales used here are powers of two.
+template <int F, bool HI>
+__device__ __forceinline__ bf16x2 cvt2(uint32_t w, float scale) {
+    if constexpr (F == 0) return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI);
+    else return __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, scale, HI);
+}
+
+// Bytes 8 s .. 8 s + 7 of a lane's 32-byte FP8 fragment as one bf16 MFMA operand.
+template <int F>
+__device__ __forceinline__ bf16x8 to_bf16x8(const i32x8& f, int s, float scale) {
+    const uint32_t w0 = (uint32_t)f[2 * s], w1 = (uint32_t)f[2 * s + 1];
+    const bf16x2 p0 = cvt2<F, false>(w0, scale), p1 = cvt2<F, true>(w0, scale);
+    const bf16x2 p2 = cvt2<F, false>(w1, scale), p3 = cvt2<F, true>(w1, scale);
+    const auto lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+    const auto hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// E8M0 code of a power-of-two fp32 scale factor: its exponent field.
-__device__ __forceinline__ int e8m0_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFFu); }
+// The E8M0 value carried by an fp32 scale factor: 2^(e - 127) for its
+// exponent field e; field 0 (zero, subnormals) is 2^-127 and field 255 (Inf,
+// NaN) is NaN. The mantissa is ignored.
+__device__ __forceinline__ float e8m0_scale(float s) {
+    const uint32_t e = (__float_as_uint(s) >> 23) & 0xFFu;
+    if (e == 0) return __uint_as_float(0x00400000u);
+    if (e == 255) return __uint_as_float(0x7FC00000u);
+    return __uint_as_float(e << 23);
+}
 
 // ------------------------------------------------------------------ output conversions
 
@@ -314,10 +344,11 @@ __global__ void __launch_bounds__(256, 1) gemm_tile(GemmArgs p) {
         for (int q = 0; q < B_INS; ++q) fix(sbase + BM * kBK + (wave * B_INS + q) * 1024 + lane * 16);
     };
 
-    // Fragment reads: lane (r, g) takes chunks g and 4 + g of row r.
+    // Fragment reads: lane (r, g) takes chunks 2g and 2g + 1 of row r, i.e.
+    // k = 32g .. 32g + 31 of the step: one 32-element scale group per lane.
     const int fr = lane & 15, fg = lane >> 4;
-    const int foff0 = fr * kBK + ((fg ^ (fr & 7)) << 4);
-    const int foff1 = fr * kBK + (((4 + fg) ^ (fr & 7)) << 4);
+    const int foff0 = fr * kBK + (((2 * fg) ^ (fr & 7)) << 4);
+    const int foff1 = fr * kBK + (((2 * fg + 1) ^ (fr & 7)) << 4);
 
     f32x4 acc[FN][FM];
 #pragma unroll
@@ -350,7 +381,7 @@ __global__ void __launch_bounds__(256, 1) gemm_tile(GemmArgs p) {
         // scales of this step
         float s_a[FM];
         float s_b[FN][4];
-        int e_a[FM], e_b[FN];
+        float c_a[FM], c_b[FN];  // per-lane conversion scales (SF32: this lane's 32-group)
         if (MODE == MODE_BLOCK) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) s_a[i] = sa_l[(int64_t)srow_a[i] * p.sa_ld + kt];
@@ -365,13 +396,19 @@ __global__ void __launch_bounds__(256, 1) gemm_tile(GemmArgs p) {
                     for (int r = 0; r < 4; ++r) s_b[j][r] = sb_l[(int64_t)min(srow_b[j] + r, p.N - 1) * p.sb_ld + kt];
                 }
             }
-        } else if (MODE == MODE_SF32) {
+        }
+        if (MODE == MODE_SF32) {
             const int grp = kt * 4 + fg;
             const bool gv = grp < p.sa_ld;  // groups past ceil(K/32) hold zero data
 #pragma unroll
-            for (int i = 0; i < FM; ++i) e_a[i] = gv ? e8m0_of(sa_l[(int64_t)srow_a[i] * p.sa_ld + grp]) : kNeutralE8M0;
+            for (int i = 0; i < FM; ++i) c_a[i] = gv ? e8m0_scale(sa_l[(int64_t)srow_a[i] * p.sa_ld + grp]) : 1.0f;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) e_b[j] = gv ? e8m0_of(sb_l[(int64_t)srow_b[j] * p.sb_ld + grp]) : kNeutralE8M0;
+            for (int j = 0; j < FN; ++j) c_b[j] = gv ? e8m0_scale(sb_l[(int64_t)srow_b[j] * p.sb_ld + grp]) : 1.0f;
+        } else {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) c_a[i] = 1.0f;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) c_b[j] = 1.0f;
         }
 
         const uint8_t* As = cur;
@@ -382,18 +419,42 @@ __global__ void __launch_bounds__(256, 1) gemm_tile(GemmArgs p) {
             const uint8_t* base = As + (wm * WTM + i * 16) * kBK;
             af[i] = cat(*(const i32x4*)(base + foff0), *(const i32x4*)(base + foff1));
         }
+        if (MODE == MODE_FAST || MODE == MODE_SF32) {
+            // one chain over K: sub-step s outermost keeps only one bf16 operand set live
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const uint8_t* base = Bs + (wn * WTN + j * 16) * kBK;
-            const i32x8 bf = cat(*(const i32x4*)(base + foff0), *(const i32x4*)(base + foff1));
+            for (int s = 0; s < 4; ++s) {
+                bf16x8 ab[FM];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                if (MODE == MODE_FAST) {
-                    acc[j][i] = mfma<FB, FA>(bf, af[i], acc[j][i], kNeutralE8M0, kNeutralE8M0);
-                } else if (MODE == MODE_SF32) {
-                    acc[j][i] = mfma<FB, FA>(bf, af[i], acc[j][i], e_b[j], e_a[i]);
-                } else {
-                    const f32x4 part = mfma<FB, FA>(bf, af[i], f32x4{0.f, 0.f, 0.f, 0.f}, kNeutralE8M0, kNeutralE8M0);
+                for (int i = 0; i < FM; ++i) ab[i] = to_bf16x8<FA>(af[i], s, c_a[i]);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const uint8_t* base = Bs + (wn * WTN + j * 16) * kBK;
+                    const i32x4 bw = *(const i32x4*)(base + (s < 2 ? foff0 : foff1));
+                    const i32x8 bf = cat(bw, bw);
+                    const bf16x8 bb = to_bf16x8<FB>(bf, s & 1, c_b[j]);
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) acc[j][i] = mfma_bf16(bb, ab[i], acc[j][i]);
+                }
+            }
+        } else {
+            // a fresh fp32 partial per 128-chunk, then promoted into the accumulator
+            bf16x8 ab[FM][4];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) ab[i][s] = to_bf16x8<FA>(af[i], s, 1.0f);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const uint8_t* base = Bs + (wn * WTN + j * 16) * kBK;
+                const i32x8 bf = cat(*(const i32x4*)(base + foff0), *(const i32x4*)(base + foff1));
+                bf16x8 bb[4];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) bb[s] = to_bf16x8<FB>(bf, s, 1.0f);
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) part = mfma_bf16(bb[s], ab[i][s], part);
                     if (MODE == MODE_SLOW) {
                         acc[j][i] += part;
                     } else {
@@ -452,7 +513,7 @@ __global__ void __launch_bounds__(256, 1) gemm_tile(GemmArgs p) {
 // ------------------------------------------------------------------ skinny kernel
 //
 // For M <= 16 * MT (MT <= 4) with per-tensor scales: the run is bound by
-// streaming B once from HBM. A workgroup owns 16 columns of the output; its 4
+// streaming B once from HBM. Each lane holds k = 32 g .. 32 g + 31 of its row. A workgroup owns 16 columns of the output; its 4
 // waves split the K steps round-robin (wave w takes steps w, w+4, ...), load
 // their B and A fragments straight from memory into registers (A is small and
 // stays in L2), keep kU steps in flight, and add their partial tiles in LDS in
@@ -466,21 +527,21 @@ __global__ void __launch_bounds__(256) gemm_skinny(GemmArgs p) {
     const int fr = lane & 15, fg = lane >> 4;
     const rsrc_t rb = make_rsrc(p.b + (int64_t)n0 * p.ldb, operand_extent(min(16, p.N - n0), p.ldb, K));
     const rsrc_t ra = make_rsrc(p.a, operand_extent(p.M, p.lda, K));
-    const uint32_t boff = (uint32_t)(fr * p.ldb + 16 * fg);
+    const uint32_t boff = (uint32_t)(fr * p.ldb + 32 * fg);
     uint32_t aoff[MT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) aoff[i] = (uint32_t)((i * 16 + fr) * p.lda + 16 * fg);
+    for (int i = 0; i < MT; ++i) aoff[i] = (uint32_t)((i * 16 + fr) * p.lda + 32 * fg);
 
     struct Frag {
         i32x8 b;
         i32x8 a[MT];
     };
-    // Load step kt: chunk k = 128 kt + 16 fg and 128 kt + 64 + 16 fg of each row.
+    // Load step kt: k = 128 kt + 32 fg .. + 31 of each row, as two 16-byte chunks.
     auto load = [&](int kt, Frag& f) {
-        const int k0 = kt * kBK + 16 * fg;
-        const int k1 = k0 + 64;
+        const int k0 = kt * kBK + 32 * fg;
+        const int k1 = k0 + 16;
         const bool tail = kt * kBK + kBK > K;
-        uint32_t o0 = (uint32_t)(kt * kBK), o1 = (uint32_t)(kt * kBK + 64);
+        uint32_t o0 = (uint32_t)(kt * kBK), o1 = (uint32_t)(kt * kBK + 16);
         // chunks starting at or past K read zero; a straddling chunk is masked below
         const bool z0 = tail && k0 >= K, z1 = tail && k1 >= K;
         i32x4 b0 = __builtin_amdgcn_raw_buffer_load_b128(rb, z0 ? kOOB : boff + o0, 0, 0);
@@ -495,10 +556,10 @@ __global__ void __launch_bounds__(256) gemm_skinny(GemmArgs p) {
     };
     auto mask = [&](int kt, Frag& f) {
         // zero bytes at k >= K in a chunk straddling K (only in the last step)
-        const int k0 = kt * kBK + 16 * fg;
+        const int k0 = kt * kBK + 32 * fg;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int ks = k0 + 64 * h;
+            const int ks = k0 + 16 * h;
             if (ks < K && K < ks + 16) {
                 const int valid = K - ks;
 #pragma unroll
@@ -531,13 +592,16 @@ __global__ void __launch_bounds__(256) gemm_skinny(GemmArgs p) {
                 const int kt = wave + 4 * s;
                 if (s + kU < nsteps) load(wave + 4 * (s + kU), buf[u]);
                 if (kt * kBK + kBK > K && (K & 15)) mask(kt, cur);
+                bf16x8 bb[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) bb[q] = to_bf16x8<FB>(cur.b, q, 1.0f);
 #pragma unroll
                 for (int i = 0; i < MT; ++i) {
-                    if (MODE == MODE_FAST) {
-                        acc[i] = mfma<FB, FA>(cur.b, cur.a[i], acc[i], kNeutralE8M0, kNeutralE8M0);
-                    } else {
-                        acc[i] += mfma<FB, FA>(cur.b, cur.a[i], f32x4{0.f, 0.f, 0.f, 0.f}, kNeutralE8M0, kNeutralE8M0);
-                    }
+                    f32x4 part = MODE == MODE_FAST ? acc[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) part = mfma_bf16(bb[q], to_bf16x8<FA>(cur.a[i], q, 1.0f), part);
+                    if (MODE == MODE_FAST) acc[i] = part;
+                    else acc[i] += part;
                 }
             }
         }
