@@ -22,6 +22,16 @@ MM_OK, MM_ERR_INVALID_ARGUMENT, MM_ERR_UNSUPPORTED, MM_ERR_MISALIGNED, MM_ERR_DE
 MM_F8_E4M3FN, MM_F8_E5M2, MM_F32, MM_BF16, MM_F16 = 0, 1, 2, 3, 4
 MM_SCALE_TENSOR, MM_SCALE_1x128, MM_SCALE_128x128 = 0, 1, 2
 
+# One HIP runtime per process. PyTorch ships its own HIP runtime with the same
+# soname as the system one libmmfp8 is linked against; loaded first, it also
+# serves libmmfp8. Loaded the other way round, the process ends up with two
+# runtimes, and the one initialised second finds no GPU. So torch, when it is
+# installed, is imported before the library.
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:
+    _torch = None
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_scaled_gemm_amd.build` "
                       "(or __graft_entry__.build()); there is no CPU fallback")

@@ -116,6 +116,17 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const i32x8& f, int s, float scale) 
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Bytes 8 q .. 8 q + 7 (q = 0, 1) of a 16-byte FP8 chunk as one bf16 MFMA operand.
+template <int F>
+__device__ __forceinline__ bf16x8 to_bf16x8(const i32x4& f, int q, float scale) {
+    const uint32_t w0 = (uint32_t)f[2 * q], w1 = (uint32_t)f[2 * q + 1];
+    const bf16x2 p0 = cvt2<F, false>(w0, scale), p1 = cvt2<F, true>(w0, scale);
+    const bf16x2 p2 = cvt2<F, false>(w1, scale), p3 = cvt2<F, true>(w1, scale);
+    const auto lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+    const auto hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 __device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -257,31 +268,40 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int t
 
 // ------------------------------------------------------------------ tiled kernel
 //
-// Workgroup tile BM x BN, 4 waves in a 2 x 2 grid, each wave (BM/2) x (BN/2)
-// made of 16 x 16 MFMA tiles. The MFMA's first operand is b (rows n) and its
-// second is a (rows m), so every lane's results share one m and hold 4
-// consecutive n: one scale_a value per lane, vector stores along N.
+// Workgroup tile BM x BN computed by WM x WN waves, each wave a
+// (BM/WM) x (BN/WN) block of 16 x 16 MFMA tiles. The MFMA's first operand is b
+// (rows n) and its second is a (rows m), so every lane's results share one m
+// and hold 4 consecutive n: one scale_a value per lane, vector stores along N.
 //
-// K is walked in steps of 128 (= one MFMA, = one "slow" chunk, = one 1x128
-// scale block, = four 32-element MX groups). Each step's A and B tiles go from
-// HBM straight to LDS with buffer_load ... lds (two stages), rows 128 bytes,
-// the 16-byte chunk c of row r stored at chunk c ^ (r & 7) so that the
-// fragment reads are free of bank conflicts.
-template <int BM, int BN, int MODE, int FA, int FB, int SBM>
-__global__ void __launch_bounds__(256, 1) gemm_tile(GemmArgs p) {
-    constexpr int NT = 256;
-    constexpr int WTM = BM / 2, WTN = BN / 2;
+// K is walked in steps of 128 (= one "slow" chunk = one 1x128 scale block =
+// four 32-element MX groups). Each step's A and B tiles go from memory straight
+// to LDS with buffer_load ... lds through STAGES rotating buffers; rows are 128
+// bytes with the 16-byte chunk c of row r stored at chunk c ^ swz(r),
+// swz(r) = (r & 7) ^ ((r >> 3) & 1): any 8 consecutive rows, and any 16
+// consecutive rows split by row parity, then hit distinct banks at one
+// logical chunk, so the fragment reads are free of bank conflicts. Lane (r, g) of a fragment holds
+// k = 32g .. 32g+31 of row r (one MX group), converted to bf16 8 values at a
+// time for the four v_mfma_f32_16x16x32_bf16 of the step.
+template <int BM, int BN, int WM, int WN, int STAGES, int MODE, int FA, int FB, int SBM>
+__global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
+    constexpr int NW = WM * WN;
+    constexpr int NT = NW * 64;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
-    constexpr int A_INS = BM / 32, B_INS = BN / 32;  // 1 KB LDS writes per wave per step (tile rows / 8 / 4 waves)
+    constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;  // 1 KB LDS-DMA writes per wave per step
+    constexpr int INS = A_INS + B_INS;
+    static_assert(A_INS * 8 * NW == BM && B_INS * 8 * NW == BN, "tile rows must split evenly over the waves");
+    static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
     constexpr int STAGE = (BM + BN) * kBK;
-    // Two distinct LDS objects (not one array indexed by stage) so that the
-    // compiler can tell a fragment read of one stage from the in-flight LDS-DMA
-    // writes into the other and does not wait for those loads.
+    // Distinct LDS objects (not one array indexed by stage) so that the compiler
+    // can tell a fragment read of one stage from the in-flight LDS-DMA writes
+    // into another and does not wait for those loads.
     __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem2[STAGES == 3 ? STAGE : 16];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     int l, tm, tn;
     tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, 8, l, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -296,39 +316,56 @@ __global__ void __launch_bounds__(256, 1) gemm_tile(GemmArgs p) {
     // Loader: wave-instruction q of a tile writes LDS bytes [1024 q, 1024 q + 1024),
     // i.e. rows 8q .. 8q+7; lane l fills row 8q + l/8, stored chunk l%8, which
     // holds logical chunk (l%8) ^ (row & 7) = (l%8) ^ (l/8).
+    // The row of wave-instruction q is 8 q + ld_row, so swz(row) = ld_row ^ (q & 1).
     const int ld_row = lane >> 3;
-    const int ld_chunk = (lane & 7) ^ ld_row;
+    auto ld_chunk = [&](int ins) { return (lane & 7) ^ ld_row ^ (ins & 1); };
     const bool k_tail = (K % kBK) != 0;
+    uint32_t aoff[A_INS], boff[B_INS];
+    int achunk[A_INS], bchunk[B_INS];
+#pragma unroll
+    for (int q = 0; q < A_INS; ++q) {
+        achunk[q] = ld_chunk(wave * A_INS + q);
+        aoff[q] = (uint32_t)(((wave * A_INS + q) * 8 + ld_row) * p.lda + achunk[q] * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < B_INS; ++q) {
+        bchunk[q] = ld_chunk(wave * B_INS + q);
+        boff[q] = (uint32_t)(((wave * B_INS + q) * 8 + ld_row) * p.ldb + bchunk[q] * 16);
+    }
 
     auto issue = [&](int kt, uint8_t* sbase) {
-        const int k0 = kt * kBK + ld_chunk * 16;
+        const uint32_t kb = (uint32_t)(kt * kBK);
+        // in the last step of a ragged K, chunks starting at or past K read zero
         const bool last = k_tail && kt == KT - 1;
+        // Steps past the end are issued too, with every offset out of range: they
+        // fetch nothing and zero a stage no later step reads, and keep the number
+        // of loads per step constant for the vmcnt bookkeeping.
+        const bool dead = kt >= KT;
+        // (the offsets are computed in statements: clang 22 drops the host stub of
+        // this kernel when a conditional expression is passed to the builtin)
 #pragma unroll
         for (int q = 0; q < A_INS; ++q) {
-            const int ins = wave * A_INS + q;
-            const int row = ins * 8 + ld_row;
-            uint32_t off = (uint32_t)(row * p.lda + k0);
-            if (last && k0 >= K) off = kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sbase + ins * 1024), 16, off, 0, 0, 0);
+            uint32_t off = aoff[q] + kb;
+            if (dead || (last && (int)kb + achunk[q] * 16 >= K)) off = kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sbase + (wave * A_INS + q) * 1024), 16, off, 0,
+                                                     0, 0);
         }
 #pragma unroll
         for (int q = 0; q < B_INS; ++q) {
-            const int ins = wave * B_INS + q;
-            const int row = ins * 8 + ld_row;
-            uint32_t off = (uint32_t)(row * p.ldb + k0);
-            if (last && k0 >= K) off = kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sbase + BM * kBK + ins * 1024), 16, off, 0, 0,
-                                                     0);
+            uint32_t off = boff[q] + kb;
+            if (dead || (last && (int)kb + bchunk[q] * 16 >= K)) off = kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sbase + BM * kBK + (wave * B_INS + q) * 1024),
+                                                     16, off, 0, 0, 0);
         }
     };
     // In the last step of a K that is not a multiple of 16, a chunk straddling K
     // holds bytes of the next row (or padding): zero them in this lane's own
     // LDS slots once its loads have landed.
     auto mask_straddle = [&](int kt, uint8_t* sbase) {
-        const int k0 = kt * kBK + ld_chunk * 16;
-        if (!(k0 < K && K < k0 + 16)) return;
-        const int valid = K - k0;
-        auto fix = [&](uint8_t* slot) {
+        auto fix = [&](uint8_t* slot, int chunk) {
+            const int k0 = kt * kBK + chunk * 16;
+            if (!(k0 < K && K < k0 + 16)) return;
+            const int valid = K - k0;
             i32x4 v = *(i32x4*)slot;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
@@ -339,16 +376,17 @@ __global__ void __launch_bounds__(256, 1) gemm_tile(GemmArgs p) {
             *(i32x4*)slot = v;
         };
 #pragma unroll
-        for (int q = 0; q < A_INS; ++q) fix(sbase + (wave * A_INS + q) * 1024 + lane * 16);
+        for (int q = 0; q < A_INS; ++q) fix(sbase + (wave * A_INS + q) * 1024 + lane * 16, achunk[q]);
 #pragma unroll
-        for (int q = 0; q < B_INS; ++q) fix(sbase + BM * kBK + (wave * B_INS + q) * 1024 + lane * 16);
+        for (int q = 0; q < B_INS; ++q) fix(sbase + BM * kBK + (wave * B_INS + q) * 1024 + lane * 16, bchunk[q]);
     };
 
     // Fragment reads: lane (r, g) takes chunks 2g and 2g + 1 of row r, i.e.
     // k = 32g .. 32g + 31 of the step: one 32-element scale group per lane.
     const int fr = lane & 15, fg = lane >> 4;
-    const int foff0 = fr * kBK + (((2 * fg) ^ (fr & 7)) << 4);
-    const int foff1 = fr * kBK + (((2 * fg + 1) ^ (fr & 7)) << 4);
+    const int fsw = (fr & 7) ^ (fr >> 3);  // swz of the fragment's row (fragments start at multiples of 16)
+    const int foff0 = fr * kBK + (((2 * fg) ^ fsw) << 4);
+    const int foff1 = fr * kBK + (((2 * fg + 1) ^ fsw) << 4);
 
     f32x4 acc[FN][FM];
 #pragma unroll
@@ -370,13 +408,59 @@ __global__ void __launch_bounds__(256, 1) gemm_tile(GemmArgs p) {
     const float* sa_l = p.sa + (int64_t)l * p.sa_batch;
     const float* sb_l = p.sb + (int64_t)l * p.sb_batch;
 
-    // One main-loop step: wait for this step's tiles, release the other stage
-    // to the next step's loads, then run the MFMAs on this stage.
-    auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
-        __builtin_amdgcn_s_waitcnt(0);
+    // Scales of one step, loaded one step ahead of their use (before that step's
+    // LDS-DMA loads are issued, so waiting for them never waits for those).
+    // Raw values only: anything computed from them here would pull the wait forward.
+    struct StepScales {
+        float a[FM];       // BLOCK: s_a of the fragment row; SF32: the lane's group scale
+        float b[FN][4];    // BLOCK: s_b of the 4 accumulator rows; SF32: b[j][0] per lane
+    };
+    auto load_scales = [&](int kt) {
+        StepScales sc;
+        if (KT == 0) return sc;  // K = 0: no step reads them (and the tables may be empty)
+        kt = min(kt, KT - 1);    // the prefetch past the last step reads a valid entry
+        if (MODE == MODE_BLOCK) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) sc.a[i] = sa_l[(int64_t)srow_a[i] * p.sa_ld + kt];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                if (SBM == SB_128x128) {
+                    sc.b[j][0] = sb_l[(int64_t)srow_b[j] * p.sb_ld + kt];
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sc.b[j][r] = sb_l[(int64_t)min(srow_b[j] + r, p.N - 1) * p.sb_ld + kt];
+                }
+            }
+        }
+        if (MODE == MODE_SF32) {
+            // groups past ceil(K/32) hold zero data; the clamp keeps the read in range
+            const int grp = min(kt * 4 + fg, p.sa_ld - 1);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) sc.a[i] = sa_l[(int64_t)srow_a[i] * p.sa_ld + grp];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) sc.b[j][0] = sb_l[(int64_t)srow_b[j] * p.sb_ld + grp];
+        }
+        return sc;
+    };
+    StepScales sc_cur;
+    if (MODE == MODE_BLOCK || MODE == MODE_SF32) sc_cur = load_scales(0);
+
+    // One main-loop step: wait for this step's tiles (the next step's may stay
+    // in flight), release the oldest stage to the loads STAGES-1 steps ahead,
+    // then run the MFMAs on this stage.
+    auto step = [&](int kt, uint8_t* cur, uint8_t* ahead) {
+        // Every step issues INS loads (after its scale loads), so vmcnt(INS)
+        // waits for this step's stage only. (__syncthreads() below then waits
+        // for everything: its workgroup fence makes the compiler drain the
+        // global->LDS loads. Issuing those loads by hand, untracked, with a
+        // fence-free barrier that keeps a stage in flight, measured no faster.)
+        constexpr int kWait = STAGES == 3 ? INS : 0;
+        __builtin_amdgcn_s_waitcnt((kWait & 15) | ((kWait >> 4) << 14) | (7 << 4) | (15 << 8));
         if (k_tail && kt == KT - 1 && (K & 15)) mask_straddle(kt, cur);
         __syncthreads();
-        if (kt + 1 < KT) issue(kt + 1, nxt);
+        StepScales sc_next;
+        if (MODE == MODE_BLOCK || MODE == MODE_SF32) sc_next = load_scales(kt + 1);
+        issue(kt + STAGES - 1, ahead);
 
         // scales of this step
         float s_a[FM];
@@ -384,92 +468,100 @@ __global__ void __launch_bounds__(256, 1) gemm_tile(GemmArgs p) {
         float c_a[FM], c_b[FN];  // per-lane conversion scales (SF32: this lane's 32-group)
         if (MODE == MODE_BLOCK) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) s_a[i] = sa_l[(int64_t)srow_a[i] * p.sa_ld + kt];
+            for (int i = 0; i < FM; ++i) s_a[i] = sc_cur.a[i];
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                if (SBM == SB_128x128) {
-                    const float v = sb_l[(int64_t)srow_b[j] * p.sb_ld + kt];
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) s_b[j][r] = v;
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) s_b[j][r] = sb_l[(int64_t)min(srow_b[j] + r, p.N - 1) * p.sb_ld + kt];
-                }
-            }
+                for (int r = 0; r < 4; ++r) s_b[j][r] = SBM == SB_128x128 ? sc_cur.b[j][0] : sc_cur.b[j][r];
         }
         if (MODE == MODE_SF32) {
-            const int grp = kt * 4 + fg;
-            const bool gv = grp < p.sa_ld;  // groups past ceil(K/32) hold zero data
+            const bool gv = kt * 4 + fg < p.sa_ld;  // groups past ceil(K/32) hold zero data
 #pragma unroll
-            for (int i = 0; i < FM; ++i) c_a[i] = gv ? e8m0_scale(sa_l[(int64_t)srow_a[i] * p.sa_ld + grp]) : 1.0f;
+            for (int i = 0; i < FM; ++i) c_a[i] = gv ? e8m0_scale(sc_cur.a[i]) : 1.0f;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) c_b[j] = gv ? e8m0_scale(sb_l[(int64_t)srow_b[j] * p.sb_ld + grp]) : 1.0f;
+            for (int j = 0; j < FN; ++j) c_b[j] = gv ? e8m0_scale(sc_cur.b[j][0]) : 1.0f;
         } else {
 #pragma unroll
             for (int i = 0; i < FM; ++i) c_a[i] = 1.0f;
 #pragma unroll
             for (int j = 0; j < FN; ++j) c_b[j] = 1.0f;
         }
+        if (MODE == MODE_BLOCK || MODE == MODE_SF32) sc_cur = sc_next;
 
-        const uint8_t* As = cur;
-        const uint8_t* Bs = cur + BM * kBK;
-        i32x8 af[FM];
+        const uint8_t* As = cur + wm * WTM * kBK;
+        const uint8_t* Bs = cur + BM * kBK + wn * WTN * kBK;
+        // Fast / MX: one chain over K straight into the accumulators. Slow / block:
+        // a fresh fp32 partial per 128-chunk, promoted into the accumulator after.
+        constexpr bool chain = MODE == MODE_FAST || MODE == MODE_SF32;
+        f32x4 part[chain ? 1 : FN][chain ? 1 : FM];
+        if constexpr (!chain) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const uint8_t* base = As + (wm * WTM + i * 16) * kBK;
-            af[i] = cat(*(const i32x4*)(base + foff0), *(const i32x4*)(base + foff1));
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int i = 0; i < FM; ++i) part[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        if (MODE == MODE_FAST || MODE == MODE_SF32) {
-            // one chain over K: sub-step s outermost keeps only one bf16 operand set live
+        // The lane's 32 bytes are read as two 16-byte halves (sub-steps 0-1, 2-3),
+        // which keeps the live FP8 operands to 4 registers per fragment.
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+        for (int h = 0; h < 2; ++h) {
+            // keep the scheduler from hoisting the second half's reads and converts
+            // above the first half's MFMAs (that costs registers, not time)
+            if (h) __builtin_amdgcn_sched_barrier(0);
+            const int fo = h ? foff1 : foff0;
+            i32x4 ar[FM], br[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) ar[i] = *(const i32x4*)(As + i * 16 * kBK + fo);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) br[j] = *(const i32x4*)(Bs + j * 16 * kBK + fo);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
                 bf16x8 ab[FM];
 #pragma unroll
-                for (int i = 0; i < FM; ++i) ab[i] = to_bf16x8<FA>(af[i], s, c_a[i]);
+                for (int i = 0; i < FM; ++i) ab[i] = to_bf16x8<FA>(ar[i], q, c_a[i]);
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    const uint8_t* base = Bs + (wn * WTN + j * 16) * kBK;
-                    const i32x4 bw = *(const i32x4*)(base + (s < 2 ? foff0 : foff1));
-                    const i32x8 bf = cat(bw, bw);
-                    const bf16x8 bb = to_bf16x8<FB>(bf, s & 1, c_b[j]);
+                    const bf16x8 bb = to_bf16x8<FB>(br[j], q, c_b[j]);
 #pragma unroll
-                    for (int i = 0; i < FM; ++i) acc[j][i] = mfma_bf16(bb, ab[i], acc[j][i]);
-                }
-            }
-        } else {
-            // a fresh fp32 partial per 128-chunk, then promoted into the accumulator
-            bf16x8 ab[FM][4];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) ab[i][s] = to_bf16x8<FA>(af[i], s, 1.0f);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const uint8_t* base = Bs + (wn * WTN + j * 16) * kBK;
-                const i32x8 bf = cat(*(const i32x4*)(base + foff0), *(const i32x4*)(base + foff1));
-                bf16x8 bb[4];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) bb[s] = to_bf16x8<FB>(bf, s, 1.0f);
-#pragma unroll
-                for (int i = 0; i < FM; ++i) {
-                    f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) part = mfma_bf16(bb[s], ab[i][s], part);
-                    if (MODE == MODE_SLOW) {
-                        acc[j][i] += part;
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[j][i][r] = __builtin_fmaf(part[r], s_a[i] * s_b[j][r], acc[j][i][r]);
+                    for (int i = 0; i < FM; ++i) {
+                        if constexpr (chain) acc[j][i] = mfma_bf16(bb, ab[i], acc[j][i]);
+                        else part[j][i] = mfma_bf16(bb, ab[i], part[j][i]);
                     }
                 }
             }
         }
+        if constexpr (!chain) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    if (MODE == MODE_SLOW) {
+                        acc[j][i] += part[j][i];
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[j][i][r] = __builtin_fmaf(part[j][i][r], s_a[i] * s_b[j][r], acc[j][i][r]);
+                    }
+                }
+        }
     };
-    if (KT > 0) issue(0, smem0);
-    for (int kt = 0; kt < KT; kt += 2) {
-        step(kt, smem0, smem1);
-        if (kt + 1 < KT) step(kt + 1, smem1, smem0);
+    if constexpr (STAGES == 2) {
+        issue(0, smem0);
+        for (int kt = 0; kt < KT; kt += 2) {
+            step(kt, smem0, smem1);
+            if (kt + 1 < KT) step(kt + 1, smem1, smem0);
+        }
+    } else {
+        issue(0, smem0);
+        issue(1, smem1);
+        for (int kt = 0; kt < KT; kt += 3) {
+            step(kt, smem0, smem2);
+            if (kt + 1 < KT) step(kt + 1, smem1, smem0);
+            if (kt + 2 < KT) step(kt + 2, smem2, smem1);
+        }
     }
+    // the loads issued for steps past the end (they fetch nothing) must land
+    // before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(0);
 
     // ---------------------------------------------------------- epilogue
     float alpha = 1.0f;

@@ -7,10 +7,15 @@
 
 namespace mmfp8 {
 
-// Workgroup tiles of gemm_tile, largest first.
-enum TileCfg : int { CFG_256x256 = 0, CFG_256x128 = 1, CFG_128x128 = 2, CFG_64x64 = 3, CFG_COUNT = 4 };
-constexpr int kCfgBM[CFG_COUNT] = {256, 256, 128, 64};
-constexpr int kCfgBN[CFG_COUNT] = {256, 128, 128, 64};
+// Workgroup tiles of gemm_tile, largest first: BM x BN, waves WM x WN, LDS stages.
+// 256x256 gives each of its 8 waves a 64x128 tile (1.5 FP8->bf16 converts per
+// MFMA); the others use 64x64 wave tiles (2 converts per MFMA).
+enum TileCfg : int { CFG_256x256 = 0, CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x64 = 3, CFG_COUNT = 4 };
+constexpr int kCfgBM[CFG_COUNT] = {256, 128, 128, 64};
+constexpr int kCfgBN[CFG_COUNT] = {256, 256, 128, 64};
+constexpr int kCfgWM[CFG_COUNT] = {4, 2, 2, 2};
+constexpr int kCfgWN[CFG_COUNT] = {2, 4, 2, 2};
+constexpr int kCfgStages[CFG_COUNT] = {2, 3, 3, 2};
 
 hipError_t launch_tile_fast(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_tile_slow(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
@@ -21,34 +26,38 @@ hipError_t launch_amax_init(uint32_t* bits, unsigned long long* key, hipStream_t
 hipError_t launch_amax_finalize(float* amax, unsigned long long* key, hipStream_t s);
 hipError_t launch_debug_convert(const float* x, void* y, int t, int64_t n, hipStream_t s);
 
-// Largest tile each mode is built for: the fast chain keeps 256 fp32
-// accumulators per lane and nothing else, the promoted and MX-scaled modes also
-// hold their partials or scale operands, so they stop at 256x128 (128x128 with
-// a 1x128 scale_b, which needs four scale values per lane and tile).
+// Largest tile each mode is built for: the fast chain keeps 128 fp32
+// accumulators per lane and little else, so only it has the 64x128 wave tile.
+// The promoted and MX modes also hold partials or scale operands and stop at
+// 128x256 (eight 64x64 waves, two per SIMD); the block-scaled mode holds up to
+// 16 scale_b values per lane besides, which two waves per SIMD cannot keep in
+// registers, so it stops at 128x128 (four waves, one per SIMD).
 constexpr int min_cfg(int mode, int sbm) {
-    return mode == MODE_FAST ? CFG_256x256 : (mode == MODE_BLOCK && sbm == SB_1x128) ? CFG_128x128 : CFG_256x128;
+    (void)sbm;
+    return mode == MODE_FAST ? CFG_256x256 : mode == MODE_BLOCK ? CFG_128x128 : CFG_128x256;
 }
 
 // Launch gemm_tile<BM, BN, MODE, fa, fb, SBM> for a runtime cfg / format pair.
 template <int MODE, int SBM>
 hipError_t tile_dispatch(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s) {
-#define MMFP8_TILE(BM, BN, A, B) \
-    hipLaunchKernelGGL((gemm_tile<BM, BN, MODE, A, B, SBM>), dim3(grid), dim3(256), 0, s, p)
-#define MMFP8_FMTS(BM, BN)                                       \
-    if (fa == 0 && fb == 0) MMFP8_TILE(BM, BN, 0, 0);            \
-    else if (fa == 1 && fb == 1) MMFP8_TILE(BM, BN, 1, 1);       \
-    else if (fa == 0 && fb == 1) MMFP8_TILE(BM, BN, 0, 1);       \
-    else MMFP8_TILE(BM, BN, 1, 0);
+#define MMFP8_TILE(C, A, B)                                                                                  \
+    hipLaunchKernelGGL((gemm_tile<kCfgBM[C], kCfgBN[C], kCfgWM[C], kCfgWN[C], kCfgStages[C], MODE, A, B, SBM>), \
+                       dim3(grid), dim3(kCfgWM[C] * kCfgWN[C] * 64), 0, s, p)
+#define MMFP8_FMTS(C)                                    \
+    if (fa == 0 && fb == 0) MMFP8_TILE(C, 0, 0);         \
+    else if (fa == 1 && fb == 1) MMFP8_TILE(C, 1, 1);    \
+    else if (fa == 0 && fb == 1) MMFP8_TILE(C, 0, 1);    \
+    else MMFP8_TILE(C, 1, 0);
     if (cfg < min_cfg(MODE, SBM)) cfg = min_cfg(MODE, SBM);
     switch (cfg) {
         case CFG_256x256:
-            if constexpr (MODE == MODE_FAST) { MMFP8_FMTS(256, 256) }
+            if constexpr (MODE == MODE_FAST) { MMFP8_FMTS(CFG_256x256) }
             break;
-        case CFG_256x128:
-            if constexpr (!(MODE == MODE_BLOCK && SBM == SB_1x128)) { MMFP8_FMTS(256, 128) }
+        case CFG_128x256:
+            if constexpr (MODE != MODE_BLOCK) { MMFP8_FMTS(CFG_128x256) }
             break;
-        case CFG_128x128: MMFP8_FMTS(128, 128) break;
-        default: MMFP8_FMTS(64, 64) break;
+        case CFG_128x128: MMFP8_FMTS(CFG_128x128) break;
+        default: MMFP8_FMTS(CFG_64x64) break;
     }
 #undef MMFP8_FMTS
 #undef MMFP8_TILE

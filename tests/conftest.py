@@ -3,6 +3,13 @@ import sys
 
 import pytest
 
+# torch before any test module loads libmmfp8: torch's bundled HIP runtime must
+# be the process's only one (the package does the same on import).
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)

@@ -132,3 +132,18 @@ def test_error_message_is_thread_local_and_cleared():
     assert mm.mm_last_error() != ""
     assert gemm(M=0, d=0) == mm.MM_OK
     assert mm.mm_last_error() == ""
+
+
+def test_single_hip_runtime_after_import():
+    """Importing the package must leave one HIP runtime in the process: torch's
+    bundled runtime and the system one share a soname, and a second runtime
+    initialised after the first finds no GPU."""
+    import subprocess
+    import sys
+    code = ("import block_scaled_gemm_amd, torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "1", r.stdout
