@@ -88,9 +88,9 @@ typedef enum mm_scale_mode {
  *           Block-scaled modes always promote per 128-chunk (the scale changes
  *           per chunk), so the flag does not change them.
  *
- * Result, per output element: the sum over k of the products is formed in
- * fp32 by the MFMA units (every product of two FP8 values is exact in fp32);
- * per-tensor scales multiply it as fp32(s_a * s_b); block scales multiply each
+ * Result, per output element: every FP8 value is converted exactly to bf16
+ * and the sum over k of the products is formed in fp32 by the bf16 MFMA units
+ * (every product of two FP8 values is exact there); per-tensor scales multiply it as fp32(s_a * s_b); block scales multiply each
  * 128-chunk partial as fp32(sa[m,kb] * sb[n,kb]) in a fused multiply-add; an
  * FP8 output is then multiplied by scale_result. The cast rounds to nearest
  * even: bf16 / f16 / f32 overflow to +-Inf, FP8 outputs saturate to +-max
@@ -143,9 +143,11 @@ mm_status mm_scaled_gemm(int64_t M, int64_t N, int64_t K,
  *           maximum, the smallest such index on ties; -1 when M*N*L == 0.
  *           Requires M*N*L < 2^33.
  *
- * The sum of each 32-element group is scaled in the MFMA units by the product
- * of its two scale factors (exact for powers of two) and accumulated over K in
- * one fp32 chain. The cast to c_type and NaN encodings follow mm_scaled_gemm.
+ * Each FP8 value is multiplied by its group's scale factor as it is
+ * converted to bf16, which is exact while the scaled value stays in bf16's
+ * range (E4M3: e in [-124, 119], E5M2: e in [-117, 112]; outside it the
+ * operand loses precision, nothing faults); the products are summed over K in
+ * one fp32 chain by the bf16 MFMA units. The cast to c_type and NaN encodings follow mm_scaled_gemm.
  * The library clears amax / amax_index itself, with its own kernels on
  * `stream`; the outputs are final when the stream reaches the end of the call.
  *
