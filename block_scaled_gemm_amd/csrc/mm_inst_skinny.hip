@@ -38,7 +38,9 @@ __global__ void debug_convert(const float* x, void* y, int t, int64_t n) {
 
 template <int MODE>
 static hipError_t skinny_mode(int mt, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s) {
-#define MMFP8_SK(MT, A, B) hipLaunchKernelGGL((gemm_skinny<MT, MODE, A, B>), dim3(grid), dim3(256), 0, s, p)
+#define MMFP8_SK(MT, A, B)                                                                                \
+    hipLaunchKernelGGL((gemm_skinny<MT, MODE, A, B, skinny_waves(MT), skinny_steps(MT)>), dim3(grid),        \
+                       dim3(skinny_waves(MT) * 64), 0, s, p)
 #define MMFP8_SKF(MT)                                         \
     if (fa == 0 && fb == 0) MMFP8_SK(MT, 0, 0);               \
     else if (fa == 1 && fb == 1) MMFP8_SK(MT, 1, 1);          \

@@ -407,6 +407,11 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
     }
     const float* sa_l = p.sa + (int64_t)l * p.sa_batch;
     const float* sb_l = p.sb + (int64_t)l * p.sb_batch;
+    // epilogue scales, read now so that their latency hides behind the main loop
+    float alpha = 1.0f;
+    if (MODE == MODE_FAST || MODE == MODE_SLOW) alpha = p.sa[0] * p.sb[0];
+    const bool fp8_out = p.d_type == T_E4M3 || p.d_type == T_E5M2;
+    const float sr = (fp8_out && p.scale_result) ? p.scale_result[0] : 1.0f;
 
     // Scales of one step, loaded one step ahead of their use (before that step's
     // LDS-DMA loads are issued, so waiting for them never waits for those).
@@ -564,10 +569,6 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
     __builtin_amdgcn_s_waitcnt(0);
 
     // ---------------------------------------------------------- epilogue
-    float alpha = 1.0f;
-    if (MODE == MODE_FAST || MODE == MODE_SLOW) alpha = p.sa[0] * p.sb[0];
-    const bool fp8_out = p.d_type == T_E4M3 || p.d_type == T_E5M2;
-    const float sr = (fp8_out && p.scale_result) ? p.scale_result[0] : 1.0f;
     const int64_t dbase = (int64_t)l * p.d_batch;
     const bool want_amax = p.amax_bits || p.amax_key;
     uint32_t kb = 0;
@@ -604,15 +605,26 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
 
 // ------------------------------------------------------------------ skinny kernel
 //
-// For M <= 16 * MT (MT <= 4) with per-tensor scales: the run is bound by
-// streaming B once from HBM. Each lane holds k = 32 g .. 32 g + 31 of its row. A workgroup owns 16 columns of the output; its 4
-// waves split the K steps round-robin (wave w takes steps w, w+4, ...), load
-// their B and A fragments straight from memory into registers (A is small and
-// stays in L2), keep kU steps in flight, and add their partial tiles in LDS in
-// a fixed order at the end.
-template <int MT, int MODE, int FA, int FB>
-__global__ void __launch_bounds__(256) gemm_skinny(GemmArgs p) {
-    constexpr int kU = MT <= 2 ? 4 : 2;  // K steps in flight per wave
+// For M <= 16 * MT (MT <= 4) with per-tensor scales the run is bound by
+// streaming B (N x K bytes) once from HBM; A is small and every workgroup reads
+// all of it from L2. A workgroup owns 16 columns of the output (one workgroup
+// per CU at N = 4096); its NW waves split the K steps round-robin (wave w
+// takes steps w, w + NW, ...) with KU steps in flight each, so that most of B
+// is in flight at once. B fragments go straight from memory into registers.
+// A is read in contiguous 1 KB pieces (8 rows of 128 bytes per instruction:
+// read in fragment order, 16 rows per instruction, the L2 -> CU path delivers
+// it at a fraction of the rate), written to the wave's own LDS slot and read
+// back as fragments. Lane (r, g) holds k = 32 g .. 32 g + 31 of row r in each
+// step. The waves' partial tiles are added in a fixed order at the end.
+template <int MT, int MODE, int FA, int FB, int NW, int KU>
+__global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs p) {
+    static_assert(KU >= 1 && KU <= 4, "steps in flight per wave");
+    constexpr int AROWS = 16 * MT;
+    constexpr int A_INS = AROWS / 8;     // 1 KB loads of A per step
+    constexpr int SLOT = AROWS * kBK;    // one step of A
+    constexpr int RED = (NW - 1) * MT * 64 * 16;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NW * SLOT > RED ? NW * SLOT : RED];
+
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = blockIdx.x * 16;
     const int K = p.K, KT = (K + kBK - 1) / kBK;
@@ -620,48 +632,71 @@ __global__ void __launch_bounds__(256) gemm_skinny(GemmArgs p) {
     const rsrc_t rb = make_rsrc(p.b + (int64_t)n0 * p.ldb, operand_extent(min(16, p.N - n0), p.ldb, K));
     const rsrc_t ra = make_rsrc(p.a, operand_extent(p.M, p.lda, K));
     const uint32_t boff = (uint32_t)(fr * p.ldb + 32 * fg);
-    uint32_t aoff[MT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) aoff[i] = (uint32_t)((i * 16 + fr) * p.lda + 32 * fg);
+    // epilogue scales, read now so that their latency hides behind the main loop
+    const float alpha = p.sa[0] * p.sb[0];
+    const bool fp8_out = p.d_type == T_E4M3 || p.d_type == T_E5M2;
+    const float sr = (fp8_out && p.scale_result) ? p.scale_result[0] : 1.0f;
 
-    struct Frag {
-        i32x8 b;
-        i32x8 a[MT];
-    };
-    // Load step kt: k = 128 kt + 32 fg .. + 31 of each row, as two 16-byte chunks.
-    auto load = [&](int kt, Frag& f) {
-        const int k0 = kt * kBK + 32 * fg;
-        const int k1 = k0 + 16;
-        const bool tail = kt * kBK + kBK > K;
-        uint32_t o0 = (uint32_t)(kt * kBK), o1 = (uint32_t)(kt * kBK + 16);
-        // chunks starting at or past K read zero; a straddling chunk is masked below
-        const bool z0 = tail && k0 >= K, z1 = tail && k1 >= K;
-        i32x4 b0 = __builtin_amdgcn_raw_buffer_load_b128(rb, z0 ? kOOB : boff + o0, 0, 0);
-        i32x4 b1 = __builtin_amdgcn_raw_buffer_load_b128(rb, z1 ? kOOB : boff + o1, 0, 0);
-        f.b = cat(b0, b1);
+    // A: instruction q reads rows 8q .. 8q+7 of the step; lane l takes row
+    // 8q + l/8, chunk c = l%8, and stores it at chunk c ^ swz(row),
+    // swz(r) = (r & 7) ^ ((r >> 3) & 1), so that the fragment reads below are
+    // free of LDS bank conflicts.
+    const int ld_row = lane >> 3, ld_chunk = lane & 7;
+    uint32_t aoff[A_INS];
+    int awr[A_INS];
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            i32x4 a0 = __builtin_amdgcn_raw_buffer_load_b128(ra, z0 ? kOOB : aoff[i] + o0, 0, 0);
-            i32x4 a1 = __builtin_amdgcn_raw_buffer_load_b128(ra, z1 ? kOOB : aoff[i] + o1, 0, 0);
-            f.a[i] = cat(a0, a1);
-        }
+    for (int q = 0; q < A_INS; ++q) {
+        const int row = q * 8 + ld_row;
+        aoff[q] = (uint32_t)(row * p.lda + ld_chunk * 16);
+        awr[q] = row * kBK + ((ld_chunk ^ ld_row ^ (q & 1)) << 4);
+    }
+    const int fsw = (fr & 7) ^ (fr >> 3);
+    const int foff0 = fr * kBK + (((2 * fg) ^ fsw) << 4);
+    const int foff1 = fr * kBK + (((2 * fg + 1) ^ fsw) << 4);
+    uint8_t* const slot = lds + wave * SLOT;
+
+    struct Step {
+        i32x4 a[A_INS];
+        i32x8 b;
     };
-    auto mask = [&](int kt, Frag& f) {
-        // zero bytes at k >= K in a chunk straddling K (only in the last step)
+    // Loads of step kt; chunks starting at or past K read zero (the range check
+    // returns 0 for an out-of-range offset); a chunk straddling K is masked below.
+    auto load = [&](int kt, Step& st) {
+        const uint32_t kb = (uint32_t)(kt * kBK);
+        const bool tail = kt * kBK + kBK > K;
+#pragma unroll
+        for (int q = 0; q < A_INS; ++q) {
+            uint32_t off = aoff[q] + kb;
+            if (tail && (int)kb + ld_chunk * 16 >= K) off = kOOB;
+            st.a[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+        }
         const int k0 = kt * kBK + 32 * fg;
+        uint32_t o0 = boff + kb, o1 = boff + kb + 16;
+        if (tail && k0 >= K) o0 = kOOB;
+        if (tail && k0 + 16 >= K) o1 = kOOB;
+        const i32x4 b0 = __builtin_amdgcn_raw_buffer_load_b128(rb, o0, 0, 0);
+        const i32x4 b1 = __builtin_amdgcn_raw_buffer_load_b128(rb, o1, 0, 0);
+        st.b = cat(b0, b1);
+    };
+    auto keep = [&](int ks, int d) -> uint32_t {  // byte mask of dword d of a chunk at ks
+        const int nb = K - ks - 4 * d;
+        return nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : ((1u << (8 * nb)) - 1u));
+    };
+    auto mask = [&](int kt, Step& st) {
+#pragma unroll
+        for (int q = 0; q < A_INS; ++q) {
+            const int ks = kt * kBK + ld_chunk * 16;
+            if (ks < K && K < ks + 16) {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) st.a[q][d] = (int)((uint32_t)st.a[q][d] & keep(ks, d));
+            }
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int ks = k0 + 16 * h;
+            const int ks = kt * kBK + 32 * fg + 16 * h;
             if (ks < K && K < ks + 16) {
-                const int valid = K - ks;
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const int nb = valid - 4 * d;
-                    const uint32_t m = nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : ((1u << (8 * nb)) - 1u));
-                    f.b[4 * h + d] = (int)((uint32_t)f.b[4 * h + d] & m);
-#pragma unroll
-                    for (int i = 0; i < MT; ++i) f.a[i][4 * h + d] = (int)((uint32_t)f.a[i][4 * h + d] & m);
-                }
+                for (int d = 0; d < 4; ++d) st.b[4 * h + d] = (int)((uint32_t)st.b[4 * h + d] & keep(ks, d));
             }
         }
     };
@@ -670,20 +705,29 @@ __global__ void __launch_bounds__(256) gemm_skinny(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nsteps = (KT - wave + 3) / 4;  // steps of this wave: wave, wave+4, ...
-    Frag buf[kU];
+    const int nsteps = KT > wave ? (KT - wave + NW - 1) / NW : 0;  // steps wave, wave + NW, ...
+    Step buf[KU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
-        if (u < nsteps) load(wave + 4 * u, buf[u]);
-    for (int s0 = 0; s0 < nsteps; s0 += kU) {
+    for (int u = 0; u < KU; ++u)
+        if (u < nsteps) load(wave + NW * u, buf[u]);
+    for (int s0 = 0; s0 < nsteps; s0 += KU) {
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
+        for (int u = 0; u < KU; ++u) {
             const int s = s0 + u;
             if (s < nsteps) {
-                Frag cur = buf[u];
-                const int kt = wave + 4 * s;
-                if (s + kU < nsteps) load(wave + 4 * (s + kU), buf[u]);
+                Step cur = buf[u];
+                const int kt = wave + NW * s;
+                if (s + KU < nsteps) load(wave + NW * (s + KU), buf[u]);
                 if (kt * kBK + kBK > K && (K & 15)) mask(kt, cur);
+                // A through the wave's slot: the previous step's fragment reads of
+                // the slot are complete (their results fed that step's MFMAs)
+#pragma unroll
+                for (int q = 0; q < A_INS; ++q) *(i32x4*)(slot + awr[q]) = cur.a[q];
+                i32x8 af[MT];
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+                    af[i] = cat(*(const i32x4*)(slot + i * 16 * kBK + foff0),
+                                *(const i32x4*)(slot + i * 16 * kBK + foff1));
                 bf16x8 bb[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) bb[q] = to_bf16x8<FB>(cur.b, q, 1.0f);
@@ -691,7 +735,7 @@ __global__ void __launch_bounds__(256) gemm_skinny(GemmArgs p) {
                 for (int i = 0; i < MT; ++i) {
                     f32x4 part = MODE == MODE_FAST ? acc[i] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) part = mfma_bf16(bb[q], to_bf16x8<FA>(cur.a[i], q, 1.0f), part);
+                    for (int q = 0; q < 4; ++q) part = mfma_bf16(bb[q], to_bf16x8<FA>(af[i], q, 1.0f), part);
                     if (MODE == MODE_FAST) acc[i] = part;
                     else acc[i] += part;
                 }
@@ -699,20 +743,21 @@ __global__ void __launch_bounds__(256) gemm_skinny(GemmArgs p) {
         }
     }
 
-    // Fixed-order reduction of the 4 waves' partial tiles.
-    __shared__ f32x4 red[3][MT][64];
+    // Fixed-order reduction of the NW waves' partial tiles (wave 0's, then waves
+    // 1, 2, ... in order), in the LDS that held the A slots.
+    __syncthreads();
+    f32x4* red = (f32x4*)lds;  // [NW - 1][MT][64]
     if (wave > 0) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i) red[wave - 1][i][lane] = acc[i];
+        for (int i = 0; i < MT; ++i) red[((wave - 1) * MT + i) * 64 + lane] = acc[i];
     }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) acc[i] = ((acc[i] + red[0][i][lane]) + red[1][i][lane]) + red[2][i][lane];
+    for (int w = 0; w < NW - 1; ++w)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[i] += red[(w * MT + i) * 64 + lane];
 
-    const float alpha = p.sa[0] * p.sb[0];
-    const bool fp8_out = p.d_type == T_E4M3 || p.d_type == T_E5M2;
-    const float sr = (fp8_out && p.scale_result) ? p.scale_result[0] : 1.0f;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
         const int m = i * 16 + fr;

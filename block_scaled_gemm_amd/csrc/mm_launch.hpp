@@ -17,6 +17,13 @@ constexpr int kCfgWM[CFG_COUNT] = {4, 2, 2, 2};
 constexpr int kCfgWN[CFG_COUNT] = {2, 4, 2, 2};
 constexpr int kCfgStages[CFG_COUNT] = {2, 3, 3, 2};
 
+// gemm_skinny: waves per workgroup and K steps in flight per wave, by MT
+// (M <= 16 MT). Sixteen waves with two steps each put a K = 4096 B tile in
+// flight at once; with MT = 4 the A fragments need more registers than 16
+// waves per CU leave, so that case runs 8 waves with one step each.
+constexpr int skinny_waves(int mt) { return mt == 4 ? 8 : 16; }
+constexpr int skinny_steps(int mt) { return mt == 4 ? 1 : 2; }
+
 hipError_t launch_tile_fast(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_tile_slow(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_tile_block(int cfg, int sbm, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
