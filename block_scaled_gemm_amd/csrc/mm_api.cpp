@@ -153,6 +153,15 @@ mm_status mm_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, int a_t
     const int mode = per_tensor ? (use_fast_accum ? mmfp8::MODE_FAST : mmfp8::MODE_SLOW) : mmfp8::MODE_BLOCK;
     const int sbm = sb_mode == MM_SCALE_128x128 ? mmfp8::SB_128x128 : mmfp8::SB_1x128;
     const int cfg = choose_cfg(M, N, 1, cu_count(), mmfp8::min_cfg(mode, sbm));
+    if (per_tensor && cfg == mmfp8::CFG_64x64) {
+        // too few 128x128 tiles to fill the chip: K split over the waves of 64x64 / 32x64 tiles
+        const int ks = cdiv(M, 64) * cdiv(N, 64) >= cu_count() ? mmfp8::KS_64x64 : mmfp8::KS_32x64;
+        p.tiles_m = (int)cdiv(M, mmfp8::kKsBM[ks]);
+        p.tiles_n = (int)cdiv(N, mmfp8::kKsBN[ks]);
+        const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+        e = mmfp8::launch_ksplit(ks, mode, fa, fb, p, (int)grid, s);
+        return device_status(e, "mm_scaled_gemm (k-split) launch");
+    }
     p.tiles_m = (int)cdiv(M, mmfp8::kCfgBM[cfg]);
     p.tiles_n = (int)cdiv(N, mmfp8::kCfgBN[cfg]);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;

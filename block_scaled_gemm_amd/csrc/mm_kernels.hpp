@@ -774,4 +774,188 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs p) {
     }
 }
 
+// ------------------------------------------------------------------ K-split tile kernel
+//
+// For mid-size M (above the skinny range, up to a few hundred rows at
+// N = K = 4096) the workgroup tiles of gemm_tile that keep its waves efficient
+// are too few to fill the chip, and small tiles leave one wave per SIMD with
+// nothing to hide latency behind. Here a workgroup owns a 16 MT x 16 NT output
+// tile and its NW waves split the K steps round-robin (wave w takes steps
+// w, w + NW, ...): each wave computes the whole tile for its steps from its own
+// LDS slot, so the main loop has no barriers and the waves drift freely. Each
+// step's A and B rows are read in contiguous 1 KB pieces (8 rows of 128 bytes
+// per instruction) into registers, written to the slot with the XOR swizzle of
+// gemm_tile, and read back as fragments; the next step's loads are in flight
+// meanwhile. At the end the NW partial tiles are added in a fixed order (wave
+// 0's first), each wave reducing and storing its share of the fragments.
+template <int MT, int NT, int MODE, int FA, int FB, int NW, int KU>
+__global__ void __launch_bounds__(NW * 64) gemm_ksplit(GemmArgs p) {
+    static_assert(KU >= 1 && KU <= 4, "steps in flight per wave");
+    constexpr int AROWS = 16 * MT, BROWS = 16 * NT;
+    constexpr int A_INS = AROWS / 8, B_INS = BROWS / 8, INS = A_INS + B_INS;  // 1 KB loads per step
+    constexpr int SLOT = INS * 1024;                                          // A rows, then B rows
+    constexpr int NFRAG = MT * NT;
+    static_assert(NFRAG % NW == 0, "the fragments split evenly over the waves for the reduction");
+    constexpr int FPW = NFRAG / NW;
+    constexpr int RED = NW * NFRAG * 1024;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NW * SLOT > RED ? NW * SLOT : RED];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int l, tm, tn;
+    tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, 8, l, tm, tn);
+    const int m0 = tm * AROWS, n0 = tn * BROWS;
+    const int K = p.K, KT = (K + kBK - 1) / kBK;
+    const int fr = lane & 15, fg = lane >> 4;
+    const rsrc_t ra = make_rsrc(p.a + (int64_t)m0 * p.lda, operand_extent(min(AROWS, p.M - m0), p.lda, K));
+    const rsrc_t rb = make_rsrc(p.b + (int64_t)n0 * p.ldb, operand_extent(min(BROWS, p.N - n0), p.ldb, K));
+    // epilogue scales, read now so that their latency hides behind the main loop
+    const float alpha = p.sa[0] * p.sb[0];
+    const bool fp8_out = p.d_type == T_E4M3 || p.d_type == T_E5M2;
+    const float sr = (fp8_out && p.scale_result) ? p.scale_result[0] : 1.0f;
+
+    // Loader: instruction q reads slot rows 8q .. 8q+7 (A rows first); lane l
+    // takes row 8q + l/8, chunk c = l%8, and stores it at chunk c ^ swz(row),
+    // swz(r) = (r & 7) ^ ((r >> 3) & 1).
+    const int ld_row = lane >> 3, ld_chunk = lane & 7;
+    uint32_t goff[INS];
+    int wr[INS];
+#pragma unroll
+    for (int q = 0; q < INS; ++q) {
+        const int grow = (q < A_INS ? q : q - A_INS) * 8 + ld_row;
+        goff[q] = (uint32_t)(grow * (q < A_INS ? p.lda : p.ldb) + ld_chunk * 16);
+        wr[q] = (q * 8 + ld_row) * kBK + ((ld_chunk ^ ld_row ^ (q & 1)) << 4);
+    }
+    const int fsw = (fr & 7) ^ (fr >> 3);
+    const int foff0 = fr * kBK + (((2 * fg) ^ fsw) << 4);
+    const int foff1 = fr * kBK + (((2 * fg + 1) ^ fsw) << 4);
+    uint8_t* const slot = lds + wave * SLOT;
+
+    struct Step {
+        i32x4 v[INS];
+    };
+    // Loads of step kt; chunks starting at or past K read zero (out-of-range
+    // offsets return 0); a chunk straddling K is masked after it lands.
+    auto load = [&](int kt, Step& st) {
+        const uint32_t kb = (uint32_t)(kt * kBK);
+        const bool z = kt * kBK + kBK > K && (int)kb + ld_chunk * 16 >= K;
+#pragma unroll
+        for (int q = 0; q < INS; ++q) {
+            uint32_t off = goff[q] + kb;
+            if (z) off = kOOB;
+            st.v[q] = q < A_INS ? __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0)
+                                : __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+        }
+    };
+    auto mask = [&](int kt, Step& st) {
+        const int ks = kt * kBK + ld_chunk * 16;
+        if (ks < K && K < ks + 16) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int nb = K - ks - 4 * d;
+                const uint32_t m = nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : ((1u << (8 * nb)) - 1u));
+#pragma unroll
+                for (int q = 0; q < INS; ++q) st.v[q][d] = (int)((uint32_t)st.v[q][d] & m);
+            }
+        }
+    };
+
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nsteps = KT > wave ? (KT - wave + NW - 1) / NW : 0;  // steps wave, wave + NW, ...
+    Step buf[KU];
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+        if (u < nsteps) load(wave + NW * u, buf[u]);
+    for (int s0 = 0; s0 < nsteps; s0 += KU)
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+        const int s = s0 + u;
+        if (s >= nsteps) break;
+        const int kt = wave + NW * s;
+        if (kt * kBK + kBK > K && (K & 15)) mask(kt, buf[u]);
+        // into the slot (the previous step's fragment reads were issued before,
+        // and LDS operations of one wave complete in order)
+#pragma unroll
+        for (int q = 0; q < INS; ++q) *(i32x4*)(slot + wr[q]) = buf[u].v[q];
+        if (s + KU < nsteps) load(kt + NW * KU, buf[u]);
+        const uint8_t* As = slot;
+        const uint8_t* Bs = slot + AROWS * kBK;
+        // Fast: one chain into the accumulators. Slow: a fresh fp32 partial per
+        // 128-chunk (this step), promoted into the accumulator after.
+        constexpr bool chain = MODE == MODE_FAST;
+        f32x4 part[chain ? 1 : MT][chain ? 1 : NT];
+        if constexpr (!chain) {
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) part[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        // two 16-byte halves of the lane's 32 bytes: sub-steps 0-1, then 2-3
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int fo = h ? foff1 : foff0;
+            i32x4 ar[MT], br[NT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i) ar[i] = *(const i32x4*)(As + i * 16 * kBK + fo);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) br[j] = *(const i32x4*)(Bs + j * 16 * kBK + fo);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                bf16x8 ab[MT];
+#pragma unroll
+                for (int i = 0; i < MT; ++i) ab[i] = to_bf16x8<FA>(ar[i], q, 1.0f);
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const bf16x8 bb = to_bf16x8<FB>(br[j], q, 1.0f);
+#pragma unroll
+                    for (int i = 0; i < MT; ++i) {
+                        if constexpr (chain) acc[i][j] = mfma_bf16(bb, ab[i], acc[i][j]);
+                        else part[i][j] = mfma_bf16(bb, ab[i], part[i][j]);
+                    }
+                }
+            }
+        }
+        if constexpr (!chain) {
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) acc[i][j] += part[i][j];
+        }
+    }
+
+    // Fixed-order reduction: every wave's partial tile goes to LDS (over the
+    // slots, once all waves are done with them); wave w then adds fragments
+    // w FPW .. w FPW + FPW - 1 over the waves in order 0, 1, ... and stores them.
+    __syncthreads();
+    f32x4* red = (f32x4*)lds;  // [NW][NFRAG][64]
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) red[(wave * NFRAG + i * NT + j) * 64 + lane] = acc[i][j];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < FPW; ++u) {
+        const int f = wave * FPW + u;
+        f32x4 v = red[f * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += red[(w * NFRAG + f) * 64 + lane];
+        const int i = f / NT, j = f % NT;
+        const int m = m0 + i * 16 + fr;
+        const int n = n0 + j * 16 + 4 * fg;
+        const int valid = (m < p.M) ? max(0, min(4, p.N - n)) : 0;
+        uint32_t out[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float x = (v[r] + 0.0f) * alpha;
+            if (fp8_out) x *= sr;
+            out[r] = convert(x, p.d_type);
+        }
+        if (valid > 0) store4(p.d, p.d_type, (int64_t)m * p.ldd + n, out, valid, p.vec_store != 0);
+    }
+}
+
 }  // namespace mmfp8

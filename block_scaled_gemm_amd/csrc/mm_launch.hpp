@@ -24,11 +24,20 @@ constexpr int kCfgStages[CFG_COUNT] = {2, 3, 3, 2};
 constexpr int skinny_waves(int mt) { return mt == 4 ? 8 : 16; }
 constexpr int skinny_steps(int mt) { return mt == 4 ? 1 : 2; }
 
+// gemm_ksplit variants for per-tensor M above the skinny range while the
+// 128x128 tiles of gemm_tile are fewer than the CUs: a 64x64 tile, or 32x64
+// when even the 64x64 tiles are fewer than the CUs; four waves split K, two K
+// steps in flight for the smaller tile.
+enum KsplitCfg : int { KS_64x64 = 0, KS_32x64 = 1 };
+constexpr int kKsBM[2] = {64, 32};
+constexpr int kKsBN[2] = {64, 64};
+
 hipError_t launch_tile_fast(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_tile_slow(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_tile_block(int cfg, int sbm, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_tile_sf32(int cfg, int f, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_skinny(int mt, int mode, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
+hipError_t launch_ksplit(int ks, int mode, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_amax_init(uint32_t* bits, unsigned long long* key, hipStream_t s);
 hipError_t launch_amax_finalize(float* amax, unsigned long long* key, hipStream_t s);
 hipError_t launch_debug_convert(const float* x, void* y, int t, int64_t n, hipStream_t s);
