@@ -275,14 +275,19 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int t
 //
 // K is walked in steps of 128 (= one "slow" chunk = one 1x128 scale block =
 // four 32-element MX groups). Each step's A and B tiles go from memory straight
-// to LDS with buffer_load ... lds through STAGES rotating buffers; rows are 128
+// to LDS with buffer_load ... lds through two alternating buffers; rows are 128
 // bytes with the 16-byte chunk c of row r stored at chunk c ^ swz(r),
 // swz(r) = (r & 7) ^ ((r >> 3) & 1): any 8 consecutive rows, and any 16
 // consecutive rows split by row parity, then hit distinct banks at one
 // logical chunk, so the fragment reads are free of bank conflicts. Lane (r, g) of a fragment holds
 // k = 32g .. 32g+31 of row r (one MX group), converted to bf16 8 values at a
 // time for the four v_mfma_f32_16x16x32_bf16 of the step.
-template <int BM, int BN, int WM, int WN, int STAGES, int MODE, int FA, int FB, int SBM>
+//
+// PIPE selects the main loop: with it the fragment reads run a half-step ahead
+// of the MFMAs (the way to hide LDS latency with one wave per SIMD, at the cost
+// of a second set of fragment registers); without it each half-step reads and
+// then multiplies, and a second wave on the SIMD hides the latency.
+template <int BM, int BN, int WM, int WN, int PIPE, int MODE, int FA, int FB, int SBM>
 __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
     constexpr int NW = WM * WN;
     constexpr int NT = NW * 64;
@@ -291,14 +296,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
     constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;  // 1 KB LDS-DMA writes per wave per step
     constexpr int INS = A_INS + B_INS;
     static_assert(A_INS * 8 * NW == BM && B_INS * 8 * NW == BN, "tile rows must split evenly over the waves");
-    static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
     constexpr int STAGE = (BM + BN) * kBK;
     // Distinct LDS objects (not one array indexed by stage) so that the compiler
     // can tell a fragment read of one stage from the in-flight LDS-DMA writes
     // into another and does not wait for those loads.
     __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t smem2[STAGES == 3 ? STAGE : 16];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -450,27 +453,50 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
     StepScales sc_cur;
     if (MODE == MODE_BLOCK || MODE == MODE_SF32) sc_cur = load_scales(0);
 
-    // One main-loop step: wait for this step's tiles (the next step's may stay
-    // in flight), release the oldest stage to the loads STAGES-1 steps ahead,
-    // then run the MFMAs on this stage.
-    auto step = [&](int kt, uint8_t* cur, uint8_t* ahead) {
-        // Every step issues INS loads (after its scale loads), so vmcnt(INS)
-        // waits for this step's stage only. (__syncthreads() below then waits
-        // for everything: its workgroup fence makes the compiler drain the
-        // global->LDS loads. Issuing those loads by hand, untracked, with a
-        // fence-free barrier that keeps a stage in flight, measured no faster.)
-        constexpr int kWait = STAGES == 3 ? INS : 0;
-        __builtin_amdgcn_s_waitcnt((kWait & 15) | ((kWait >> 4) << 14) | (7 << 4) | (15 << 8));
-        if (k_tail && kt == KT - 1 && (K & 15)) mask_straddle(kt, cur);
-        __syncthreads();
-        StepScales sc_next;
-        if (MODE == MODE_BLOCK || MODE == MODE_SF32) sc_next = load_scales(kt + 1);
-        issue(kt + STAGES - 1, ahead);
-
-        // scales of this step
-        float s_a[FM];
-        float s_b[FN][4];
-        float c_a[FM], c_b[FN];  // per-lane conversion scales (SF32: this lane's 32-group)
+    // Main loop, two LDS stages, software-pipelined by half-steps: the lane's
+    // 32 bytes of a step are read as two 16-byte halves (sub-steps 0-1, 2-3),
+    // and each half's fragment reads are issued before the MFMAs of the half
+    // before it, so the LDS latency hides behind MFMA work. The stage barrier
+    // sits in the middle of a step, once that step's second-half fragments are
+    // read: past it the stage just read is free for the loads two steps ahead,
+    // and the next step's first-half fragments can be read.
+    struct Frag {
+        i32x4 a[FM];
+        i32x4 b[FN];
+    };
+    auto read_frag = [&](const uint8_t* stage, int h, Frag& f) {
+        const int fo = h ? foff1 : foff0;
+        const uint8_t* As = stage + wm * WTM * kBK;
+        const uint8_t* Bs = stage + BM * kBK + wn * WTN * kBK;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) f.a[i] = *(const i32x4*)(As + i * 16 * kBK + fo);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) f.b[j] = *(const i32x4*)(Bs + j * 16 * kBK + fo);
+    };
+    // Fast / MX: one chain over K straight into the accumulators. Slow / block:
+    // a fresh fp32 partial per 128-chunk, promoted into the accumulator after.
+    constexpr bool chain = MODE == MODE_FAST || MODE == MODE_SF32;
+    f32x4 part[chain ? 1 : FN][chain ? 1 : FM];
+    auto mma_half = [&](const Frag& f, const float* c_a, const float* c_b) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            bf16x8 ab[FM];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) ab[i] = to_bf16x8<FA>(f.a[i], q, c_a[i]);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const bf16x8 bb = to_bf16x8<FB>(f.b[j], q, c_b[j]);
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    if constexpr (chain) acc[j][i] = mfma_bf16(bb, ab[i], acc[j][i]);
+                    else part[j][i] = mfma_bf16(bb, ab[i], part[j][i]);
+                }
+            }
+        }
+    };
+    // The scales of step kt: s_a / s_b fold a block-scaled partial into the
+    // accumulator, c_a / c_b ride in the FP8 -> bf16 conversion (MX groups).
+    auto step_scales = [&](int kt, float* s_a, float (*s_b)[4], float* c_a, float* c_b) {
         if (MODE == MODE_BLOCK) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) s_a[i] = sc_cur.a[i];
@@ -491,49 +517,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) c_b[j] = 1.0f;
         }
-        if (MODE == MODE_BLOCK || MODE == MODE_SF32) sc_cur = sc_next;
-
-        const uint8_t* As = cur + wm * WTM * kBK;
-        const uint8_t* Bs = cur + BM * kBK + wn * WTN * kBK;
-        // Fast / MX: one chain over K straight into the accumulators. Slow / block:
-        // a fresh fp32 partial per 128-chunk, promoted into the accumulator after.
-        constexpr bool chain = MODE == MODE_FAST || MODE == MODE_SF32;
-        f32x4 part[chain ? 1 : FN][chain ? 1 : FM];
-        if constexpr (!chain) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int i = 0; i < FM; ++i) part[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        // The lane's 32 bytes are read as two 16-byte halves (sub-steps 0-1, 2-3),
-        // which keeps the live FP8 operands to 4 registers per fragment.
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            // keep the scheduler from hoisting the second half's reads and converts
-            // above the first half's MFMAs (that costs registers, not time)
-            if (h) __builtin_amdgcn_sched_barrier(0);
-            const int fo = h ? foff1 : foff0;
-            i32x4 ar[FM], br[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) ar[i] = *(const i32x4*)(As + i * 16 * kBK + fo);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) br[j] = *(const i32x4*)(Bs + j * 16 * kBK + fo);
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                bf16x8 ab[FM];
-#pragma unroll
-                for (int i = 0; i < FM; ++i) ab[i] = to_bf16x8<FA>(ar[i], q, c_a[i]);
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const bf16x8 bb = to_bf16x8<FB>(br[j], q, c_b[j]);
-#pragma unroll
-                    for (int i = 0; i < FM; ++i) {
-                        if constexpr (chain) acc[j][i] = mfma_bf16(bb, ab[i], acc[j][i]);
-                        else part[j][i] = mfma_bf16(bb, ab[i], part[j][i]);
-                    }
-                }
-            }
-        }
+    };
+    auto promote = [&](const float* s_a, const float (*s_b)[4]) {
         if constexpr (!chain) {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
@@ -549,19 +534,74 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
                 }
         }
     };
-    if constexpr (STAGES == 2) {
+    auto zero_part = [&]() {
+        if constexpr (!chain) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int i = 0; i < FM; ++i) part[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    // The stage of step kt has landed in every wave: wait for this wave's loads,
+    // mask a chunk straddling a ragged K, then the workgroup barrier (its
+    // workgroup fence also makes the compiler drain every outstanding load;
+    // issuing the loads untracked with a fence-free barrier measured no faster).
+    auto stage_ready = [&](int kt, uint8_t* stage) {
+        __builtin_amdgcn_s_waitcnt(0);
+        if (k_tail && kt == KT - 1 && (K & 15)) mask_straddle(kt, stage);
+        __syncthreads();
+    };
+
+    if constexpr (PIPE) {
+        Frag f0, f1;
+        auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
+            float s_a[FM], s_b[FN][4], c_a[FM], c_b[FN];
+            step_scales(kt, s_a, s_b, c_a, c_b);
+            if (MODE == MODE_BLOCK || MODE == MODE_SF32) sc_cur = load_scales(kt + 1);
+            zero_part();
+            read_frag(cur, 1, f1);  // second half of this step, under the first half's MFMAs
+            mma_half(f0, c_a, c_b);
+            stage_ready(kt + 1, nxt);
+            issue(kt + 2, cur);  // the stage just read, for the step after next
+            if (kt + 1 < KT) read_frag(nxt, 0, f0);  // next step's first half, under this half's MFMAs
+            mma_half(f1, c_a, c_b);
+            promote(s_a, s_b);
+        };
+        if (KT > 0) {
+            issue(0, smem0);
+            stage_ready(0, smem0);
+            issue(1, smem1);
+            read_frag(smem0, 0, f0);
+            for (int kt = 0; kt < KT; kt += 2) {
+                step(kt, smem0, smem1);
+                if (kt + 1 < KT) step(kt + 1, smem1, smem0);
+            }
+        }
+    } else {
+        // Each half-step reads its fragments and then multiplies; a second wave
+        // on the SIMD covers the read latency.
+        auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
+            stage_ready(kt, cur);
+            float s_a[FM], s_b[FN][4], c_a[FM], c_b[FN];
+            step_scales(kt, s_a, s_b, c_a, c_b);
+            if (MODE == MODE_BLOCK || MODE == MODE_SF32) sc_cur = load_scales(kt + 1);
+            issue(kt + 1, nxt);
+            zero_part();
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                // keep the scheduler from hoisting the second half's reads and
+                // converts above the first half's MFMAs (that costs registers, not time)
+                if (h) __builtin_amdgcn_sched_barrier(0);
+                Frag f;
+                read_frag(cur, h, f);
+                mma_half(f, c_a, c_b);
+            }
+            promote(s_a, s_b);
+        };
         issue(0, smem0);
         for (int kt = 0; kt < KT; kt += 2) {
             step(kt, smem0, smem1);
             if (kt + 1 < KT) step(kt + 1, smem1, smem0);
-        }
-    } else {
-        issue(0, smem0);
-        issue(1, smem1);
-        for (int kt = 0; kt < KT; kt += 3) {
-            step(kt, smem0, smem2);
-            if (kt + 1 < KT) step(kt + 1, smem1, smem0);
-            if (kt + 2 < KT) step(kt + 2, smem2, smem1);
         }
     }
     // the loads issued for steps past the end (they fetch nothing) must land

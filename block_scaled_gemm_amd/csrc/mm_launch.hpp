@@ -7,7 +7,9 @@
 
 namespace mmfp8 {
 
-// Workgroup tiles of gemm_tile, largest first: BM x BN, waves WM x WN, LDS stages.
+// Workgroup tiles of gemm_tile, largest first: BM x BN, waves WM x WN, and
+// whether the main loop runs its fragment reads a half-step ahead (the 4-wave
+// tile has one wave per SIMD and needs it to hide LDS latency).
 // 256x256 gives each of its 8 waves a 64x128 tile (1.5 FP8->bf16 converts per
 // MFMA); the others use 64x64 wave tiles (2 converts per MFMA).
 enum TileCfg : int { CFG_256x256 = 0, CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x64 = 3, CFG_COUNT = 4 };
@@ -15,7 +17,7 @@ constexpr int kCfgBM[CFG_COUNT] = {256, 128, 128, 64};
 constexpr int kCfgBN[CFG_COUNT] = {256, 256, 128, 64};
 constexpr int kCfgWM[CFG_COUNT] = {4, 2, 2, 2};
 constexpr int kCfgWN[CFG_COUNT] = {2, 4, 2, 2};
-constexpr int kCfgStages[CFG_COUNT] = {2, 3, 3, 2};
+constexpr int kCfgPipe[CFG_COUNT] = {0, 0, 1, 0};
 
 // gemm_skinny: waves per workgroup and K steps in flight per wave, by MT
 // (M <= 16 MT). Sixteen waves with two steps each put a K = 4096 B tile in
@@ -57,7 +59,7 @@ constexpr int min_cfg(int mode, int sbm) {
 template <int MODE, int SBM>
 hipError_t tile_dispatch(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s) {
 #define MMFP8_TILE(C, A, B)                                                                                  \
-    hipLaunchKernelGGL((gemm_tile<kCfgBM[C], kCfgBN[C], kCfgWM[C], kCfgWN[C], kCfgStages[C], MODE, A, B, SBM>), \
+    hipLaunchKernelGGL((gemm_tile<kCfgBM[C], kCfgBN[C], kCfgWM[C], kCfgWN[C], kCfgPipe[C], MODE, A, B, SBM>), \
                        dim3(grid), dim3(kCfgWM[C] * kCfgWN[C] * 64), 0, s, p)
 #define MMFP8_FMTS(C)                                    \
     if (fa == 0 && fb == 0) MMFP8_TILE(C, 0, 0);         \
