@@ -303,7 +303,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the LDS addressing scalar
     const int wm = wave / WN, wn = wave % WN;
     int l, tm, tn;
     tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, 8, l, tm, tn);
@@ -337,28 +338,27 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
     }
 
     auto issue = [&](int kt, uint8_t* sbase) {
+        if (kt >= KT) return;  // past the end: nothing to load
+        // The step's K offset rides in the scalar offset, so the per-lane offsets
+        // stay fixed. In the last step of a ragged K the lanes whose chunk starts
+        // at or past K get an out-of-range offset and read zero.
         const uint32_t kb = (uint32_t)(kt * kBK);
-        // in the last step of a ragged K, chunks starting at or past K read zero
         const bool last = k_tail && kt == KT - 1;
-        // Steps past the end are issued too, with every offset out of range: they
-        // fetch nothing and zero a stage no later step reads, and keep the number
-        // of loads per step constant for the vmcnt bookkeeping.
-        const bool dead = kt >= KT;
         // (the offsets are computed in statements: clang 22 drops the host stub of
         // this kernel when a conditional expression is passed to the builtin)
 #pragma unroll
         for (int q = 0; q < A_INS; ++q) {
-            uint32_t off = aoff[q] + kb;
-            if (dead || (last && (int)kb + achunk[q] * 16 >= K)) off = kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sbase + (wave * A_INS + q) * 1024), 16, off, 0,
-                                                     0, 0);
+            uint32_t off = aoff[q];
+            if (last && (int)kb + achunk[q] * 16 >= K) off = kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sbase + (wave * A_INS + q) * 1024), 16, off,
+                                                     (int)kb, 0, 0);
         }
 #pragma unroll
         for (int q = 0; q < B_INS; ++q) {
-            uint32_t off = boff[q] + kb;
-            if (dead || (last && (int)kb + bchunk[q] * 16 >= K)) off = kOOB;
+            uint32_t off = boff[q];
+            if (last && (int)kb + bchunk[q] * 16 >= K) off = kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sbase + BM * kBK + (wave * B_INS + q) * 1024),
-                                                     16, off, 0, 0, 0);
+                                                     16, off, (int)kb, 0, 0);
         }
     };
     // In the last step of a K that is not a multiple of 16, a chunk straddling K
