@@ -38,7 +38,7 @@ N = K = 4096
 PEAK_FP8_TFLOPS = 5033.0      # MI355X dense FP8 MFMA: 256 CUs x 8192 flop/clk x 2.4 GHz
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CUs x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-COUNTERS = os.path.join(ROOT, "profiles", "gemm_tile_128x256_slow_M8192_N4096_K4096_counters.md")
+COUNTERS = os.path.join(ROOT, "profiles", "gemm_tile_M8192_N4096_K4096_slow_counters.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_scaled_gemm_amd", "csrc", f) for f in ("mm_kernels.hpp", "mm_launch.hpp")]
 ROTATION_BYTES = 512 << 20    # 2x the Infinity Cache
 METRIC = "FP8 scaled-GEMM TFLOP/s and % of MI355X FP8 MFMA peak, M=16..8192"
