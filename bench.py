@@ -123,6 +123,100 @@ def cpu_baseline():
                       f"{secs:.1f} s"}
 
 
+# ------------------------------------------------------------------ other workloads
+# Single-GEMM timings of the remaining configurations, for their own roofline
+# lines (`--workload NAME`); the default run above is the benchmark itself.
+
+OTHER = {
+    "block": "E4M3 1x128 / 128x128 block-scaled GEMM, M=4096, N=14336, K=4096, bf16 out",
+    "mx_amax": "batched E4M3 GEMM with power-of-two scales per 32 K, L=8, M=N=2048, K=8192, f32 C + amax + index",
+    "e4m3_out": "E4M3 GEMM, M=8192, N=28672, K=8200 (lda 8200), slow, E4M3 out via scale_result=1/16",
+    "e5m2_f16": "E5M2 GEMM, M=8192, N=28672, K=8200 (lda 8200), slow, f16 out",
+}
+
+
+def run_other(name, steps, warmup):
+    import torch
+    import block_scaled_gemm_amd as mm
+    import datagen
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    t0 = time.time()
+    if name == "block":
+        d = datagen.workload3()
+        M, K = d["a"].shape; N = d["b"].shape[0]; L = 1
+        a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
+        sa = torch.from_numpy(d["scale_a"]).to(dev); sb = torch.from_numpy(d["scale_b"]).to(dev)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        out_bytes = 2
+
+        def launch():
+            return mm.mm_scaled_gemm(M, N, K, a.data_ptr(), mm.MM_F8_E4M3FN, K, b.data_ptr(), mm.MM_F8_E4M3FN, K,
+                                     sa.data_ptr(), mm.MM_SCALE_1x128, sb.data_ptr(), mm.MM_SCALE_128x128, 0,
+                                     out.data_ptr(), mm.MM_BF16, N, 0, stream)
+        scale_bytes = 4 * (sa.numel() + sb.numel())
+    elif name == "mx_amax":
+        d = datagen.workload4()
+        L, M, K = d["a"].shape; N = d["b"].shape[1]
+        a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
+        sfa = torch.from_numpy(d["sfa"]).to(dev); sfb = torch.from_numpy(d["sfb"]).to(dev)
+        c = torch.empty((L, M, N), dtype=torch.float32, device=dev)
+        amax = torch.empty((1,), dtype=torch.float32, device=dev)
+        idx = torch.empty((1,), dtype=torch.int64, device=dev)
+        out_bytes = 4
+
+        def launch():
+            return mm.mm_blockscaled_gemm_amax(M, N, K, L, a.data_ptr(), b.data_ptr(), mm.MM_F8_E4M3FN,
+                                               sfa.data_ptr(), sfb.data_ptr(), 32, c.data_ptr(), mm.MM_F32,
+                                               amax.data_ptr(), idx.data_ptr(), stream)
+        scale_bytes = 4 * (sfa.numel() + sfb.numel()) + 12
+    else:
+        d = datagen.workload5a() if name == "e4m3_out" else datagen.workload5b()
+        M, K = d["a"].shape; N = d["b"].shape[0]; L = 1
+        fa = mm.MM_F8_E4M3FN if name == "e4m3_out" else mm.MM_F8_E5M2
+        a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
+        sa = torch.tensor([float(d["scale_a"])], dtype=torch.float32, device=dev)
+        sb = torch.tensor([float(d["scale_b"])], dtype=torch.float32, device=dev)
+        sr = torch.tensor([float(d.get("scale_result", 1.0))], dtype=torch.float32, device=dev)
+        dt = mm.MM_F8_E4M3FN if name == "e4m3_out" else mm.MM_F16
+        out_bytes = 1 if name == "e4m3_out" else 2
+        out = torch.empty((M * N * out_bytes,), dtype=torch.uint8, device=dev)
+
+        def launch():
+            return mm.mm_scaled_gemm(M, N, K, a.data_ptr(), fa, K, b.data_ptr(), fa, K, sa.data_ptr(),
+                                     mm.MM_SCALE_TENSOR, sb.data_ptr(), mm.MM_SCALE_TENSOR,
+                                     sr.data_ptr() if name == "e4m3_out" else 0, out.data_ptr(), dt, N, 0, stream)
+        scale_bytes = 12
+    torch.cuda.synchronize()
+    log(f"{name}: inputs ready in {time.time() - t0:.1f}s")
+    for _ in range(warmup):
+        if launch() != mm.MM_OK:
+            raise RuntimeError(mm.mm_last_error())
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        launch()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / steps
+    flops = 2.0 * L * M * N * K
+    tf = flops / us / 1e6
+    nbytes = L * (M * K + N * K + M * N * out_bytes) + scale_bytes
+    result = {
+        "metric": f"{OTHER[name]}: TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "data": "synthetic",
+        "config": {"workload": OTHER[name], "L": L, "M": M, "N": N, "K": K},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None, "algorithmic_bytes": nbytes,
+                     "hbm_gbs_algorithmic": round(nbytes / us / 1e3, 1)},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,11 +227,17 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device (reads and writes that many bytes) so that "
                          "profiler byte counters can be scaled against a kernel of known traffic")
+    ap.add_argument("--workload", choices=sorted(OTHER), default=None,
+                    help="time one of the other configurations instead of the benchmark step")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: the GEMM runs on one GPU; --gpus {args.gpus} is not supported (across GPUs the "
+              "output tiles would be split by N or by the batch L, with one all-reduce of the amax)",
+              file=sys.stderr)
         sys.exit(2)
+    if args.workload:
+        run_other(args.workload, args.steps if args.steps != 200 else 20, args.warmup if args.warmup != 20 else 3)
+        return
 
     import torch
     import block_scaled_gemm_amd as mm

@@ -339,26 +339,33 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
 
     auto issue = [&](int kt, uint8_t* sbase) {
         if (kt >= KT) return;  // past the end: nothing to load
-        // The step's K offset rides in the scalar offset, so the per-lane offsets
-        // stay fixed. In the last step of a ragged K the lanes whose chunk starts
-        // at or past K get an out-of-range offset and read zero.
         const uint32_t kb = (uint32_t)(kt * kBK);
+        // Where every chunk of the step lies inside its row, the step's K offset
+        // rides in the scalar offset and the per-lane offsets stay loop-invariant
+        // (rows past the matrix still read zero: their per-lane offset alone is
+        // past the buffer's extent). In the last step of a ragged K the whole
+        // offset goes in the per-lane part, which the range check covers (the
+        // scalar part is not checked), so a chunk straddling the end of the last
+        // row reads zeros past it; chunks starting at or past K get an
+        // out-of-range offset.
         const bool last = k_tail && kt == KT - 1;
+        const int soff = last ? 0 : (int)kb;
         // (the offsets are computed in statements: clang 22 drops the host stub of
-        // this kernel when a conditional expression is passed to the builtin)
+        // this kernel when a conditional expression is passed to the builtin, or
+        // when the builtin is called from two branches)
 #pragma unroll
         for (int q = 0; q < A_INS; ++q) {
             uint32_t off = aoff[q];
-            if (last && (int)kb + achunk[q] * 16 >= K) off = kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sbase + (wave * A_INS + q) * 1024), 16, off,
-                                                     (int)kb, 0, 0);
+            if (last) off = (int)kb + achunk[q] * 16 >= K ? kOOB : off + kb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sbase + (wave * A_INS + q) * 1024), 16, off, soff,
+                                                     0, 0);
         }
 #pragma unroll
         for (int q = 0; q < B_INS; ++q) {
             uint32_t off = boff[q];
-            if (last && (int)kb + bchunk[q] * 16 >= K) off = kOOB;
+            if (last) off = (int)kb + bchunk[q] * 16 >= K ? kOOB : off + kb;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sbase + BM * kBK + (wave * B_INS + q) * 1024),
-                                                     16, off, (int)kb, 0, 0);
+                                                     16, off, soff, 0, 0);
         }
     };
     // In the last step of a K that is not a multiple of 16, a chunk straddling K

@@ -46,13 +46,13 @@ hipError_t launch_debug_convert(const float* x, void* y, int t, int64_t n, hipSt
 
 // Largest tile each mode is built for: the fast chain keeps 128 fp32
 // accumulators per lane and little else, so only it has the 64x128 wave tile.
-// The promoted and MX modes also hold partials or scale operands and stop at
-// 128x256 (eight 64x64 waves, two per SIMD); the block-scaled mode holds up to
-// 16 scale_b values per lane besides, which two waves per SIMD cannot keep in
-// registers, so it stops at 128x128 (four waves, one per SIMD).
+// The promoted, MX and 128x128-block-scaled modes also hold partials or scale
+// operands and stop at 128x256 (eight 64x64 waves, two per SIMD). With a 1x128
+// scale_b the block-scaled mode holds 16 scale_b values per lane besides, which
+// two waves per SIMD cannot keep in registers, so it stops at 128x128 (four
+// waves, one per SIMD).
 constexpr int min_cfg(int mode, int sbm) {
-    (void)sbm;
-    return mode == MODE_FAST ? CFG_256x256 : mode == MODE_BLOCK ? CFG_128x128 : CFG_128x256;
+    return mode == MODE_FAST ? CFG_256x256 : (mode == MODE_BLOCK && sbm == SB_1x128) ? CFG_128x128 : CFG_128x256;
 }
 
 // Launch gemm_tile<BM, BN, MODE, fa, fb, SBM> for a runtime cfg / format pair.
@@ -72,7 +72,7 @@ hipError_t tile_dispatch(int cfg, int fa, int fb, const GemmArgs& p, int grid, h
             if constexpr (MODE == MODE_FAST) { MMFP8_FMTS(CFG_256x256) }
             break;
         case CFG_128x256:
-            if constexpr (MODE != MODE_BLOCK) { MMFP8_FMTS(CFG_128x256) }
+            if constexpr (!(MODE == MODE_BLOCK && SBM == SB_1x128)) { MMFP8_FMTS(CFG_128x256) }
             break;
         case CFG_128x128: MMFP8_FMTS(CFG_128x128) break;
         default: MMFP8_FMTS(CFG_64x64) break;
