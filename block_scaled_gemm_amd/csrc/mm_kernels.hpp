@@ -296,7 +296,16 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
     constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;  // 1 KB LDS-DMA writes per wave per step
     constexpr int INS = A_INS + B_INS;
     static_assert(A_INS * 8 * NW == BM && B_INS * 8 * NW == BN, "tile rows must split evenly over the waves");
-    constexpr int STAGE = (BM + BN) * kBK;
+    // Per-row scales travel with the tiles, into the end of each stage: MX, the
+    // step's four 32-groups of every A and B row; block-scaled, the step's
+    // scale_a of every A row (and scale_b of every B row when it is 1x128; a
+    // 128x128 scale_b is one value per 128 columns, read from memory directly).
+    // One 4-byte-per-lane load fills one scale column of 64 rows.
+    constexpr int SA_W = MODE == MODE_SF32 ? 4 : (MODE == MODE_BLOCK ? 1 : 0);
+    constexpr int SB_W = MODE == MODE_SF32 ? 4 : ((MODE == MODE_BLOCK && SBM == SB_1x128) ? 1 : 0);
+    constexpr int SC_A_INS = BM / 64 * SA_W, SC_INS = SC_A_INS + BN / 64 * SB_W;
+    static_assert(BM % 64 == 0 && BN % 64 == 0, "scale columns are loaded 64 rows at a time");
+    constexpr int STAGE = (BM + BN) * kBK + SC_INS * 256;
     // Distinct LDS objects (not one array indexed by stage) so that the compiler
     // can tell a fragment read of one stage from the in-flight LDS-DMA writes
     // into another and does not wait for those loads.
@@ -337,6 +346,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
         boff[q] = (uint32_t)(((wave * B_INS + q) * 8 + ld_row) * p.ldb + bchunk[q] * 16);
     }
 
+    const float* sa_l = p.sa + (int64_t)l * p.sa_batch;
+    const float* sb_l = p.sb + (int64_t)l * p.sb_batch;
+    // the tile's scale rows (rows past the matrix read zero; their results are discarded)
+    const rsrc_t rsa = make_rsrc(sa_l + (int64_t)m0 * p.sa_ld, SA_W ? (uint32_t)(min(BM, p.M - m0) * p.sa_ld * 4) : 0u);
+    const rsrc_t rsb = make_rsrc(sb_l + (int64_t)n0 * p.sb_ld, SB_W ? (uint32_t)(min(BN, p.N - n0) * p.sb_ld * 4) : 0u);
+
     auto issue = [&](int kt, uint8_t* sbase) {
         if (kt >= KT) return;  // past the end: nothing to load
         const uint32_t kb = (uint32_t)(kt * kBK);
@@ -366,6 +381,26 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
             if (last) off = (int)kb + bchunk[q] * 16 >= K ? kOOB : off + kb;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sbase + BM * kBK + (wave * B_INS + q) * 1024),
                                                      16, off, soff, 0, 0);
+        }
+        // Scale columns: load t fills column j of rows 64 rg .. 64 rg + 63, at
+        // LDS [j][row] after the tiles. MX groups past ceil(K/32) read whatever
+        // follows (the next row, or zero past the last): their data is zero and
+        // their conversion scale is replaced by 1 at use.
+        if constexpr (SC_A_INS > 0) {
+            for (int t = wave; t < SC_A_INS; t += NW) {
+                const int j = t % SA_W, rg = t / SA_W;
+                const uint32_t off = (uint32_t)(((rg * 64 + lane) * p.sa_ld + kt * SA_W + j) * 4);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsa, (lds_void*)(sbase + (BM + BN) * kBK + (j * BM + rg * 64) * 4), 4, off, 0, 0, 0);
+            }
+        }
+        if constexpr (SC_INS > SC_A_INS) {
+            for (int t = wave; t < SC_INS - SC_A_INS; t += NW) {
+                const int j = t % SB_W, rg = t / SB_W;
+                const uint32_t off = (uint32_t)(((rg * 64 + lane) * p.sb_ld + kt * SB_W + j) * 4);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsb, (lds_void*)(sbase + (BM + BN) * kBK + (BM * SA_W + j * BN + rg * 64) * 4), 4, off, 0, 0, 0);
+            }
         }
     };
     // In the last step of a K that is not a multiple of 16, a chunk straddling K
@@ -404,61 +439,33 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Per-lane scale rows (clamped to the matrix: results of clamped rows are discarded).
-    int srow_a[FM];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) srow_a[i] = min(m0 + wm * WTM + i * 16 + fr, p.M - 1);
+    // 128x128 scale_b: one value per 128 columns, the same for the whole
+    // fragment (clamped to the matrix: results of clamped columns are discarded).
     int srow_b[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        if (MODE == MODE_SF32) srow_b[j] = min(n0 + wn * WTN + j * 16 + fr, p.N - 1);
-        else if (SBM == SB_128x128) srow_b[j] = min((n0 + wn * WTN + j * 16) / 128, (p.N - 1) / 128);
-        else srow_b[j] = n0 + wn * WTN + j * 16 + 4 * fg;  // first of 4 rows, clamped at use
-    }
-    const float* sa_l = p.sa + (int64_t)l * p.sa_batch;
-    const float* sb_l = p.sb + (int64_t)l * p.sb_batch;
+    for (int j = 0; j < FN; ++j) srow_b[j] = min((n0 + wn * WTN + j * 16) / 128, (p.N - 1) / 128);
     // epilogue scales, read now so that their latency hides behind the main loop
     float alpha = 1.0f;
     if (MODE == MODE_FAST || MODE == MODE_SLOW) alpha = p.sa[0] * p.sb[0];
     const bool fp8_out = p.d_type == T_E4M3 || p.d_type == T_E5M2;
     const float sr = (fp8_out && p.scale_result) ? p.scale_result[0] : 1.0f;
 
-    // Scales of one step, loaded one step ahead of their use (before that step's
-    // LDS-DMA loads are issued, so waiting for them never waits for those).
-    // Raw values only: anything computed from them here would pull the wait forward.
+    // 128x128 scale_b of one step, loaded one step ahead of its use (the other
+    // scales come through LDS with the tiles).
+    constexpr bool kSbMem = MODE == MODE_BLOCK && SBM == SB_128x128;
     struct StepScales {
-        float a[FM];       // BLOCK: s_a of the fragment row; SF32: the lane's group scale
-        float b[FN][4];    // BLOCK: s_b of the 4 accumulator rows; SF32: b[j][0] per lane
+        float b[FN];
     };
     auto load_scales = [&](int kt) {
         StepScales sc;
         if (KT == 0) return sc;  // K = 0: no step reads them (and the tables may be empty)
         kt = min(kt, KT - 1);    // the prefetch past the last step reads a valid entry
-        if (MODE == MODE_BLOCK) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) sc.a[i] = sa_l[(int64_t)srow_a[i] * p.sa_ld + kt];
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                if (SBM == SB_128x128) {
-                    sc.b[j][0] = sb_l[(int64_t)srow_b[j] * p.sb_ld + kt];
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sc.b[j][r] = sb_l[(int64_t)min(srow_b[j] + r, p.N - 1) * p.sb_ld + kt];
-                }
-            }
-        }
-        if (MODE == MODE_SF32) {
-            // groups past ceil(K/32) hold zero data; the clamp keeps the read in range
-            const int grp = min(kt * 4 + fg, p.sa_ld - 1);
-#pragma unroll
-            for (int i = 0; i < FM; ++i) sc.a[i] = sa_l[(int64_t)srow_a[i] * p.sa_ld + grp];
-#pragma unroll
-            for (int j = 0; j < FN; ++j) sc.b[j][0] = sb_l[(int64_t)srow_b[j] * p.sb_ld + grp];
-        }
+        for (int j = 0; j < FN; ++j) sc.b[j] = sb_l[(int64_t)srow_b[j] * p.sb_ld + kt];
         return sc;
     };
     StepScales sc_cur;
-    if (MODE == MODE_BLOCK || MODE == MODE_SF32) sc_cur = load_scales(0);
+    if (kSbMem) sc_cur = load_scales(0);
 
     // Main loop, two LDS stages, software-pipelined by half-steps: the lane's
     // 32 bytes of a step are read as two 16-byte halves (sub-steps 0-1, 2-3),
@@ -503,21 +510,24 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
     };
     // The scales of step kt: s_a / s_b fold a block-scaled partial into the
     // accumulator, c_a / c_b ride in the FP8 -> bf16 conversion (MX groups).
-    auto step_scales = [&](int kt, float* s_a, float (*s_b)[4], float* c_a, float* c_b) {
+    // They are read from the step's stage before the barrier that frees it.
+    auto step_scales = [&](int kt, const uint8_t* stage, float* s_a, float (*s_b)[4], float* c_a, float* c_b) {
+        const float* scA = (const float*)(stage + (BM + BN) * kBK);
+        const float* scB = scA + BM * SA_W;
         if (MODE == MODE_BLOCK) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) s_a[i] = sc_cur.a[i];
+            for (int i = 0; i < FM; ++i) s_a[i] = scA[wm * WTM + i * 16 + fr];
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) s_b[j][r] = SBM == SB_128x128 ? sc_cur.b[j][0] : sc_cur.b[j][r];
+                for (int r = 0; r < 4; ++r) s_b[j][r] = kSbMem ? sc_cur.b[j] : scB[wn * WTN + j * 16 + 4 * fg + r];
         }
         if (MODE == MODE_SF32) {
             const bool gv = kt * 4 + fg < p.sa_ld;  // groups past ceil(K/32) hold zero data
 #pragma unroll
-            for (int i = 0; i < FM; ++i) c_a[i] = gv ? e8m0_scale(sc_cur.a[i]) : 1.0f;
+            for (int i = 0; i < FM; ++i) c_a[i] = gv ? e8m0_scale(scA[fg * BM + wm * WTM + i * 16 + fr]) : 1.0f;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) c_b[j] = gv ? e8m0_scale(sc_cur.b[j][0]) : 1.0f;
+            for (int j = 0; j < FN; ++j) c_b[j] = gv ? e8m0_scale(scB[fg * BN + wn * WTN + j * 16 + fr]) : 1.0f;
         } else {
 #pragma unroll
             for (int i = 0; i < FM; ++i) c_a[i] = 1.0f;
@@ -563,8 +573,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
         Frag f0, f1;
         auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
             float s_a[FM], s_b[FN][4], c_a[FM], c_b[FN];
-            step_scales(kt, s_a, s_b, c_a, c_b);
-            if (MODE == MODE_BLOCK || MODE == MODE_SF32) sc_cur = load_scales(kt + 1);
+            step_scales(kt, cur, s_a, s_b, c_a, c_b);
+            if (kSbMem) sc_cur = load_scales(kt + 1);
             zero_part();
             read_frag(cur, 1, f1);  // second half of this step, under the first half's MFMAs
             mma_half(f0, c_a, c_b);
@@ -590,8 +600,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
         auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
             stage_ready(kt, cur);
             float s_a[FM], s_b[FN][4], c_a[FM], c_b[FN];
-            step_scales(kt, s_a, s_b, c_a, c_b);
-            if (MODE == MODE_BLOCK || MODE == MODE_SF32) sc_cur = load_scales(kt + 1);
+            step_scales(kt, cur, s_a, s_b, c_a, c_b);
+            if (kSbMem) sc_cur = load_scales(kt + 1);
             issue(kt + 1, nxt);
             zero_part();
 #pragma unroll
