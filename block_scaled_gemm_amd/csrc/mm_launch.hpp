@@ -44,15 +44,13 @@ hipError_t launch_amax_init(uint32_t* bits, unsigned long long* key, hipStream_t
 hipError_t launch_amax_finalize(float* amax, unsigned long long* key, hipStream_t s);
 hipError_t launch_debug_convert(const float* x, void* y, int t, int64_t n, hipStream_t s);
 
-// Largest tile each mode is built for: the fast chain keeps 128 fp32
-// accumulators per lane and little else, so only it has the 64x128 wave tile.
-// The promoted, MX and 128x128-block-scaled modes also hold partials or scale
-// operands and stop at 128x256 (eight 64x64 waves, two per SIMD). With a 1x128
-// scale_b the block-scaled mode holds 16 scale_b values per lane besides, which
-// two waves per SIMD cannot keep in registers, so it stops at 128x128 (four
-// waves, one per SIMD).
+// Largest tile each mode is built for. The chained modes (fast, MX) keep 128
+// fp32 accumulators per lane and little else, so they take the 64x128 wave
+// tile; the promoted modes (slow, block-scaled) also hold a 128-chunk partial
+// per accumulator and stop at 128x256 (eight 64x64 waves, two per SIMD).
 constexpr int min_cfg(int mode, int sbm) {
-    return mode == MODE_FAST ? CFG_256x256 : (mode == MODE_BLOCK && sbm == SB_1x128) ? CFG_128x128 : CFG_128x256;
+    (void)sbm;
+    return (mode == MODE_FAST || mode == MODE_SF32) ? CFG_256x256 : CFG_128x256;
 }
 
 // Launch gemm_tile<BM, BN, MODE, fa, fb, SBM> for a runtime cfg / format pair.
@@ -69,11 +67,9 @@ hipError_t tile_dispatch(int cfg, int fa, int fb, const GemmArgs& p, int grid, h
     if (cfg < min_cfg(MODE, SBM)) cfg = min_cfg(MODE, SBM);
     switch (cfg) {
         case CFG_256x256:
-            if constexpr (MODE == MODE_FAST) { MMFP8_FMTS(CFG_256x256) }
+            if constexpr (MODE == MODE_FAST || MODE == MODE_SF32) { MMFP8_FMTS(CFG_256x256) }
             break;
-        case CFG_128x256:
-            if constexpr (!(MODE == MODE_BLOCK && SBM == SB_1x128)) { MMFP8_FMTS(CFG_128x256) }
-            break;
+        case CFG_128x256: MMFP8_FMTS(CFG_128x256) break;
         case CFG_128x128: MMFP8_FMTS(CFG_128x128) break;
         default: MMFP8_FMTS(CFG_64x64) break;
     }
