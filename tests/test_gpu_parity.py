@@ -160,6 +160,43 @@ def test_mixed_and_e5m2_formats(fa, fb):
         check_gemm(d, 0, 0, dt, False, what=f"mixed {fa}x{fb} {DT_NAME[dt]}")
 
 
+# ------------------------------------------------------------------ every production tile shape
+
+# (M, N, K, fast) chosen so that each workgroup tile the library picks for
+# per-tensor scales runs at least once at a size that selects it, with a ragged
+# K whose last chunk straddles a 16-byte boundary (K % 16 == 8).
+TILE_CASES = [(4096, 4096, 1032, True),    # fast: 256x256 tile, eight 64x128 waves
+              (2048, 4096, 1032, True),    # fast: 128x256
+              (1024, 4096, 1032, True),    # fast: 128x128, pipelined fragment reads
+              (2048, 4096, 1032, False),   # slow: 128x256
+              (1024, 4096, 1032, False),   # slow: 128x128, pipelined
+              (256, 4096, 1032, False),    # K split over the waves, 64x64 tiles
+              (100, 4096, 1032, True)]     # K split over the waves, 32x64 tiles
+
+
+@pytest.mark.parametrize("M,N,K,fast", TILE_CASES)
+def test_production_tiles_per_tensor(M, N, K, fast):
+    g = np.random.default_rng(M + K + int(fast))
+    a = datagen.gauss_codes(g, (M, K), 64.0)
+    b = datagen.gauss_codes(g, (N, K), 64.0)
+    d = dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN, scale_a=np.float32(0.5), scale_b=np.float32(0.25))
+    check_gemm(d, 0, 0, BF16, fast, rows=sample_rows(M, 8), what=f"{M}x{N}x{K} fast={fast}")
+
+
+@pytest.mark.parametrize("sb_mode", [1, 2], ids=["1x128", "128x128"])
+@pytest.mark.parametrize("M", [2048, 1024], ids=["128x256", "128x128"])
+def test_production_tiles_block_scaled(M, sb_mode):
+    N, K = 4096, 1032
+    g = np.random.default_rng(M + sb_mode)
+    a = datagen.gauss_codes(g, (M, K), 64.0)
+    b = datagen.gauss_codes(g, (N, K), 64.0)
+    kb = -(-K // 128)
+    sa = datagen.log_uniform_scales(g, (M, kb))
+    sb = datagen.log_uniform_scales(g, (N if sb_mode == 1 else -(-N // 128), kb))
+    d = dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN, scale_a=sa, scale_b=sb)
+    check_gemm(d, 1, sb_mode, BF16, False, rows=sample_rows(M, 8), what=f"block {M}x{N}x{K} sb={sb_mode}")
+
+
 # ------------------------------------------------------------------ workload 3: block scales
 
 @pytest.mark.parametrize("sb_mode", [1, 2], ids=["1x128", "128x128"])
@@ -250,6 +287,17 @@ def test_sf32_e5m2_unit_scales_is_plain_gemm():
     b = datagen.gauss_codes(g, (1, 256, 256), 1.0, E5M2)
     w = dict(a=a, b=b, ab_fmt=E5M2, sfa=np.ones((1, 512, 8), np.float32), sfb=np.ones((1, 256, 8), np.float32))
     check_amax_case(w, F32)
+
+
+@pytest.mark.parametrize("L", [2, 1], ids=["128x256", "128x128"])
+def test_production_tiles_sf32(L):
+    """MX-scaled GEMM + amax at sizes that select the 128x256 and the
+    (pipelined) 128x128 tile; the full-size workload below selects 256x256."""
+    w = datagen.workload4(L, 2048, 2048, 1040)
+    rows = sample_rows(2048, 4)
+    c, amax, idx, value, sabs = check_amax_case(w, F32, rows=rows)
+    cf = np.abs(c.view(np.float32).reshape(-1))
+    assert amax == float(cf.max()) and idx == int(np.argmax(cf))
 
 
 def test_workload4_full_size():
