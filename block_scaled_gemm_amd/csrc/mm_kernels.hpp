@@ -167,13 +167,39 @@ __device__ __forceinline__ uint32_t cvt_e5m2(float v) {
     return __builtin_isnan(v) ? 0x7Fu : code;
 }
 
+template <int T>
+__device__ __forceinline__ uint32_t convert_t(float v) {
+    if constexpr (T == T_F32) return cvt_f32(v);
+    else if constexpr (T == T_BF16) return cvt_bf16(v);
+    else if constexpr (T == T_F16) return cvt_f16(v);
+    else if constexpr (T == T_E4M3) return cvt_e4m3(v);
+    else return cvt_e5m2(v);
+}
 __device__ __forceinline__ uint32_t convert(float v, int t) {
     switch (t) {
-        case T_F32: return cvt_f32(v);
-        case T_BF16: return cvt_bf16(v);
-        case T_F16: return cvt_f16(v);
-        case T_E4M3: return cvt_e4m3(v);
-        default: return cvt_e5m2(v);
+        case T_F32: return convert_t<T_F32>(v);
+        case T_BF16: return convert_t<T_BF16>(v);
+        case T_F16: return convert_t<T_F16>(v);
+        case T_E4M3: return convert_t<T_E4M3>(v);
+        default: return convert_t<T_E5M2>(v);
+    }
+}
+
+// A compile-time int, to hand a runtime choice to a generic lambda.
+template <int V>
+struct IC {
+    static constexpr int value = V;
+};
+// Call f(IC<t>{}) for the output type t, so that the epilogue is compiled once
+// per type instead of branching on the type at every element.
+template <class F>
+__device__ __forceinline__ void with_out_type(int t, F&& f) {
+    switch (t) {
+        case T_F32: f(IC<T_F32>{}); break;
+        case T_BF16: f(IC<T_BF16>{}); break;
+        case T_F16: f(IC<T_F16>{}); break;
+        case T_E4M3: f(IC<T_E4M3>{}); break;
+        default: f(IC<T_E5M2>{}); break;
     }
 }
 
@@ -181,12 +207,13 @@ __device__ __forceinline__ int elem_bytes(int t) { return t == T_F32 ? 4 : (t ==
 
 // Store 4 consecutive converted outputs starting at element e (row-major
 // index); `valid` of them (0..4) exist. Vector store when aligned and whole.
-__device__ __forceinline__ void store4(void* d, int t, int64_t e, const uint32_t v[4], int valid, bool vec) {
-    if (t == T_F32) {
+template <int T>
+__device__ __forceinline__ void store4(void* d, int64_t e, const uint32_t v[4], int valid, bool vec) {
+    if constexpr (T == T_F32) {
         uint32_t* p = (uint32_t*)d + e;
         if (vec && valid == 4) { *(i32x4*)p = i32x4{(int)v[0], (int)v[1], (int)v[2], (int)v[3]}; return; }
         for (int r = 0; r < valid; ++r) p[r] = v[r];
-    } else if (t == T_BF16 || t == T_F16) {
+    } else if constexpr (T == T_BF16 || T == T_F16) {
         uint16_t* p = (uint16_t*)d + e;
         if (vec && valid == 4) {
             *(i32x2*)p = i32x2{(int)(v[0] | (v[1] << 16)), (int)(v[2] | (v[3] << 16))};
@@ -626,36 +653,53 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
     __builtin_amdgcn_s_waitcnt(0);
 
     // ---------------------------------------------------------- epilogue
+    // Compiled once per output type and amax kind (AM: 0 none, 1 |x| bits,
+    // 2 key with index); amax is only asked of the MX entry.
     const int64_t dbase = (int64_t)l * p.d_batch;
     const bool want_amax = p.amax_bits || p.amax_key;
+    const bool vec = p.vec_store != 0;
     uint32_t kb = 0;
     unsigned long long kk = 0;
+    auto epilogue = [&](auto ot, auto am) {
+        constexpr int OT = decltype(ot)::value, AM = decltype(am)::value;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * WTM + i * 16 + fr;
+        for (int i = 0; i < FM; ++i) {
+            const int m = m0 + wm * WTM + i * 16 + fr;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int n = n0 + wn * WTN + j * 16 + 4 * fg;
-            const int valid = (m < p.M) ? max(0, min(4, p.N - n)) : 0;
-            uint32_t out[4];
+            for (int j = 0; j < FN; ++j) {
+                const int n = n0 + wn * WTN + j * 16 + 4 * fg;
+                const int valid = (m < p.M) ? max(0, min(4, p.N - n)) : 0;
+                uint32_t out[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                // +0.0f turns a -0 sum into +0: a sum of products starts from +0
-                float v = (acc[j][i][r] + 0.0f) * alpha;
-                if (want_amax && r < valid) {
-                    if (p.amax_key) {
+                for (int r = 0; r < 4; ++r) {
+                    // +0.0f turns a -0 sum into +0: a sum of products starts from +0
+                    float v = (acc[j][i][r] + 0.0f) * alpha;
+                    if constexpr (AM == 2) {
                         const unsigned long long key = amax_key(v, (int64_t)l * p.M * p.N + (int64_t)m * p.N + n + r);
-                        kk = key > kk ? key : kk;
-                    } else {
+                        if (r < valid) kk = key > kk ? key : kk;
+                    } else if constexpr (AM == 1) {
                         const uint32_t a = abs_bits(v);
-                        kb = a > kb ? a : kb;
+                        if (r < valid) kb = a > kb ? a : kb;
                     }
+                    if constexpr (OT == T_E4M3 || OT == T_E5M2) v *= sr;
+                    out[r] = convert_t<OT>(v);
                 }
-                if (fp8_out) v *= sr;
-                out[r] = convert(v, p.d_type);
+                if (valid > 0) store4<OT>(p.d, dbase + (int64_t)m * p.ldd + n, out, valid, vec);
             }
-            if (valid > 0) store4(p.d, p.d_type, dbase + (int64_t)m * p.ldd + n, out, valid, p.vec_store != 0);
         }
+    };
+    if constexpr (MODE == MODE_SF32) {
+        // the MX entry writes f32, bf16 or f16 (it rejects FP8 outputs)
+        auto with_amax = [&](auto ot) {
+            if (p.amax_key) epilogue(ot, IC<2>{});
+            else if (p.amax_bits) epilogue(ot, IC<1>{});
+            else epilogue(ot, IC<0>{});
+        };
+        if (p.d_type == T_BF16) with_amax(IC<T_BF16>{});
+        else if (p.d_type == T_F16) with_amax(IC<T_F16>{});
+        else with_amax(IC<T_F32>{});
+    } else {
+        with_out_type(p.d_type, [&](auto ot) { epilogue(ot, IC<0>{}); });
     }
     if (want_amax) amax_commit<NT>(p, kb, kk);
 }
@@ -815,20 +859,23 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < MT; ++i) acc[i] += red[(w * MT + i) * 64 + lane];
 
+    with_out_type(p.d_type, [&](auto ot) {
+        constexpr int OT = decltype(ot)::value;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        const int m = i * 16 + fr;
-        const int n = n0 + 4 * fg;
-        const int valid = (m < p.M) ? max(0, min(4, p.N - n)) : 0;
-        uint32_t out[4];
+        for (int i = 0; i < MT; ++i) {
+            const int m = i * 16 + fr;
+            const int n = n0 + 4 * fg;
+            const int valid = (m < p.M) ? max(0, min(4, p.N - n)) : 0;
+            uint32_t out[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float v = (acc[i][r] + 0.0f) * alpha;
-            if (fp8_out) v *= sr;
-            out[r] = convert(v, p.d_type);
+            for (int r = 0; r < 4; ++r) {
+                float v = (acc[i][r] + 0.0f) * alpha;
+                if constexpr (OT == T_E4M3 || OT == T_E5M2) v *= sr;
+                out[r] = convert_t<OT>(v);
+            }
+            if (valid > 0) store4<OT>(p.d, (int64_t)m * p.ldd + n, out, valid, p.vec_store != 0);
         }
-        if (valid > 0) store4(p.d, p.d_type, (int64_t)m * p.ldd + n, out, valid, p.vec_store != 0);
-    }
+    });
 }
 
 // ------------------------------------------------------------------ K-split tile kernel
@@ -994,25 +1041,28 @@ __global__ void __launch_bounds__(NW * 64) gemm_ksplit(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) red[(wave * NFRAG + i * NT + j) * 64 + lane] = acc[i][j];
     __syncthreads();
+    with_out_type(p.d_type, [&](auto ot) {
+        constexpr int OT = decltype(ot)::value;
 #pragma unroll
-    for (int u = 0; u < FPW; ++u) {
-        const int f = wave * FPW + u;
-        f32x4 v = red[f * 64 + lane];
+        for (int u = 0; u < FPW; ++u) {
+            const int f = wave * FPW + u;
+            f32x4 v = red[f * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) v += red[(w * NFRAG + f) * 64 + lane];
-        const int i = f / NT, j = f % NT;
-        const int m = m0 + i * 16 + fr;
-        const int n = n0 + j * 16 + 4 * fg;
-        const int valid = (m < p.M) ? max(0, min(4, p.N - n)) : 0;
-        uint32_t out[4];
+            for (int w = 1; w < NW; ++w) v += red[(w * NFRAG + f) * 64 + lane];
+            const int i = f / NT, j = f % NT;
+            const int m = m0 + i * 16 + fr;
+            const int n = n0 + j * 16 + 4 * fg;
+            const int valid = (m < p.M) ? max(0, min(4, p.N - n)) : 0;
+            uint32_t out[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float x = (v[r] + 0.0f) * alpha;
-            if (fp8_out) x *= sr;
-            out[r] = convert(x, p.d_type);
+            for (int r = 0; r < 4; ++r) {
+                float x = (v[r] + 0.0f) * alpha;
+                if constexpr (OT == T_E4M3 || OT == T_E5M2) x *= sr;
+                out[r] = convert_t<OT>(x);
+            }
+            if (valid > 0) store4<OT>(p.d, (int64_t)m * p.ldd + n, out, valid, p.vec_store != 0);
         }
-        if (valid > 0) store4(p.d, p.d_type, (int64_t)m * p.ldd + n, out, valid, p.vec_store != 0);
-    }
+    });
 }
 
 }  // namespace mmfp8
