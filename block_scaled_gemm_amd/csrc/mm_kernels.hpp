@@ -390,25 +390,28 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
         // scalar part is not checked), so a chunk straddling the end of the last
         // row reads zeros past it; chunks starting at or past K get an
         // out-of-range offset.
-        const bool last = k_tail && kt == KT - 1;
-        const int soff = last ? 0 : (int)kb;
-        // (the offsets are computed in statements: clang 22 drops the host stub of
-        // this kernel when a conditional expression is passed to the builtin, or
-        // when the builtin is called from two branches)
+        // The common path has loop-invariant per-lane offsets and no per-lane
+        // arithmetic; the tail path is taken (a uniform branch) once per tile.
+        auto load_ab = [&](auto tail) {
+            constexpr bool TAIL = decltype(tail)::value;
+            const int soff = TAIL ? 0 : (int)kb;
 #pragma unroll
-        for (int q = 0; q < A_INS; ++q) {
-            uint32_t off = aoff[q];
-            if (last) off = (int)kb + achunk[q] * 16 >= K ? kOOB : off + kb;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sbase + (wave * A_INS + q) * 1024), 16, off, soff,
-                                                     0, 0);
-        }
+            for (int q = 0; q < A_INS; ++q) {
+                uint32_t off = aoff[q];
+                if constexpr (TAIL) off = (int)kb + achunk[q] * 16 >= K ? kOOB : off + kb;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sbase + (wave * A_INS + q) * 1024), 16, off,
+                                                         soff, 0, 0);
+            }
 #pragma unroll
-        for (int q = 0; q < B_INS; ++q) {
-            uint32_t off = boff[q];
-            if (last) off = (int)kb + bchunk[q] * 16 >= K ? kOOB : off + kb;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sbase + BM * kBK + (wave * B_INS + q) * 1024),
-                                                     16, off, soff, 0, 0);
-        }
+            for (int q = 0; q < B_INS; ++q) {
+                uint32_t off = boff[q];
+                if constexpr (TAIL) off = (int)kb + bchunk[q] * 16 >= K ? kOOB : off + kb;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sbase + BM * kBK + (wave * B_INS + q) * 1024),
+                                                         16, off, soff, 0, 0);
+            }
+        };
+        if (k_tail && kt == KT - 1) load_ab(IC<1>{});
+        else load_ab(IC<0>{});
         // Scale columns: load t fills column j of rows 64 rg .. 64 rg + 63, at
         // LDS [j][row] after the tiles. MX groups past ceil(K/32) read whatever
         // follows (the next row, or zero past the last): their data is zero and
