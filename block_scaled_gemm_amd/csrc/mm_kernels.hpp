@@ -315,7 +315,7 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int t
 // of a second set of fragment registers); without it each half-step reads and
 // then multiplies, and a second wave on the SIMD hides the latency.
 template <int BM, int BN, int WM, int WN, int PIPE, int MODE, int FA, int FB, int SBM>
-__global__ void __launch_bounds__(WM * WN * 64, 1) gemm_tile(GemmArgs p) {
+__global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1) gemm_tile(GemmArgs p) {
     constexpr int NW = WM * WN;
     constexpr int NT = NW * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;

@@ -7,9 +7,7 @@
 
 namespace mmfp8 {
 
-// Workgroup tiles of gemm_tile, largest first: BM x BN, waves WM x WN, and
-// whether the main loop runs its fragment reads a half-step ahead (the 4-wave
-// tile has one wave per SIMD and needs it to hide LDS latency).
+// Workgroup tiles of gemm_tile, largest first: BM x BN and waves WM x WN.
 // 256x256 gives each of its 8 waves a 64x128 tile (1.5 FP8->bf16 converts per
 // MFMA); the others use 64x64 wave tiles (2 converts per MFMA).
 enum TileCfg : int { CFG_256x256 = 0, CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x64 = 3, CFG_COUNT = 4 };
@@ -17,7 +15,15 @@ constexpr int kCfgBM[CFG_COUNT] = {256, 128, 128, 64};
 constexpr int kCfgBN[CFG_COUNT] = {256, 256, 128, 64};
 constexpr int kCfgWM[CFG_COUNT] = {4, 2, 2, 2};
 constexpr int kCfgWN[CFG_COUNT] = {2, 4, 2, 2};
-constexpr int kCfgPipe[CFG_COUNT] = {0, 0, 1, 0};
+// Whether the main loop runs its fragment reads a half-step ahead. Only the
+// chained modes on the 4-wave 128x128 tile do: that workgroup has one wave per
+// SIMD and runs alone on its CU (the second fragment set takes the registers a
+// second workgroup would need). The promoted modes keep 64x64 partials as
+// well, so there the 128x128 tile runs without it, two workgroups per CU whose
+// waves share the SIMDs and cover each other's LDS latency.
+constexpr int cfg_pipe(int cfg, int mode) {
+    return cfg == CFG_128x128 && (mode == MODE_FAST || mode == MODE_SF32) ? 1 : 0;
+}
 
 // gemm_skinny: waves per workgroup and K steps in flight per wave, by MT
 // (M <= 16 MT). Sixteen waves with two steps each put a K = 4096 B tile in
@@ -46,18 +52,21 @@ hipError_t launch_debug_convert(const float* x, void* y, int t, int64_t n, hipSt
 
 // Largest tile each mode is built for. The chained modes (fast, MX) keep 128
 // fp32 accumulators per lane and little else, so they take the 64x128 wave
-// tile; the promoted modes (slow, block-scaled) also hold a 128-chunk partial
-// per accumulator and stop at 128x256 (eight 64x64 waves, two per SIMD).
+// tile. The promoted modes (slow, block-scaled) also hold a 128-chunk partial
+// per accumulator; their largest tile is 128x128 at two workgroups per CU,
+// which measured faster than 128x256 at one (eight waves that all meet at
+// every step's barrier, where the older wave of each SIMD pair finishes first
+// and the younger then runs alone).
 constexpr int min_cfg(int mode, int sbm) {
     (void)sbm;
-    return (mode == MODE_FAST || mode == MODE_SF32) ? CFG_256x256 : CFG_128x256;
+    return (mode == MODE_FAST || mode == MODE_SF32) ? CFG_256x256 : CFG_128x128;
 }
 
 // Launch gemm_tile<BM, BN, MODE, fa, fb, SBM> for a runtime cfg / format pair.
 template <int MODE, int SBM>
 hipError_t tile_dispatch(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s) {
 #define MMFP8_TILE(C, A, B)                                                                                  \
-    hipLaunchKernelGGL((gemm_tile<kCfgBM[C], kCfgBN[C], kCfgWM[C], kCfgWN[C], kCfgPipe[C], MODE, A, B, SBM>), \
+    hipLaunchKernelGGL((gemm_tile<kCfgBM[C], kCfgBN[C], kCfgWM[C], kCfgWN[C], cfg_pipe(C, MODE), MODE, A, B, SBM>), \
                        dim3(grid), dim3(kCfgWM[C] * kCfgWN[C] * 64), 0, s, p)
 #define MMFP8_FMTS(C)                                    \
     if (fa == 0 && fb == 0) MMFP8_TILE(C, 0, 0);         \
@@ -69,7 +78,9 @@ hipError_t tile_dispatch(int cfg, int fa, int fb, const GemmArgs& p, int grid, h
         case CFG_256x256:
             if constexpr (MODE == MODE_FAST || MODE == MODE_SF32) { MMFP8_FMTS(CFG_256x256) }
             break;
-        case CFG_128x256: MMFP8_FMTS(CFG_128x256) break;
+        case CFG_128x256:
+            if constexpr (MODE == MODE_FAST || MODE == MODE_SF32) { MMFP8_FMTS(CFG_128x256) }
+            break;
         case CFG_128x128: MMFP8_FMTS(CFG_128x128) break;
         default: MMFP8_FMTS(CFG_64x64) break;
     }
