@@ -663,8 +663,60 @@ __global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1)
     const bool vec = p.vec_store != 0;
     uint32_t kb = 0;
     unsigned long long kk = 0;
+    // 2-byte outputs of a whole tile go out through LDS: each wave writes its
+    // converted results into its own region of the (now idle) stages, row-major
+    // with 16-byte chunk c of row r at chunk c ^ (r mod chunks-per-row), and
+    // reads them back as 16 bytes per lane along rows, so that every store
+    // instruction writes whole 128-byte row segments. (Written straight from
+    // the MFMA layout, each store covers 16 rows with 32 bytes each.)
+    const bool full_tile = m0 + BM <= p.M && n0 + BN <= p.N;
+    const bool st16 = ((uintptr_t)p.d & 15) == 0 && (p.ldd & 7) == 0 && (p.d_batch & 7) == 0;
+    constexpr int RB = WTN * 2;  // bytes per row of a wave's region
+    constexpr int CH = RB / 16;  // 16-byte chunks per row
+    static_assert((NW / 2) * WTM * RB <= STAGE, "the output regions of half the waves fit in one stage");
     auto epilogue = [&](auto ot, auto am) {
         constexpr int OT = decltype(ot)::value, AM = decltype(am)::value;
+        if constexpr (OT == T_BF16 || OT == T_F16) {
+            if (full_tile && st16) {
+                uint8_t* region = (wave < NW / 2 ? smem0 : smem1) + (wave % (NW / 2)) * (WTM * RB);
+                __syncthreads();  // every wave is done with the stages
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int r = i * 16 + fr;
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        uint32_t out[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float v = (acc[j][i][e] + 0.0f) * alpha;
+                            if constexpr (AM == 2) {
+                                const unsigned long long key = amax_key(
+                                    v, (int64_t)l * p.M * p.N + (int64_t)(m0 + wm * WTM + r) * p.N + n0 + wn * WTN +
+                                           j * 16 + 4 * fg + e);
+                                kk = key > kk ? key : kk;
+                            } else if constexpr (AM == 1) {
+                                const uint32_t a = abs_bits(v);
+                                kb = a > kb ? a : kb;
+                            }
+                            out[e] = convert_t<OT>(v);
+                        }
+                        const int c = 2 * j + (fg >> 1);
+                        *(i32x2*)(region + r * RB + ((c ^ (r & (CH - 1))) << 4) + ((fg & 1) << 3)) =
+                            i32x2{(int)(out[0] | (out[1] << 16)), (int)(out[2] | (out[3] << 16))};
+                    }
+                }
+                // each wave reads back only its own region
+                constexpr int RPI = 64 / CH;  // rows per instruction
+#pragma unroll
+                for (int it = 0; it < WTM / RPI; ++it) {
+                    const int r = it * RPI + lane / CH, c = lane % CH;
+                    const i32x4 v = *(const i32x4*)(region + r * RB + ((c ^ (r & (CH - 1))) << 4));
+                    uint16_t* d = (uint16_t*)p.d + dbase + (int64_t)(m0 + wm * WTM + r) * p.ldd + n0 + wn * WTN + c * 8;
+                    *(i32x4*)d = v;
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int m = m0 + wm * WTM + i * 16 + fr;
