@@ -77,6 +77,8 @@ mm_status device_status(hipError_t e, const char* what) {
 
 }  // namespace
 
+int mmfp8::device_cus() { return cu_count(); }
+
 extern "C" {
 
 const char* mm_last_error(void) { return g_error.c_str(); }

@@ -314,10 +314,17 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int t
 // of the MFMAs (the way to hide LDS latency with one wave per SIMD, at the cost
 // of a second set of fragment registers); without it each half-step reads and
 // then multiplies, and a second wave on the SIMD hides the latency.
-template <int BM, int BN, int WM, int WN, int PIPE, int MODE, int FA, int FB, int SBM>
-__global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1) gemm_tile(GemmArgs p) {
-    constexpr int NW = WM * WN;
-    constexpr int NT = NW * 64;
+//
+// KG = 2 splits the K steps of a tile between two groups of WM x WN waves (even
+// steps to group 0, odd steps to group 1), each with its own pair of stages;
+// at the end the groups add their partial tiles, group 0's first, and each
+// group stores half of the rows. It gives a tile two waves per SIMD when the
+// tiles are too few for two workgroups per CU.
+template <int BM, int BN, int WM, int WN, int PIPE, int MODE, int FA, int FB, int SBM, int KG = 1>
+__global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE) ? 2 : 1) gemm_tile(GemmArgs p) {
+    static_assert(KG == 1 || (KG == 2 && !PIPE), "K groups use the plain main loop");
+    constexpr int NW = WM * WN;       // waves per K group
+    constexpr int NT = NW * KG * 64;  // threads of the workgroup
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
     constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;  // 1 KB LDS-DMA writes per wave per step
@@ -336,12 +343,14 @@ __global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1)
     // Distinct LDS objects (not one array indexed by stage) so that the compiler
     // can tell a fragment read of one stage from the in-flight LDS-DMA writes
     // into another and does not wait for those loads.
-    __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem0[KG * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem1[KG * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the LDS addressing scalar
-    const int wm = wave / WN, wn = wave % WN;
+    const int kg = KG > 1 ? wave / NW : 0;                       // K group
+    const int gw = KG > 1 ? wave % NW : wave;                    // wave within its group
+    const int wm = gw / WN, wn = gw % WN;
     int l, tm, tn;
     tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, 8, l, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -364,13 +373,13 @@ __global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1)
     int achunk[A_INS], bchunk[B_INS];
 #pragma unroll
     for (int q = 0; q < A_INS; ++q) {
-        achunk[q] = ld_chunk(wave * A_INS + q);
-        aoff[q] = (uint32_t)(((wave * A_INS + q) * 8 + ld_row) * p.lda + achunk[q] * 16);
+        achunk[q] = ld_chunk(gw * A_INS + q);
+        aoff[q] = (uint32_t)(((gw * A_INS + q) * 8 + ld_row) * p.lda + achunk[q] * 16);
     }
 #pragma unroll
     for (int q = 0; q < B_INS; ++q) {
-        bchunk[q] = ld_chunk(wave * B_INS + q);
-        boff[q] = (uint32_t)(((wave * B_INS + q) * 8 + ld_row) * p.ldb + bchunk[q] * 16);
+        bchunk[q] = ld_chunk(gw * B_INS + q);
+        boff[q] = (uint32_t)(((gw * B_INS + q) * 8 + ld_row) * p.ldb + bchunk[q] * 16);
     }
 
     const float* sa_l = p.sa + (int64_t)l * p.sa_batch;
@@ -399,14 +408,14 @@ __global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1)
             for (int q = 0; q < A_INS; ++q) {
                 uint32_t off = aoff[q];
                 if constexpr (TAIL) off = (int)kb + achunk[q] * 16 >= K ? kOOB : off + kb;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sbase + (wave * A_INS + q) * 1024), 16, off,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sbase + (gw * A_INS + q) * 1024), 16, off,
                                                          soff, 0, 0);
             }
 #pragma unroll
             for (int q = 0; q < B_INS; ++q) {
                 uint32_t off = boff[q];
                 if constexpr (TAIL) off = (int)kb + bchunk[q] * 16 >= K ? kOOB : off + kb;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sbase + BM * kBK + (wave * B_INS + q) * 1024),
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sbase + BM * kBK + (gw * B_INS + q) * 1024),
                                                          16, off, soff, 0, 0);
             }
         };
@@ -417,7 +426,7 @@ __global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1)
         // follows (the next row, or zero past the last): their data is zero and
         // their conversion scale is replaced by 1 at use.
         if constexpr (SC_A_INS > 0) {
-            for (int t = wave; t < SC_A_INS; t += NW) {
+            for (int t = gw; t < SC_A_INS; t += NW) {
                 const int j = t % SA_W, rg = t / SA_W;
                 const uint32_t off = (uint32_t)(((rg * 64 + lane) * p.sa_ld + kt * SA_W + j) * 4);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -425,7 +434,7 @@ __global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1)
             }
         }
         if constexpr (SC_INS > SC_A_INS) {
-            for (int t = wave; t < SC_INS - SC_A_INS; t += NW) {
+            for (int t = gw; t < SC_INS - SC_A_INS; t += NW) {
                 const int j = t % SB_W, rg = t / SB_W;
                 const uint32_t off = (uint32_t)(((rg * 64 + lane) * p.sb_ld + kt * SB_W + j) * 4);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -451,9 +460,9 @@ __global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1)
             *(i32x4*)slot = v;
         };
 #pragma unroll
-        for (int q = 0; q < A_INS; ++q) fix(sbase + (wave * A_INS + q) * 1024 + lane * 16, achunk[q]);
+        for (int q = 0; q < A_INS; ++q) fix(sbase + (gw * A_INS + q) * 1024 + lane * 16, achunk[q]);
 #pragma unroll
-        for (int q = 0; q < B_INS; ++q) fix(sbase + BM * kBK + (wave * B_INS + q) * 1024 + lane * 16, bchunk[q]);
+        for (int q = 0; q < B_INS; ++q) fix(sbase + BM * kBK + (gw * B_INS + q) * 1024 + lane * 16, bchunk[q]);
     };
 
     // Fragment reads: lane (r, g) takes chunks 2g and 2g + 1 of row r, i.e.
@@ -495,7 +504,7 @@ __global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1)
         return sc;
     };
     StepScales sc_cur;
-    if (kSbMem) sc_cur = load_scales(0);
+    if (kSbMem) sc_cur = load_scales(kg);
 
     // Main loop, two LDS stages, software-pipelined by half-steps: the lane's
     // 32 bytes of a step are read as two 16-byte halves (sub-steps 0-1, 2-3),
@@ -627,33 +636,71 @@ __global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1)
     } else {
         // Each half-step reads its fragments and then multiplies; a second wave
         // on the SIMD covers the read latency.
-        auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
-            stage_ready(kt, cur);
+        // One step of each K group (super-step s: K step s * KG + kg of group kg,
+        // in that group's part of the stage); every wave takes the barrier.
+        auto step = [&](int s, uint8_t* cur, uint8_t* nxt) {
+            const int kt = s * KG + kg;
+            uint8_t* cs = cur + kg * STAGE;
+            stage_ready(kt, cs);
             float s_a[FM], s_b[FN][4], c_a[FM], c_b[FN];
-            step_scales(kt, cur, s_a, s_b, c_a, c_b);
-            if (kSbMem) sc_cur = load_scales(kt + 1);
-            issue(kt + 1, nxt);
-            zero_part();
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                // keep the scheduler from hoisting the second half's reads and
-                // converts above the first half's MFMAs (that costs registers, not time)
-                if (h) __builtin_amdgcn_sched_barrier(0);
-                Frag f;
-                read_frag(cur, h, f);
-                mma_half(f, c_a, c_b);
+            if (kt < KT) {
+                step_scales(kt, cs, s_a, s_b, c_a, c_b);
+                if (kSbMem) sc_cur = load_scales(kt + KG);
             }
-            promote(s_a, s_b);
+            issue(kt + KG, nxt + kg * STAGE);
+            if (kt < KT) {
+                zero_part();
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    // keep the scheduler from hoisting the second half's reads and
+                    // converts above the first half's MFMAs (that costs registers, not time)
+                    if (h) __builtin_amdgcn_sched_barrier(0);
+                    Frag f;
+                    read_frag(cs, h, f);
+                    mma_half(f, c_a, c_b);
+                }
+                promote(s_a, s_b);
+            }
         };
-        issue(0, smem0);
-        for (int kt = 0; kt < KT; kt += 2) {
-            step(kt, smem0, smem1);
-            if (kt + 1 < KT) step(kt + 1, smem1, smem0);
+        issue(kg, smem0 + kg * STAGE);
+        const int KS = (KT + KG - 1) / KG;
+        for (int s = 0; s < KS; s += 2) {
+            step(s, smem0, smem1);
+            if (s + 1 < KS) step(s + 1, smem1, smem0);
         }
     }
     // the loads issued for steps past the end (they fetch nothing) must land
     // before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(0);
+
+    // K groups: group g keeps fragment rows [g FM / 2, (g + 1) FM / 2) of its
+    // wave tile and receives the other group's partial for them through LDS.
+    // The two partials are added in one fp32 addition, the same either way round.
+    constexpr int FMG = FM / KG;  // fragment rows each group stores
+    if constexpr (KG > 1) {
+        static_assert(KG == 2 && FM % 2 == 0, "two K groups, even fragment rows");
+        static_assert(2 * NW * FN * FMG * 64 * 16 <= KG * STAGE, "the exchange fits in one stage pair");
+        f32x4* xch = (f32x4*)smem0;  // [to group][wave][j][ii][lane]
+        // (the group is a template argument here: indexing acc by a runtime
+        // group would put the accumulators in scratch memory)
+        auto exchange = [&](auto grp) {
+            constexpr int G = decltype(grp)::value, O = 1 - G;
+            __syncthreads();  // every wave is done with the stages
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int ii = 0; ii < FMG; ++ii)
+                    xch[(((O * NW + gw) * FN + j) * FMG + ii) * 64 + lane] = acc[j][O * FMG + ii];
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int ii = 0; ii < FMG; ++ii)
+                    acc[j][G * FMG + ii] += xch[(((G * NW + gw) * FN + j) * FMG + ii) * 64 + lane];
+        };
+        if (kg) exchange(IC<1>{});
+        else exchange(IC<0>{});
+    }
 
     // ---------------------------------------------------------- epilogue
     // Compiled once per output type and amax kind (AM: 0 none, 1 |x| bits,
@@ -673,16 +720,18 @@ __global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1)
     const bool st16 = ((uintptr_t)p.d & 15) == 0 && (p.ldd & 7) == 0 && (p.d_batch & 7) == 0;
     constexpr int RB = WTN * 2;  // bytes per row of a wave's region
     constexpr int CH = RB / 16;  // 16-byte chunks per row
-    static_assert((NW / 2) * WTM * RB <= STAGE, "the output regions of half the waves fit in one stage");
-    auto epilogue = [&](auto ot, auto am) {
-        constexpr int OT = decltype(ot)::value, AM = decltype(am)::value;
+    constexpr int RROWS = WTM / KG;  // rows of a wave's region
+    static_assert((NW * KG / 2) * RROWS * RB <= KG * STAGE, "the output regions of half the waves fit in one stage");
+    auto epilogue = [&](auto ot, auto am, auto grp) {
+        constexpr int OT = decltype(ot)::value, AM = decltype(am)::value, G = decltype(grp)::value;
         if constexpr (OT == T_BF16 || OT == T_F16) {
             if (full_tile && st16) {
-                uint8_t* region = (wave < NW / 2 ? smem0 : smem1) + (wave % (NW / 2)) * (WTM * RB);
+                uint8_t* region = (wave < NW * KG / 2 ? smem0 : smem1) + (wave % (NW * KG / 2)) * (RROWS * RB);
                 __syncthreads();  // every wave is done with the stages
+                const int mr = m0 + wm * WTM + G * RROWS;  // first row of the region
 #pragma unroll
-                for (int i = 0; i < FM; ++i) {
-                    const int r = i * 16 + fr;
+                for (int ii = 0; ii < FMG; ++ii) {
+                    const int i = G * FMG + ii, r = ii * 16 + fr;
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
                         uint32_t out[4];
@@ -691,8 +740,8 @@ __global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1)
                             const float v = (acc[j][i][e] + 0.0f) * alpha;
                             if constexpr (AM == 2) {
                                 const unsigned long long key = amax_key(
-                                    v, (int64_t)l * p.M * p.N + (int64_t)(m0 + wm * WTM + r) * p.N + n0 + wn * WTN +
-                                           j * 16 + 4 * fg + e);
+                                    v, (int64_t)l * p.M * p.N + (int64_t)(mr + r) * p.N + n0 + wn * WTN + j * 16 +
+                                           4 * fg + e);
                                 kk = key > kk ? key : kk;
                             } else if constexpr (AM == 1) {
                                 const uint32_t a = abs_bits(v);
@@ -708,17 +757,18 @@ __global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1)
                 // each wave reads back only its own region
                 constexpr int RPI = 64 / CH;  // rows per instruction
 #pragma unroll
-                for (int it = 0; it < WTM / RPI; ++it) {
+                for (int it = 0; it < RROWS / RPI; ++it) {
                     const int r = it * RPI + lane / CH, c = lane % CH;
                     const i32x4 v = *(const i32x4*)(region + r * RB + ((c ^ (r & (CH - 1))) << 4));
-                    uint16_t* d = (uint16_t*)p.d + dbase + (int64_t)(m0 + wm * WTM + r) * p.ldd + n0 + wn * WTN + c * 8;
+                    uint16_t* d = (uint16_t*)p.d + dbase + (int64_t)(mr + r) * p.ldd + n0 + wn * WTN + c * 8;
                     *(i32x4*)d = v;
                 }
                 return;
             }
         }
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+        for (int ii = 0; ii < FMG; ++ii) {
+            const int i = G * FMG + ii;
             const int m = m0 + wm * WTM + i * 16 + fr;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
@@ -743,18 +793,23 @@ __global__ void __launch_bounds__(WM * WN * 64, (WM * WN == 4 && !PIPE) ? 2 : 1)
             }
         }
     };
+    // the group's half of the rows (K groups), with compile-time fragment indices
+    auto epilogue_g = [&](auto ot, auto am) {
+        if (KG > 1 && kg) epilogue(ot, am, IC<KG - 1>{});
+        else epilogue(ot, am, IC<0>{});
+    };
     if constexpr (MODE == MODE_SF32) {
         // the MX entry writes f32, bf16 or f16 (it rejects FP8 outputs)
         auto with_amax = [&](auto ot) {
-            if (p.amax_key) epilogue(ot, IC<2>{});
-            else if (p.amax_bits) epilogue(ot, IC<1>{});
-            else epilogue(ot, IC<0>{});
+            if (p.amax_key) epilogue_g(ot, IC<2>{});
+            else if (p.amax_bits) epilogue_g(ot, IC<1>{});
+            else epilogue_g(ot, IC<0>{});
         };
         if (p.d_type == T_BF16) with_amax(IC<T_BF16>{});
         else if (p.d_type == T_F16) with_amax(IC<T_F16>{});
         else with_amax(IC<T_F32>{});
     } else {
-        with_out_type(p.d_type, [&](auto ot) { epilogue(ot, IC<0>{}); });
+        with_out_type(p.d_type, [&](auto ot) { epilogue_g(ot, IC<0>{}); });
     }
     if (want_amax) amax_commit<NT>(p, kb, kk);
 }

@@ -62,12 +62,33 @@ constexpr int min_cfg(int mode, int sbm) {
     return (mode == MODE_FAST || mode == MODE_SF32) ? CFG_256x256 : CFG_128x128;
 }
 
-// Launch gemm_tile<BM, BN, MODE, fa, fb, SBM> for a runtime cfg / format pair.
+// Compute units of the current device.
+int device_cus();
+
+// Launch gemm_tile<BM, BN, MODE, fa, fb, SBM> for a runtime cfg / format pair
+// over `grid` tiles. 128x128 tiles that are no more than the CUs (one per CU)
+// run with two K groups of four waves (eight waves per workgroup) in the
+// modes that have them: it measured 5-7% faster there than four waves with
+// one wave per SIMD, and slower as soon as two workgroups per CU are possible.
 template <int MODE, int SBM>
 hipError_t tile_dispatch(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s) {
-#define MMFP8_TILE(C, A, B)                                                                                  \
-    hipLaunchKernelGGL((gemm_tile<kCfgBM[C], kCfgBN[C], kCfgWM[C], kCfgWN[C], cfg_pipe(C, MODE), MODE, A, B, SBM>), \
-                       dim3(grid), dim3(kCfgWM[C] * kCfgWN[C] * 64), 0, s, p)
+    constexpr int kKG = MODE == MODE_SF32 ? 1 : 2;
+    const bool kgroups = kKG > 1 && cfg == CFG_128x128 && grid <= device_cus();
+#define MMFP8_TILE(C, A, B)                                                                                        \
+    do {                                                                                                           \
+        bool done = false;                                                                                         \
+        if constexpr (C == CFG_128x128 && kKG > 1) {                                                               \
+            if (kgroups) {                                                                                         \
+                hipLaunchKernelGGL((gemm_tile<kCfgBM[C], kCfgBN[C], kCfgWM[C], kCfgWN[C], 0, MODE, A, B, SBM, kKG>), \
+                                   dim3(grid), dim3(kCfgWM[C] * kCfgWN[C] * kKG * 64), 0, s, p);                   \
+                done = true;                                                                                       \
+            }                                                                                                      \
+        }                                                                                                          \
+        if (!done)                                                                                                 \
+            hipLaunchKernelGGL((gemm_tile<kCfgBM[C], kCfgBN[C], kCfgWM[C], kCfgWN[C], cfg_pipe(C, MODE), MODE, A, B, \
+                                          SBM>),                                                                   \
+                               dim3(grid), dim3(kCfgWM[C] * kCfgWN[C] * 64), 0, s, p);                             \
+    } while (0)
 #define MMFP8_FMTS(C)                                    \
     if (fa == 0 && fb == 0) MMFP8_TILE(C, 0, 0);         \
     else if (fa == 1 && fb == 1) MMFP8_TILE(C, 1, 1);    \

@@ -167,9 +167,10 @@ def test_mixed_and_e5m2_formats(fa, fb):
 # K whose last chunk straddles a 16-byte boundary (K % 16 == 8).
 TILE_CASES = [(4096, 4096, 1032, True),    # fast: 256x256 tile, eight 64x128 waves
               (2048, 4096, 1032, True),    # fast: 128x256
-              (1024, 4096, 1032, True),    # fast: 128x128, pipelined fragment reads
+              (1024, 4096, 1032, True),    # fast: 128x128, one per CU: two K groups of four waves
+              (1536, 4096, 1032, True),    # fast: 128x128, pipelined fragment reads
               (2048, 4096, 1032, False),   # slow: 128x128, two workgroups per CU
-              (1000, 4096, 1032, False),   # slow: 128x128, ragged M
+              (1000, 4096, 1032, False),   # slow: 128x128, ragged M, one per CU: two K groups
               (256, 4096, 1032, False),    # K split over the waves, 64x64 tiles
               (100, 4096, 1032, True)]     # K split over the waves, 32x64 tiles
 
@@ -184,7 +185,7 @@ def test_production_tiles_per_tensor(M, N, K, fast):
 
 
 @pytest.mark.parametrize("sb_mode", [1, 2], ids=["1x128", "128x128"])
-@pytest.mark.parametrize("M", [2048, 200], ids=["128x128", "64x64"])
+@pytest.mark.parametrize("M", [2048, 1024, 200], ids=["128x128", "128x128-kgroups", "64x64"])
 def test_production_tiles_block_scaled(M, sb_mode):
     N, K = 4096, 1032
     g = np.random.default_rng(M + sb_mode)
