@@ -6,9 +6,10 @@ memory and the current stream. Importing the package loads libmmfp8.so from
 this directory and raises if it is missing: there is no fallback path.
 
 Raw C-ABI wrappers (same names as the C functions, integer pointers):
-``mm_scaled_gemm``, ``mm_blockscaled_gemm_amax``, ``mm_debug_convert``,
-``mm_last_error``, ``mm_version``. Tensor-level helpers: ``scaled_gemm`` and
-``blockscaled_gemm_amax``.
+``mm_scaled_gemm``, ``mm_scaled_gemm_bias``, ``mm_scaled_gemm_batched``,
+``mm_blockscaled_gemm_amax``, ``mm_debug_convert``,
+``mm_last_error``, ``mm_version``. Tensor-level helpers: ``scaled_gemm`` (with
+an optional bias), ``scaled_bmm`` and ``blockscaled_gemm_amax``.
 """
 from __future__ import annotations
 
@@ -40,6 +41,12 @@ _lib = ctypes.CDLL(LIB_PATH)
 _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 _lib.mm_scaled_gemm.argtypes = [_I64, _I64, _I64, _P, _I, _I64, _P, _I, _I64, _P, _I, _P, _I, _P, _P, _I, _I64, _I, _P]
 _lib.mm_scaled_gemm.restype = _I
+_lib.mm_scaled_gemm_bias.argtypes = [_I64, _I64, _I64, _P, _I, _I64, _P, _I, _I64, _P, _I, _P, _I, _P, _P, _I, _I64,
+                                     _I, _P]
+_lib.mm_scaled_gemm_bias.restype = _I
+_lib.mm_scaled_gemm_batched.argtypes = [_I64, _I64, _I64, _I64, _P, _I, _I64, _I64, _P, _I, _I64, _I64, _P, _P, _P,
+                                        _P, _I, _I64, _I64, _I, _P]
+_lib.mm_scaled_gemm_batched.restype = _I
 _lib.mm_blockscaled_gemm_amax.argtypes = [_I64, _I64, _I64, _I64, _P, _P, _I, _P, _P, _I, _P, _I, _P, _P, _P]
 _lib.mm_blockscaled_gemm_amax.restype = _I
 _lib.mm_debug_convert.argtypes = [_P, _P, _I, _I64, _P]
@@ -47,7 +54,8 @@ _lib.mm_debug_convert.restype = _I
 _lib.mm_last_error.restype = ctypes.c_char_p
 _lib.mm_version.restype = ctypes.c_char_p
 
-EXPORTED = ("mm_scaled_gemm", "mm_blockscaled_gemm_amax", "mm_last_error", "mm_version", "mm_debug_convert")
+EXPORTED = ("mm_scaled_gemm", "mm_scaled_gemm_bias", "mm_scaled_gemm_batched", "mm_blockscaled_gemm_amax",
+            "mm_last_error", "mm_version", "mm_debug_convert")
 
 
 class MMError(RuntimeError):
@@ -70,6 +78,22 @@ def mm_scaled_gemm(M, N, K, a, a_type, lda, b, b_type, ldb, scale_a, sa_mode, sc
     return _lib.mm_scaled_gemm(M, N, K, a or None, a_type, lda, b or None, b_type, ldb, scale_a or None, sa_mode,
                                scale_b or None, sb_mode, scale_result or None, d or None, d_type, ldd,
                                int(use_fast_accum), stream or None)
+
+
+def mm_scaled_gemm_bias(M, N, K, a, a_type, lda, b, b_type, ldb, scale_a, sa_mode, scale_b, sb_mode, bias,
+                        d, d_type, ldd, use_fast_accum, stream) -> int:
+    """Raw call of the C function; pointers and the stream are integers (0 = NULL). Returns the status."""
+    return _lib.mm_scaled_gemm_bias(M, N, K, a or None, a_type, lda, b or None, b_type, ldb, scale_a or None,
+                                    sa_mode, scale_b or None, sb_mode, bias or None, d or None, d_type, ldd,
+                                    int(use_fast_accum), stream or None)
+
+
+def mm_scaled_gemm_batched(L, M, N, K, a, a_type, lda, stride_a, b, b_type, ldb, stride_b, scale_a, scale_b,
+                           scale_result, d, d_type, ldd, stride_d, use_fast_accum, stream) -> int:
+    """Raw call of the C function; pointers and the stream are integers (0 = NULL). Returns the status."""
+    return _lib.mm_scaled_gemm_batched(L, M, N, K, a or None, a_type, lda, stride_a, b or None, b_type, ldb,
+                                       stride_b, scale_a or None, scale_b or None, scale_result or None,
+                                       d or None, d_type, ldd, stride_d, int(use_fast_accum), stream or None)
 
 
 def mm_blockscaled_gemm_amax(M, N, K, L, a, b, ab_type, sfa, sfb, sf_vec_size, c, c_type, amax, amax_index,
@@ -126,14 +150,16 @@ def _rows(t):
 
 
 def scaled_gemm(a, b, scale_a, scale_b, out_dtype, scale_result=None, use_fast_accum=False, out=None,
-                a_format=None, b_format=None):
-    """d = (a * scale_a) @ (b * scale_b)^T on the current stream.
+                a_format=None, b_format=None, bias=None):
+    """d = (a * scale_a) @ (b * scale_b)^T (+ bias) on the current stream.
 
     a: [M, K] FP8 (or uint8 codes with a_format) with contiguous rows.
     b: [N, K] FP8 with contiguous rows, or torch._scaled_mm's column-major
        mat2 [K, N] (detected by its strides and read as its [N, K] transpose).
     scale_a / scale_b: fp32 tensors, per-tensor (one element), 1x128 [M, ceil(K/128)],
        or for b 1x128 [N, ceil(K/128)] / 128x128 [ceil(N/128), ceil(K/128)].
+    bias: optional contiguous [N] tensor of out_dtype (f32, bf16 or f16), added
+       after the scales (mm_scaled_gemm_bias).
     """
     torch = _torch()
     if b.dim() == 2 and a.dim() == 2 and b.shape[0] == a.shape[1] and b.stride(0) == 1 and b.shape[1] != a.shape[1]:
@@ -161,11 +187,57 @@ def scaled_gemm(a, b, scale_a, scale_b, out_dtype, scale_result=None, use_fast_a
     d_type = dtype_code(out_dtype)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    if bias is not None:
+        if bias.dtype != out_dtype or tuple(bias.shape) != (N,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous [N] tensor of out_dtype")
+        if scale_result is not None:
+            raise ValueError("scale_result applies to FP8 outputs, which take no bias")
+        st = mm_scaled_gemm_bias(M, N, K, a.data_ptr(), _fp8_code(a, a_format), _rows(a) if M else K,
+                                 b.data_ptr(), _fp8_code(b, b_format), _rows(b) if N else K,
+                                 scale_a.data_ptr(), sa_mode, scale_b.data_ptr(), sb_mode, bias.data_ptr(),
+                                 out.data_ptr(), d_type, _rows(out) if M else N, use_fast_accum, _stream())
+        _check(st)
+        return out
     sr = 0 if scale_result is None else scale_result.data_ptr()
     st = mm_scaled_gemm(M, N, K, a.data_ptr(), _fp8_code(a, a_format), _rows(a) if M else K,
                         b.data_ptr(), _fp8_code(b, b_format), _rows(b) if N else K,
                         scale_a.data_ptr(), sa_mode, scale_b.data_ptr(), sb_mode, sr,
                         out.data_ptr(), d_type, _rows(out) if M else N, use_fast_accum, _stream())
+    _check(st)
+    return out
+
+
+def scaled_bmm(a, b, scale_a, scale_b, out_dtype, scale_result=None, use_fast_accum=False, out=None,
+               a_format=None, b_format=None):
+    """d[l] = (a[l] * scale_a) @ (b[l] * scale_b)^T for every l, on the current stream.
+
+    a: [L, M, K] and b: [L, N, K] FP8 (K innermost, contiguous rows; a b held as
+    [L, K, N] must be transposed by the caller first). scale_a / scale_b: one
+    fp32 element each, shared by the batch. Returns d [L, M, N] of out_dtype.
+    """
+    torch = _torch()
+    if a.dim() != 3 or b.dim() != 3 or a.shape[0] != b.shape[0] or a.shape[2] != b.shape[2]:
+        raise ValueError(f"expected a [L, M, K] and b [L, N, K], got {tuple(a.shape)} and {tuple(b.shape)}")
+    L, M, K = a.shape
+    N = b.shape[1]
+    for t in (a, b):
+        if t.shape[2] > 1 and t.stride(2) != 1:
+            raise ValueError("operands need K innermost (b as [L, N, K]); transpose b first")
+    for s in (scale_a, scale_b):
+        if s.dtype != torch.float32 or s.numel() != 1:
+            raise TypeError("scale_a and scale_b must be one-element float32 tensors")
+    if out is None:
+        out = torch.empty((L, M, N), dtype=out_dtype, device=a.device)
+    if out.dim() != 3 or (N > 1 and out.stride(2) != 1):
+        raise ValueError("out must be [L, M, N] with contiguous rows")
+    sr = 0 if scale_result is None else scale_result.data_ptr()
+    lda = a.stride(1) if M > 1 else K
+    ldb = b.stride(1) if N > 1 else K
+    ldd = out.stride(1) if M > 1 else N
+    st = mm_scaled_gemm_batched(L, M, N, K, a.data_ptr(), _fp8_code(a, a_format), lda, a.stride(0),
+                                b.data_ptr(), _fp8_code(b, b_format), ldb, b.stride(0),
+                                scale_a.data_ptr(), scale_b.data_ptr(), sr,
+                                out.data_ptr(), dtype_code(out_dtype), ldd, out.stride(0), use_fast_accum, _stream())
     _check(st)
     return out
 

@@ -85,15 +85,24 @@ const char* mm_last_error(void) { return g_error.c_str(); }
 
 const char* mm_version(void) { return "mmfp8 0.1.0 gfx950"; }
 
-mm_status mm_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, int a_type, int64_t lda, const void* b,
-                         int b_type, int64_t ldb, const float* scale_a, int sa_mode, const float* scale_b,
-                         int sb_mode, const float* scale_result, void* d, int d_type, int64_t ldd,
-                         int use_fast_accum, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The dense FP8 GEMM behind mm_scaled_gemm, mm_scaled_gemm_bias and
+// mm_scaled_gemm_batched: L items (L = 1 for the first two) at byte strides
+// stride_a / stride_b and element stride stride_d, an optional bias [N].
+mm_status scaled_gemm(const char* who, int64_t L, int64_t M, int64_t N, int64_t K, const void* a, int a_type,
+                      int64_t lda, int64_t stride_a, const void* b, int b_type, int64_t ldb, int64_t stride_b,
+                      const float* scale_a, int sa_mode, const float* scale_b, int sb_mode, const float* scale_result,
+                      const void* bias, void* d, int d_type, int64_t ldd, int64_t stride_d, int use_fast_accum,
+                      void* stream) {
     g_error.clear();
-    if (M < 0 || N < 0 || K < 0) return fail(MM_ERR_INVALID_ARGUMENT, "M, N and K must be >= 0 (got %lld, %lld, %lld)",
-                                             (long long)M, (long long)N, (long long)K);
-    if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
-        return fail(MM_ERR_UNSUPPORTED, "M, N and K must be below 2^31");
+    if (L < 0 || M < 0 || N < 0 || K < 0)
+        return fail(MM_ERR_INVALID_ARGUMENT, "L, M, N and K must be >= 0 (got %lld, %lld, %lld, %lld)", (long long)L,
+                    (long long)M, (long long)N, (long long)K);
+    if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim || L >= kMaxDim)
+        return fail(MM_ERR_UNSUPPORTED, "L, M, N and K must be below 2^31");
     if (!is_fp8(a_type) || !is_fp8(b_type))
         return fail(MM_ERR_INVALID_ARGUMENT, "a_type and b_type must be MM_F8_E4M3FN or MM_F8_E5M2 (got %d, %d)",
                     a_type, b_type);
@@ -110,13 +119,22 @@ mm_status mm_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, int a_t
     if (lda < K || ldb < K) return fail(MM_ERR_INVALID_ARGUMENT, "lda and ldb must be >= K");
     if (ldd < N) return fail(MM_ERR_INVALID_ARGUMENT, "ldd must be >= N");
     if (lda > kMaxPitch || ldb > kMaxPitch) return fail(MM_ERR_UNSUPPORTED, "lda and ldb must be at most 2^22 bytes");
-    if (M == 0 || N == 0) return MM_OK;
+    if (stride_a < 0 || stride_b < 0 || stride_d < 0)
+        return fail(MM_ERR_INVALID_ARGUMENT, "batch strides must be >= 0");
+    if (bias && is_fp8(d_type))
+        return fail(MM_ERR_UNSUPPORTED, "a bias needs an f32, bf16 or f16 output (got d_type %d)", d_type);
+    // (the workgroup count is checked against 2^31 below; 64x64 tiles are the smallest)
+    if (L > 0 && cdiv(M, 64) * cdiv(N, 64) >= kMaxDim / L) return fail(MM_ERR_UNSUPPORTED, "too many output tiles");
+    if (L == 0 || M == 0 || N == 0) return MM_OK;
     if (!d) return fail(MM_ERR_INVALID_ARGUMENT, "d is NULL");
     if (K > 0 && (!a || !b)) return fail(MM_ERR_INVALID_ARGUMENT, "a or b is NULL");
     if ((per_tensor || K > 0) && (!scale_a || !scale_b)) return fail(MM_ERR_INVALID_ARGUMENT, "scale_a or scale_b is NULL");
     if (!aligned(a, 16) || !aligned(b, 16)) return fail(MM_ERR_MISALIGNED, "a and b must be 16-byte aligned");
     if (lda % 8 || ldb % 8) return fail(MM_ERR_MISALIGNED, "lda and ldb must be multiples of 8 bytes");
+    if (L > 1 && (stride_a % 16 || stride_b % 16))
+        return fail(MM_ERR_MISALIGNED, "stride_a and stride_b must be multiples of 16 bytes");
     if (!aligned(d, elem_size(d_type))) return fail(MM_ERR_MISALIGNED, "d must be aligned to its element size");
+    if (!aligned(bias, elem_size(d_type))) return fail(MM_ERR_MISALIGNED, "bias must be aligned to its element size");
     if (!aligned(scale_a, 4) || !aligned(scale_b, 4) || !aligned(scale_result, 4))
         return fail(MM_ERR_MISALIGNED, "scale pointers must be 4-byte aligned");
     if (forced_launch_failure()) return fail(MM_ERR_DEVICE, "launch failure forced by MM_TEST_FORCE_FAIL");
@@ -127,53 +145,87 @@ mm_status mm_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, int a_t
     p.b = static_cast<const uint8_t*>(b);
     p.lda = lda;
     p.ldb = ldb;
+    p.a_batch = L > 1 ? stride_a : 0;
+    p.b_batch = L > 1 ? stride_b : 0;
     p.M = (int)M;
     p.N = (int)N;
     p.K = (int)K;
-    p.L = 1;
+    p.L = (int)L;
     p.sa = scale_a;
     p.sb = scale_b;
     const int64_t kb = cdiv(K, 128);
     p.sa_ld = kb;
     p.sb_ld = kb;
     p.scale_result = scale_result;
+    p.bias = bias;
     p.d = d;
     p.ldd = ldd;
+    p.d_batch = L > 1 ? stride_d : 0;
     p.d_type = d_type;
     const int es = elem_size(d_type);
-    p.vec_store = (ldd % 4 == 0) && aligned(d, 4 * es);
+    p.vec_store = (ldd % 4 == 0) && (p.d_batch % 4 == 0) && aligned(d, 4 * es);
 
     const int fa = a_type == MM_F8_E5M2 ? 1 : 0;
     const int fb = b_type == MM_F8_E5M2 ? 1 : 0;
     hipError_t e;
-    if (per_tensor && M <= 64) {
+    // the skinny and K-split kernels serve one item; batches go to the tiles
+    if (per_tensor && L == 1 && M <= 64) {
         const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
         const int grid = (int)cdiv(N, 16);
         e = mmfp8::launch_skinny(mt, use_fast_accum ? mmfp8::MODE_FAST : mmfp8::MODE_SLOW, fa, fb, p, grid, s);
-        return device_status(e, "mm_scaled_gemm (skinny) launch");
+        return device_status(e, who);
     }
     const int mode = per_tensor ? (use_fast_accum ? mmfp8::MODE_FAST : mmfp8::MODE_SLOW) : mmfp8::MODE_BLOCK;
     const int sbm = sb_mode == MM_SCALE_128x128 ? mmfp8::SB_128x128 : mmfp8::SB_1x128;
-    const int cfg = choose_cfg(M, N, 1, cu_count(), mmfp8::min_cfg(mode, sbm));
-    if (per_tensor && cfg == mmfp8::CFG_64x64) {
+    const int cfg = choose_cfg(M, N, L, cu_count(), mmfp8::min_cfg(mode, sbm));
+    if (per_tensor && L == 1 && cfg == mmfp8::CFG_64x64) {
         // too few 128x128 tiles to fill the chip: K split over the waves of 64x64 / 32x64 tiles
         const int ks = cdiv(M, 64) * cdiv(N, 64) >= cu_count() ? mmfp8::KS_64x64 : mmfp8::KS_32x64;
         p.tiles_m = (int)cdiv(M, mmfp8::kKsBM[ks]);
         p.tiles_n = (int)cdiv(N, mmfp8::kKsBN[ks]);
         const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
         e = mmfp8::launch_ksplit(ks, mode, fa, fb, p, (int)grid, s);
-        return device_status(e, "mm_scaled_gemm (k-split) launch");
+        return device_status(e, who);
     }
     p.tiles_m = (int)cdiv(M, mmfp8::kCfgBM[cfg]);
     p.tiles_n = (int)cdiv(N, mmfp8::kCfgBN[cfg]);
-    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * L;
     if (per_tensor) {
         e = use_fast_accum ? mmfp8::launch_tile_fast(cfg, fa, fb, p, (int)grid, s)
                            : mmfp8::launch_tile_slow(cfg, fa, fb, p, (int)grid, s);
     } else {
         e = mmfp8::launch_tile_block(cfg, sbm, fa, fb, p, (int)grid, s);
     }
-    return device_status(e, "mm_scaled_gemm launch");
+    return device_status(e, who);
+}
+
+}  // namespace
+
+extern "C" {
+
+mm_status mm_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, int a_type, int64_t lda, const void* b,
+                         int b_type, int64_t ldb, const float* scale_a, int sa_mode, const float* scale_b,
+                         int sb_mode, const float* scale_result, void* d, int d_type, int64_t ldd,
+                         int use_fast_accum, void* stream) {
+    return scaled_gemm("mm_scaled_gemm launch", 1, M, N, K, a, a_type, lda, 0, b, b_type, ldb, 0, scale_a, sa_mode,
+                       scale_b, sb_mode, scale_result, nullptr, d, d_type, ldd, 0, use_fast_accum, stream);
+}
+
+mm_status mm_scaled_gemm_bias(int64_t M, int64_t N, int64_t K, const void* a, int a_type, int64_t lda, const void* b,
+                              int b_type, int64_t ldb, const float* scale_a, int sa_mode, const float* scale_b,
+                              int sb_mode, const void* bias, void* d, int d_type, int64_t ldd, int use_fast_accum,
+                              void* stream) {
+    return scaled_gemm("mm_scaled_gemm_bias launch", 1, M, N, K, a, a_type, lda, 0, b, b_type, ldb, 0, scale_a,
+                       sa_mode, scale_b, sb_mode, nullptr, bias, d, d_type, ldd, 0, use_fast_accum, stream);
+}
+
+mm_status mm_scaled_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K, const void* a, int a_type, int64_t lda,
+                                 int64_t stride_a, const void* b, int b_type, int64_t ldb, int64_t stride_b,
+                                 const float* scale_a, const float* scale_b, const float* scale_result, void* d,
+                                 int d_type, int64_t ldd, int64_t stride_d, int use_fast_accum, void* stream) {
+    return scaled_gemm("mm_scaled_gemm_batched launch", L, M, N, K, a, a_type, lda, stride_a, b, b_type, ldb,
+                       stride_b, scale_a, MM_SCALE_TENSOR, scale_b, MM_SCALE_TENSOR, scale_result, nullptr, d, d_type,
+                       ldd, stride_d, use_fast_accum, stream);
 }
 
 mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L, const void* a, const void* b,

@@ -75,6 +75,7 @@ struct GemmArgs {
     uint32_t* amax_bits;          // amax without index (atomic max of |x| bits) or null
     unsigned long long* amax_key; // (|x| bits << 33) | (2^33 - 1 - index), or null
     int tiles_m, tiles_n;
+    const void* bias;   // [N] of d_type (f32, bf16 or f16), added after the scales; or null
 };
 
 // ------------------------------------------------------------------ helpers
@@ -183,6 +184,14 @@ __device__ __forceinline__ uint32_t convert(float v, int t) {
         case T_E4M3: return convert_t<T_E4M3>(v);
         default: return convert_t<T_E5M2>(v);
     }
+}
+
+// Element n of a bias vector of output type T, as fp32 (exact).
+template <int T>
+__device__ __forceinline__ float load_bias(const void* bias, int n) {
+    if constexpr (T == T_F32) return ((const float*)bias)[n];
+    else if constexpr (T == T_BF16) return __uint_as_float((uint32_t)((const uint16_t*)bias)[n] << 16);
+    else return (float)((const _Float16*)bias)[n];
 }
 
 // A compile-time int, to hand a runtime choice to a generic lambda.
@@ -722,8 +731,20 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     constexpr int CH = RB / 16;  // 16-byte chunks per row
     constexpr int RROWS = WTM / KG;  // rows of a wave's region
     static_assert((NW * KG / 2) * RROWS * RB <= KG * STAGE, "the output regions of half the waves fit in one stage");
-    auto epilogue = [&](auto ot, auto am, auto grp) {
+    auto epilogue = [&](auto ot, auto am, auto grp, auto bi) {
         constexpr int OT = decltype(ot)::value, AM = decltype(am)::value, G = decltype(grp)::value;
+        constexpr bool BI = decltype(bi)::value != 0;
+        // the bias of this lane's columns (the same for every row)
+        float bv[FN][4];
+        if constexpr (BI) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int n = n0 + wn * WTN + j * 16 + 4 * fg + e;
+                    bv[j][e] = n < p.N ? load_bias<OT>(p.bias, n) : 0.0f;
+                }
+        }
         if constexpr (OT == T_BF16 || OT == T_F16) {
             if (full_tile && st16) {
                 uint8_t* region = (wave < NW * KG / 2 ? smem0 : smem1) + (wave % (NW * KG / 2)) * (RROWS * RB);
@@ -737,7 +758,8 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
                         uint32_t out[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const float v = (acc[j][i][e] + 0.0f) * alpha;
+                            float v = (acc[j][i][e] + 0.0f) * alpha;
+                            if constexpr (BI) v += bv[j][e];
                             if constexpr (AM == 2) {
                                 const unsigned long long key = amax_key(
                                     v, (int64_t)l * p.M * p.N + (int64_t)(mr + r) * p.N + n0 + wn * WTN + j * 16 +
@@ -779,6 +801,7 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
                 for (int r = 0; r < 4; ++r) {
                     // +0.0f turns a -0 sum into +0: a sum of products starts from +0
                     float v = (acc[j][i][r] + 0.0f) * alpha;
+                    if constexpr (BI) v += bv[j][r];
                     if constexpr (AM == 2) {
                         const unsigned long long key = amax_key(v, (int64_t)l * p.M * p.N + (int64_t)m * p.N + n + r);
                         if (r < valid) kk = key > kk ? key : kk;
@@ -794,22 +817,31 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
         }
     };
     // the group's half of the rows (K groups), with compile-time fragment indices
-    auto epilogue_g = [&](auto ot, auto am) {
-        if (KG > 1 && kg) epilogue(ot, am, IC<KG - 1>{});
-        else epilogue(ot, am, IC<0>{});
+    auto epilogue_g = [&](auto ot, auto am, auto bi) {
+        if (KG > 1 && kg) epilogue(ot, am, IC<KG - 1>{}, bi);
+        else epilogue(ot, am, IC<0>{}, bi);
     };
     if constexpr (MODE == MODE_SF32) {
         // the MX entry writes f32, bf16 or f16 (it rejects FP8 outputs)
         auto with_amax = [&](auto ot) {
-            if (p.amax_key) epilogue_g(ot, IC<2>{});
-            else if (p.amax_bits) epilogue_g(ot, IC<1>{});
-            else epilogue_g(ot, IC<0>{});
+            if (p.amax_key) epilogue_g(ot, IC<2>{}, IC<0>{});
+            else if (p.amax_bits) epilogue_g(ot, IC<1>{}, IC<0>{});
+            else epilogue_g(ot, IC<0>{}, IC<0>{});
         };
         if (p.d_type == T_BF16) with_amax(IC<T_BF16>{});
         else if (p.d_type == T_F16) with_amax(IC<T_F16>{});
         else with_amax(IC<T_F32>{});
     } else {
-        with_out_type(p.d_type, [&](auto ot) { epilogue_g(ot, IC<0>{}); });
+        // a bias (f32, bf16 and f16 outputs) is another compile-time variant
+        with_out_type(p.d_type, [&](auto ot) {
+            constexpr int OT = decltype(ot)::value;
+            if constexpr (OT == T_F32 || OT == T_BF16 || OT == T_F16) {
+                if (p.bias) epilogue_g(ot, IC<0>{}, IC<1>{});
+                else epilogue_g(ot, IC<0>{}, IC<0>{});
+            } else {
+                epilogue_g(ot, IC<0>{}, IC<0>{});
+            }
+        });
     }
     if (want_amax) amax_commit<NT>(p, kb, kk);
 }
@@ -969,8 +1001,14 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < MT; ++i) acc[i] += red[(w * MT + i) * 64 + lane];
 
-    with_out_type(p.d_type, [&](auto ot) {
+    auto epilogue = [&](auto ot, auto bi) {
         constexpr int OT = decltype(ot)::value;
+        constexpr bool BI = decltype(bi)::value != 0;
+        float bv[4];
+        if constexpr (BI) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bv[r] = n0 + 4 * fg + r < p.N ? load_bias<OT>(p.bias, n0 + 4 * fg + r) : 0.0f;
+        }
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             const int m = i * 16 + fr;
@@ -980,10 +1018,20 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float v = (acc[i][r] + 0.0f) * alpha;
+                if constexpr (BI) v += bv[r];
                 if constexpr (OT == T_E4M3 || OT == T_E5M2) v *= sr;
                 out[r] = convert_t<OT>(v);
             }
             if (valid > 0) store4<OT>(p.d, (int64_t)m * p.ldd + n, out, valid, p.vec_store != 0);
+        }
+    };
+    with_out_type(p.d_type, [&](auto ot) {
+        constexpr int OT = decltype(ot)::value;
+        if constexpr (OT == T_F32 || OT == T_BF16 || OT == T_F16) {
+            if (p.bias) epilogue(ot, IC<1>{});
+            else epilogue(ot, IC<0>{});
+        } else {
+            epilogue(ot, IC<0>{});
         }
     });
 }
@@ -1151,8 +1199,9 @@ __global__ void __launch_bounds__(NW * 64) gemm_ksplit(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) red[(wave * NFRAG + i * NT + j) * 64 + lane] = acc[i][j];
     __syncthreads();
-    with_out_type(p.d_type, [&](auto ot) {
+    auto epilogue = [&](auto ot, auto bi) {
         constexpr int OT = decltype(ot)::value;
+        constexpr bool BI = decltype(bi)::value != 0;
 #pragma unroll
         for (int u = 0; u < FPW; ++u) {
             const int f = wave * FPW + u;
@@ -1167,10 +1216,20 @@ __global__ void __launch_bounds__(NW * 64) gemm_ksplit(GemmArgs p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float x = (v[r] + 0.0f) * alpha;
+                if constexpr (BI) x += n + r < p.N ? load_bias<OT>(p.bias, n + r) : 0.0f;
                 if constexpr (OT == T_E4M3 || OT == T_E5M2) x *= sr;
                 out[r] = convert_t<OT>(x);
             }
             if (valid > 0) store4<OT>(p.d, (int64_t)m * p.ldd + n, out, valid, p.vec_store != 0);
+        }
+    };
+    with_out_type(p.d_type, [&](auto ot) {
+        constexpr int OT = decltype(ot)::value;
+        if constexpr (OT == T_F32 || OT == T_BF16 || OT == T_F16) {
+            if (p.bias) epilogue(ot, IC<1>{});
+            else epilogue(ot, IC<0>{});
+        } else {
+            epilogue(ot, IC<0>{});
         }
     });
 }

@@ -115,6 +115,66 @@ mm_status mm_scaled_gemm(int64_t M, int64_t N, int64_t K,
                          void* stream);
 
 /*
+ * mm_scaled_gemm_bias -- mm_scaled_gemm with a bias added after the scales.
+ *
+ * Defined by "TileOPs: Linear Algebra Operators", tileops.gemm.GemmFP8FwdOp,
+ * forward(a, b, scale_a, scale_b, bias): the product with its scales applied,
+ * plus an optional bias vector of the output type, one value per column.
+ *
+ *  bias     [N] of d_type, or NULL (then the call is mm_scaled_gemm's). d_type
+ *           must be F32, BF16 or F16 when bias is given (the page's outputs
+ *           are bf16 and f16); an FP8 d_type with a bias -> MM_ERR_UNSUPPORTED.
+ *           Aligned to its element size, else MM_ERR_MISALIGNED.
+ *  Every other argument is mm_scaled_gemm's (there is no scale_result: it only
+ *  applies to FP8 outputs).
+ *
+ * Result: d[m, n] = cast(v + bias[n]) where v is mm_scaled_gemm's fp32 value
+ * before the cast (the scaled sum); the bias is widened exactly to fp32 and
+ * added in one fp32 addition, then the result is rounded once to d_type.
+ */
+mm_status mm_scaled_gemm_bias(int64_t M, int64_t N, int64_t K,
+                              const void* a, int a_type, int64_t lda,
+                              const void* b, int b_type, int64_t ldb,
+                              const float* scale_a, int sa_mode,
+                              const float* scale_b, int sb_mode,
+                              const void* bias,
+                              void* d, int d_type, int64_t ldd,
+                              int use_fast_accum,
+                              void* stream);
+
+/*
+ * mm_scaled_gemm_batched -- L independent per-tensor-scaled FP8 GEMMs,
+ * d[l] = (a[l] * s_a) @ (b[l] * s_b)^T cast to d_type, for l = 0 .. L-1.
+ *
+ * Defined by "TileOPs: Linear Algebra Operators", tileops.gemm.BmmFP8FwdOp
+ * (batched FP8 GEMM, one per-tensor scale for a and one for b shared by the
+ * whole batch). b is taken with K innermost, the page's trans_b layout
+ * [B, N, K], which the page names as the layout that needs no transposed
+ * copy; a caller holding b as [B, K, N] transposes it first.
+ *
+ *  L        batch count, in [0, 2^31); L == 0 returns MM_OK, nothing enqueued.
+ *  a        item l at a + l * stride_a bytes: [M, K], row pitch lda bytes.
+ *  b        item l at b + l * stride_b bytes: [N, K], row pitch ldb bytes.
+ *  scale_a, scale_b  fp32 [1] each, for every item.
+ *  scale_result, d_type, use_fast_accum  as in mm_scaled_gemm.
+ *  d        item l at d + l * stride_d ELEMENTS: [M, N], row pitch ldd.
+ *  Strides are >= 0 (items may alias for the inputs; outputs that overlap
+ *  give an unspecified result). With L > 1, stride_a and stride_b must be
+ *  multiples of 16 bytes (MM_ERR_MISALIGNED otherwise). The other rules are
+ *  mm_scaled_gemm's, applied to every item.
+ *
+ * Result: item by item, exactly mm_scaled_gemm's with TENSOR scale modes.
+ */
+mm_status mm_scaled_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K,
+                                 const void* a, int a_type, int64_t lda, int64_t stride_a,
+                                 const void* b, int b_type, int64_t ldb, int64_t stride_b,
+                                 const float* scale_a, const float* scale_b,
+                                 const float* scale_result,
+                                 void* d, int d_type, int64_t ldd, int64_t stride_d,
+                                 int use_fast_accum,
+                                 void* stream);
+
+/*
  * mm_blockscaled_gemm_amax -- batched block-scaled GEMM with a global amax.
  *
  * Defined by "cuDNN frontend: GEMM + Amax (SM100)", Overview, Shapes and

@@ -57,7 +57,7 @@ def _load():
         I = ctypes.c_int
         lib.orc_decode_fp8.argtypes = [P, I64, I, P]
         lib.orc_round.argtypes = [P, I64, I, P]
-        lib.orc_scaled_gemm.argtypes = [I64, I64, I64, P, I, I64, P, I, I64, P, I, P, I, P, I, I,
+        lib.orc_scaled_gemm.argtypes = [I64, I64, I64, P, I, I64, P, I, I64, P, I, P, I, P, P, I, I,
                                         P, I64, P, P, P, I]
         lib.orc_blockscaled_gemm_amax.argtypes = [I64, I64, I64, I64, P, P, I, P, P, I, I, P, I64,
                                                   P, P, P, P, P, I]
@@ -103,8 +103,11 @@ def round_to(x: np.ndarray, dtype: int) -> np.ndarray:
 
 
 def scaled_gemm(a, a_fmt, b, b_fmt, scale_a, sa_mode, scale_b, sb_mode, d_type,
-                scale_result=None, accum=ACC_EXACT, rows=None, threads=None):
-    """d = (a*s_a) @ (b*s_b)^T for a [M, lda>=K] and b [N, ldb>=K] uint8 codes.
+                scale_result=None, accum=ACC_EXACT, rows=None, threads=None, bias=None):
+    """d = (a*s_a) @ (b*s_b)^T (+ bias) for a [M, lda>=K] and b [N, ldb>=K] uint8 codes.
+
+    ``bias``: optional [N] float64 values (the decoded bias), added after the
+    scales; not allowed with FP8 outputs.
 
     ``a`` and ``b`` are 2-D uint8 arrays whose first K columns are used (pass K
     via ``a.shape[1]`` unless the arrays are wider, see ``K`` below). Returns
@@ -112,11 +115,11 @@ def scaled_gemm(a, a_fmt, b, b_fmt, scale_a, sa_mode, scale_b, sb_mode, d_type,
     ``rows`` (all rows when None).
     """
     return scaled_gemm_k(a, a_fmt, b, b_fmt, a.shape[1], scale_a, sa_mode, scale_b, sb_mode,
-                         d_type, scale_result, accum, rows, threads)
+                         d_type, scale_result, accum, rows, threads, bias)
 
 
 def scaled_gemm_k(a, a_fmt, b, b_fmt, K, scale_a, sa_mode, scale_b, sb_mode, d_type,
-                  scale_result=None, accum=ACC_EXACT, rows=None, threads=None):
+                  scale_result=None, accum=ACC_EXACT, rows=None, threads=None, bias=None):
     """As scaled_gemm, with an explicit K <= row pitch of a and b."""
     a = np.ascontiguousarray(a, dtype=np.uint8)
     b = np.ascontiguousarray(b, dtype=np.uint8)
@@ -125,13 +128,16 @@ def scaled_gemm_k(a, a_fmt, b, b_fmt, K, scale_a, sa_mode, scale_b, sb_mode, d_t
     sa = np.ascontiguousarray(scale_a, dtype=np.float32).reshape(-1)
     sb = np.ascontiguousarray(scale_b, dtype=np.float32).reshape(-1)
     sr = None if scale_result is None else np.asarray([scale_result], dtype=np.float32).reshape(-1)
+    bi = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64).reshape(-1)
+    if bi is not None and bi.size != N:
+        raise ValueError("bias must have N values")
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     R = M if r is None else r.size
     value = np.empty((R, N), dtype=np.float64)
     sabs = np.empty((R, N), dtype=np.float64)
     bits = np.empty((R, N), dtype=_BITS_DTYPE[d_type])
     _check(_load().orc_scaled_gemm(M, N, K, _ptr(a), a_fmt, lda, _ptr(b), b_fmt, ldb,
-                                   _ptr(sa), sa_mode, _ptr(sb), sb_mode, _ptr(sr), d_type, accum,
+                                   _ptr(sa), sa_mode, _ptr(sb), sb_mode, _ptr(sr), _ptr(bi), d_type, accum,
                                    _ptr(r), R, _ptr(value), _ptr(sabs), _ptr(bits),
                                    _threads(threads)))
     return value, sabs, bits

@@ -235,20 +235,24 @@ int orc_round(const double* x, int64_t n, int dtype, void* out_bits) {
 /*
  * The scaled GEMM for the rows listed in `rows` (all M rows when rows is NULL).
  * Output arrays are [n_rows, N] row-major. value: the result before the output
- * cast, after every scale. sum_abs (may be NULL): sum over k of |term|, each
- * term with every scale applied. d_bits: value rounded to d_type.
+ * cast, after every scale and the bias. sum_abs (may be NULL): sum over k of
+ * |term|, each term with every scale applied. d_bits: value rounded to d_type.
+ * bias (may be NULL): [N] values added to the scaled sum (TileOPs
+ * GemmFP8FwdOp: "apply the scales, and add the bias"); only for non-FP8
+ * outputs. In the emulated-fp32 mode the addition is an fp32 addition.
  */
 int orc_scaled_gemm(int64_t M, int64_t N, int64_t K,
                     const uint8_t* a, int a_fmt, int64_t lda,
                     const uint8_t* b, int b_fmt, int64_t ldb,
                     const float* scale_a, int sa_mode,
                     const float* scale_b, int sb_mode,
-                    const float* scale_result, int d_type, int accum,
+                    const float* scale_result, const double* bias, int d_type, int accum,
                     const int64_t* rows, int64_t n_rows,
                     double* value, double* sum_abs, void* d_bits, int threads) {
     if (fpenv_flushes()) return ORC_ERR_FPENV;
     if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K) return ORC_ERR_ARG;
     if (d_type < ORC_E4M3FN || d_type > ORC_F16) return ORC_ERR_ARG;
+    if (bias && (d_type == ORC_E4M3FN || d_type == ORC_E5M2)) return ORC_ERR_ARG;
     const bool block = sa_mode != ORC_SCALE_TENSOR;
     if (block != (sb_mode != ORC_SCALE_TENSOR) || sa_mode == ORC_SCALE_128x128) return ORC_ERR_ARG;
     if (!rows) n_rows = M;
@@ -334,6 +338,7 @@ int orc_scaled_gemm(int64_t M, int64_t N, int64_t K,
             }
             v *= sr;
             sabs *= std::fabs(sr);
+            if (bias) v = accum == ORC_ACC_EXACT ? v + bias[n] : (double)to_f32(v + bias[n]);
             const size_t o = (size_t)i * N + n;
             if (value) value[o] = v;
             if (sum_abs) sum_abs[o] = sabs;

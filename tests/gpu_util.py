@@ -71,3 +71,47 @@ def debug_convert(x: np.ndarray, dtype: int) -> np.ndarray:
     assert st == mm.MM_OK, (st, mm.mm_last_error())
     torch.cuda.synchronize()
     return ty.cpu().numpy().view(BITS_NP[dtype])
+
+
+def scaled_gemm_bias(a, a_fmt, b, b_fmt, K, sa, sa_mode, sb, sb_mode, bias_bits, d_type, fast=False, ldd=None):
+    """mm_scaled_gemm_bias; bias_bits [N] are the bit patterns of the bias in d_type."""
+    M, lda = a.shape
+    N, ldb = b.shape
+    ldd = ldd or N
+    ta, tb = dev_u8(a), dev_u8(b)
+    tsa, tsb = dev_f32(sa), dev_f32(sb)
+    es = np.dtype(BITS_NP[d_type]).itemsize
+    tbias = torch.from_numpy(np.ascontiguousarray(bias_bits, dtype=BITS_NP[d_type]).view(np.uint8).copy()).to(DEV)
+    td = torch.full((max(M, 1) * ldd * es,), 0x5A, dtype=torch.uint8, device=DEV)
+    st = mm.mm_scaled_gemm_bias(M, N, K, ta.data_ptr(), a_fmt, lda, tb.data_ptr(), b_fmt, ldb, tsa.data_ptr(),
+                                sa_mode, tsb.data_ptr(), sb_mode, tbias.data_ptr(), td.data_ptr(), d_type, ldd,
+                                int(fast), stream())
+    assert st == mm.MM_OK, (st, mm.mm_last_error())
+    torch.cuda.synchronize()
+    out = td.cpu().numpy().view(BITS_NP[d_type])[: M * ldd].reshape(M, ldd)[:, :N]
+    return np.ascontiguousarray(out)
+
+
+def scaled_gemm_batched(a, a_fmt, b, b_fmt, K, sa, sb, d_type, scale_result=None, fast=False, pad_a=0, pad_b=0,
+                        pad_d=0):
+    """mm_scaled_gemm_batched on a [L, M, lda], b [L, N, ldb] uint8 codes, items pad_* bytes / elements apart
+    beyond their size (pad_a, pad_b multiples of 16). Returns the output bits [L, M, N]."""
+    L, M, lda = a.shape
+    N, ldb = b.shape[1], b.shape[2]
+    sa_bytes, sb_bytes = M * lda + pad_a, N * ldb + pad_b
+    abuf = np.zeros((L, sa_bytes), np.uint8); abuf[:, : M * lda] = a.reshape(L, -1)
+    bbuf = np.zeros((L, sb_bytes), np.uint8); bbuf[:, : N * ldb] = b.reshape(L, -1)
+    ta, tb = dev_u8(abuf), dev_u8(bbuf)
+    tsa, tsb = dev_f32(sa), dev_f32(sb)
+    tsr = dev_f32(scale_result) if scale_result is not None else None
+    es = np.dtype(BITS_NP[d_type]).itemsize
+    stride_d = M * N + pad_d
+    td = torch.full((max(L * stride_d, 1) * es,), 0x5A, dtype=torch.uint8, device=DEV)
+    st = mm.mm_scaled_gemm_batched(L, M, N, K, ta.data_ptr(), a_fmt, lda, sa_bytes, tb.data_ptr(), b_fmt, ldb,
+                                   sb_bytes, tsa.data_ptr(), tsb.data_ptr(),
+                                   tsr.data_ptr() if tsr is not None else 0, td.data_ptr(), d_type, N, stride_d,
+                                   int(fast), stream())
+    assert st == mm.MM_OK, (st, mm.mm_last_error())
+    torch.cuda.synchronize()
+    out = td.cpu().numpy().view(BITS_NP[d_type])[: L * stride_d].reshape(L, stride_d)[:, : M * N]
+    return np.ascontiguousarray(out.reshape(L, M, N))

@@ -27,8 +27,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) == {"mm_scaled_gemm", "mm_blockscaled_gemm_amax", "mm_last_error", "mm_version",
-                          "mm_debug_convert"}
+    assert set(names) == {"mm_scaled_gemm", "mm_scaled_gemm_bias", "mm_scaled_gemm_batched",
+                          "mm_blockscaled_gemm_amax", "mm_last_error", "mm_version", "mm_debug_convert"}
     lib = ctypes.CDLL(mm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -80,6 +80,63 @@ def test_scaled_gemm_zero_sizes_launch_nothing():
     assert mm.mm_last_error() == ""
 
 
+def gemm_bias(**kw):
+    args = dict(M=64, N=64, K=128, a=P, a_type=0, lda=128, b=P, b_type=0, ldb=128, scale_a=P, sa_mode=0,
+                scale_b=P, sb_mode=0, bias=P, d=P, d_type=3, ldd=64, use_fast_accum=0, stream=0)
+    args.update(kw)
+    return mm.mm_scaled_gemm_bias(**args)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(d_type=0), mm.MM_ERR_UNSUPPORTED, "bias needs an f32, bf16 or f16 output"),
+    (dict(d_type=1), mm.MM_ERR_UNSUPPORTED, "bias needs an f32, bf16 or f16 output"),
+    (dict(bias=P + 1), mm.MM_ERR_MISALIGNED, "bias must be aligned"),
+    (dict(d_type=2, bias=P + 2), mm.MM_ERR_MISALIGNED, "bias must be aligned"),
+    (dict(sa_mode=1, sb_mode=0), mm.MM_ERR_UNSUPPORTED, "scale pair"),
+    (dict(M=-1), mm.MM_ERR_INVALID_ARGUMENT, "must be >= 0"),
+])
+def test_scaled_gemm_bias_validation(kw, status, msg):
+    assert gemm_bias(**kw) == status
+    assert msg in mm.mm_last_error()
+
+
+def test_scaled_gemm_bias_zero_sizes_launch_nothing():
+    assert gemm_bias(M=0, d=0, a=0) == mm.MM_OK
+    assert gemm_bias(N=0, d=0, b=0, bias=0) == mm.MM_OK
+
+
+def bmm(**kw):
+    args = dict(L=4, M=64, N=64, K=128, a=P, a_type=0, lda=128, stride_a=64 * 128, b=P, b_type=0, ldb=128,
+                stride_b=64 * 128, scale_a=P, scale_b=P, scale_result=0, d=P, d_type=3, ldd=64,
+                stride_d=64 * 64, use_fast_accum=0, stream=0)
+    args.update(kw)
+    return mm.mm_scaled_gemm_batched(**args)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(L=-1), mm.MM_ERR_INVALID_ARGUMENT, "must be >= 0"),
+    (dict(L=1 << 31), mm.MM_ERR_UNSUPPORTED, "below 2^31"),
+    (dict(stride_a=-16), mm.MM_ERR_INVALID_ARGUMENT, "batch strides"),
+    (dict(stride_d=-1), mm.MM_ERR_INVALID_ARGUMENT, "batch strides"),
+    (dict(stride_a=64 * 128 + 8), mm.MM_ERR_MISALIGNED, "multiples of 16 bytes"),
+    (dict(stride_b=8), mm.MM_ERR_MISALIGNED, "multiples of 16 bytes"),
+    (dict(L=1 << 20, M=1 << 16, N=1 << 16, ldd=1 << 16), mm.MM_ERR_UNSUPPORTED, "too many output tiles"),
+    (dict(a_type=4), mm.MM_ERR_INVALID_ARGUMENT, "a_type and b_type"),
+    (dict(ldd=63), mm.MM_ERR_INVALID_ARGUMENT, "ldd"),
+    (dict(scale_a=0), mm.MM_ERR_INVALID_ARGUMENT, "scale_a or scale_b"),
+])
+def test_scaled_gemm_batched_validation(kw, status, msg):
+    assert bmm(**kw) == status
+    assert msg in mm.mm_last_error()
+
+
+def test_scaled_gemm_batched_zero_sizes_launch_nothing():
+    assert bmm(L=0, a=0, b=0, d=0) == mm.MM_OK
+    assert bmm(M=0, a=0, d=0) == mm.MM_OK
+    # one item: the strides are not used, so they need no alignment
+    assert bmm(L=1, M=0, stride_a=8, d=0) == mm.MM_OK
+
+
 def amax_call(**kw):
     args = dict(M=64, N=64, K=256, L=2, a=P, b=P, ab_type=0, sfa=P, sfb=P, sf_vec_size=32, c=P, c_type=2,
                 amax=P, amax_index=P, stream=0)
@@ -117,6 +174,8 @@ def test_forced_launch_failure(monkeypatch):
     assert gemm() == mm.MM_ERR_DEVICE
     assert "forced" in mm.mm_last_error()
     assert amax_call() == mm.MM_ERR_DEVICE
+    assert gemm_bias() == mm.MM_ERR_DEVICE
+    assert bmm() == mm.MM_ERR_DEVICE
     assert mm.mm_debug_convert(P, P, 2, 16, 0) == mm.MM_ERR_DEVICE
 
 

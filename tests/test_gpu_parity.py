@@ -332,3 +332,82 @@ def test_workload5_full_size(which):
         d, dt, sr = datagen.workload5b(), F16, None
     rows = np.array([0, 1, 2, 4095, 8190, 8191])
     check_gemm(d, 0, 0, dt, False, rows=rows, scale_result=sr, what=f"workload5{which} full size")
+
+
+# ------------------------------------------------------------------ bias (TileOPs GemmFP8FwdOp, forward)
+
+def _bias_bits(rng, N, d_type):
+    x = rng.normal(0, 16, size=N).astype(np.float32)
+    if d_type == BF16:
+        return (x.view(np.uint32) >> 16).astype(np.uint16)
+    if d_type == F16:
+        return x.astype(np.float16).view(np.uint16)
+    return x.view(np.uint32)
+
+
+def _bias_values(bits, d_type):
+    if d_type == BF16:
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if d_type == F16:
+        return bits.view(np.float16).astype(np.float64)
+    return bits.view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("d_type", [BF16, F16, F32], ids=["bf16", "f16", "f32"])
+@pytest.mark.parametrize("M,N,K,fast", [(16, 4100, 1032, False),    # skinny
+                                        (200, 4096, 1032, True),     # K split
+                                        (1000, 1030, 1032, False),   # 128x128 tiles, ragged N and K
+                                        (2048, 2048, 520, True)])    # 256x256 / 128x256 tiles
+def test_bias_per_tensor(M, N, K, fast, d_type):
+    g = np.random.default_rng(M + N + d_type)
+    a = datagen.gauss_codes(g, (M, K), 64.0)
+    b = datagen.gauss_codes(g, (N, K), 64.0)
+    bias_bits = _bias_bits(g, N, d_type)
+    gpu = gu.scaled_gemm_bias(a, E4M3FN, b, E4M3FN, K, 0.5, 0, 0.25, 0, bias_bits, d_type, fast=fast)
+    rows = sample_rows(M, 8)
+    value, sabs, bits = oracle.scaled_gemm(a, E4M3FN, b, E4M3FN, np.float32(0.5), 0, np.float32(0.25), 0, d_type,
+                                           rows=rows, bias=_bias_values(bias_bits, d_type))
+    compare.check(gpu[rows], value, sabs, bits, d_type, f"bias {M}x{N}x{K} fast={fast}")
+
+
+@pytest.mark.parametrize("sb_mode", [1, 2], ids=["1x128", "128x128"])
+def test_bias_block_scaled(sb_mode):
+    M, N, K = 1024, 2056, 1032
+    g = np.random.default_rng(40 + sb_mode)
+    a = datagen.gauss_codes(g, (M, K), 64.0)
+    b = datagen.gauss_codes(g, (N, K), 64.0)
+    kb = -(-K // 128)
+    sa = datagen.log_uniform_scales(g, (M, kb))
+    sb = datagen.log_uniform_scales(g, (N if sb_mode == 1 else -(-N // 128), kb))
+    bias_bits = _bias_bits(g, N, BF16)
+    gpu = gu.scaled_gemm_bias(a, E4M3FN, b, E4M3FN, K, sa, 1, sb, sb_mode, bias_bits, BF16)
+    rows = sample_rows(M, 8)
+    value, sabs, bits = oracle.scaled_gemm(a, E4M3FN, b, E4M3FN, sa, 1, sb, sb_mode, BF16, rows=rows,
+                                           bias=_bias_values(bias_bits, BF16))
+    compare.check(gpu[rows], value, sabs, bits, BF16, f"bias block sb={sb_mode}")
+
+
+# ------------------------------------------------------------------ batched (TileOPs BmmFP8FwdOp)
+
+@pytest.mark.parametrize("L,M,N,K,fast,d_type,fmt", [
+    (3, 100, 300, 520, False, BF16, E4M3FN),     # 64x64 tiles, ragged
+    (8, 64, 64, 256, True, F32, E4M3FN),         # small items: tiles, not the skinny kernel
+    (16, 256, 1024, 136, True, BF16, E4M3FN),    # 128x128 tiles, one per CU: K groups
+    (4, 512, 1024, 1032, False, F16, E5M2),      # 128x128 tiles, two per CU, ragged K
+    (2, 2048, 1024, 264, True, BF16, E4M3FN),    # 256x256 tiles
+    (3, 70, 200, 136, False, E4M3FN, E4M3FN),    # FP8 out with scale_result
+])
+def test_batched_per_item_against_oracle(L, M, N, K, fast, d_type, fmt):
+    g = np.random.default_rng(L * 1000 + M)
+    a = np.stack([datagen.gauss_codes(g, (M, K), 64.0) for _ in range(L)]) if fmt == E4M3FN else \
+        g.integers(0, 256, size=(L, M, K)).astype(np.uint8) & 0xFB
+    b = np.stack([datagen.gauss_codes(g, (N, K), 64.0) for _ in range(L)]) if fmt == E4M3FN else \
+        g.integers(0, 256, size=(L, N, K)).astype(np.uint8) & 0xFB
+    sr = 0.0625 if d_type in (E4M3FN, E5M2) else None
+    gpu = gu.scaled_gemm_batched(a, fmt, b, fmt, K, 0.5, 0.25, d_type, scale_result=sr, fast=fast,
+                                 pad_a=32, pad_b=16, pad_d=8)
+    rows = sample_rows(M, 6)
+    for l in range(L):
+        value, sabs, bits = oracle.scaled_gemm(a[l], fmt, b[l], fmt, np.float32(0.5), 0, np.float32(0.25), 0,
+                                               d_type, scale_result=sr, rows=rows)
+        compare.check(gpu[l][rows], value, sabs, bits, d_type, f"batched item {l} of {L}: {M}x{N}x{K}")

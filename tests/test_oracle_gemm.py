@@ -362,3 +362,79 @@ def test_row_pitch_is_respected():
     v1, _, _ = oracle.scaled_gemm_k(a, 0, b, 0, 100, np.float32(1), 0, np.float32(1), 0, F32)
     v2, _, _ = oracle.scaled_gemm(d["a"], 0, d["b"], 0, np.float32(1), 0, np.float32(1), 0, F32)
     assert np.array_equal(v1, v2)
+
+
+# ------------------------------------------------------------------ bias (TileOPs GemmFP8FwdOp, forward)
+
+def _bias_values(rng, N, d_type):
+    """Random bias values exactly representable in d_type, as float64."""
+    x = rng.normal(0, 4, size=N).astype(np.float32)
+    if d_type == BF16:
+        return (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+    if d_type == F16:
+        return x.astype(np.float16).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def _bits_of(vals, d_type):
+    """Bit patterns of values exactly representable in d_type (numpy, not the oracle)."""
+    v = np.asarray(vals, dtype=np.float64)
+    if d_type == BF16:
+        return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    if d_type == F16:
+        return v.astype(np.float16).view(np.uint16)
+    return v.astype(np.float32).view(np.uint32)
+
+
+@pytest.mark.parametrize("d_type", [F32, BF16, F16])
+@pytest.mark.parametrize("accum", [ACC_EXACT, ACC_F32_CHUNKS])
+def test_bias_alone_when_the_product_is_zero(d_type, accum):
+    # zero codes give a zero sum; the result is the bias itself, bit for bit
+    rng = np.random.default_rng(11)
+    M, N, K = 5, 37, 200
+    a = np.zeros((M, K), dtype=np.uint8)
+    b = finite_random_codes(rng, (N, K), E4M3FN)
+    bias = _bias_values(rng, N, d_type)
+    _, _, bits = oracle.scaled_gemm(a, E4M3FN, b, E4M3FN, np.float32(0.5), SCALE_TENSOR, np.float32(2.0),
+                                    SCALE_TENSOR, d_type, accum=accum, bias=bias)
+    assert np.array_equal(bits, np.broadcast_to(_bits_of(bias, d_type), (M, N)))
+
+
+@pytest.mark.parametrize("d_type", [F32, BF16, F16])
+def test_bias_closed_form_all_ones(d_type):
+    # every code 0x38 = 1.0: the sum is K, times 0.5 * 0.25, plus small integer biases
+    M, N, K = 3, 9, 256
+    a = np.full((M, K), 0x38, dtype=np.uint8)
+    b = np.full((N, K), 0x38, dtype=np.uint8)
+    bias = np.arange(N, dtype=np.float64) - 4.0
+    value, _, bits = oracle.scaled_gemm(a, E4M3FN, b, E4M3FN, np.float32(0.5), SCALE_TENSOR, np.float32(0.25),
+                                        SCALE_TENSOR, d_type, bias=bias)
+    want = K * 0.125 + bias
+    assert np.array_equal(value, np.broadcast_to(want, (M, N)))
+    assert np.array_equal(bits, np.broadcast_to(_bits_of(want, d_type), (M, N)))
+
+
+def test_bias_block_scaled_matches_the_exact_sum_plus_bias():
+    # block scales: the exact rational sum (torch-decoded operands) plus the bias
+    rng = np.random.default_rng(12)
+    M, N, K = 4, 20, 300
+    a = finite_random_codes(rng, (M, K), E4M3FN)
+    b = finite_random_codes(rng, (N, K), E4M3FN)
+    kb = -(-K // 128)
+    sa = datagen.log_uniform_scales(rng, (M, kb))
+    sb = datagen.log_uniform_scales(rng, (N, kb))
+    bias = _bias_values(rng, N, F32)
+    v, sabs, _ = oracle.scaled_gemm(a, E4M3FN, b, E4M3FN, sa, SCALE_1x128, sb, SCALE_1x128, F32, bias=bias)
+    ex = exact_gemm(a, E4M3FN, b, E4M3FN, lambda m, k: Fraction(float(sa[m, k // 128])),
+                    lambda n, k: Fraction(float(sb[n, k // 128])), K)
+    for m in range(M):
+        for n in range(N):
+            err = abs(Fraction(float(v[m, n])) - (ex[m, n] + Fraction(float(bias[n]))))
+            assert err <= Fraction(2) ** -40 * (Fraction(float(sabs[m, n])) + abs(Fraction(float(bias[n]))))
+
+
+def test_bias_with_fp8_output_is_rejected():
+    a = np.zeros((2, 32), dtype=np.uint8)
+    with pytest.raises(ValueError):
+        oracle.scaled_gemm(a, E4M3FN, a, E4M3FN, np.float32(1), SCALE_TENSOR, np.float32(1), SCALE_TENSOR,
+                           E4M3FN, bias=np.zeros(2))

@@ -41,6 +41,10 @@ MUTANTS = {
     "amax_tie_last": ("(av == best && idx < best_idx)", "(av == best && idx > best_idx)"),
     "sf_group_index": ("(double)sfa[(l * M + m) * KS + k / sf_vec];", "(double)sfa[(l * M + m) * KS + k / (2 * sf_vec)];"),
     "nan_not_canonical": ("if (std::isnan(r)) return f.nan_bits;", "if (std::isnan(r)) return f.nan_bits - 1;"),
+    "bias_dropped": ("if (bias) v = accum == ORC_ACC_EXACT ? v + bias[n] : (double)to_f32(v + bias[n]);",
+                     "if (bias) v = v;"),
+    "bias_exact_rounded_f32": ("if (bias) v = accum == ORC_ACC_EXACT ? v + bias[n] : (double)to_f32(v + bias[n]);",
+                               "if (bias) v = (double)to_f32(v + bias[n]);"),
     "zero_chain_negative": ("double S = +0.0, T = 0.0;\n                    for (int64_t k = 0; k < K; ++k) {\n                        const double t = Am[k] * Bn[k];\n                        S += t;",
                             "double S = -0.0, T = 0.0;\n                    for (int64_t k = 0; k < K; ++k) {\n                        const double t = Am[k] * Bn[k];\n                        S += t;"),
 }
