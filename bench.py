@@ -132,6 +132,8 @@ OTHER = {
     "mx_amax": "batched E4M3 GEMM with power-of-two scales per 32 K, L=8, M=N=2048, K=8192, f32 C + amax + index",
     "e4m3_out": "E4M3 GEMM, M=8192, N=28672, K=8200 (lda 8200), slow, E4M3 out via scale_result=1/16",
     "e5m2_f16": "E5M2 GEMM, M=8192, N=28672, K=8200 (lda 8200), slow, f16 out",
+    "block_bias": "E4M3 1x128 / 128x128 block-scaled GEMM + bf16 bias [N], M=4096, N=14336, K=4096, bf16 out",
+    "bmm": "batched per-tensor E4M3 GEMM, L=8, M=N=2048, K=4096, slow, bf16 out",
 }
 
 
@@ -139,11 +141,12 @@ def run_other(name, steps, warmup):
     import torch
     import block_scaled_gemm_amd as mm
     import datagen
+    import numpy as np
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream().cuda_stream
     t0 = time.time()
-    if name == "block":
+    if name in ("block", "block_bias"):
         d = datagen.workload3()
         M, K = d["a"].shape; N = d["b"].shape[0]; L = 1
         a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
@@ -151,11 +154,35 @@ def run_other(name, steps, warmup):
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         out_bytes = 2
 
+        if name == "block":
+            def launch():
+                return mm.mm_scaled_gemm(M, N, K, a.data_ptr(), mm.MM_F8_E4M3FN, K, b.data_ptr(), mm.MM_F8_E4M3FN,
+                                         K, sa.data_ptr(), mm.MM_SCALE_1x128, sb.data_ptr(), mm.MM_SCALE_128x128, 0,
+                                         out.data_ptr(), mm.MM_BF16, N, 0, stream)
+            scale_bytes = 4 * (sa.numel() + sb.numel())
+        else:
+            bias = torch.from_numpy(datagen.bias_bf16_bits(N).view(np.int16)).to(dev)
+
+            def launch():
+                return mm.mm_scaled_gemm_bias(M, N, K, a.data_ptr(), mm.MM_F8_E4M3FN, K, b.data_ptr(),
+                                              mm.MM_F8_E4M3FN, K, sa.data_ptr(), mm.MM_SCALE_1x128, sb.data_ptr(),
+                                              mm.MM_SCALE_128x128, bias.data_ptr(), out.data_ptr(), mm.MM_BF16, N, 0,
+                                              stream)
+            scale_bytes = 4 * (sa.numel() + sb.numel()) + 2 * N
+    elif name == "bmm":
+        d = datagen.workload_bmm()
+        L, M, K = d["a"].shape; N = d["b"].shape[1]
+        a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
+        sa = torch.tensor([float(d["scale_a"])], dtype=torch.float32, device=dev)
+        sb = torch.tensor([float(d["scale_b"])], dtype=torch.float32, device=dev)
+        out = torch.empty((L, M, N), dtype=torch.bfloat16, device=dev)
+        out_bytes = 2
+
         def launch():
-            return mm.mm_scaled_gemm(M, N, K, a.data_ptr(), mm.MM_F8_E4M3FN, K, b.data_ptr(), mm.MM_F8_E4M3FN, K,
-                                     sa.data_ptr(), mm.MM_SCALE_1x128, sb.data_ptr(), mm.MM_SCALE_128x128, 0,
-                                     out.data_ptr(), mm.MM_BF16, N, 0, stream)
-        scale_bytes = 4 * (sa.numel() + sb.numel())
+            return mm.mm_scaled_gemm_batched(L, M, N, K, a.data_ptr(), mm.MM_F8_E4M3FN, K, M * K, b.data_ptr(),
+                                             mm.MM_F8_E4M3FN, K, N * K, sa.data_ptr(), sb.data_ptr(), 0,
+                                             out.data_ptr(), mm.MM_BF16, N, M * N, 0, stream)
+        scale_bytes = 8
     elif name == "mx_amax":
         d = datagen.workload4()
         L, M, K = d["a"].shape; N = d["b"].shape[1]

@@ -189,3 +189,17 @@ def workload5b(M=8192, N=28672, K=8200):
     b = gauss_codes(rng(6, 1), (N, K), 32.0, E5M2, 0.01)
     return dict(a=a, b=b, K=K, a_fmt=E5M2, b_fmt=E5M2,
                 scale_a=np.float32(2.0 ** -10), scale_b=np.float32(2.0 ** -10))
+
+
+def workload_bmm(L=8, M=2048, N=2048, K=4096):
+    """Batched per-tensor set (TileOPs BmmFP8FwdOp): Gaussian codes as workload 3, one scale per operand."""
+    a = gauss_codes(rng(7, 0), (L, M, K), 64.0)
+    b = gauss_codes(rng(7, 1), (L, N, K), 64.0)
+    return dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN,
+                scale_a=np.float32(0.5), scale_b=np.float32(0.25))
+
+
+def bias_bf16_bits(N: int, config: int = 3):
+    """A bf16 bias [N] (bit patterns), N(0, 16) values truncated to bf16."""
+    x = rng(config, 3).normal(0.0, 16.0, size=N).astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
