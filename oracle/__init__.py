@@ -7,11 +7,15 @@ benchmark's ``cpu_baseline`` leg may import this package. The product path
 All arithmetic lives in ``oracle.cpp`` (plain C++, float64); this module only
 marshals numpy arrays through ctypes. Its format numbers are its own:
 E4M3FN = 0, E5M2 = 1, F32 = 2, BF16 = 3, F16 = 4; scale modes TENSOR = 0,
-1x128 = 1, 128x128 = 2; accumulation EXACT = 0, F32_CHUNKS = 1.
+1x128 = 1, 128x128 = 2; accumulation EXACT = 0, F32_CHUNKS = 1; scale-factor
+element types SF_E8M0 = 0, SF_E4M3FN = 1.
 
 Parity status of each function (what pins it is in tests/test_oracle_*.py):
 decode_fp8, round_to, scaled_gemm (exact and f32-chunk modes),
-blockscaled_gemm_amax: pinned.
+blockscaled_gemm_amax: pinned. sf_atom_unpack: element decoding, the
+storage-to-logical permutation and the padding rule pinned; the order of the
+rows and groups inside a 128 x 4 atom is a reading of the page's shapes
+(parity unpinned for that order).
 """
 from __future__ import annotations
 
@@ -24,6 +28,7 @@ import numpy as np
 E4M3FN, E5M2, F32, BF16, F16 = 0, 1, 2, 3, 4
 SCALE_TENSOR, SCALE_1x128, SCALE_128x128 = 0, 1, 2
 ACC_EXACT, ACC_F32_CHUNKS = 0, 1
+SF_E8M0, SF_E4M3FN = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.cpp")
@@ -61,8 +66,9 @@ def _load():
                                         P, I64, P, P, P, I]
         lib.orc_blockscaled_gemm_amax.argtypes = [I64, I64, I64, I64, P, P, I, P, P, I, I, P, I64,
                                                   P, P, P, P, P, I]
+        lib.orc_sf_atom_unpack.argtypes = [P, I, I64, I64, I64, I, P]
         for f in (lib.orc_decode_fp8, lib.orc_round, lib.orc_scaled_gemm,
-                  lib.orc_blockscaled_gemm_amax):
+                  lib.orc_blockscaled_gemm_amax, lib.orc_sf_atom_unpack):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -166,3 +172,28 @@ def blockscaled_gemm_amax(a, b, ab_fmt, sfa, sfb, sf_vec, c_type, rows=None, thr
                                              _ptr(sabs), _ptr(bits), _ptr(amax), _ptr(idx),
                                              _threads(threads)))
     return value, sabs, bits, float(amax[0]), int(idx[0])
+
+
+def sf_atom_shape(MN: int, K: int, L: int, sf_vec: int):
+    """Storage shape (L, ceil(MN/128), ceil(K/(4 sf)), 32, 4, 4) of a page-native scale tensor."""
+    return (L, -(-MN // 128), -(-K // (4 * sf_vec)), 32, 4, 4)
+
+
+def sf_atom_unpack(sf, sf_type: int, MN: int, K: int, L: int, sf_vec: int) -> np.ndarray:
+    """Page-native scale bytes (storage order, any shape of the right size) -> float32 [L, MN, ceil(K/sf)]."""
+    sf = np.ascontiguousarray(sf, dtype=np.uint8).reshape(-1)
+    if sf.size != int(np.prod(sf_atom_shape(MN, K, L, sf_vec))):
+        raise ValueError("scale tensor size does not match the atom shape")
+    G = -(-K // sf_vec)
+    out = np.full((L, MN, G), np.nan, dtype=np.float32)
+    _check(_load().orc_sf_atom_unpack(_ptr(sf), sf_type, MN, K, L, sf_vec, _ptr(out)))
+    return out
+
+
+def blockscaled_gemm_amax_atom(a, b, ab_fmt, sfa, sfb, sf_type, sf_vec, c_type, rows=None, threads=None):
+    """blockscaled_gemm_amax with page-native scale tensors (storage bytes, see sf_atom_unpack)."""
+    L, M, K = np.shape(a)
+    N = np.shape(b)[1]
+    fa = sf_atom_unpack(sfa, sf_type, M, K, L, sf_vec)
+    fb = sf_atom_unpack(sfb, sf_type, N, K, L, sf_vec)
+    return blockscaled_gemm_amax(a, b, ab_fmt, fa, fb, sf_vec, c_type, rows=rows, threads=threads)

@@ -24,6 +24,10 @@
  *  - block-scaled GEMM + amax: C[m,n,l] = sum_k A^[m,k,l] B^[n,k,l] with
  *    A^ = A * SFA[l, m, k / sf_vec_size]; Amax = max over m,n,l of |C|
  *    ("cuDNN frontend: GEMM + Amax (SM100)", Equations).
+ *  - The page-native scale-factor tensors of that operator ("cuDNN frontend:
+ *    GEMM + Amax (SM100)", Shapes, Parameters and the JAX contract) are
+ *    unpacked into plain [L][MN][groups] factors first (orc_sf_atom_unpack);
+ *    the GEMM itself is then the one above.
  *
  * Arithmetic:
  *  - accum = ORC_ACC_EXACT: the sum is taken in float64 from +0 in increasing
@@ -71,6 +75,7 @@ enum { ORC_E4M3FN = 0, ORC_E5M2 = 1, ORC_F32 = 2, ORC_BF16 = 3, ORC_F16 = 4 };
 enum { ORC_SCALE_TENSOR = 0, ORC_SCALE_1x128 = 1, ORC_SCALE_128x128 = 2 };
 enum { ORC_ACC_EXACT = 0, ORC_ACC_F32_CHUNKS = 1 };
 enum { ORC_OK = 0, ORC_ERR_ARG = 1, ORC_ERR_FPENV = 2 };
+enum { ORC_SF_E8M0 = 0, ORC_SF_E4M3FN = 1 };
 
 }  // extern "C"
 
@@ -102,6 +107,14 @@ double decode_e5m2(uint8_t c) {
 }
 
 double decode(uint8_t c, int fmt) { return fmt == ORC_E4M3FN ? decode_e4m3fn(c) : decode_e5m2(c); }
+
+/* E8M0 (the float8_e8m0fnu scale-factor type of "cuDNN frontend: GEMM + Amax
+ * (SM100)", Parameters): an unsigned, biased exponent only, value 2^(e - 127);
+ * the code 0xFF is NaN; there is no zero and no infinity. */
+double decode_e8m0(uint8_t e) {
+    if (e == 0xFF) return std::nan("");
+    return std::ldexp(1.0, (int)e - 127);
+}
 
 /* ---------------------------------------------------------------- rounding */
 
@@ -428,6 +441,49 @@ int orc_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L,
         }
     if (amax) *amax = seen_nan ? std::nanf("") : to_f32(best);
     if (amax_index) *amax_index = best_idx;
+    return ORC_OK;
+}
+
+/*
+ * Page-native scale factors -> plain factors.
+ *
+ * "cuDNN frontend: GEMM + Amax (SM100)" gives SFA / SFB the logical shape
+ * (32, 4, ceil(MN/128), 4, ceil(K/(4 sf)), L) and says (JAX contract) that this
+ * is a view of the C-contiguous storage (L, ceil(MN/128), ceil(K/(4 sf)), 32,
+ * 4, 4) permuted by (3, 4, 1, 5, 2, 0): logical coordinate (i0, i1, i2, j0, j1,
+ * l) is storage element [l][i2][j1][i0][i1][j0]. The page gives the shapes
+ * only; the reading taken here (parity unpinned beyond the permutation) is
+ * that the two M-side atom modes enumerate the rows of a 128-row block
+ * first-mode-fastest, row mn = i0 + 32 i1 + 128 i2, and the two K-side modes
+ * the scale groups likewise, g = j0 + 4 j1.
+ *
+ * sf: the storage bytes; sf_type ORC_SF_E8M0 (int8 tensors are read as E8M0,
+ * as the page says) or ORC_SF_E4M3FN. Writes out[l][mn][g] for mn < MN and
+ * g < ceil(K/sf_vec) as fp32 (every E8M0 and E4M3 value is an fp32 value);
+ * storage elements past MN or past the last group are padding and are not
+ * read.
+ */
+int orc_sf_atom_unpack(const uint8_t* sf, int sf_type, int64_t MN, int64_t K, int64_t L, int sf_vec,
+                       float* out) {
+    if (MN < 0 || K < 0 || L < 0 || sf_vec <= 0) return ORC_ERR_ARG;
+    if (sf_type != ORC_SF_E8M0 && sf_type != ORC_SF_E4M3FN) return ORC_ERR_ARG;
+    const int64_t G = ceil_div(K, sf_vec);       /* scale groups along K */
+    const int64_t MB = ceil_div(MN, 128);        /* 128-row blocks */
+    const int64_t KB = ceil_div(K, 4 * sf_vec);  /* 4-group blocks */
+    for (int64_t l = 0; l < L; ++l)
+        for (int64_t i2 = 0; i2 < MB; ++i2)
+            for (int64_t j1 = 0; j1 < KB; ++j1)
+                for (int64_t i0 = 0; i0 < 32; ++i0)
+                    for (int64_t i1 = 0; i1 < 4; ++i1)
+                        for (int64_t j0 = 0; j0 < 4; ++j0) {
+                            const int64_t storage = ((((l * MB + i2) * KB + j1) * 32 + i0) * 4 + i1) * 4 + j0;
+                            const int64_t mn = i0 + 32 * i1 + 128 * i2;
+                            const int64_t g = j0 + 4 * j1;
+                            if (mn >= MN || g >= G) continue; /* padding */
+                            const uint8_t c = sf[storage];
+                            const double v = sf_type == ORC_SF_E8M0 ? decode_e8m0(c) : decode_e4m3fn(c);
+                            out[(l * MN + mn) * G + g] = (float)v;
+                        }
     return ORC_OK;
 }
 

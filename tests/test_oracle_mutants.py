@@ -19,7 +19,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.cpp")
-PINS = [os.path.join(ROOT, "tests", "test_oracle_fp8.py"), os.path.join(ROOT, "tests", "test_oracle_gemm.py")]
+PINS = [os.path.join(ROOT, "tests", "test_oracle_fp8.py"), os.path.join(ROOT, "tests", "test_oracle_gemm.py"),
+        os.path.join(ROOT, "tests", "test_oracle_atom.py")]
 
 # name -> (old text, new text); old text must occur exactly once
 MUTANTS = {
@@ -45,6 +46,11 @@ MUTANTS = {
                      "if (bias) v = v;"),
     "bias_exact_rounded_f32": ("if (bias) v = accum == ORC_ACC_EXACT ? v + bias[n] : (double)to_f32(v + bias[n]);",
                                "if (bias) v = (double)to_f32(v + bias[n]);"),
+    "e8m0_bias": ("std::ldexp(1.0, (int)e - 127)", "std::ldexp(1.0, (int)e - 126)"),
+    "e8m0_nan_code": ("if (e == 0xFF) return std::nan(\"\");", "if (e == 0xFE) return std::nan(\"\");"),
+    "atom_storage_inner_swapped": ("* 32 + i0) * 4 + i1) * 4 + j0;", "* 32 + i0) * 4 + j0) * 4 + i1;"),
+    "atom_rows_i1_fastest": ("const int64_t mn = i0 + 32 * i1 + 128 * i2;", "const int64_t mn = 4 * i0 + i1 + 128 * i2;"),
+    "atom_block_order": ("((((l * MB + i2) * KB + j1) * 32", "((((l * KB + j1) * MB + i2) * 32"),
     "zero_chain_negative": ("double S = +0.0, T = 0.0;\n                    for (int64_t k = 0; k < K; ++k) {\n                        const double t = Am[k] * Bn[k];\n                        S += t;",
                             "double S = -0.0, T = 0.0;\n                    for (int64_t k = 0; k < K; ++k) {\n                        const double t = Am[k] * Bn[k];\n                        S += t;"),
 }
