@@ -134,6 +134,8 @@ OTHER = {
     "e5m2_f16": "E5M2 GEMM, M=8192, N=28672, K=8200 (lda 8200), slow, f16 out",
     "block_bias": "E4M3 1x128 / 128x128 block-scaled GEMM + bf16 bias [N], M=4096, N=14336, K=4096, bf16 out",
     "bmm": "batched per-tensor E4M3 GEMM, L=8, M=N=2048, K=4096, slow, bf16 out",
+    "mx_atom": "batched E4M3 GEMM with E8M0 factors per 32 K in the page-native atom layout, L=8, M=N=2048, "
+               "K=8192, f32 C + amax + index",
 }
 
 
@@ -198,6 +200,21 @@ def run_other(name, steps, warmup):
                                                sfa.data_ptr(), sfb.data_ptr(), 32, c.data_ptr(), mm.MM_F32,
                                                amax.data_ptr(), idx.data_ptr(), stream)
         scale_bytes = 4 * (sfa.numel() + sfb.numel()) + 12
+    elif name == "mx_atom":
+        d = datagen.workload4_atom()
+        L, M, K = d["a"].shape; N = d["b"].shape[1]
+        a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
+        sfa = torch.from_numpy(d["sfa"]).to(dev); sfb = torch.from_numpy(d["sfb"]).to(dev)
+        c = torch.empty((L, M, N), dtype=torch.float32, device=dev)
+        amax = torch.empty((1,), dtype=torch.float32, device=dev)
+        idx = torch.empty((1,), dtype=torch.int64, device=dev)
+        out_bytes = 4
+
+        def launch():
+            return mm.mm_blockscaled_gemm_amax_atom(M, N, K, L, a.data_ptr(), b.data_ptr(), mm.MM_F8_E4M3FN,
+                                                    sfa.data_ptr(), sfb.data_ptr(), mm.MM_SF_E8M0, 32, c.data_ptr(),
+                                                    mm.MM_F32, amax.data_ptr(), idx.data_ptr(), stream)
+        scale_bytes = sfa.numel() + sfb.numel() + 12
     else:
         d = datagen.workload5a() if name == "e4m3_out" else datagen.workload5b()
         M, K = d["a"].shape; N = d["b"].shape[0]; L = 1

@@ -7,9 +7,10 @@ this directory and raises if it is missing: there is no fallback path.
 
 Raw C-ABI wrappers (same names as the C functions, integer pointers):
 ``mm_scaled_gemm``, ``mm_scaled_gemm_bias``, ``mm_scaled_gemm_batched``,
-``mm_blockscaled_gemm_amax``, ``mm_debug_convert``,
-``mm_last_error``, ``mm_version``. Tensor-level helpers: ``scaled_gemm`` (with
-an optional bias), ``scaled_bmm`` and ``blockscaled_gemm_amax``.
+``mm_blockscaled_gemm_amax``, ``mm_blockscaled_gemm_amax_atom``,
+``mm_debug_convert``, ``mm_last_error``, ``mm_version``. Tensor-level helpers:
+``scaled_gemm`` (with an optional bias), ``scaled_bmm`` and
+``blockscaled_gemm_amax`` (fp32 factors, or the page-native E8M0 bytes).
 """
 from __future__ import annotations
 
@@ -22,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libmmfp8.so")
 MM_OK, MM_ERR_INVALID_ARGUMENT, MM_ERR_UNSUPPORTED, MM_ERR_MISALIGNED, MM_ERR_DEVICE = 0, 1, 2, 3, 4
 MM_F8_E4M3FN, MM_F8_E5M2, MM_F32, MM_BF16, MM_F16 = 0, 1, 2, 3, 4
 MM_SCALE_TENSOR, MM_SCALE_1x128, MM_SCALE_128x128 = 0, 1, 2
+MM_SF_E8M0, MM_SF_E4M3FN = 0, 1
 
 # One HIP runtime per process. PyTorch ships its own HIP runtime with the same
 # soname as the system one libmmfp8 is linked against; loaded first, it also
@@ -49,13 +51,16 @@ _lib.mm_scaled_gemm_batched.argtypes = [_I64, _I64, _I64, _I64, _P, _I, _I64, _I
 _lib.mm_scaled_gemm_batched.restype = _I
 _lib.mm_blockscaled_gemm_amax.argtypes = [_I64, _I64, _I64, _I64, _P, _P, _I, _P, _P, _I, _P, _I, _P, _P, _P]
 _lib.mm_blockscaled_gemm_amax.restype = _I
+_lib.mm_blockscaled_gemm_amax_atom.argtypes = [_I64, _I64, _I64, _I64, _P, _P, _I, _P, _P, _I, _I, _P, _I, _P, _P,
+                                               _P]
+_lib.mm_blockscaled_gemm_amax_atom.restype = _I
 _lib.mm_debug_convert.argtypes = [_P, _P, _I, _I64, _P]
 _lib.mm_debug_convert.restype = _I
 _lib.mm_last_error.restype = ctypes.c_char_p
 _lib.mm_version.restype = ctypes.c_char_p
 
 EXPORTED = ("mm_scaled_gemm", "mm_scaled_gemm_bias", "mm_scaled_gemm_batched", "mm_blockscaled_gemm_amax",
-            "mm_last_error", "mm_version", "mm_debug_convert")
+            "mm_blockscaled_gemm_amax_atom", "mm_last_error", "mm_version", "mm_debug_convert")
 
 
 class MMError(RuntimeError):
@@ -102,6 +107,14 @@ def mm_blockscaled_gemm_amax(M, N, K, L, a, b, ab_type, sfa, sfb, sf_vec_size, c
     return _lib.mm_blockscaled_gemm_amax(M, N, K, L, a or None, b or None, ab_type, sfa or None, sfb or None,
                                          sf_vec_size, c or None, c_type, amax or None, amax_index or None,
                                          stream or None)
+
+
+def mm_blockscaled_gemm_amax_atom(M, N, K, L, a, b, ab_type, sfa, sfb, sf_type, sf_vec_size, c, c_type, amax,
+                                  amax_index, stream) -> int:
+    """Raw call of the C function; pointers and the stream are integers (0 = NULL). Returns the status."""
+    return _lib.mm_blockscaled_gemm_amax_atom(M, N, K, L, a or None, b or None, ab_type, sfa or None, sfb or None,
+                                              sf_type, sf_vec_size, c or None, c_type, amax or None,
+                                              amax_index or None, stream or None)
 
 
 def mm_debug_convert(x, y, dtype, n, stream) -> int:
@@ -245,8 +258,11 @@ def scaled_bmm(a, b, scale_a, scale_b, out_dtype, scale_result=None, use_fast_ac
 def blockscaled_gemm_amax(a, b, sfa, sfb, c_dtype=None, sf_vec_size=32, with_index=False, ab_format=None):
     """C[l] = (A[l] * SFA[l]) @ (B[l] * SFB[l])^T and the global amax of C.
 
-    a: [L, M, K] FP8, b: [L, N, K] FP8 (same format), sfa: [L, M, ceil(K/32)],
-    sfb: [L, N, ceil(K/32)] float32 powers of two. Returns (c [L, M, N], amax [1])
+    a: [L, M, K] FP8, b: [L, N, K] FP8 (same format). The scale factors are
+    either float32 powers of two, sfa [L, M, ceil(K/32)] and sfb
+    [L, N, ceil(K/32)], or the cuDNN page's own tensors: E8M0 bytes
+    (float8_e8m0fnu, uint8 or int8) of storage shape
+    (L, ceil(MN/128), ceil(K/128), 32, 4, 4). Returns (c [L, M, N], amax [1])
     or (c, amax, amax_index [1]) with with_index.
     """
     torch = _torch()
@@ -259,8 +275,19 @@ def blockscaled_gemm_amax(a, b, sfa, sfb, c_dtype=None, sf_vec_size=32, with_ind
     c = torch.empty((L, M, N), dtype=c_dtype, device=a.device)
     amax = torch.empty((1,), dtype=torch.float32, device=a.device)
     idx = torch.empty((1,), dtype=torch.int64, device=a.device) if with_index else None
-    st = mm_blockscaled_gemm_amax(M, N, K, L, a.data_ptr(), b.data_ptr(), _fp8_code(a, ab_format),
-                                  sfa.data_ptr(), sfb.data_ptr(), sf_vec_size, c.data_ptr(), dtype_code(c_dtype),
-                                  amax.data_ptr(), idx.data_ptr() if with_index else 0, _stream())
+    if sfa.element_size() == 1 and sfb.element_size() == 1:
+        for t, rows in ((sfa, M), (sfb, N)):
+            if t.numel() != L * -(-rows // 128) * -(-K // 128) * 512:
+                raise ValueError("E8M0 scale factors must have the storage shape (L, ceil(MN/128), ceil(K/128), 32, 4, 4)")
+        st = mm_blockscaled_gemm_amax_atom(M, N, K, L, a.data_ptr(), b.data_ptr(), _fp8_code(a, ab_format),
+                                           sfa.data_ptr(), sfb.data_ptr(), MM_SF_E8M0, sf_vec_size, c.data_ptr(),
+                                           dtype_code(c_dtype), amax.data_ptr(), idx.data_ptr() if with_index else 0,
+                                           _stream())
+    else:
+        if sfa.dtype != torch.float32 or sfb.dtype != torch.float32:
+            raise ValueError("scale factors must be float32, or E8M0 bytes for both operands")
+        st = mm_blockscaled_gemm_amax(M, N, K, L, a.data_ptr(), b.data_ptr(), _fp8_code(a, ab_format),
+                                      sfa.data_ptr(), sfb.data_ptr(), sf_vec_size, c.data_ptr(), dtype_code(c_dtype),
+                                      amax.data_ptr(), idx.data_ptr() if with_index else 0, _stream())
     _check(st)
     return (c, amax, idx) if with_index else (c, amax)

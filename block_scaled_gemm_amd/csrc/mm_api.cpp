@@ -228,10 +228,16 @@ mm_status mm_scaled_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K, con
                        ldd, stride_d, use_fast_accum, stream);
 }
 
-mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L, const void* a, const void* b,
-                                   int ab_type, const float* sfa, const float* sfb, int sf_vec_size, void* c,
-                                   int c_type, float* amax, int64_t* amax_index, void* stream) {
-    g_error.clear();
+}  // extern "C"
+
+namespace {
+
+// The batched MX GEMM + amax behind both entry points; `layout` is
+// mmfp8::SF_F32 (fp32 factors [L][MN][ceil(K/32)]) or mmfp8::SF_ATOM_E8M0
+// (the page-native E8M0 bytes).
+mm_status blockscaled_amax(const char* who, int64_t M, int64_t N, int64_t K, int64_t L, const void* a,
+                           const void* b, int ab_type, const void* sfa, const void* sfb, int layout, int sf_vec_size,
+                           void* c, int c_type, float* amax, int64_t* amax_index, void* stream) {
     if (M < 0 || N < 0 || K < 0 || L < 0)
         return fail(MM_ERR_INVALID_ARGUMENT, "M, N, K and L must be >= 0");
     if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim || L >= kMaxDim)
@@ -258,6 +264,9 @@ mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L, c
     if (!aligned(sfa, 4) || !aligned(sfb, 4) || !aligned(amax, 4))
         return fail(MM_ERR_MISALIGNED, "sfa, sfb and amax must be 4-byte aligned");
     if (!aligned(amax_index, 8)) return fail(MM_ERR_MISALIGNED, "amax_index must be 8-byte aligned");
+    const int64_t kblocks = cdiv(K, 128);
+    if (layout == mmfp8::SF_ATOM_E8M0 && (cdiv(M, 128) * kblocks * 512 >= kMaxDim || cdiv(N, 128) * kblocks * 512 >= kMaxDim))
+        return fail(MM_ERR_UNSUPPORTED, "each batch item's scale-factor tensor must be below 2^31 bytes");
     if (outs == 0 && !amax && !amax_index) return MM_OK;
     if (forced_launch_failure()) return fail(MM_ERR_DEVICE, "launch failure forced by MM_TEST_FORCE_FAIL");
 
@@ -281,12 +290,17 @@ mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L, c
         p.K = (int)K;
         p.L = (int)L;
         const int64_t ks = cdiv(K, 32);
-        p.sa = sfa;
-        p.sb = sfb;
+        p.sa = static_cast<const float*>(sfa);
+        p.sb = static_cast<const float*>(sfb);
         p.sa_ld = ks;
         p.sb_ld = ks;
-        p.sa_batch = M * ks;
-        p.sb_batch = N * ks;
+        if (layout == mmfp8::SF_ATOM_E8M0) {  // 4-byte units: 128 per 128 rows and 4 groups
+            p.sa_batch = cdiv(M, 128) * kblocks * 128;
+            p.sb_batch = cdiv(N, 128) * kblocks * 128;
+        } else {
+            p.sa_batch = M * ks;
+            p.sb_batch = N * ks;
+        }
         p.d = c;
         p.ldd = N;
         p.d_batch = M * N;
@@ -299,12 +313,36 @@ mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L, c
         p.tiles_n = (int)cdiv(N, mmfp8::kCfgBN[cfg]);
         const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * L;
         if (grid >= kMaxDim) return fail(MM_ERR_UNSUPPORTED, "too many output tiles");
-        mm_status st = device_status(mmfp8::launch_tile_sf32(cfg, ab_type == MM_F8_E5M2 ? 1 : 0, p, (int)grid, s),
-                                     "mm_blockscaled_gemm_amax launch");
+        mm_status st =
+            device_status(mmfp8::launch_tile_sf32(cfg, layout, ab_type == MM_F8_E5M2 ? 1 : 0, p, (int)grid, s), who);
         if (st != MM_OK) return st;
     }
     if (amax_index) return device_status(mmfp8::launch_amax_finalize(amax, key, s), "amax finalize launch");
     return MM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L, const void* a, const void* b,
+                                   int ab_type, const float* sfa, const float* sfb, int sf_vec_size, void* c,
+                                   int c_type, float* amax, int64_t* amax_index, void* stream) {
+    g_error.clear();
+    return blockscaled_amax("mm_blockscaled_gemm_amax launch", M, N, K, L, a, b, ab_type, sfa, sfb, mmfp8::SF_F32,
+                            sf_vec_size, c, c_type, amax, amax_index, stream);
+}
+
+mm_status mm_blockscaled_gemm_amax_atom(int64_t M, int64_t N, int64_t K, int64_t L, const void* a, const void* b,
+                                        int ab_type, const void* sfa, const void* sfb, int sf_type,
+                                        int sf_vec_size, void* c, int c_type, float* amax, int64_t* amax_index,
+                                        void* stream) {
+    g_error.clear();
+    if (sf_type == MM_SF_E4M3FN)
+        return fail(MM_ERR_UNSUPPORTED, "E4M3 scale factors go with FP4 operands and sf_vec_size 16 (not provided)");
+    if (sf_type != MM_SF_E8M0) return fail(MM_ERR_INVALID_ARGUMENT, "unknown sf_type %d", sf_type);
+    return blockscaled_amax("mm_blockscaled_gemm_amax_atom launch", M, N, K, L, a, b, ab_type, sfa, sfb,
+                            mmfp8::SF_ATOM_E8M0, sf_vec_size, c, c_type, amax, amax_index, stream);
 }
 
 mm_status mm_debug_convert(const float* x, void* y, int dtype, int64_t n, void* stream) {

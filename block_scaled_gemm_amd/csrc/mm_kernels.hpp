@@ -52,6 +52,11 @@ enum : int { T_E4M3 = 0, T_E5M2 = 1, T_F32 = 2, T_BF16 = 3, T_F16 = 4 };
 enum : int { MODE_FAST = 0, MODE_SLOW = 1, MODE_BLOCK = 2, MODE_SF32 = 3 };
 // Granularity of scale_b in MODE_BLOCK.
 enum : int { SB_1x128 = 0, SB_128x128 = 1 };
+// Scale-factor storage in MODE_SF32 (the same template slot): fp32 factors
+// [L][MN][groups], or the cuDNN page's native layout of E8M0 bytes, where for
+// every 128 rows and 4 groups the 512 bytes hold row r's 4 groups as one
+// dword at byte 16 (r % 32) + 4 (r / 32), blocks ordered [L][MN/128][K/128].
+enum : int { SF_F32 = 0, SF_ATOM_E8M0 = 1 };
 
 constexpr int kBK = 128;                 // K per main-loop step = one MFMA = one 128-element chunk
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 buffer descriptor dword 3 (raw, 32-bit format)
@@ -63,10 +68,10 @@ struct GemmArgs {
     int64_t lda, ldb;   // bytes
     int64_t a_batch, b_batch;  // bytes between batch items
     int M, N, K, L;
-    const float* sa;    // TENSOR: [1]; BLOCK: [M][sa_ld]; SF32: [L][M][sa_ld]
-    const float* sb;    // TENSOR: [1]; BLOCK: [N or ceil(N/128)][sb_ld]; SF32: [L][N][sb_ld]
-    int64_t sa_ld, sb_ld;
-    int64_t sa_batch, sb_batch;   // elements between batch items (SF32)
+    const float* sa;    // TENSOR: [1]; BLOCK: [M][sa_ld]; SF32: [L][M][sa_ld]; atom: E8M0 bytes
+    const float* sb;    // TENSOR: [1]; BLOCK: [N or ceil(N/128)][sb_ld]; SF32: [L][N][sb_ld]; atom: E8M0 bytes
+    int64_t sa_ld, sb_ld;         // SF32 (both layouts): ceil(K/32) groups
+    int64_t sa_batch, sb_batch;   // 4-byte elements between batch items (SF32, both layouts)
     const float* scale_result;    // FP8 outputs only; may be null
     void* d;            // [L][M] rows of ldd elements
     int64_t ldd, d_batch;         // elements
@@ -132,15 +137,17 @@ __device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// The E8M0 value carried by an fp32 scale factor: 2^(e - 127) for its
-// exponent field e; field 0 (zero, subnormals) is 2^-127 and field 255 (Inf,
-// NaN) is NaN. The mantissa is ignored.
-__device__ __forceinline__ float e8m0_scale(float s) {
-    const uint32_t e = (__float_as_uint(s) >> 23) & 0xFFu;
+// The value of an E8M0 code e: 2^(e - 127), 2^-127 (an fp32 subnormal) for
+// e = 0, NaN for e = 255.
+__device__ __forceinline__ float e8m0_code_scale(uint32_t e) {
     if (e == 0) return __uint_as_float(0x00400000u);
     if (e == 255) return __uint_as_float(0x7FC00000u);
     return __uint_as_float(e << 23);
 }
+// The E8M0 value carried by an fp32 scale factor: that of its exponent field
+// (field 0 for zero and subnormals, 255 for Inf and NaN); the mantissa is
+// ignored.
+__device__ __forceinline__ float e8m0_scale(float s) { return e8m0_code_scale((__float_as_uint(s) >> 23) & 0xFFu); }
 
 // ------------------------------------------------------------------ output conversions
 
@@ -344,8 +351,16 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     // scale_a of every A row (and scale_b of every B row when it is 1x128; a
     // 128x128 scale_b is one value per 128 columns, read from memory directly).
     // One 4-byte-per-lane load fills one scale column of 64 rows.
-    constexpr int SA_W = MODE == MODE_SF32 ? 4 : (MODE == MODE_BLOCK ? 1 : 0);
-    constexpr int SB_W = MODE == MODE_SF32 ? 4 : ((MODE == MODE_BLOCK && SBM == SB_1x128) ? 1 : 0);
+    // The page-native E8M0 layout keeps a row's 4 groups of a step in one
+    // dword: one gathering load per 64 rows, into LDS [row] in row order.
+    // The 256x256 tile issues each of these loads four times (the same bytes
+    // into the same LDS slots, as many loads as the fp32 factors take): its
+    // main loop then fits in 256 VGPRs, where with one issue the compiler
+    // spills 38 of them, which measured 17% slower.
+    constexpr bool kAtom = MODE == MODE_SF32 && SBM == SF_ATOM_E8M0;
+    constexpr int kAtomRep = kAtom && BM == 256 && BN == 256 ? 4 : 1;
+    constexpr int SA_W = MODE == MODE_SF32 ? (kAtom ? kAtomRep : 4) : (MODE == MODE_BLOCK ? 1 : 0);
+    constexpr int SB_W = MODE == MODE_SF32 ? (kAtom ? kAtomRep : 4) : ((MODE == MODE_BLOCK && SBM == SB_1x128) ? 1 : 0);
     constexpr int SC_A_INS = BM / 64 * SA_W, SC_INS = SC_A_INS + BN / 64 * SB_W;
     static_assert(BM % 64 == 0 && BN % 64 == 0, "scale columns are loaded 64 rows at a time");
     constexpr int STAGE = (BM + BN) * kBK + SC_INS * 256;
@@ -393,9 +408,24 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
 
     const float* sa_l = p.sa + (int64_t)l * p.sa_batch;
     const float* sb_l = p.sb + (int64_t)l * p.sb_batch;
-    // the tile's scale rows (rows past the matrix read zero; their results are discarded)
-    const rsrc_t rsa = make_rsrc(sa_l + (int64_t)m0 * p.sa_ld, SA_W ? (uint32_t)(min(BM, p.M - m0) * p.sa_ld * 4) : 0u);
-    const rsrc_t rsb = make_rsrc(sb_l + (int64_t)n0 * p.sb_ld, SB_W ? (uint32_t)(min(BN, p.N - n0) * p.sb_ld * 4) : 0u);
+    // the tile's scale rows (rows past the matrix read zero, or the atom
+    // layout's padding; their results are discarded)
+    const void* sa_t = kAtom ? (const void*)((const uint8_t*)sa_l + (int64_t)(m0 >> 7) * KT * 512)
+                             : (const void*)(sa_l + (int64_t)m0 * p.sa_ld);
+    const void* sb_t = kAtom ? (const void*)((const uint8_t*)sb_l + (int64_t)(n0 >> 7) * KT * 512)
+                             : (const void*)(sb_l + (int64_t)n0 * p.sb_ld);
+    const uint32_t sa_ext = kAtom ? (uint32_t)(((p.M + 127) / 128 - (m0 >> 7)) * KT * 512)
+                                  : (SA_W ? (uint32_t)(min(BM, p.M - m0) * p.sa_ld * 4) : 0u);
+    const uint32_t sb_ext = kAtom ? (uint32_t)(((p.N + 127) / 128 - (n0 >> 7)) * KT * 512)
+                                  : (SB_W ? (uint32_t)(min(BN, p.N - n0) * p.sb_ld * 4) : 0u);
+    const rsrc_t rsa = make_rsrc(sa_t, sa_ext);
+    const rsrc_t rsb = make_rsrc(sb_t, sb_ext);
+    // Atom layout: a load of 64 rows starting at row r0 (a multiple of 64)
+    // of the 128-row blocks gathers, in lane order, row r0 + lane's dword of
+    // the step's 512 bytes: byte (lane % 32) * 16 + 4 * ((r0 / 32) % 4 + lane / 32)
+    // of its block, i.e. a per-lane part common to every load plus a uniform part.
+    const uint32_t atom_lane = (uint32_t)((lane & 31) * 16 + (lane >> 5) * 4);
+    auto atom_uni = [&](int r0) { return (r0 >> 7) * KT * 512 + ((r0 >> 5) & 3) * 4; };
 
     auto issue = [&](int kt, uint8_t* sbase) {
         if (kt >= KT) return;  // past the end: nothing to load
@@ -434,7 +464,25 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
         // LDS [j][row] after the tiles. MX groups past ceil(K/32) read whatever
         // follows (the next row, or zero past the last): their data is zero and
         // their conversion scale is replaced by 1 at use.
-        if constexpr (SC_A_INS > 0) {
+        if constexpr (kAtom) {
+            // Load t brings rows 64 (t % RA) .. + 63 of the tile (repeats when
+            // kAtomRep > 1). The block part rides in the range-checked per-lane
+            // offset, so blocks past the tensor's last (rows past M / N only)
+            // read zero; the step's 512 bytes ride in the scalar offset.
+            constexpr int RA = BM < 128 ? 1 : BM / 64, RB = BN < 128 ? 1 : BN / 64;
+            for (int t = gw; t < SC_A_INS; t += NW) {
+                const int ta = t % RA;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(sbase + (BM + BN) * kBK + ta * 256), 4,
+                                                         atom_lane + atom_uni((BM < 128 ? (m0 & 127) : 0) + ta * 64),
+                                                         kt * 512, 0, 0);
+            }
+            for (int t = gw; t < SC_INS - SC_A_INS; t += NW) {
+                const int tb = t % RB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsb, (lds_void*)(sbase + (BM + BN) * kBK + (SC_A_INS + tb) * 256), 4,
+                    atom_lane + atom_uni((BN < 128 ? (n0 & 127) : 0) + tb * 64), kt * 512, 0, 0);
+            }
+        } else if constexpr (SC_A_INS > 0) {
             for (int t = gw; t < SC_A_INS; t += NW) {
                 const int j = t % SA_W, rg = t / SA_W;
                 const uint32_t off = (uint32_t)(((rg * 64 + lane) * p.sa_ld + kt * SA_W + j) * 4);
@@ -442,7 +490,7 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
                     rsa, (lds_void*)(sbase + (BM + BN) * kBK + (j * BM + rg * 64) * 4), 4, off, 0, 0, 0);
             }
         }
-        if constexpr (SC_INS > SC_A_INS) {
+        if constexpr (!kAtom && SC_INS > SC_A_INS) {
             for (int t = gw; t < SC_INS - SC_A_INS; t += NW) {
                 const int j = t % SB_W, rg = t / SB_W;
                 const uint32_t off = (uint32_t)(((rg * 64 + lane) * p.sb_ld + kt * SB_W + j) * 4);
@@ -570,7 +618,18 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
 #pragma unroll
                 for (int r = 0; r < 4; ++r) s_b[j][r] = kSbMem ? sc_cur.b[j] : scB[wn * WTN + j * 16 + 4 * fg + r];
         }
-        if (MODE == MODE_SF32) {
+        if (MODE == MODE_SF32 && kAtom) {
+            // the row's dword holds the step's 4 groups; byte fg is this lane's
+            const bool gv = kt * 4 + fg < p.sa_ld;  // groups past ceil(K/32) hold zero data
+            const uint32_t* wA = (const uint32_t*)scA;
+            const uint32_t* wB = wA + SC_A_INS * 64;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                c_a[i] = gv ? e8m0_code_scale((wA[wm * WTM + i * 16 + fr] >> (8 * fg)) & 0xFFu) : 1.0f;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                c_b[j] = gv ? e8m0_code_scale((wB[wn * WTN + j * 16 + fr] >> (8 * fg)) & 0xFFu) : 1.0f;
+        } else if (MODE == MODE_SF32) {
             const bool gv = kt * 4 + fg < p.sa_ld;  // groups past ceil(K/32) hold zero data
 #pragma unroll
             for (int i = 0; i < FM; ++i) c_a[i] = gv ? e8m0_scale(scA[fg * BM + wm * WTM + i * 16 + fr]) : 1.0f;

@@ -43,7 +43,7 @@ constexpr int kKsBN[2] = {64, 64};
 hipError_t launch_tile_fast(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_tile_slow(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_tile_block(int cfg, int sbm, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
-hipError_t launch_tile_sf32(int cfg, int f, const GemmArgs& p, int grid, hipStream_t s);
+hipError_t launch_tile_sf32(int cfg, int layout, int f, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_skinny(int mt, int mode, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_ksplit(int ks, int mode, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_amax_init(uint32_t* bits, unsigned long long* key, hipStream_t s);

@@ -59,6 +59,15 @@ typedef enum mm_scale_mode {
     MM_SCALE_128x128 = 2  /* [ceil(rows/128), ceil(K/128)]       */
 } mm_scale_mode;
 
+/* Element types of page-native scale-factor tensors ("cuDNN frontend: GEMM +
+ * Amax (SM100)", Parameters, SFA / SFB dtypes). E8M0 is an unsigned biased
+ * exponent, value 2^(e - 127), code 0xFF NaN; the page's int8 scale tensors
+ * are read as E8M0, so they are passed as MM_SF_E8M0. */
+typedef enum mm_sf_type {
+    MM_SF_E8M0 = 0,
+    MM_SF_E4M3FN = 1
+} mm_sf_type;
+
 /*
  * mm_scaled_gemm -- d = (a * s_a) @ (b * s_b)^T, cast to d_type.
  *
@@ -223,6 +232,39 @@ mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L,
                                    void* c, int c_type,
                                    float* amax, int64_t* amax_index,
                                    void* stream);
+
+/*
+ * mm_blockscaled_gemm_amax_atom -- mm_blockscaled_gemm_amax with the scale
+ * factors in the page's own format: E8M0 bytes in the atom layout of
+ * "cuDNN frontend: GEMM + Amax (SM100)", Shapes and Parameters (SFA, SFB).
+ *
+ *  sfa      the page's SFA of logical shape (32, 4, ceil(M/128), 4,
+ *           ceil(K/(4*32)), L), passed as its C-contiguous storage
+ *           (L, ceil(M/128), ceil(K/128), 32, 4, 4) bytes, which the page's
+ *           JAX contract says the logical view is a permutation of
+ *           (3, 4, 1, 5, 2, 0). Row m and 32-group g of batch item l use the
+ *           byte at [l][m / 128][g / 4][m % 32][(m / 32) % 4][g % 4] (the page
+ *           gives shapes only: row m = i0 + 32 i1 + 128 i2 and group
+ *           g = j0 + 4 j1 of the logical coordinates is the reading taken).
+ *           Every byte of the padded shape must be readable; bytes of rows
+ *           past M or groups past ceil(K/32) are never used.
+ *  sfb      the same for B with N rows.
+ *  sf_type  MM_SF_E8M0 (int8 tensors included). MM_SF_E4M3FN factors go with
+ *           sf_vec_size 16 and FP4 operands on the page, neither of which this
+ *           entry takes -> MM_ERR_UNSUPPORTED; other values ->
+ *           MM_ERR_INVALID_ARGUMENT.
+ *
+ * Everything else (a, b, ab_type, sf_vec_size, c, c_type, amax, amax_index,
+ * stream, the arithmetic, sizes, alignment and errors) is as
+ * mm_blockscaled_gemm_amax; in addition each batch item's factor tensor must
+ * stay below 2^31 bytes (else MM_ERR_UNSUPPORTED).
+ */
+mm_status mm_blockscaled_gemm_amax_atom(int64_t M, int64_t N, int64_t K, int64_t L,
+                                        const void* a, const void* b, int ab_type,
+                                        const void* sfa, const void* sfb, int sf_type, int sf_vec_size,
+                                        void* c, int c_type,
+                                        float* amax, int64_t* amax_index,
+                                        void* stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if
  * none). The pointer stays valid until the thread's next mm_* call. */

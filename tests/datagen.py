@@ -203,3 +203,18 @@ def bias_bf16_bits(N: int, config: int = 3):
     """A bf16 bias [N] (bit patterns), N(0, 16) values truncated to bf16."""
     x = rng(config, 3).normal(0.0, 16.0, size=N).astype(np.float32)
     return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def e8m0_atom_codes(g, MN, K, L, sf=32, lo=-8, hi=4):
+    """E8M0 scale-factor codes 127 + U{lo..hi} (factors 2^lo .. 2^hi) for every byte of the cuDNN
+    GEMM + Amax page's scale tensor, in its storage shape (L, ceil(MN/128), ceil(K/(4 sf)), 32, 4, 4)."""
+    shape = (L, -(-MN // 128), -(-K // (4 * sf)), 32, 4, 4)
+    return (127 + g.integers(lo, hi + 1, size=shape)).astype(np.uint8)
+
+
+def workload4_atom(L=8, M=2048, N=2048, K=8192):
+    """Workload 4 with the page's own scale format: the same codes, E8M0 factors in the atom layout."""
+    a = gauss_codes(rng(4, 0), (L, M, K), 64.0)
+    b = gauss_codes(rng(4, 1), (L, N, K), 64.0)
+    return dict(a=a, b=b, ab_fmt=E4M3FN, sfa=e8m0_atom_codes(rng(4, 5), M, K, L),
+                sfb=e8m0_atom_codes(rng(4, 6), N, K, L), sf_vec=32)

@@ -63,6 +63,26 @@ def blockscaled_gemm_amax(a, b, fmt, sfa, sfb, c_type, with_amax=True, with_inde
             int(tix.item()) if with_index else None)
 
 
+def blockscaled_gemm_amax_atom(a, b, fmt, sfa, sfb, c_type, with_amax=True, with_index=True):
+    """As blockscaled_gemm_amax with E8M0 scale bytes in the page's storage shape."""
+    L, M, K = a.shape
+    N = b.shape[1]
+    ta, tb, tsa, tsb = dev_u8(a), dev_u8(b), dev_u8(sfa), dev_u8(sfb)
+    es = np.dtype(BITS_NP[c_type]).itemsize
+    tc = torch.full((max(L * M * N, 1) * es,), 0x5A, dtype=torch.uint8, device=DEV)
+    tam = torch.full((1,), 123.0, dtype=torch.float32, device=DEV)
+    tix = torch.full((1,), 777, dtype=torch.int64, device=DEV)
+    st = mm.mm_blockscaled_gemm_amax_atom(M, N, K, L, ta.data_ptr(), tb.data_ptr(), fmt, tsa.data_ptr(),
+                                          tsb.data_ptr(), mm.MM_SF_E8M0, 32, tc.data_ptr(), c_type,
+                                          tam.data_ptr() if with_amax else 0, tix.data_ptr() if with_index else 0,
+                                          stream())
+    assert st == mm.MM_OK, (st, mm.mm_last_error())
+    torch.cuda.synchronize()
+    c = tc.cpu().numpy().view(BITS_NP[c_type])[: L * M * N].reshape(L, M, N)
+    return (np.ascontiguousarray(c), float(tam.item()) if with_amax else None,
+            int(tix.item()) if with_index else None)
+
+
 def debug_convert(x: np.ndarray, dtype: int) -> np.ndarray:
     tx = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
     es = np.dtype(BITS_NP[dtype]).itemsize

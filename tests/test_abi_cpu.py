@@ -28,7 +28,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"mm_scaled_gemm", "mm_scaled_gemm_bias", "mm_scaled_gemm_batched",
-                          "mm_blockscaled_gemm_amax", "mm_last_error", "mm_version", "mm_debug_convert"}
+                          "mm_blockscaled_gemm_amax", "mm_blockscaled_gemm_amax_atom", "mm_last_error",
+                          "mm_version", "mm_debug_convert"}
     lib = ctypes.CDLL(mm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -169,11 +170,43 @@ def test_amax_zero_size_without_outputs_launches_nothing():
     assert amax_call(M=0, amax=0, amax_index=0, c=0) == mm.MM_OK
 
 
+def atom_call(**kw):
+    args = dict(M=64, N=64, K=256, L=2, a=P, b=P, ab_type=0, sfa=P, sfb=P, sf_type=mm.MM_SF_E8M0, sf_vec_size=32,
+                c=P, c_type=2, amax=P, amax_index=P, stream=0)
+    args.update(kw)
+    return mm.mm_blockscaled_gemm_amax_atom(**args)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(sf_type=mm.MM_SF_E4M3FN), mm.MM_ERR_UNSUPPORTED, "E4M3 scale factors"),
+    (dict(sf_type=5), mm.MM_ERR_INVALID_ARGUMENT, "unknown sf_type"),
+    (dict(L=-1), mm.MM_ERR_INVALID_ARGUMENT, "must be >= 0"),
+    (dict(ab_type=2), mm.MM_ERR_INVALID_ARGUMENT, "ab_type"),
+    (dict(sf_vec_size=16), mm.MM_ERR_UNSUPPORTED, "sf_vec_size 16"),
+    (dict(c_type=1), mm.MM_ERR_UNSUPPORTED, "FP8 C"),
+    (dict(sfa=0), mm.MM_ERR_INVALID_ARGUMENT, "NULL"),
+    (dict(sfb=P + 2), mm.MM_ERR_MISALIGNED, "4-byte"),
+    (dict(K=264), mm.MM_ERR_MISALIGNED, "multiple of 16"),
+    # ceil(M/128) * ceil(K/128) * 512 bytes per item must stay below 2^31
+    (dict(M=1 << 20, K=1 << 16, L=1), mm.MM_ERR_UNSUPPORTED, "below 2^31 bytes"),
+    (dict(N=1 << 20, K=1 << 16, L=1, amax_index=0), mm.MM_ERR_UNSUPPORTED, "below 2^31 bytes"),
+])
+def test_atom_validation(kw, status, msg):
+    assert atom_call(**kw) == status
+    assert msg in mm.mm_last_error()
+
+
+def test_atom_zero_sizes_launch_nothing():
+    assert atom_call(L=0, amax=0, amax_index=0, c=0) == mm.MM_OK
+    assert atom_call(N=0, amax=0, amax_index=0, c=0, sfa=0, sfb=0) == mm.MM_OK
+
+
 def test_forced_launch_failure(monkeypatch):
     monkeypatch.setenv("MM_TEST_FORCE_FAIL", "launch")
     assert gemm() == mm.MM_ERR_DEVICE
     assert "forced" in mm.mm_last_error()
     assert amax_call() == mm.MM_ERR_DEVICE
+    assert atom_call() == mm.MM_ERR_DEVICE
     assert gemm_bias() == mm.MM_ERR_DEVICE
     assert bmm() == mm.MM_ERR_DEVICE
     assert mm.mm_debug_convert(P, P, 2, 16, 0) == mm.MM_ERR_DEVICE

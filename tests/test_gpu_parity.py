@@ -309,6 +309,91 @@ def test_workload4_full_size():
     assert amax == float(cf.max()) and idx == int(np.argmax(cf))
 
 
+# ------------------------------------------------------------------ page-native E8M0 factors (atom layout)
+
+def check_atom_case(w, c_type, rows=None):
+    c, amax, idx = gu.blockscaled_gemm_amax_atom(w["a"], w["b"], w["ab_fmt"], w["sfa"], w["sfb"], c_type)
+    value, sabs, bits, _, _ = oracle.blockscaled_gemm_amax_atom(w["a"], w["b"], w["ab_fmt"], w["sfa"], w["sfb"],
+                                                                oracle.SF_E8M0, 32, c_type, rows=rows)
+    cg = c if rows is None else c[:, rows]
+    compare.check(cg, value, sabs, bits, c_type, "atom gemm")
+    return c, amax, idx, value, sabs
+
+
+def atom_padding_mask(MN, K, L, sf=32):
+    """True on the storage bytes no factor uses: logical (i0, i1, i2, j0, j1, l) is storage
+    [l][i2][j1][i0][i1][j0] (the page's permutation); row i0 + 32 i1 + 128 i2 and group j0 + 4 j1
+    (the reading of the page's shapes) past MN or ceil(K/sf) are padding."""
+    shape = oracle.sf_atom_shape(MN, K, L, sf)
+    l, i2, j1, i0, i1, j0 = np.indices(shape)
+    return (i0 + 32 * i1 + 128 * i2 >= MN) | (j0 + 4 * j1 >= -(-K // sf))
+
+
+@pytest.mark.parametrize("L,M,N,K,c_type", [(3, 200, 136, 1024, F32), (2, 96, 200, 512, BF16),
+                                            (1, 130, 70, 1008, F16), (2, 257, 129, 96, F32)])
+def test_atom_against_oracle(L, M, N, K, c_type):
+    w = datagen.workload4_atom(L, M, N, K)
+    c, amax, idx, value, sabs = check_atom_case(w, c_type)
+    v = np.abs(value.reshape(-1))
+    assert abs(amax - v.max()) <= 2.0 ** -20 * sabs.reshape(-1)[np.argmax(v)]
+    if c_type == F32:  # bit-exact against the GPU's own C
+        cf = np.abs(c.view(np.float32).astype(np.float64).reshape(-1))
+        assert amax == float(cf.max()) and idx == int(np.argmax(cf))
+
+
+@pytest.mark.parametrize("L,M,N,K", [(3, 200, 136, 1024), (1, 130, 70, 1008), (2, 2048, 2048, 1040),
+                                     (1, 2048, 2048, 1040)], ids=["64x64", "64x64-ragged", "128x256", "128x128"])
+def test_atom_equals_fp32_factor_entry(L, M, N, K):
+    """The same factors as fp32 powers of two through mm_blockscaled_gemm_amax: bitwise the same C,
+    amax and index (the two entries differ only in how the factors are read)."""
+    w = datagen.workload4_atom(L, M, N, K)
+    c1, a1, i1 = gu.blockscaled_gemm_amax_atom(w["a"], w["b"], 0, w["sfa"], w["sfb"], F32)
+    fa = oracle.sf_atom_unpack(w["sfa"], oracle.SF_E8M0, M, K, L, 32)
+    fb = oracle.sf_atom_unpack(w["sfb"], oracle.SF_E8M0, N, K, L, 32)
+    c2, a2, i2 = gu.blockscaled_gemm_amax(w["a"], w["b"], 0, fa, fb, F32)
+    compare.assert_bitwise_equal(c1, c2, "atom vs fp32 factors")
+    assert a1 == a2 and i1 == i2
+
+
+def test_atom_padding_is_not_read():
+    L, M, N, K = 2, 100, 72, 208  # 28 / 56 padding rows, group 7 of the second 4-group block unused
+    w = datagen.workload4_atom(L, M, N, K)
+    c1, a1, i1 = gu.blockscaled_gemm_amax_atom(w["a"], w["b"], 0, w["sfa"], w["sfb"], F32)
+    sfa, sfb = w["sfa"].copy(), w["sfb"].copy()
+    sfa[atom_padding_mask(M, K, L)] = 0xFF  # NaN factors
+    sfb[atom_padding_mask(N, K, L)] = 0xFF
+    assert (sfa == 0xFF).sum() > 0 and (sfb == 0xFF).sum() > 0
+    c2, a2, i2 = gu.blockscaled_gemm_amax_atom(w["a"], w["b"], 0, sfa, sfb, F32)
+    compare.assert_bitwise_equal(c1, c2, "padding factors")
+    assert a1 == a2 and i1 == i2 and not np.isnan(a2)
+
+
+def test_atom_nan_factor_poisons_one_row():
+    L, M, N, K = 2, 72, 80, 256
+    w = datagen.workload4_atom(L, M, N, K)
+    # row 5, group 2 of item 1 (storage [l][m/128][g/4][m%32][(m/32)%4][g%4])
+    w["sfa"][1, 0, 0, 5, 0, 2] = 0xFF
+    c, amax, idx, value, sabs = check_atom_case(w, F32)
+    cf = c.view(np.float32)
+    assert np.isnan(cf[1, 5]).all() and not np.isnan(np.delete(cf.reshape(L * M, N), M + 5, axis=0)).any()
+    assert np.isnan(amax) and idx == 1 * M * N + 5 * N
+
+
+def test_atom_workload4_full_size():
+    """Workload 4 (L=8, 2048 x 2048 x 8192) with E8M0 atom factors, on the 256x256 tile: sampled rows
+    against the oracle, the whole C bitwise against the fp32-factor entry."""
+    w = datagen.workload4_atom()
+    rows = sample_rows(2048, 4)
+    c, amax, idx, value, sabs = check_atom_case(w, F32, rows=rows)
+    cf = np.abs(c.view(np.float32).reshape(-1))
+    assert amax == float(cf.max()) and idx == int(np.argmax(cf))
+    fa = oracle.sf_atom_unpack(w["sfa"], oracle.SF_E8M0, 2048, 8192, 8, 32)
+    fb = oracle.sf_atom_unpack(w["sfb"], oracle.SF_E8M0, 2048, 8192, 8, 32)
+    c2, a2, i2 = gu.blockscaled_gemm_amax(w["a"], w["b"], 0, fa, fb, F32)
+    compare.assert_bitwise_equal(c, c2, "atom vs fp32 factors, full size")
+    assert amax == a2 and idx == i2
+
+
 # ------------------------------------------------------------------ workload 5: K tail, FP8 / f16 out
 
 def test_workload5_small():
