@@ -6,12 +6,12 @@ benchmark's ``cpu_baseline`` leg may import this package. The product path
 
 All arithmetic lives in ``oracle.cpp`` (plain C++, float64); this module only
 marshals numpy arrays through ctypes. Its format numbers are its own:
-E4M3FN = 0, E5M2 = 1, F32 = 2, BF16 = 3, F16 = 4; scale modes TENSOR = 0,
+E4M3FN = 0, E5M2 = 1, F32 = 2, BF16 = 3, F16 = 4, E2M1 = 5 (FP4, two per byte); scale modes TENSOR = 0,
 1x128 = 1, 128x128 = 2; accumulation EXACT = 0, F32_CHUNKS = 1; scale-factor
 element types SF_E8M0 = 0, SF_E4M3FN = 1.
 
 Parity status of each function (what pins it is in tests/test_oracle_*.py):
-decode_fp8, round_to, scaled_gemm (exact and f32-chunk modes),
+decode_fp8, decode_fp4, round_to, scaled_gemm (exact and f32-chunk modes),
 blockscaled_gemm_amax: pinned. sf_atom_unpack: element decoding, the
 storage-to-logical permutation and the padding rule pinned; the order of the
 rows and groups inside a 128 x 4 atom is a reading of the page's shapes
@@ -25,7 +25,7 @@ import subprocess
 
 import numpy as np
 
-E4M3FN, E5M2, F32, BF16, F16 = 0, 1, 2, 3, 4
+E4M3FN, E5M2, F32, BF16, F16, E2M1 = 0, 1, 2, 3, 4, 5
 SCALE_TENSOR, SCALE_1x128, SCALE_128x128 = 0, 1, 2
 ACC_EXACT, ACC_F32_CHUNKS = 0, 1
 SF_E8M0, SF_E4M3FN = 0, 1
@@ -67,8 +67,9 @@ def _load():
         lib.orc_blockscaled_gemm_amax.argtypes = [I64, I64, I64, I64, P, P, I, P, P, I, I, P, I64,
                                                   P, P, P, P, P, I]
         lib.orc_sf_atom_unpack.argtypes = [P, I, I64, I64, I64, I, P]
+        lib.orc_decode_fp4.argtypes = [P, I64, P]
         for f in (lib.orc_decode_fp8, lib.orc_round, lib.orc_scaled_gemm,
-                  lib.orc_blockscaled_gemm_amax, lib.orc_sf_atom_unpack):
+                  lib.orc_blockscaled_gemm_amax, lib.orc_sf_atom_unpack, lib.orc_decode_fp4):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -97,6 +98,14 @@ def decode_fp8(codes: np.ndarray, fmt: int) -> np.ndarray:
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     out = np.empty(codes.shape, dtype=np.float64)
     _check(_load().orc_decode_fp8(_ptr(codes), codes.size, fmt, _ptr(out)))
+    return out
+
+
+def decode_fp4(codes: np.ndarray) -> np.ndarray:
+    """E2M1 codes (0..15, one per array element) to float64."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape, dtype=np.float64)
+    _check(_load().orc_decode_fp4(_ptr(codes), codes.size, _ptr(out)))
     return out
 
 
@@ -150,13 +159,16 @@ def scaled_gemm_k(a, a_fmt, b, b_fmt, K, scale_a, sa_mode, scale_b, sb_mode, d_t
 
 
 def blockscaled_gemm_amax(a, b, ab_fmt, sfa, sfb, sf_vec, c_type, rows=None, threads=None):
-    """C[l,m,n] = sum_k A^ B^ with A^ = A*SFA[l,m,k//sf]; a [L,M,K], b [L,N,K] uint8.
+    """C[l,m,n] = sum_k A^ B^ with A^ = A*SFA[l,m,k//sf]; a [L,M,K], b [L,N,K] uint8
+    (E2M1: [L,M,K/2] and [L,N,K/2] bytes, two elements each).
 
     Returns (value [L,R,N], sum_abs [L,R,N], c_bits [L,R,N], amax float32, amax_index int).
     """
     a = np.ascontiguousarray(a, dtype=np.uint8)
     b = np.ascontiguousarray(b, dtype=np.uint8)
     L, M, K = a.shape
+    if ab_fmt == E2M1:
+        K *= 2
     N = b.shape[1]
     sfa = np.ascontiguousarray(sfa, dtype=np.float32)
     sfb = np.ascontiguousarray(sfb, dtype=np.float32)
@@ -194,6 +206,8 @@ def blockscaled_gemm_amax_atom(a, b, ab_fmt, sfa, sfb, sf_type, sf_vec, c_type, 
     """blockscaled_gemm_amax with page-native scale tensors (storage bytes, see sf_atom_unpack)."""
     L, M, K = np.shape(a)
     N = np.shape(b)[1]
+    if ab_fmt == E2M1:
+        K *= 2
     fa = sf_atom_unpack(sfa, sf_type, M, K, L, sf_vec)
     fb = sf_atom_unpack(sfb, sf_type, N, K, L, sf_vec)
     return blockscaled_gemm_amax(a, b, ab_fmt, fa, fb, sf_vec, c_type, rows=rows, threads=threads)

@@ -12,7 +12,8 @@
  *  - Operands are FP8 codes, decoded by their bit fields (OCP 8-bit floating
  *    point formats E4M3FN and E5M2, the float8_e4m3fn / float8_e5m2 dtypes of
  *    "mmaemu API reference (v0.1)", scaled_mm argument table, and of
- *    "cuDNN frontend: GEMM + Amax (SM100)", Parameters).
+ *    "cuDNN frontend: GEMM + Amax (SM100)", Parameters), or, for the
+ *    block-scaled GEMM + amax, E2M1 pairs (that page's float4_e2m1fn_x2).
  *  - scaled GEMM: d[m,n] = (a * s_a) @ (b * s_b)^T with a [M,K] and b [N,K]
  *    ("TileOPs: Linear Algebra Operators", tileops.gemm.GemmFP8FwdOp). With
  *    per-tensor scales the unscaled sum is multiplied by both scales
@@ -71,7 +72,7 @@ extern "C" {
 
 /* Format numbers used by this file's C interface (its own, documented in
  * oracle.py; nothing here is shared with the GPU library). */
-enum { ORC_E4M3FN = 0, ORC_E5M2 = 1, ORC_F32 = 2, ORC_BF16 = 3, ORC_F16 = 4 };
+enum { ORC_E4M3FN = 0, ORC_E5M2 = 1, ORC_F32 = 2, ORC_BF16 = 3, ORC_F16 = 4, ORC_E2M1 = 5 };
 enum { ORC_SCALE_TENSOR = 0, ORC_SCALE_1x128 = 1, ORC_SCALE_128x128 = 2 };
 enum { ORC_ACC_EXACT = 0, ORC_ACC_F32_CHUNKS = 1 };
 enum { ORC_OK = 0, ORC_ERR_ARG = 1, ORC_ERR_FPENV = 2 };
@@ -107,6 +108,28 @@ double decode_e5m2(uint8_t c) {
 }
 
 double decode(uint8_t c, int fmt) { return fmt == ORC_E4M3FN ? decode_e4m3fn(c) : decode_e5m2(c); }
+
+/* E2M1 (FP4, the float4_e2m1fn_x2 operand type of "cuDNN frontend: GEMM +
+ * Amax (SM100)", Parameters): sign bit 3, 2 exponent bits (bias 1), 1 mantissa
+ * bit, no infinities or NaNs; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double decode_e2m1(uint8_t c) {
+    const int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    const double mag = (e == 0) ? std::ldexp((double)m, -1)          /* m/2 * 2^(1-1) */
+                                : std::ldexp((double)(2 + m), e - 2); /* (1+m/2) * 2^(e-1) */
+    return s ? -mag : mag;
+}
+
+/* Element k of an operand row: FP8 formats take one byte per element; E2M1
+ * packs two per byte ("float4_e2m1fn_x2": the row holds K/2 bytes). The page
+ * does not say which nibble comes first; the reading here is element 2i in
+ * the low nibble of byte i and 2i+1 in the high nibble. (A sum over k pairs
+ * every element of a with the element of b at the same k and the two
+ * elements of a byte always share a scale group, so C does not depend on
+ * this order.) */
+double element(const uint8_t* row, int64_t k, int fmt) {
+    if (fmt == ORC_E2M1) return decode_e2m1((uint8_t)((row[k >> 1] >> (4 * (k & 1))) & 15));
+    return decode(row[k], fmt);
+}
 
 /* E8M0 (the float8_e8m0fnu scale-factor type of "cuDNN frontend: GEMM + Amax
  * (SM100)", Parameters): an unsigned, biased exponent only, value 2^(e - 127);
@@ -238,6 +261,15 @@ int orc_decode_fp8(const uint8_t* codes, int64_t n, int fmt, double* out) {
 
 /* Round n float64 values to dtype (RNE, the output rules above) and store the
  * bit patterns (uint8 / uint16 / uint32 by width). */
+/* Decode n E2M1 codes (one per byte, values 0..15) to float64. */
+int orc_decode_fp4(const uint8_t* codes, int64_t n, double* out) {
+    for (int64_t i = 0; i < n; ++i) {
+        if (codes[i] > 15) return ORC_ERR_ARG;
+        out[i] = decode_e2m1(codes[i]);
+    }
+    return ORC_OK;
+}
+
 int orc_round(const double* x, int64_t n, int dtype, void* out_bits) {
     if (dtype < ORC_E4M3FN || dtype > ORC_F16) return ORC_ERR_ARG;
     const Format f = format_of(dtype);
@@ -363,7 +395,8 @@ int orc_scaled_gemm(int64_t M, int64_t N, int64_t K,
 
 /*
  * The batched block-scaled GEMM + amax. a[l][m][k], b[l][n][k] FP8 codes of one
- * format (row pitch K); sfa[l][m][ceil(K/sf)], sfb[l][n][ceil(K/sf)] fp32 scale
+ * format (row pitch K bytes), or E2M1 pairs (ab_fmt ORC_E2M1, K even, row pitch
+ * K/2 bytes); sfa[l][m][ceil(K/sf)], sfb[l][n][ceil(K/sf)] fp32 scale
  * factors; outputs for the listed rows m (all M when NULL) of every batch item:
  * value / sum_abs / c_bits are [L, n_rows, N]. amax and amax_index cover the
  * computed outputs (linear index l*M*N + m*N + n).
@@ -377,6 +410,9 @@ int orc_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L,
     if (fpenv_flushes()) return ORC_ERR_FPENV;
     if (M < 0 || N < 0 || K < 0 || L < 0 || sf_vec <= 0) return ORC_ERR_ARG;
     if (c_type < ORC_E4M3FN || c_type > ORC_F16) return ORC_ERR_ARG;
+    if (ab_fmt != ORC_E4M3FN && ab_fmt != ORC_E5M2 && ab_fmt != ORC_E2M1) return ORC_ERR_ARG;
+    if (ab_fmt == ORC_E2M1 && (K & 1)) return ORC_ERR_ARG;
+    const int64_t pitch = ab_fmt == ORC_E2M1 ? K / 2 : K; /* bytes per operand row */
     if (!rows) n_rows = M;
     for (int64_t i = 0; i < n_rows; ++i)
         if (rows && (rows[i] < 0 || rows[i] >= M)) return ORC_ERR_ARG;
@@ -390,12 +426,12 @@ int orc_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L,
         for (int64_t i = 0; i < n_rows; ++i) {
             const int64_t m = rows ? rows[i] : i;
             for (int64_t k = 0; k < K; ++k)
-                Ah[(size_t)i * K + k] = decode(a[(l * M + m) * K + k], ab_fmt) *
+                Ah[(size_t)i * K + k] = element(&a[(l * M + m) * pitch], k, ab_fmt) *
                                         (double)sfa[(l * M + m) * KS + k / sf_vec];
         }
         for (int64_t n = 0; n < N; ++n)
             for (int64_t k = 0; k < K; ++k)
-                Bh[(size_t)n * K + k] = decode(b[(l * N + n) * K + k], ab_fmt) *
+                Bh[(size_t)n * K + k] = element(&b[(l * N + n) * pitch], k, ab_fmt) *
                                         (double)sfb[(l * N + n) * KS + k / sf_vec];
         parallel_rows(n_rows, threads, [&](int64_t i) {
             const double* Am = &Ah[(size_t)i * K];

@@ -20,7 +20,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.cpp")
 PINS = [os.path.join(ROOT, "tests", "test_oracle_fp8.py"), os.path.join(ROOT, "tests", "test_oracle_gemm.py"),
-        os.path.join(ROOT, "tests", "test_oracle_atom.py")]
+        os.path.join(ROOT, "tests", "test_oracle_atom.py"), os.path.join(ROOT, "tests", "test_oracle_fp4.py")]
 
 # name -> (old text, new text); old text must occur exactly once
 MUTANTS = {
@@ -51,6 +51,9 @@ MUTANTS = {
     "atom_storage_inner_swapped": ("* 32 + i0) * 4 + i1) * 4 + j0;", "* 32 + i0) * 4 + j0) * 4 + i1;"),
     "atom_rows_i1_fastest": ("const int64_t mn = i0 + 32 * i1 + 128 * i2;", "const int64_t mn = 4 * i0 + i1 + 128 * i2;"),
     "atom_block_order": ("((((l * MB + i2) * KB + j1) * 32", "((((l * KB + j1) * MB + i2) * 32"),
+    "e2m1_bias": ("std::ldexp((double)(2 + m), e - 2)", "std::ldexp((double)(2 + m), e - 1)"),
+    "e2m1_subnormal": ("std::ldexp((double)m, -1)", "std::ldexp((double)m, 0)"),
+    "fp4_sign_dropped": ("(row[k >> 1] >> (4 * (k & 1))) & 15", "(row[k >> 1] >> (4 * (k & 1))) & 7"),
     "zero_chain_negative": ("double S = +0.0, T = 0.0;\n                    for (int64_t k = 0; k < K; ++k) {\n                        const double t = Am[k] * Bn[k];\n                        S += t;",
                             "double S = -0.0, T = 0.0;\n                    for (int64_t k = 0; k < K; ++k) {\n                        const double t = Am[k] * Bn[k];\n                        S += t;"),
 }
