@@ -136,6 +136,8 @@ OTHER = {
     "bmm": "batched per-tensor E4M3 GEMM, L=8, M=N=2048, K=4096, slow, bf16 out",
     "mx_atom": "batched E4M3 GEMM with E8M0 factors per 32 K in the page-native atom layout, L=8, M=N=2048, "
                "K=8192, f32 C + amax + index",
+    "mx_fp4": "batched FP4 (E2M1) GEMM with E8M0 factors per 32 K in the page-native atom layout, L=8, "
+              "M=N=2048, K=8192, f32 C + amax + index",
 }
 
 
@@ -200,9 +202,11 @@ def run_other(name, steps, warmup):
                                                sfa.data_ptr(), sfb.data_ptr(), 32, c.data_ptr(), mm.MM_F32,
                                                amax.data_ptr(), idx.data_ptr(), stream)
         scale_bytes = 4 * (sfa.numel() + sfb.numel()) + 12
-    elif name == "mx_atom":
-        d = datagen.workload4_atom()
+    elif name in ("mx_atom", "mx_fp4"):
+        d = datagen.workload4_atom() if name == "mx_atom" else datagen.workload_fp4()
         L, M, K = d["a"].shape; N = d["b"].shape[1]
+        ab_type = mm.MM_F8_E4M3FN if name == "mx_atom" else mm.MM_F4_E2M1
+        K = K if name == "mx_atom" else 2 * K
         a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
         sfa = torch.from_numpy(d["sfa"]).to(dev); sfb = torch.from_numpy(d["sfb"]).to(dev)
         c = torch.empty((L, M, N), dtype=torch.float32, device=dev)
@@ -211,7 +215,7 @@ def run_other(name, steps, warmup):
         out_bytes = 4
 
         def launch():
-            return mm.mm_blockscaled_gemm_amax_atom(M, N, K, L, a.data_ptr(), b.data_ptr(), mm.MM_F8_E4M3FN,
+            return mm.mm_blockscaled_gemm_amax_atom(M, N, K, L, a.data_ptr(), b.data_ptr(), ab_type,
                                                     sfa.data_ptr(), sfb.data_ptr(), mm.MM_SF_E8M0, 32, c.data_ptr(),
                                                     mm.MM_F32, amax.data_ptr(), idx.data_ptr(), stream)
         scale_bytes = sfa.numel() + sfb.numel() + 12
@@ -247,7 +251,8 @@ def run_other(name, steps, warmup):
     us = 1e3 * e0.elapsed_time(e1) / steps
     flops = 2.0 * L * M * N * K
     tf = flops / us / 1e6
-    nbytes = L * (M * K + N * K + M * N * out_bytes) + scale_bytes
+    op_bytes = 0.5 if name == "mx_fp4" else 1.0  # operand bytes per element (FP4: two per byte)
+    nbytes = L * ((M + N) * K * op_bytes + M * N * out_bytes) + scale_bytes
     result = {
         "metric": f"{OTHER[name]}: TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": True,

@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmmfp8.so")
 
 MM_OK, MM_ERR_INVALID_ARGUMENT, MM_ERR_UNSUPPORTED, MM_ERR_MISALIGNED, MM_ERR_DEVICE = 0, 1, 2, 3, 4
-MM_F8_E4M3FN, MM_F8_E5M2, MM_F32, MM_BF16, MM_F16 = 0, 1, 2, 3, 4
+MM_F8_E4M3FN, MM_F8_E5M2, MM_F32, MM_BF16, MM_F16, MM_F4_E2M1 = 0, 1, 2, 3, 4, 5
 MM_SCALE_TENSOR, MM_SCALE_1x128, MM_SCALE_128x128 = 0, 1, 2
 MM_SF_E8M0, MM_SF_E4M3FN = 0, 1
 
@@ -137,6 +137,8 @@ def dtype_code(dt) -> int:
     torch = _torch()
     table = {torch.float8_e4m3fn: MM_F8_E4M3FN, torch.float8_e5m2: MM_F8_E5M2, torch.float32: MM_F32,
              torch.bfloat16: MM_BF16, torch.float16: MM_F16}
+    if hasattr(torch, "float4_e2m1fn_x2"):
+        table[torch.float4_e2m1fn_x2] = MM_F4_E2M1
     if dt not in table:
         raise TypeError(f"unsupported dtype {dt}")
     return table[dt]
@@ -146,7 +148,7 @@ def _fp8_code(t, fmt):
     torch = _torch()
     if t.dtype == torch.uint8:
         if fmt is None:
-            raise TypeError("uint8 operands need an explicit format (MM_F8_E4M3FN or MM_F8_E5M2)")
+            raise TypeError("uint8 operands need an explicit format (MM_F8_E4M3FN, MM_F8_E5M2 or MM_F4_E2M1)")
         return fmt
     return dtype_code(t.dtype)
 
@@ -258,17 +260,21 @@ def scaled_bmm(a, b, scale_a, scale_b, out_dtype, scale_result=None, use_fast_ac
 def blockscaled_gemm_amax(a, b, sfa, sfb, c_dtype=None, sf_vec_size=32, with_index=False, ab_format=None):
     """C[l] = (A[l] * SFA[l]) @ (B[l] * SFB[l])^T and the global amax of C.
 
-    a: [L, M, K] FP8, b: [L, N, K] FP8 (same format). The scale factors are
-    either float32 powers of two, sfa [L, M, ceil(K/32)] and sfb
-    [L, N, ceil(K/32)], or the cuDNN page's own tensors: E8M0 bytes
-    (float8_e8m0fnu, uint8 or int8) of storage shape
-    (L, ceil(MN/128), ceil(K/128), 32, 4, 4). Returns (c [L, M, N], amax [1])
-    or (c, amax, amax_index [1]) with with_index.
+    a: [L, M, K] FP8, b: [L, N, K] FP8 (same format), or FP4 pairs
+    (float4_e2m1fn_x2, or uint8 with ab_format=MM_F4_E2M1) [L, M, K/2] and
+    [L, N, K/2]. The scale factors are either float32 powers of two (FP8
+    only), sfa [L, M, ceil(K/32)] and sfb [L, N, ceil(K/32)], or the cuDNN
+    page's own tensors: E8M0 bytes (float8_e8m0fnu, uint8 or int8) of storage
+    shape (L, ceil(MN/128), ceil(K/(4 sf)), 32, 4, 4). Returns
+    (c [L, M, N], amax [1]) or (c, amax, amax_index [1]) with with_index.
     """
     torch = _torch()
     c_dtype = c_dtype or torch.float32
     L, M, K = a.shape
     N = b.shape[1]
+    ab_type = _fp8_code(a, ab_format)
+    if ab_type == MM_F4_E2M1:
+        K *= 2
     for t in (a, b, sfa, sfb):
         if not t.is_contiguous():
             raise ValueError("operands must be contiguous")
@@ -277,16 +283,17 @@ def blockscaled_gemm_amax(a, b, sfa, sfb, c_dtype=None, sf_vec_size=32, with_ind
     idx = torch.empty((1,), dtype=torch.int64, device=a.device) if with_index else None
     if sfa.element_size() == 1 and sfb.element_size() == 1:
         for t, rows in ((sfa, M), (sfb, N)):
-            if t.numel() != L * -(-rows // 128) * -(-K // 128) * 512:
-                raise ValueError("E8M0 scale factors must have the storage shape (L, ceil(MN/128), ceil(K/128), 32, 4, 4)")
-        st = mm_blockscaled_gemm_amax_atom(M, N, K, L, a.data_ptr(), b.data_ptr(), _fp8_code(a, ab_format),
+            if t.numel() != L * -(-rows // 128) * -(-K // (4 * sf_vec_size)) * 512:
+                raise ValueError("E8M0 scale factors must have the storage shape "
+                                 "(L, ceil(MN/128), ceil(K/(4 sf)), 32, 4, 4)")
+        st = mm_blockscaled_gemm_amax_atom(M, N, K, L, a.data_ptr(), b.data_ptr(), ab_type,
                                            sfa.data_ptr(), sfb.data_ptr(), MM_SF_E8M0, sf_vec_size, c.data_ptr(),
                                            dtype_code(c_dtype), amax.data_ptr(), idx.data_ptr() if with_index else 0,
                                            _stream())
     else:
         if sfa.dtype != torch.float32 or sfb.dtype != torch.float32:
             raise ValueError("scale factors must be float32, or E8M0 bytes for both operands")
-        st = mm_blockscaled_gemm_amax(M, N, K, L, a.data_ptr(), b.data_ptr(), _fp8_code(a, ab_format),
+        st = mm_blockscaled_gemm_amax(M, N, K, L, a.data_ptr(), b.data_ptr(), ab_type,
                                       sfa.data_ptr(), sfb.data_ptr(), sf_vec_size, c.data_ptr(), dtype_code(c_dtype),
                                       amax.data_ptr(), idx.data_ptr() if with_index else 0, _stream())
     _check(st)

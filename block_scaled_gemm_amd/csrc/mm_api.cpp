@@ -232,11 +232,10 @@ mm_status mm_scaled_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K, con
 
 namespace {
 
-// The batched MX GEMM + amax behind both entry points; `layout` is
-// mmfp8::SF_F32 (fp32 factors [L][MN][ceil(K/32)]) or mmfp8::SF_ATOM_E8M0
-// (the page-native E8M0 bytes).
+// The batched MX GEMM + amax behind both entry points; `atom` selects the
+// page-native E8M0 bytes (FP8 or FP4 operands) over fp32 factors (FP8).
 mm_status blockscaled_amax(const char* who, int64_t M, int64_t N, int64_t K, int64_t L, const void* a,
-                           const void* b, int ab_type, const void* sfa, const void* sfb, int layout, int sf_vec_size,
+                           const void* b, int ab_type, const void* sfa, const void* sfb, bool atom, int sf_vec_size,
                            void* c, int c_type, float* amax, int64_t* amax_index, void* stream) {
     if (M < 0 || N < 0 || K < 0 || L < 0)
         return fail(MM_ERR_INVALID_ARGUMENT, "M, N, K and L must be >= 0");
@@ -245,11 +244,17 @@ mm_status blockscaled_amax(const char* who, int64_t M, int64_t N, int64_t K, int
     const int64_t lim = (int64_t)1 << 48;
     if ((K && L * M > lim / K) || (K && L * N > lim / K) || (N && L * M > lim / N))
         return fail(MM_ERR_UNSUPPORTED, "L*M*K, L*N*K and L*M*N must be below 2^48");
-    if (!is_fp8(ab_type)) return fail(MM_ERR_INVALID_ARGUMENT, "ab_type must be MM_F8_E4M3FN or MM_F8_E5M2");
-    if (sf_vec_size == 16)
+    const bool fp4 = ab_type == MM_F4_E2M1;
+    if (fp4 && !atom)
+        return fail(MM_ERR_UNSUPPORTED, "FP4 operands take E8M0 factors in the page's layout (the _atom entry)");
+    if (!is_fp8(ab_type) && !fp4)
+        return fail(MM_ERR_INVALID_ARGUMENT, "ab_type must be MM_F8_E4M3FN, MM_F8_E5M2%s", atom ? " or MM_F4_E2M1" : "");
+    if (sf_vec_size == 16 && !fp4)
         return fail(MM_ERR_UNSUPPORTED, "sf_vec_size 16 is not supported with FP8 operands; use 32");
-    if (sf_vec_size != 32) return fail(MM_ERR_INVALID_ARGUMENT, "sf_vec_size must be 32 (got %d)", sf_vec_size);
-    if (is_fp8(c_type)) return fail(MM_ERR_UNSUPPORTED, "FP8 C with FP8 operands is not supported");
+    if (sf_vec_size != 32 && sf_vec_size != 16)
+        return fail(MM_ERR_INVALID_ARGUMENT, "sf_vec_size must be 32%s (got %d)", fp4 ? " or 16" : "", sf_vec_size);
+    if (is_fp8(c_type) && !fp4) return fail(MM_ERR_UNSUPPORTED, "FP8 C with FP8 operands is not supported");
+    if (c_type == MM_F4_E2M1) return fail(MM_ERR_UNSUPPORTED, "FP4 C is not provided");
     if (!is_dtype(c_type)) return fail(MM_ERR_INVALID_ARGUMENT, "unknown c_type %d", c_type);
     if (K > kMaxPitch) return fail(MM_ERR_UNSUPPORTED, "K must be at most 2^22");
     const int64_t outs = L * M * N;
@@ -260,12 +265,13 @@ mm_status blockscaled_amax(const char* who, int64_t M, int64_t N, int64_t K, int
         return fail(MM_ERR_INVALID_ARGUMENT, "a, b, sfa or sfb is NULL");
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16))
         return fail(MM_ERR_MISALIGNED, "a, b and c must be 16-byte aligned");
-    if (K % 16) return fail(MM_ERR_MISALIGNED, "K must be a multiple of 16 (16-byte aligned rows)");
+    if (K % (fp4 ? 32 : 16))
+        return fail(MM_ERR_MISALIGNED, "K must be a multiple of %d (16-byte aligned rows)", fp4 ? 32 : 16);
     if (!aligned(sfa, 4) || !aligned(sfb, 4) || !aligned(amax, 4))
         return fail(MM_ERR_MISALIGNED, "sfa, sfb and amax must be 4-byte aligned");
     if (!aligned(amax_index, 8)) return fail(MM_ERR_MISALIGNED, "amax_index must be 8-byte aligned");
-    const int64_t kblocks = cdiv(K, 128);
-    if (layout == mmfp8::SF_ATOM_E8M0 && (cdiv(M, 128) * kblocks * 512 >= kMaxDim || cdiv(N, 128) * kblocks * 512 >= kMaxDim))
+    const int64_t groups = cdiv(K, sf_vec_size), kblocks = cdiv(groups, 4);
+    if (atom && (cdiv(M, 128) * kblocks * 512 >= kMaxDim || cdiv(N, 128) * kblocks * 512 >= kMaxDim))
         return fail(MM_ERR_UNSUPPORTED, "each batch item's scale-factor tensor must be below 2^31 bytes");
     if (outs == 0 && !amax && !amax_index) return MM_OK;
     if (forced_launch_failure()) return fail(MM_ERR_DEVICE, "launch failure forced by MM_TEST_FORCE_FAIL");
@@ -278,28 +284,28 @@ mm_status blockscaled_amax(const char* who, int64_t M, int64_t N, int64_t K, int
         if (st != MM_OK) return st;
     }
     if (outs > 0) {
+        const int64_t kbytes = fp4 ? K / 2 : K;  // operand row in bytes
         mmfp8::GemmArgs p{};
         p.a = static_cast<const uint8_t*>(a);
         p.b = static_cast<const uint8_t*>(b);
-        p.lda = K;
-        p.ldb = K;
-        p.a_batch = M * K;
-        p.b_batch = N * K;
+        p.lda = kbytes;
+        p.ldb = kbytes;
+        p.a_batch = M * kbytes;
+        p.b_batch = N * kbytes;
         p.M = (int)M;
         p.N = (int)N;
-        p.K = (int)K;
+        p.K = (int)kbytes;  // the kernels load K bytes per row
         p.L = (int)L;
-        const int64_t ks = cdiv(K, 32);
         p.sa = static_cast<const float*>(sfa);
         p.sb = static_cast<const float*>(sfb);
-        p.sa_ld = ks;
-        p.sb_ld = ks;
-        if (layout == mmfp8::SF_ATOM_E8M0) {  // 4-byte units: 128 per 128 rows and 4 groups
+        p.sa_ld = groups;
+        p.sb_ld = groups;
+        if (atom) {  // 4-byte units: 128 per 128 rows and 4 groups
             p.sa_batch = cdiv(M, 128) * kblocks * 128;
             p.sb_batch = cdiv(N, 128) * kblocks * 128;
         } else {
-            p.sa_batch = M * ks;
-            p.sb_batch = N * ks;
+            p.sa_batch = M * groups;
+            p.sb_batch = N * groups;
         }
         p.d = c;
         p.ldd = N;
@@ -308,13 +314,15 @@ mm_status blockscaled_amax(const char* who, int64_t M, int64_t N, int64_t K, int
         p.vec_store = (N % 4 == 0);
         p.amax_bits = amax_bits;
         p.amax_key = key;
-        const int cfg = choose_cfg(M, N, L, cu_count(), mmfp8::min_cfg(mmfp8::MODE_SF32, 0));
+        const int cfg = choose_cfg(M, N, L, cu_count(), mmfp8::min_cfg(mmfp8::MODE_SF32, 0, ab_type));
         p.tiles_m = (int)cdiv(M, mmfp8::kCfgBM[cfg]);
         p.tiles_n = (int)cdiv(N, mmfp8::kCfgBN[cfg]);
         const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * L;
         if (grid >= kMaxDim) return fail(MM_ERR_UNSUPPORTED, "too many output tiles");
-        mm_status st =
-            device_status(mmfp8::launch_tile_sf32(cfg, layout, ab_type == MM_F8_E5M2 ? 1 : 0, p, (int)grid, s), who);
+        const int layout = !atom ? mmfp8::SF_F32 : sf_vec_size == 16 ? mmfp8::SF_ATOM_E8M0_16 : mmfp8::SF_ATOM_E8M0;
+        const hipError_t e = fp4 ? mmfp8::launch_tile_fp4(cfg, layout, p, (int)grid, s)
+                                 : mmfp8::launch_tile_sf32(cfg, layout, ab_type == MM_F8_E5M2 ? 1 : 0, p, (int)grid, s);
+        mm_status st = device_status(e, who);
         if (st != MM_OK) return st;
     }
     if (amax_index) return device_status(mmfp8::launch_amax_finalize(amax, key, s), "amax finalize launch");
@@ -329,7 +337,7 @@ mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L, c
                                    int ab_type, const float* sfa, const float* sfb, int sf_vec_size, void* c,
                                    int c_type, float* amax, int64_t* amax_index, void* stream) {
     g_error.clear();
-    return blockscaled_amax("mm_blockscaled_gemm_amax launch", M, N, K, L, a, b, ab_type, sfa, sfb, mmfp8::SF_F32,
+    return blockscaled_amax("mm_blockscaled_gemm_amax launch", M, N, K, L, a, b, ab_type, sfa, sfb, false,
                             sf_vec_size, c, c_type, amax, amax_index, stream);
 }
 
@@ -339,10 +347,10 @@ mm_status mm_blockscaled_gemm_amax_atom(int64_t M, int64_t N, int64_t K, int64_t
                                         void* stream) {
     g_error.clear();
     if (sf_type == MM_SF_E4M3FN)
-        return fail(MM_ERR_UNSUPPORTED, "E4M3 scale factors go with FP4 operands and sf_vec_size 16 (not provided)");
+        return fail(MM_ERR_UNSUPPORTED, "E4M3 scale factors (the page's FP4 with sf_vec_size 16) are not provided");
     if (sf_type != MM_SF_E8M0) return fail(MM_ERR_INVALID_ARGUMENT, "unknown sf_type %d", sf_type);
-    return blockscaled_amax("mm_blockscaled_gemm_amax_atom launch", M, N, K, L, a, b, ab_type, sfa, sfb,
-                            mmfp8::SF_ATOM_E8M0, sf_vec_size, c, c_type, amax, amax_index, stream);
+    return blockscaled_amax("mm_blockscaled_gemm_amax_atom launch", M, N, K, L, a, b, ab_type, sfa, sfb, true,
+                            sf_vec_size, c, c_type, amax, amax_index, stream);
 }
 
 mm_status mm_debug_convert(const float* x, void* y, int dtype, int64_t n, void* stream) {

@@ -46,17 +46,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Element types (the values of mm_dtype).
-enum : int { T_E4M3 = 0, T_E5M2 = 1, T_F32 = 2, T_BF16 = 3, T_F16 = 4 };
+// Element types (the values of mm_dtype). T_E2M1: FP4, two per byte.
+enum : int { T_E4M3 = 0, T_E5M2 = 1, T_F32 = 2, T_BF16 = 3, T_F16 = 4, T_E2M1 = 5 };
 // Accumulation / scaling modes of the main loop.
 enum : int { MODE_FAST = 0, MODE_SLOW = 1, MODE_BLOCK = 2, MODE_SF32 = 3 };
 // Granularity of scale_b in MODE_BLOCK.
 enum : int { SB_1x128 = 0, SB_128x128 = 1 };
 // Scale-factor storage in MODE_SF32 (the same template slot): fp32 factors
-// [L][MN][groups], or the cuDNN page's native layout of E8M0 bytes, where for
-// every 128 rows and 4 groups the 512 bytes hold row r's 4 groups as one
-// dword at byte 16 (r % 32) + 4 (r / 32), blocks ordered [L][MN/128][K/128].
-enum : int { SF_F32 = 0, SF_ATOM_E8M0 = 1 };
+// [L][MN][groups] of 32 K, or the cuDNN page's native layout of E8M0 bytes
+// with groups of 32 or 16 K, where for every 128 rows and 4 groups the 512
+// bytes hold row r's 4 groups as one dword at byte 16 (r % 32) + 4 (r / 32),
+// blocks ordered [L][MN/128][ceil(groups/4)].
+enum : int { SF_F32 = 0, SF_ATOM_E8M0 = 1, SF_ATOM_E8M0_16 = 2 };
 
 constexpr int kBK = 128;                 // K per main-loop step = one MFMA = one 128-element chunk
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 buffer descriptor dword 3 (raw, 32-bit format)
@@ -109,6 +110,20 @@ template <int F, bool HI>
 __device__ __forceinline__ bf16x2 cvt2(uint32_t w, float scale) {
     if constexpr (F == 0) return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI);
     else return __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, scale, HI);
+}
+
+// Dword q (q = 0..3) of a 16-byte FP4 chunk, i.e. 8 E2M1 values, as one bf16
+// MFMA operand times `scale`: each byte's two values, low nibble first. Exact:
+// every E2M1 value times a power of two in range is a bf16 value.
+__device__ __forceinline__ bf16x8 fp4_to_bf16x8(const i32x4& f, int q, float scale) {
+    const uint32_t w = (uint32_t)f[q];
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+    const auto lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+    const auto hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Bytes 8 s .. 8 s + 7 of a lane's 32-byte FP8 fragment as one bf16 MFMA operand.
@@ -351,16 +366,28 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     // scale_a of every A row (and scale_b of every B row when it is 1x128; a
     // 128x128 scale_b is one value per 128 columns, read from memory directly).
     // One 4-byte-per-lane load fills one scale column of 64 rows.
-    // The page-native E8M0 layout keeps a row's 4 groups of a step in one
-    // dword: one gathering load per 64 rows, into LDS [row] in row order.
-    // The 256x256 tile issues each of these loads four times (the same bytes
-    // into the same LDS slots, as many loads as the fp32 factors take): its
-    // main loop then fits in 256 VGPRs, where with one issue the compiler
+    // FP4 operands (MX only): a step's 128 bytes of a row hold 256 values;
+    // each 16-byte fragment chunk feeds four MFMA k-slices instead of two.
+    constexpr bool kFp4 = FA == T_E2M1;
+    static_assert(FA == FB || !kFp4, "FP4 operands come in pairs");
+    static_assert(!kFp4 || (MODE == MODE_SF32 && SBM != SF_F32 && !PIPE), "FP4: page-native factors, plain loop");
+    constexpr int NQ = kFp4 ? 4 : 2;
+    // The page-native E8M0 layout keeps a row's 4 groups in one dword per 4
+    // groups: NKB dwords per row and step (1 for FP8, 2 / 4 for FP4 with 32 /
+    // 16 values per group), one gathering load per 64 rows and dword, into
+    // LDS [dword][row].
+    // The FP8 256x256 tile issues each of these loads four times (the same
+    // bytes into the same LDS slots, as many loads as the fp32 factors take):
+    // its main loop then fits in 256 VGPRs, where with one issue the compiler
     // spills 38 of them, which measured 17% slower.
-    constexpr bool kAtom = MODE == MODE_SF32 && SBM == SF_ATOM_E8M0;
-    constexpr int kAtomRep = kAtom && BM == 256 && BN == 256 ? 4 : 1;
-    constexpr int SA_W = MODE == MODE_SF32 ? (kAtom ? kAtomRep : 4) : (MODE == MODE_BLOCK ? 1 : 0);
-    constexpr int SB_W = MODE == MODE_SF32 ? (kAtom ? kAtomRep : 4) : ((MODE == MODE_BLOCK && SBM == SB_1x128) ? 1 : 0);
+    constexpr bool kAtom = MODE == MODE_SF32 && SBM != SF_F32;
+    constexpr int SFV = SBM == SF_ATOM_E8M0_16 ? 16 : 32;  // values per scale group
+    constexpr int GPS = (kFp4 ? 2 * kBK : kBK) / SFV;      // scale groups per step
+    constexpr int NKB = kAtom ? GPS / 4 : 1;
+    constexpr int kAtomRep = kAtom && !kFp4 && BM == 256 && BN == 256 ? 4 : 1;
+    constexpr int SA_W = MODE == MODE_SF32 ? (kAtom ? kAtomRep * NKB : 4) : (MODE == MODE_BLOCK ? 1 : 0);
+    constexpr int SB_W = MODE == MODE_SF32 ? (kAtom ? kAtomRep * NKB : 4)
+                                           : ((MODE == MODE_BLOCK && SBM == SB_1x128) ? 1 : 0);
     constexpr int SC_A_INS = BM / 64 * SA_W, SC_INS = SC_A_INS + BN / 64 * SB_W;
     static_assert(BM % 64 == 0 && BN % 64 == 0, "scale columns are loaded 64 rows at a time");
     constexpr int STAGE = (BM + BN) * kBK + SC_INS * 256;
@@ -410,13 +437,14 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     const float* sb_l = p.sb + (int64_t)l * p.sb_batch;
     // the tile's scale rows (rows past the matrix read zero, or the atom
     // layout's padding; their results are discarded)
-    const void* sa_t = kAtom ? (const void*)((const uint8_t*)sa_l + (int64_t)(m0 >> 7) * KT * 512)
+    const int KB4 = (int)((p.sa_ld + 3) >> 2);  // atom layout: 4-group blocks per 128 rows
+    const void* sa_t = kAtom ? (const void*)((const uint8_t*)sa_l + (int64_t)(m0 >> 7) * KB4 * 512)
                              : (const void*)(sa_l + (int64_t)m0 * p.sa_ld);
-    const void* sb_t = kAtom ? (const void*)((const uint8_t*)sb_l + (int64_t)(n0 >> 7) * KT * 512)
+    const void* sb_t = kAtom ? (const void*)((const uint8_t*)sb_l + (int64_t)(n0 >> 7) * KB4 * 512)
                              : (const void*)(sb_l + (int64_t)n0 * p.sb_ld);
-    const uint32_t sa_ext = kAtom ? (uint32_t)(((p.M + 127) / 128 - (m0 >> 7)) * KT * 512)
+    const uint32_t sa_ext = kAtom ? (uint32_t)(((p.M + 127) / 128 - (m0 >> 7)) * KB4 * 512)
                                   : (SA_W ? (uint32_t)(min(BM, p.M - m0) * p.sa_ld * 4) : 0u);
-    const uint32_t sb_ext = kAtom ? (uint32_t)(((p.N + 127) / 128 - (n0 >> 7)) * KT * 512)
+    const uint32_t sb_ext = kAtom ? (uint32_t)(((p.N + 127) / 128 - (n0 >> 7)) * KB4 * 512)
                                   : (SB_W ? (uint32_t)(min(BN, p.N - n0) * p.sb_ld * 4) : 0u);
     const rsrc_t rsa = make_rsrc(sa_t, sa_ext);
     const rsrc_t rsb = make_rsrc(sb_t, sb_ext);
@@ -425,7 +453,7 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     // the step's 512 bytes: byte (lane % 32) * 16 + 4 * ((r0 / 32) % 4 + lane / 32)
     // of its block, i.e. a per-lane part common to every load plus a uniform part.
     const uint32_t atom_lane = (uint32_t)((lane & 31) * 16 + (lane >> 5) * 4);
-    auto atom_uni = [&](int r0) { return (r0 >> 7) * KT * 512 + ((r0 >> 5) & 3) * 4; };
+    auto atom_uni = [&](int r0) { return (r0 >> 7) * KB4 * 512 + ((r0 >> 5) & 3) * 4; };
 
     auto issue = [&](int kt, uint8_t* sbase) {
         if (kt >= KT) return;  // past the end: nothing to load
@@ -465,22 +493,30 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
         // follows (the next row, or zero past the last): their data is zero and
         // their conversion scale is replaced by 1 at use.
         if constexpr (kAtom) {
-            // Load t brings rows 64 (t % RA) .. + 63 of the tile (repeats when
+            // Load t brings dword u / RA (of the step's NKB) of rows
+            // 64 (u % RA) .. + 63 of the tile, u = t % (RA NKB) (repeats when
             // kAtomRep > 1). The block part rides in the range-checked per-lane
             // offset, so blocks past the tensor's last (rows past M / N only)
-            // read zero; the step's 512 bytes ride in the scalar offset.
+            // read zero. FP8 steps are exactly the tensor's 4-group blocks, so
+            // the step's 512 bytes ride in the scalar offset; an FP4 step's last
+            // blocks can lie past a row block's end (groups past ceil(K/sf),
+            // ignored at use), so its block index goes in the per-lane part too.
             constexpr int RA = BM < 128 ? 1 : BM / 64, RB = BN < 128 ? 1 : BN / 64;
             for (int t = gw; t < SC_A_INS; t += NW) {
-                const int ta = t % RA;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(sbase + (BM + BN) * kBK + ta * 256), 4,
-                                                         atom_lane + atom_uni((BM < 128 ? (m0 & 127) : 0) + ta * 64),
-                                                         kt * 512, 0, 0);
+                const int u = t % (RA * NKB), ta = u % RA, kb = u / RA;
+                const uint32_t vo = atom_lane + atom_uni((BM < 128 ? (m0 & 127) : 0) + ta * 64);
+                const uint32_t voff = kFp4 ? vo + (uint32_t)((kt * NKB + kb) * 512) : vo;
+                const int soff = kFp4 ? 0 : kt * 512;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(sbase + (BM + BN) * kBK + u * 256), 4, voff,
+                                                         soff, 0, 0);
             }
             for (int t = gw; t < SC_INS - SC_A_INS; t += NW) {
-                const int tb = t % RB;
+                const int u = t % (RB * NKB), tb = u % RB, kb = u / RB;
+                const uint32_t vo = atom_lane + atom_uni((BN < 128 ? (n0 & 127) : 0) + tb * 64);
+                const uint32_t voff = kFp4 ? vo + (uint32_t)((kt * NKB + kb) * 512) : vo;
+                const int soff = kFp4 ? 0 : kt * 512;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsb, (lds_void*)(sbase + (BM + BN) * kBK + (SC_A_INS + tb) * 256), 4,
-                    atom_lane + atom_uni((BN < 128 ? (n0 & 127) : 0) + tb * 64), kt * 512, 0, 0);
+                    rsb, (lds_void*)(sbase + (BM + BN) * kBK + (SC_A_INS + u) * 256), 4, voff, soff, 0, 0);
             }
         } else if constexpr (SC_A_INS > 0) {
             for (int t = gw; t < SC_A_INS; t += NW) {
@@ -604,6 +640,41 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
             }
         }
     };
+    // FP4: the scale group of a lane's values changes within a step. Chunk
+    // 2 fg + h holds values [32 (2 fg + h), + 32) of the step: group 2 fg + h
+    // with 32 values per group, or 4 fg + 2 h + qp (k-slices 2 qp, 2 qp + 1)
+    // with 16. Byte g % 4 of LDS dword [g / 4][row] holds the factor.
+    auto fp4_scales = [&](int kt, const uint8_t* stage, int h, int qp, float* c_a, float* c_b) {
+        const int g = SFV == 32 ? 2 * fg + h : 4 * fg + 2 * h + qp;
+        const bool gv = kt * GPS + g < p.sa_ld;  // groups past ceil(K/sf) hold zero data
+        const uint8_t* eA = stage + (BM + BN) * kBK + (g >> 2) * BM * 4 + (g & 3);
+        const uint8_t* eB = stage + (BM + BN) * kBK + SC_A_INS * 256 + (g >> 2) * BN * 4 + (g & 3);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) c_a[i] = gv ? e8m0_code_scale(eA[(wm * WTM + i * 16 + fr) * 4]) : 1.0f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) c_b[j] = gv ? e8m0_code_scale(eB[(wn * WTN + j * 16 + fr) * 4]) : 1.0f;
+    };
+    auto mma_half4 = [&](const Frag& f, int kt, const uint8_t* stage, int h) {
+        constexpr int QPS = SFV == 32 ? 4 : 2;  // k-slices per scale group
+#pragma unroll
+        for (int qp = 0; qp < 4 / QPS; ++qp) {
+            float c_a[FM], c_b[FN];
+            fp4_scales(kt, stage, h, qp, c_a, c_b);
+#pragma unroll
+            for (int qq = 0; qq < QPS; ++qq) {
+                const int q = qp * QPS + qq;
+                bf16x8 ab[FM];
+#pragma unroll
+                for (int i = 0; i < FM; ++i) ab[i] = fp4_to_bf16x8(f.a[i], q, c_a[i]);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const bf16x8 bb = fp4_to_bf16x8(f.b[j], q, c_b[j]);
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) acc[j][i] = mfma_bf16(bb, ab[i], acc[j][i]);
+                }
+            }
+        }
+    };
     // The scales of step kt: s_a / s_b fold a block-scaled partial into the
     // accumulator, c_a / c_b ride in the FP8 -> bf16 conversion (MX groups).
     // They are read from the step's stage before the barrier that frees it.
@@ -712,7 +783,7 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
             stage_ready(kt, cs);
             float s_a[FM], s_b[FN][4], c_a[FM], c_b[FN];
             if (kt < KT) {
-                step_scales(kt, cs, s_a, s_b, c_a, c_b);
+                if constexpr (!kFp4) step_scales(kt, cs, s_a, s_b, c_a, c_b);
                 if (kSbMem) sc_cur = load_scales(kt + KG);
             }
             issue(kt + KG, nxt + kg * STAGE);
@@ -725,7 +796,8 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
                     if (h) __builtin_amdgcn_sched_barrier(0);
                     Frag f;
                     read_frag(cs, h, f);
-                    mma_half(f, c_a, c_b);
+                    if constexpr (kFp4) mma_half4(f, kt, cs, h);
+                    else mma_half(f, c_a, c_b);
                 }
                 promote(s_a, s_b);
             }
@@ -881,7 +953,7 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
         else epilogue(ot, am, IC<0>{}, bi);
     };
     if constexpr (MODE == MODE_SF32) {
-        // the MX entry writes f32, bf16 or f16 (it rejects FP8 outputs)
+        // the MX entries write f32, bf16 or f16, and FP8 with FP4 operands
         auto with_amax = [&](auto ot) {
             if (p.amax_key) epilogue_g(ot, IC<2>{}, IC<0>{});
             else if (p.amax_bits) epilogue_g(ot, IC<1>{}, IC<0>{});
@@ -889,7 +961,11 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
         };
         if (p.d_type == T_BF16) with_amax(IC<T_BF16>{});
         else if (p.d_type == T_F16) with_amax(IC<T_F16>{});
-        else with_amax(IC<T_F32>{});
+        else if (p.d_type == T_F32 || !kFp4) with_amax(IC<T_F32>{});
+        else if constexpr (kFp4) {
+            if (p.d_type == T_E4M3) with_amax(IC<T_E4M3>{});
+            else with_amax(IC<T_E5M2>{});
+        }
     } else {
         // a bias (f32, bf16 and f16 outputs) is another compile-time variant
         with_out_type(p.d_type, [&](auto ot) {

@@ -21,8 +21,10 @@ constexpr int kCfgWN[CFG_COUNT] = {2, 4, 2, 2};
 // second workgroup would need). The promoted modes keep 64x64 partials as
 // well, so there the 128x128 tile runs without it, two workgroups per CU whose
 // waves share the SIMDs and cover each other's LDS latency.
-constexpr int cfg_pipe(int cfg, int mode) {
-    return cfg == CFG_128x128 && (mode == MODE_FAST || mode == MODE_SF32) ? 1 : 0;
+// FP4 operands read their scale factors from the stage during the whole
+// step, so they take the plain loop.
+constexpr int cfg_pipe(int cfg, int mode, int fmt) {
+    return cfg == CFG_128x128 && (mode == MODE_FAST || mode == MODE_SF32) && fmt != T_E2M1 ? 1 : 0;
 }
 
 // gemm_skinny: waves per workgroup and K steps in flight per wave, by MT
@@ -44,6 +46,7 @@ hipError_t launch_tile_fast(int cfg, int fa, int fb, const GemmArgs& p, int grid
 hipError_t launch_tile_slow(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_tile_block(int cfg, int sbm, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_tile_sf32(int cfg, int layout, int f, const GemmArgs& p, int grid, hipStream_t s);
+hipError_t launch_tile_fp4(int cfg, int layout, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_skinny(int mt, int mode, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_ksplit(int ks, int mode, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s);
 hipError_t launch_amax_init(uint32_t* bits, unsigned long long* key, hipStream_t s);
@@ -56,58 +59,64 @@ hipError_t launch_debug_convert(const float* x, void* y, int t, int64_t n, hipSt
 // per accumulator; their largest tile is 128x128 at two workgroups per CU,
 // which measured faster than 128x256 at one (eight waves that all meet at
 // every step's barrier, where the older wave of each SIMD pair finishes first
-// and the younger then runs alone).
-constexpr int min_cfg(int mode, int sbm) {
+// and the younger then runs alone). FP4 operands on the 64x128 wave tile
+// spill over a hundred registers (their scale factors change within a step),
+// so they start at 128x256.
+constexpr int min_cfg(int mode, int sbm, int fmt = 0) {
     (void)sbm;
+    if (fmt == T_E2M1) return CFG_128x256;
     return (mode == MODE_FAST || mode == MODE_SF32) ? CFG_256x256 : CFG_128x128;
 }
 
 // Compute units of the current device.
 int device_cus();
 
-// Launch gemm_tile<BM, BN, MODE, fa, fb, SBM> for a runtime cfg / format pair
-// over `grid` tiles. 128x128 tiles that are no more than the CUs (one per CU)
-// run with two K groups of four waves (eight waves per workgroup) in the
-// modes that have them: it measured 5-7% faster there than four waves with
-// one wave per SIMD, and slower as soon as two workgroups per CU are possible.
-template <int MODE, int SBM>
-hipError_t tile_dispatch(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s) {
+// Launch gemm_tile<BM, BN, MODE, FA, FB, SBM> for a runtime cfg over `grid`
+// tiles. 128x128 tiles that are no more than the CUs (one per CU) run with two
+// K groups of four waves (eight waves per workgroup) in the modes that have
+// them: it measured 5-7% faster there than four waves with one wave per SIMD,
+// and slower as soon as two workgroups per CU are possible.
+template <int MODE, int SBM, int FA, int FB>
+hipError_t tile_launch(int cfg, const GemmArgs& p, int grid, hipStream_t s) {
     constexpr int kKG = MODE == MODE_SF32 ? 1 : 2;
     const bool kgroups = kKG > 1 && cfg == CFG_128x128 && grid <= device_cus();
-#define MMFP8_TILE(C, A, B)                                                                                        \
+#define MMFP8_TILE(C)                                                                                              \
     do {                                                                                                           \
         bool done = false;                                                                                         \
         if constexpr (C == CFG_128x128 && kKG > 1) {                                                               \
             if (kgroups) {                                                                                         \
-                hipLaunchKernelGGL((gemm_tile<kCfgBM[C], kCfgBN[C], kCfgWM[C], kCfgWN[C], 0, MODE, A, B, SBM, kKG>), \
+                hipLaunchKernelGGL((gemm_tile<kCfgBM[C], kCfgBN[C], kCfgWM[C], kCfgWN[C], 0, MODE, FA, FB, SBM, kKG>), \
                                    dim3(grid), dim3(kCfgWM[C] * kCfgWN[C] * kKG * 64), 0, s, p);                   \
                 done = true;                                                                                       \
             }                                                                                                      \
         }                                                                                                          \
         if (!done)                                                                                                 \
-            hipLaunchKernelGGL((gemm_tile<kCfgBM[C], kCfgBN[C], kCfgWM[C], kCfgWN[C], cfg_pipe(C, MODE), MODE, A, B, \
-                                          SBM>),                                                                   \
+            hipLaunchKernelGGL((gemm_tile<kCfgBM[C], kCfgBN[C], kCfgWM[C], kCfgWN[C], cfg_pipe(C, MODE, FA), MODE, FA, \
+                                          FB, SBM>),                                                               \
                                dim3(grid), dim3(kCfgWM[C] * kCfgWN[C] * 64), 0, s, p);                             \
     } while (0)
-#define MMFP8_FMTS(C)                                    \
-    if (fa == 0 && fb == 0) MMFP8_TILE(C, 0, 0);         \
-    else if (fa == 1 && fb == 1) MMFP8_TILE(C, 1, 1);    \
-    else if (fa == 0 && fb == 1) MMFP8_TILE(C, 0, 1);    \
-    else MMFP8_TILE(C, 1, 0);
-    if (cfg < min_cfg(MODE, SBM)) cfg = min_cfg(MODE, SBM);
+    if (cfg < min_cfg(MODE, SBM, FA)) cfg = min_cfg(MODE, SBM, FA);
     switch (cfg) {
         case CFG_256x256:
-            if constexpr (MODE == MODE_FAST || MODE == MODE_SF32) { MMFP8_FMTS(CFG_256x256) }
+            if constexpr ((MODE == MODE_FAST || MODE == MODE_SF32) && FA != T_E2M1) MMFP8_TILE(CFG_256x256);
             break;
         case CFG_128x256:
-            if constexpr (MODE == MODE_FAST || MODE == MODE_SF32) { MMFP8_FMTS(CFG_128x256) }
+            if constexpr (MODE == MODE_FAST || MODE == MODE_SF32) MMFP8_TILE(CFG_128x256);
             break;
-        case CFG_128x128: MMFP8_FMTS(CFG_128x128) break;
-        default: MMFP8_FMTS(CFG_64x64) break;
+        case CFG_128x128: MMFP8_TILE(CFG_128x128); break;
+        default: MMFP8_TILE(CFG_64x64); break;
     }
-#undef MMFP8_FMTS
 #undef MMFP8_TILE
     return hipGetLastError();
+}
+
+// tile_launch for a runtime pair of FP8 formats.
+template <int MODE, int SBM>
+hipError_t tile_dispatch(int cfg, int fa, int fb, const GemmArgs& p, int grid, hipStream_t s) {
+    if (fa == 0 && fb == 0) return tile_launch<MODE, SBM, 0, 0>(cfg, p, grid, s);
+    if (fa == 1 && fb == 1) return tile_launch<MODE, SBM, 1, 1>(cfg, p, grid, s);
+    if (fa == 0 && fb == 1) return tile_launch<MODE, SBM, 0, 1>(cfg, p, grid, s);
+    return tile_launch<MODE, SBM, 1, 0>(cfg, p, grid, s);
 }
 
 }  // namespace mmfp8

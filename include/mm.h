@@ -41,13 +41,18 @@ typedef enum mm_status {
 /* Element types. FP8 codes follow the OCP 8-bit formats E4M3FN (largest
  * finite 448, no infinities, NaN = 0x7F / 0xFF) and E5M2 (largest finite
  * 57344, IEEE-like infinities and NaNs): the float8_e4m3fn / float8_e5m2
- * dtypes of the "mmaemu API reference (v0.1)", scaled_mm argument table. */
+ * dtypes of the "mmaemu API reference (v0.1)", scaled_mm argument table.
+ * MM_F4_E2M1 is FP4 (sign, 2 exponent bits with bias 1, 1 mantissa bit:
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no Inf or NaN) packed two per byte,
+ * the float4_e2m1fn_x2 operands of "cuDNN frontend: GEMM + Amax (SM100)";
+ * only mm_blockscaled_gemm_amax_atom takes it, as operands. */
 typedef enum mm_dtype {
     MM_F8_E4M3FN = 0,
     MM_F8_E5M2 = 1,
     MM_F32 = 2,
     MM_BF16 = 3,
-    MM_F16 = 4
+    MM_F16 = 4,
+    MM_F4_E2M1 = 5
 } mm_dtype;
 
 /* Scale granularities ("TileOPs: Linear Algebra Operators",
@@ -235,29 +240,42 @@ mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L,
 
 /*
  * mm_blockscaled_gemm_amax_atom -- mm_blockscaled_gemm_amax with the scale
- * factors in the page's own format: E8M0 bytes in the atom layout of
- * "cuDNN frontend: GEMM + Amax (SM100)", Shapes and Parameters (SFA, SFB).
+ * factors in the page's own format (E8M0 bytes in the atom layout of
+ * "cuDNN frontend: GEMM + Amax (SM100)", Shapes and Parameters, SFA and SFB),
+ * and with the page's FP4 operands.
  *
+ *  a, b     ab_type MM_F8_E4M3FN or MM_F8_E5M2: [L][M][K] and [L][N][K]
+ *           codes, as mm_blockscaled_gemm_amax. MM_F4_E2M1: [L][M][K/2] and
+ *           [L][N][K/2] bytes of two E2M1 values each (element 2i in the low
+ *           nibble of byte i: the page does not say, and C does not depend
+ *           on it), K a multiple of 32.
+ *  sf_vec_size  32, or 16 with FP4 operands (16 with FP8 operands ->
+ *           MM_ERR_UNSUPPORTED, as on the page).
  *  sfa      the page's SFA of logical shape (32, 4, ceil(M/128), 4,
- *           ceil(K/(4*32)), L), passed as its C-contiguous storage
- *           (L, ceil(M/128), ceil(K/128), 32, 4, 4) bytes, which the page's
- *           JAX contract says the logical view is a permutation of
- *           (3, 4, 1, 5, 2, 0). Row m and 32-group g of batch item l use the
- *           byte at [l][m / 128][g / 4][m % 32][(m / 32) % 4][g % 4] (the page
- *           gives shapes only: row m = i0 + 32 i1 + 128 i2 and group
- *           g = j0 + 4 j1 of the logical coordinates is the reading taken).
- *           Every byte of the padded shape must be readable; bytes of rows
- *           past M or groups past ceil(K/32) are never used.
+ *           ceil(K/(4 sf)), L), sf = sf_vec_size, passed as its C-contiguous
+ *           storage (L, ceil(M/128), ceil(K/(4 sf)), 32, 4, 4) bytes, which the
+ *           page's JAX contract says the logical view is a permutation of
+ *           (3, 4, 1, 5, 2, 0). Row m and group g (values [g sf, g sf + sf))
+ *           of batch item l use the byte at
+ *           [l][m / 128][g / 4][m % 32][(m / 32) % 4][g % 4] (the page gives
+ *           shapes only: row m = i0 + 32 i1 + 128 i2 and group g = j0 + 4 j1 of
+ *           the logical coordinates is the reading taken). Every byte of the
+ *           padded shape must be readable; bytes of rows past M or groups past
+ *           ceil(K/sf) are never used.
  *  sfb      the same for B with N rows.
- *  sf_type  MM_SF_E8M0 (int8 tensors included). MM_SF_E4M3FN factors go with
- *           sf_vec_size 16 and FP4 operands on the page, neither of which this
- *           entry takes -> MM_ERR_UNSUPPORTED; other values ->
+ *  sf_type  MM_SF_E8M0 (int8 tensors included). MM_SF_E4M3FN (the page's FP4
+ *           with sf_vec_size 16) -> MM_ERR_UNSUPPORTED; other values ->
  *           MM_ERR_INVALID_ARGUMENT.
+ *  c_type   F32, BF16 or F16; with FP4 operands also MM_F8_E4M3FN or
+ *           MM_F8_E5M2 (rounded to nearest even, saturating, as
+ *           mm_scaled_gemm's FP8 outputs with scale_result 1). FP8 C with FP8
+ *           operands and FP4 C -> MM_ERR_UNSUPPORTED.
  *
- * Everything else (a, b, ab_type, sf_vec_size, c, c_type, amax, amax_index,
- * stream, the arithmetic, sizes, alignment and errors) is as
- * mm_blockscaled_gemm_amax; in addition each batch item's factor tensor must
- * stay below 2^31 bytes (else MM_ERR_UNSUPPORTED).
+ * Everything else (amax, amax_index, stream, the arithmetic, sizes, alignment
+ * and errors) is as mm_blockscaled_gemm_amax; in addition each batch item's
+ * factor tensor must stay below 2^31 bytes (else MM_ERR_UNSUPPORTED). Every
+ * E2M1 value times a factor 2^e is a bf16 value for e <= 125, so FP4 operands
+ * are converted exactly with every E8M0 factor but 2^126 and 2^127.
  */
 mm_status mm_blockscaled_gemm_amax_atom(int64_t M, int64_t N, int64_t K, int64_t L,
                                         const void* a, const void* b, int ab_type,

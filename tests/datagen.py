@@ -218,3 +218,12 @@ def workload4_atom(L=8, M=2048, N=2048, K=8192):
     b = gauss_codes(rng(4, 1), (L, N, K), 64.0)
     return dict(a=a, b=b, ab_fmt=E4M3FN, sfa=e8m0_atom_codes(rng(4, 5), M, K, L),
                 sfb=e8m0_atom_codes(rng(4, 6), N, K, L), sf_vec=32)
+
+
+def workload_fp4(L=8, M=2048, N=2048, K=8192, sf=32, config=8):
+    """FP4 set: uniform random bytes (each two E2M1 codes, all 16 codes equally likely) as a
+    [L, M, K/2] and b [L, N, K/2]; E8M0 factors 2^U{-8..4} in the page's storage shape."""
+    a = rng(config, 0).integers(0, 256, size=(L, M, K // 2), dtype=np.uint8)
+    b = rng(config, 1).integers(0, 256, size=(L, N, K // 2), dtype=np.uint8)
+    return dict(a=a, b=b, ab_fmt=5, sfa=e8m0_atom_codes(rng(config, 2), M, K, L, sf),
+                sfb=e8m0_atom_codes(rng(config, 3), N, K, L, sf), sf_vec=sf, K=K)

@@ -190,10 +190,31 @@ def atom_call(**kw):
     # ceil(M/128) * ceil(K/128) * 512 bytes per item must stay below 2^31
     (dict(M=1 << 20, K=1 << 16, L=1), mm.MM_ERR_UNSUPPORTED, "below 2^31 bytes"),
     (dict(N=1 << 20, K=1 << 16, L=1, amax_index=0), mm.MM_ERR_UNSUPPORTED, "below 2^31 bytes"),
+    # FP4 operands
+    (dict(ab_type=mm.MM_F4_E2M1, K=272), mm.MM_ERR_MISALIGNED, "multiple of 32"),
+    (dict(ab_type=mm.MM_F4_E2M1, sf_vec_size=64), mm.MM_ERR_INVALID_ARGUMENT, "32 or 16"),
+    (dict(ab_type=mm.MM_F4_E2M1, c_type=mm.MM_F4_E2M1), mm.MM_ERR_UNSUPPORTED, "FP4 C"),
+    (dict(ab_type=mm.MM_F4_E2M1, c_type=7), mm.MM_ERR_INVALID_ARGUMENT, "unknown c_type"),
+    (dict(ab_type=6), mm.MM_ERR_INVALID_ARGUMENT, "MM_F4_E2M1"),
 ])
 def test_atom_validation(kw, status, msg):
     assert atom_call(**kw) == status
     assert msg in mm.mm_last_error()
+
+
+def test_fp4_needs_the_atom_entry():
+    assert amax_call(ab_type=mm.MM_F4_E2M1) == mm.MM_ERR_UNSUPPORTED
+    assert "_atom entry" in mm.mm_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(ab_type=mm.MM_F4_E2M1), dict(ab_type=mm.MM_F4_E2M1, sf_vec_size=16),
+                                dict(ab_type=mm.MM_F4_E2M1, c_type=mm.MM_F8_E4M3FN, K=32),
+                                dict(ab_type=mm.MM_F4_E2M1, c_type=mm.MM_F8_E5M2, sf_vec_size=16, K=4096)])
+def test_fp4_calls_pass_validation(kw, monkeypatch):
+    # a launch failure forced after validation shows the call was accepted
+    monkeypatch.setenv("MM_TEST_FORCE_FAIL", "launch")
+    assert atom_call(**kw) == mm.MM_ERR_DEVICE
+    assert "forced" in mm.mm_last_error()
 
 
 def test_atom_zero_sizes_launch_nothing():

@@ -394,6 +394,61 @@ def test_atom_workload4_full_size():
     assert amax == a2 and idx == i2
 
 
+# ------------------------------------------------------------------ FP4 (E2M1) operands, page-native factors
+
+def check_fp4_case(w, c_type, rows=None):
+    c, amax, idx = gu.blockscaled_gemm_amax_atom(w["a"], w["b"], 5, w["sfa"], w["sfb"], c_type, sf=w["sf_vec"])
+    value, sabs, bits, _, _ = oracle.blockscaled_gemm_amax_atom(w["a"], w["b"], oracle.E2M1, w["sfa"], w["sfb"],
+                                                                oracle.SF_E8M0, w["sf_vec"], c_type, rows=rows)
+    cg = c if rows is None else c[:, rows]
+    compare.check(cg, value, sabs, bits, c_type, "fp4 gemm")
+    return c, amax, idx, value, sabs
+
+
+@pytest.mark.parametrize("L,M,N,K,sf,c_type", [
+    (3, 200, 136, 1024, 32, F32), (2, 96, 200, 512, 16, BF16), (1, 130, 70, 992, 16, F16),
+    (2, 257, 129, 800, 32, F32),  # the last step's second factor block lies past the tensor's
+    (1, 100, 72, 256, 32, E4M3FN), (2, 64, 96, 1056, 16, E5M2), (1, 40, 48, 32, 16, F32)])
+def test_fp4_against_oracle(L, M, N, K, sf, c_type):
+    w = datagen.workload_fp4(L, M, N, K, sf)
+    c, amax, idx, value, sabs = check_fp4_case(w, c_type)
+    v = np.abs(value.reshape(-1))
+    assert abs(amax - v.max()) <= 2.0 ** -20 * sabs.reshape(-1)[np.argmax(v)]
+    if c_type == F32:
+        cf = np.abs(c.view(np.float32).astype(np.float64).reshape(-1))
+        assert amax == float(cf.max()) and idx == int(np.argmax(cf))
+
+
+@pytest.mark.parametrize("L,sf", [(2, 32), (1, 16)], ids=["128x256", "128x128"])
+def test_fp4_production_tiles(L, sf):
+    w = datagen.workload_fp4(L, 2048, 2048, 1024, sf)
+    rows = sample_rows(2048, 4)
+    c, amax, idx, value, sabs = check_fp4_case(w, F32, rows=rows)
+    cf = np.abs(c.view(np.float32).reshape(-1))
+    assert amax == float(cf.max()) and idx == int(np.argmax(cf))
+
+
+def test_fp4_padding_is_not_read():
+    L, M, N, K, sf = 2, 100, 72, 224, 16  # 14 groups: two unused in the last 4-group block
+    w = datagen.workload_fp4(L, M, N, K, sf)
+    c1, a1, i1 = gu.blockscaled_gemm_amax_atom(w["a"], w["b"], 5, w["sfa"], w["sfb"], F32, sf=sf)
+    sfa, sfb = w["sfa"].copy(), w["sfb"].copy()
+    sfa[atom_padding_mask(M, K, L, sf)] = 0xFF
+    sfb[atom_padding_mask(N, K, L, sf)] = 0xFF
+    c2, a2, i2 = gu.blockscaled_gemm_amax_atom(w["a"], w["b"], 5, sfa, sfb, F32, sf=sf)
+    compare.assert_bitwise_equal(c1, c2, "padding factors")
+    assert a1 == a2 and i1 == i2 and not np.isnan(a2)
+
+
+def test_fp4_full_size():
+    """L=8, 2048 x 2048 x 8192 FP4 with factors per 32 (the FP4 bench workload): sampled rows."""
+    w = datagen.workload_fp4()
+    rows = sample_rows(2048, 4)
+    c, amax, idx, value, sabs = check_fp4_case(w, F32, rows=rows)
+    cf = np.abs(c.view(np.float32).reshape(-1))
+    assert amax == float(cf.max()) and idx == int(np.argmax(cf))
+
+
 # ------------------------------------------------------------------ workload 5: K tail, FP8 / f16 out
 
 def test_workload5_small():
