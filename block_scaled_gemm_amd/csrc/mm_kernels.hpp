@@ -152,17 +152,15 @@ __device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// The value of an E8M0 code e: 2^(e - 127), 2^-127 (an fp32 subnormal) for
-// e = 0, NaN for e = 255.
-__device__ __forceinline__ float e8m0_code_scale(uint32_t e) {
-    if (e == 0) return __uint_as_float(0x00400000u);
-    if (e == 255) return __uint_as_float(0x7FC00000u);
-    return __uint_as_float(e << 23);
-}
-// The E8M0 value carried by an fp32 scale factor: that of its exponent field
-// (field 0 for zero and subnormals, 255 for Inf and NaN); the mantissa is
-// ignored.
-__device__ __forceinline__ float e8m0_scale(float s) { return e8m0_code_scale((__float_as_uint(s) >> 23) & 0xFFu); }
+// Scale operands of the scaled conversions. The gfx950 conversions
+// (v_cvt_scalef32_pk_bf16_fp8 / _bf8 / _fp4) read only the exponent field of
+// their fp32 scale, as an E8M0 code: field e multiplies by 2^(e - 127), field 0
+// by 2^-127, field 255 gives NaN; sign and mantissa are ignored (measured on
+// MI355X for every field class, FP8, BF8 and FP4 sources). So an E8M0 code is
+// passed as the float whose exponent field it is, and an fp32 factor is passed
+// as it is.
+__device__ __forceinline__ float e8m0_code_scale(uint32_t e) { return __uint_as_float(e << 23); }
+__device__ __forceinline__ float e8m0_scale(float s) { return s; }
 
 // ------------------------------------------------------------------ output conversions
 
