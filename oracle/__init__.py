@@ -12,7 +12,7 @@ element types SF_E8M0 = 0, SF_E4M3FN = 1.
 
 Parity status of each function (what pins it is in tests/test_oracle_*.py):
 decode_fp8, decode_fp4, round_to, scaled_gemm (exact and f32-chunk modes),
-blockscaled_gemm_amax: pinned. sf_atom_unpack: element decoding, the
+grouped_gemm, blockscaled_gemm_amax: pinned. sf_atom_unpack: element decoding, the
 storage-to-logical permutation and the padding rule pinned; the order of the
 rows and groups inside a 128 x 4 atom is a reading of the page's shapes
 (parity unpinned for that order).
@@ -68,8 +68,11 @@ def _load():
                                                   P, P, P, P, P, I]
         lib.orc_sf_atom_unpack.argtypes = [P, I, I64, I64, I64, I, P]
         lib.orc_decode_fp4.argtypes = [P, I64, P]
+        lib.orc_grouped_gemm.argtypes = [I64, I64, I64, I64, P, I, I64, P, I, I64, I64, P, P, P, P, P, I, I, P, P, P,
+                                         I]
         for f in (lib.orc_decode_fp8, lib.orc_round, lib.orc_scaled_gemm,
-                  lib.orc_blockscaled_gemm_amax, lib.orc_sf_atom_unpack, lib.orc_decode_fp4):
+                  lib.orc_blockscaled_gemm_amax, lib.orc_sf_atom_unpack, lib.orc_decode_fp4,
+                  lib.orc_grouped_gemm):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -155,6 +158,31 @@ def scaled_gemm_k(a, a_fmt, b, b_fmt, K, scale_a, sa_mode, scale_b, sb_mode, d_t
                                    _ptr(sa), sa_mode, _ptr(sb), sb_mode, _ptr(sr), _ptr(bi), d_type, accum,
                                    _ptr(r), R, _ptr(value), _ptr(sabs), _ptr(bits),
                                    _threads(threads)))
+    return value, sabs, bits
+
+
+def grouped_gemm(a, a_fmt, b, b_fmt, sizes, offsets, scale_a, scale_b, d_type, scale_result=None,
+                 accum=ACC_EXACT, threads=None):
+    """Grouped GEMM (NT): a [batch_sum, K], b [G, N, K] uint8 codes, sizes / offsets int32 [G]; group g's rows
+    offsets[g] .. +sizes[g] times b[g]^T, per-tensor scales. Returns (value, sum_abs, d_bits), each
+    [batch_sum, N]; rows of no group hold NaN / NaN / 0."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    batch_sum, K = a.shape
+    G, N, _ = b.shape
+    sz = np.ascontiguousarray(sizes, dtype=np.int32)
+    of = np.ascontiguousarray(offsets, dtype=np.int32)
+    if sz.size != G or of.size != G:
+        raise ValueError("sizes and offsets need one entry per group")
+    sa = np.asarray([scale_a], dtype=np.float32).reshape(-1)
+    sb = np.asarray([scale_b], dtype=np.float32).reshape(-1)
+    sr = None if scale_result is None else np.asarray([scale_result], dtype=np.float32).reshape(-1)
+    value = np.full((batch_sum, N), np.nan)
+    sabs = np.full((batch_sum, N), np.nan)
+    bits = np.zeros((batch_sum, N), dtype=_BITS_DTYPE[d_type])
+    _check(_load().orc_grouped_gemm(batch_sum, N, K, G, _ptr(a), a_fmt, K, _ptr(b), b_fmt, K, N * K, _ptr(sz),
+                                    _ptr(of), _ptr(sa), _ptr(sb), _ptr(sr), d_type, accum, _ptr(value), _ptr(sabs),
+                                    _ptr(bits), _threads(threads)))
     return value, sabs, bits
 
 

@@ -22,6 +22,11 @@
  *    before the product (GemmFP8FwdOp, scale shapes).
  *  - FP8 outputs are additionally multiplied by scale_result (mmaemu API
  *    reference, scaled_mm argument table; None means 1).
+ *  - grouped GEMM ("TileOPs: Linear Algebra Operators",
+ *    tileops.gemm.GroupedGemmFwdOp, NT layout): group g owns a run of rows of
+ *    a and multiplies them by its own b; with FP8 operands each scaled by one
+ *    factor (tileops.gemm.BmmFP8FwdOp's per-tensor scales). Each group is the
+ *    scaled GEMM above on its rows.
  *  - block-scaled GEMM + amax: C[m,n,l] = sum_k A^[m,k,l] B^[n,k,l] with
  *    A^ = A * SFA[l, m, k / sf_vec_size]; Amax = max over m,n,l of |C|
  *    ("cuDNN frontend: GEMM + Amax (SM100)", Equations).
@@ -390,6 +395,43 @@ int orc_scaled_gemm(int64_t M, int64_t N, int64_t K,
             if (d_bits) store_bits(d_bits, (int64_t)o, encode(round_to(v, out_f), out_f), out_f.bits);
         }
     });
+    return ORC_OK;
+}
+
+/*
+ * Grouped GEMM: group g owns rows offsets[g] .. offsets[g] + sizes[g] - 1 of
+ * a [batch_sum][lda] and multiplies them by its operand b + g * stride_b
+ * ([N][ldb]), per-tensor scales as orc_scaled_gemm. value / sum_abs / d_bits
+ * are [batch_sum][N]; each group writes its own rows. The metadata must be
+ * what the page asks for: sizes >= 0 adding up to batch_sum, offsets their
+ * exclusive prefix sum (ORC_ERR_ARG otherwise).
+ */
+int orc_grouped_gemm(int64_t batch_sum, int64_t N, int64_t K, int64_t G,
+                     const uint8_t* a, int a_fmt, int64_t lda,
+                     const uint8_t* b, int b_fmt, int64_t ldb, int64_t stride_b,
+                     const int32_t* sizes, const int32_t* offsets,
+                     const float* scale_a, const float* scale_b, const float* scale_result,
+                     int d_type, int accum,
+                     double* value, double* sum_abs, void* d_bits, int threads) {
+    if (batch_sum < 0 || N < 0 || K < 0 || G < 0 || stride_b < 0) return ORC_ERR_ARG;
+    if (d_type < ORC_E4M3FN || d_type > ORC_F16) return ORC_ERR_ARG;
+    int64_t next = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        if (sizes[g] < 0 || offsets[g] != next) return ORC_ERR_ARG;
+        next += sizes[g];
+    }
+    if (next != batch_sum) return ORC_ERR_ARG;
+    const int width = format_of(d_type).bits / 8;
+    for (int64_t g = 0; g < G; ++g) {
+        if (sizes[g] == 0) continue;
+        const int64_t r0 = offsets[g];
+        const int rc = orc_scaled_gemm(sizes[g], N, K, a + r0 * lda, a_fmt, lda, b + g * stride_b, b_fmt, ldb,
+                                       scale_a, ORC_SCALE_TENSOR, scale_b, ORC_SCALE_TENSOR, scale_result, nullptr,
+                                       d_type, accum, nullptr, sizes[g], value ? value + r0 * N : nullptr,
+                                       sum_abs ? sum_abs + r0 * N : nullptr,
+                                       d_bits ? (uint8_t*)d_bits + r0 * N * width : nullptr, threads);
+        if (rc != ORC_OK) return rc;
+    }
     return ORC_OK;
 }
 

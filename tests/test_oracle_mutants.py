@@ -20,7 +20,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.cpp")
 PINS = [os.path.join(ROOT, "tests", "test_oracle_fp8.py"), os.path.join(ROOT, "tests", "test_oracle_gemm.py"),
-        os.path.join(ROOT, "tests", "test_oracle_atom.py"), os.path.join(ROOT, "tests", "test_oracle_fp4.py")]
+        os.path.join(ROOT, "tests", "test_oracle_atom.py"), os.path.join(ROOT, "tests", "test_oracle_fp4.py"),
+        os.path.join(ROOT, "tests", "test_oracle_grouped.py")]
 
 # name -> (old text, new text); old text must occur exactly once
 MUTANTS = {
@@ -54,6 +55,11 @@ MUTANTS = {
     "e2m1_bias": ("std::ldexp((double)(2 + m), e - 2)", "std::ldexp((double)(2 + m), e - 1)"),
     "e2m1_subnormal": ("std::ldexp((double)m, -1)", "std::ldexp((double)m, 0)"),
     "fp4_sign_dropped": ("(row[k >> 1] >> (4 * (k & 1))) & 15", "(row[k >> 1] >> (4 * (k & 1))) & 7"),
+    "group_b_operand": ("b + g * stride_b, b_fmt", "b + (g / 2) * stride_b, b_fmt"),
+    "group_a_rows": ("a + r0 * lda, a_fmt", "a + (r0 / 2) * lda, a_fmt"),
+    "group_output_rows": ("value ? value + r0 * N : nullptr", "value ? value + (r0 / 2) * N : nullptr"),
+    "group_prefix_unchecked": ("if (sizes[g] < 0 || offsets[g] != next) return ORC_ERR_ARG;",
+                               "if (sizes[g] < 0) return ORC_ERR_ARG;"),
     "zero_chain_negative": ("double S = +0.0, T = 0.0;\n                    for (int64_t k = 0; k < K; ++k) {\n                        const double t = Am[k] * Bn[k];\n                        S += t;",
                             "double S = -0.0, T = 0.0;\n                    for (int64_t k = 0; k < K; ++k) {\n                        const double t = Am[k] * Bn[k];\n                        S += t;"),
 }
