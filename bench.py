@@ -138,6 +138,8 @@ OTHER = {
                "K=8192, f32 C + amax + index",
     "mx_fp4": "batched FP4 (E2M1) GEMM with E8M0 factors per 32 K in the page-native atom layout, L=8, "
               "M=N=2048, K=8192, f32 C + amax + index",
+    "grouped": "grouped per-tensor E4M3 GEMM (NT), 8 groups of ragged sizes packing 8192 rows, N=K=4096, slow, "
+               "bf16 out",
 }
 
 
@@ -202,6 +204,22 @@ def run_other(name, steps, warmup):
                                                sfa.data_ptr(), sfb.data_ptr(), 32, c.data_ptr(), mm.MM_F32,
                                                amax.data_ptr(), idx.data_ptr(), stream)
         scale_bytes = 4 * (sfa.numel() + sfb.numel()) + 12
+    elif name == "grouped":
+        d = datagen.workload_grouped()
+        M, K = d["a"].shape; N = d["b"].shape[1]; L = 1; G = d["b"].shape[0]
+        a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
+        gs = torch.from_numpy(d["sizes"]).to(dev); go = torch.from_numpy(d["offsets"]).to(dev)
+        sa = torch.tensor([float(d["scale_a"])], dtype=torch.float32, device=dev)
+        sb = torch.tensor([float(d["scale_b"])], dtype=torch.float32, device=dev)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        out_bytes = 2
+
+        def launch():
+            return mm.mm_scaled_gemm_grouped(M, N, K, G, a.data_ptr(), mm.MM_F8_E4M3FN, K, b.data_ptr(),
+                                             mm.MM_F8_E4M3FN, K, N * K, gs.data_ptr(), go.data_ptr(), sa.data_ptr(),
+                                             sb.data_ptr(), 0, out.data_ptr(), mm.MM_BF16, N, 0, stream)
+        # every group's b is read: G N K bytes in place of N K
+        scale_bytes = 8 + 8 * G + (G - 1) * N * K
     elif name in ("mx_atom", "mx_fp4"):
         d = datagen.workload4_atom() if name == "mx_atom" else datagen.workload_fp4()
         L, M, K = d["a"].shape; N = d["b"].shape[1]

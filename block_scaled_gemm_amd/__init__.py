@@ -6,10 +6,10 @@ memory and the current stream. Importing the package loads libmmfp8.so from
 this directory and raises if it is missing: there is no fallback path.
 
 Raw C-ABI wrappers (same names as the C functions, integer pointers):
-``mm_scaled_gemm``, ``mm_scaled_gemm_bias``, ``mm_scaled_gemm_batched``,
+``mm_scaled_gemm``, ``mm_scaled_gemm_bias``, ``mm_scaled_gemm_batched``, ``mm_scaled_gemm_grouped``,
 ``mm_blockscaled_gemm_amax``, ``mm_blockscaled_gemm_amax_atom``,
 ``mm_debug_convert``, ``mm_last_error``, ``mm_version``. Tensor-level helpers:
-``scaled_gemm`` (with an optional bias), ``scaled_bmm`` and
+``scaled_gemm`` (with an optional bias), ``scaled_bmm``, ``scaled_grouped_mm`` and
 ``blockscaled_gemm_amax`` (fp32 factors, or the page-native E8M0 bytes).
 """
 from __future__ import annotations
@@ -49,6 +49,9 @@ _lib.mm_scaled_gemm_bias.restype = _I
 _lib.mm_scaled_gemm_batched.argtypes = [_I64, _I64, _I64, _I64, _P, _I, _I64, _I64, _P, _I, _I64, _I64, _P, _P, _P,
                                         _P, _I, _I64, _I64, _I, _P]
 _lib.mm_scaled_gemm_batched.restype = _I
+_lib.mm_scaled_gemm_grouped.argtypes = [_I64, _I64, _I64, _I64, _P, _I, _I64, _P, _I, _I64, _I64, _P, _P, _P, _P,
+                                        _P, _P, _I, _I64, _I, _P]
+_lib.mm_scaled_gemm_grouped.restype = _I
 _lib.mm_blockscaled_gemm_amax.argtypes = [_I64, _I64, _I64, _I64, _P, _P, _I, _P, _P, _I, _P, _I, _P, _P, _P]
 _lib.mm_blockscaled_gemm_amax.restype = _I
 _lib.mm_blockscaled_gemm_amax_atom.argtypes = [_I64, _I64, _I64, _I64, _P, _P, _I, _P, _P, _I, _I, _P, _I, _P, _P,
@@ -59,7 +62,8 @@ _lib.mm_debug_convert.restype = _I
 _lib.mm_last_error.restype = ctypes.c_char_p
 _lib.mm_version.restype = ctypes.c_char_p
 
-EXPORTED = ("mm_scaled_gemm", "mm_scaled_gemm_bias", "mm_scaled_gemm_batched", "mm_blockscaled_gemm_amax",
+EXPORTED = ("mm_scaled_gemm", "mm_scaled_gemm_bias", "mm_scaled_gemm_batched", "mm_scaled_gemm_grouped",
+            "mm_blockscaled_gemm_amax",
             "mm_blockscaled_gemm_amax_atom", "mm_last_error", "mm_version", "mm_debug_convert")
 
 
@@ -99,6 +103,16 @@ def mm_scaled_gemm_batched(L, M, N, K, a, a_type, lda, stride_a, b, b_type, ldb,
     return _lib.mm_scaled_gemm_batched(L, M, N, K, a or None, a_type, lda, stride_a, b or None, b_type, ldb,
                                        stride_b, scale_a or None, scale_b or None, scale_result or None,
                                        d or None, d_type, ldd, stride_d, int(use_fast_accum), stream or None)
+
+
+def mm_scaled_gemm_grouped(batch_sum, N, K, G, a, a_type, lda, b, b_type, ldb, stride_b, batch_sizes,
+                           batch_offsets, scale_a, scale_b, scale_result, d, d_type, ldd, use_fast_accum,
+                           stream) -> int:
+    """Raw call of the C function; pointers and the stream are integers (0 = NULL). Returns the status."""
+    return _lib.mm_scaled_gemm_grouped(batch_sum, N, K, G, a or None, a_type, lda, b or None, b_type, ldb, stride_b,
+                                       batch_sizes or None, batch_offsets or None, scale_a or None, scale_b or None,
+                                       scale_result or None, d or None, d_type, ldd, int(use_fast_accum),
+                                       stream or None)
 
 
 def mm_blockscaled_gemm_amax(M, N, K, L, a, b, ab_type, sfa, sfb, sf_vec_size, c, c_type, amax, amax_index,
@@ -253,6 +267,31 @@ def scaled_bmm(a, b, scale_a, scale_b, out_dtype, scale_result=None, use_fast_ac
                                 b.data_ptr(), _fp8_code(b, b_format), ldb, b.stride(0),
                                 scale_a.data_ptr(), scale_b.data_ptr(), sr,
                                 out.data_ptr(), dtype_code(out_dtype), ldd, out.stride(0), use_fast_accum, _stream())
+    _check(st)
+    return out
+
+
+def scaled_grouped_mm(a, b, batch_sizes, batch_offsets, scale_a, scale_b, out_dtype, scale_result=None,
+                      use_fast_accum=False, out=None, ab_formats=None):
+    """Grouped FP8 GEMM (NT): a [batch_sum, K] with the groups' rows packed, b [G, N, K] (K innermost),
+    batch_sizes / batch_offsets int32 [G] on the device; returns d [batch_sum, N] with group g's rows
+    a[rows] @ b[g]^T * scale_a * scale_b."""
+    torch = _torch()
+    if a.dim() != 2 or b.dim() != 3 or a.stride(1) != 1 or b.stride(2) != 1 or b.stride(1) < b.shape[2]:
+        raise ValueError("a must be [batch_sum, K] and b [G, N, K], both K innermost")
+    for t in (batch_sizes, batch_offsets):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != b.shape[0]:
+            raise ValueError("batch_sizes and batch_offsets must be contiguous int32 [G]")
+    batch_sum, K = a.shape
+    G, N = b.shape[0], b.shape[1]
+    if out is None:
+        out = torch.empty((batch_sum, N), dtype=out_dtype, device=a.device)
+    fa = _fp8_code(a, ab_formats[0] if ab_formats else None)
+    fb = _fp8_code(b, ab_formats[1] if ab_formats else None)
+    st = mm_scaled_gemm_grouped(batch_sum, N, K, G, a.data_ptr(), fa, a.stride(0), b.data_ptr(), fb, b.stride(1),
+                                b.stride(0), batch_sizes.data_ptr(), batch_offsets.data_ptr(), scale_a.data_ptr(),
+                                scale_b.data_ptr(), scale_result.data_ptr() if scale_result is not None else 0,
+                                out.data_ptr(), dtype_code(out_dtype), out.stride(0), use_fast_accum, _stream())
     _check(st)
     return out
 

@@ -89,14 +89,17 @@ const char* mm_version(void) { return "mmfp8 0.1.0 gfx950"; }
 
 namespace {
 
-// The dense FP8 GEMM behind mm_scaled_gemm, mm_scaled_gemm_bias and
-// mm_scaled_gemm_batched: L items (L = 1 for the first two) at byte strides
-// stride_a / stride_b and element stride stride_d, an optional bias [N].
+// The dense FP8 GEMM behind mm_scaled_gemm, mm_scaled_gemm_bias,
+// mm_scaled_gemm_batched and mm_scaled_gemm_grouped: L items (L = 1 for the
+// first two) at byte strides stride_a / stride_b and element stride stride_d,
+// an optional bias [N]; or, grouped, G groups packed along M (L = 1), group
+// g's b at g * stride_b bytes, rows and first rows in gsizes / goffsets.
 mm_status scaled_gemm(const char* who, int64_t L, int64_t M, int64_t N, int64_t K, const void* a, int a_type,
                       int64_t lda, int64_t stride_a, const void* b, int b_type, int64_t ldb, int64_t stride_b,
                       const float* scale_a, int sa_mode, const float* scale_b, int sb_mode, const float* scale_result,
                       const void* bias, void* d, int d_type, int64_t ldd, int64_t stride_d, int use_fast_accum,
-                      void* stream) {
+                      void* stream, bool grouped = false, int64_t G = 0, const int32_t* gsizes = nullptr,
+                      const int32_t* goffsets = nullptr) {
     g_error.clear();
     if (L < 0 || M < 0 || N < 0 || K < 0)
         return fail(MM_ERR_INVALID_ARGUMENT, "L, M, N and K must be >= 0 (got %lld, %lld, %lld, %lld)", (long long)L,
@@ -125,18 +128,26 @@ mm_status scaled_gemm(const char* who, int64_t L, int64_t M, int64_t N, int64_t 
         return fail(MM_ERR_UNSUPPORTED, "a bias needs an f32, bf16 or f16 output (got d_type %d)", d_type);
     // (the workgroup count is checked against 2^31 below; 64x64 tiles are the smallest)
     if (L > 0 && cdiv(M, 64) * cdiv(N, 64) >= kMaxDim / L) return fail(MM_ERR_UNSUPPORTED, "too many output tiles");
+    if (G < 0) return fail(MM_ERR_INVALID_ARGUMENT, "the group count must be >= 0");
+    if (G >= kMaxDim || (cdiv(M, 64) + G) * cdiv(N, 64) >= kMaxDim)
+        return fail(MM_ERR_UNSUPPORTED, "too many groups or output tiles");
     if (L == 0 || M == 0 || N == 0) return MM_OK;
+    if (grouped && G > 0 && (!gsizes || !goffsets))
+        return fail(MM_ERR_INVALID_ARGUMENT, "batch_sizes or batch_offsets is NULL");
+    if (!aligned(gsizes, 4) || !aligned(goffsets, 4))
+        return fail(MM_ERR_MISALIGNED, "batch_sizes and batch_offsets must be 4-byte aligned");
     if (!d) return fail(MM_ERR_INVALID_ARGUMENT, "d is NULL");
     if (K > 0 && (!a || !b)) return fail(MM_ERR_INVALID_ARGUMENT, "a or b is NULL");
     if ((per_tensor || K > 0) && (!scale_a || !scale_b)) return fail(MM_ERR_INVALID_ARGUMENT, "scale_a or scale_b is NULL");
     if (!aligned(a, 16) || !aligned(b, 16)) return fail(MM_ERR_MISALIGNED, "a and b must be 16-byte aligned");
     if (lda % 8 || ldb % 8) return fail(MM_ERR_MISALIGNED, "lda and ldb must be multiples of 8 bytes");
-    if (L > 1 && (stride_a % 16 || stride_b % 16))
+    if ((L > 1 || G > 1) && (stride_a % 16 || stride_b % 16))
         return fail(MM_ERR_MISALIGNED, "stride_a and stride_b must be multiples of 16 bytes");
     if (!aligned(d, elem_size(d_type))) return fail(MM_ERR_MISALIGNED, "d must be aligned to its element size");
     if (!aligned(bias, elem_size(d_type))) return fail(MM_ERR_MISALIGNED, "bias must be aligned to its element size");
     if (!aligned(scale_a, 4) || !aligned(scale_b, 4) || !aligned(scale_result, 4))
         return fail(MM_ERR_MISALIGNED, "scale pointers must be 4-byte aligned");
+    if (grouped && G == 0) return MM_OK;  // no groups: no rows to compute
     if (forced_launch_failure()) return fail(MM_ERR_DEVICE, "launch failure forced by MM_TEST_FORCE_FAIL");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -146,7 +157,7 @@ mm_status scaled_gemm(const char* who, int64_t L, int64_t M, int64_t N, int64_t 
     p.lda = lda;
     p.ldb = ldb;
     p.a_batch = L > 1 ? stride_a : 0;
-    p.b_batch = L > 1 ? stride_b : 0;
+    p.b_batch = (L > 1 || G > 1) ? stride_b : 0;
     p.M = (int)M;
     p.N = (int)N;
     p.K = (int)K;
@@ -168,6 +179,21 @@ mm_status scaled_gemm(const char* who, int64_t L, int64_t M, int64_t N, int64_t 
     const int fa = a_type == MM_F8_E5M2 ? 1 : 0;
     const int fb = b_type == MM_F8_E5M2 ? 1 : 0;
     hipError_t e;
+    if (grouped) {
+        // groups: the tile kernel over ceil(M / BM) + G tile rows, each mapped to its group on the device
+        // (partial tiles of each group; the rows past the groups' tiles leave at once)
+        const int mode = use_fast_accum ? mmfp8::MODE_FAST : mmfp8::MODE_SLOW;
+        const int cfg = choose_cfg(M, N, 1, cu_count(), mmfp8::min_cfg(mode, 0));
+        p.groups = (int)G;
+        p.grp_sizes = gsizes;
+        p.grp_offsets = goffsets;
+        p.tiles_m = (int)(cdiv(M, mmfp8::kCfgBM[cfg]) + G);
+        p.tiles_n = (int)cdiv(N, mmfp8::kCfgBN[cfg]);
+        const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+        e = use_fast_accum ? mmfp8::launch_tile_fast(cfg, fa, fb, p, (int)grid, s)
+                           : mmfp8::launch_tile_slow(cfg, fa, fb, p, (int)grid, s);
+        return device_status(e, who);
+    }
     // the skinny and K-split kernels serve one item; batches go to the tiles
     if (per_tensor && L == 1 && M <= 64) {
         const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
@@ -332,6 +358,16 @@ mm_status blockscaled_amax(const char* who, int64_t M, int64_t N, int64_t K, int
 }  // namespace
 
 extern "C" {
+
+mm_status mm_scaled_gemm_grouped(int64_t batch_sum, int64_t N, int64_t K, int64_t G, const void* a, int a_type,
+                                 int64_t lda, const void* b, int b_type, int64_t ldb, int64_t stride_b,
+                                 const int32_t* batch_sizes, const int32_t* batch_offsets, const float* scale_a,
+                                 const float* scale_b, const float* scale_result, void* d, int d_type, int64_t ldd,
+                                 int use_fast_accum, void* stream) {
+    return scaled_gemm("mm_scaled_gemm_grouped launch", 1, batch_sum, N, K, a, a_type, lda, 0, b, b_type, ldb,
+                       stride_b, scale_a, MM_SCALE_TENSOR, scale_b, MM_SCALE_TENSOR, scale_result, nullptr, d, d_type,
+                       ldd, 0, use_fast_accum, stream, true, G, batch_sizes, batch_offsets);
+}
 
 mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L, const void* a, const void* b,
                                    int ab_type, const float* sfa, const float* sfb, int sf_vec_size, void* c,

@@ -82,6 +82,13 @@ struct GemmArgs {
     unsigned long long* amax_key; // (|x| bits << 33) | (2^33 - 1 - index), or null
     int tiles_m, tiles_n;
     const void* bias;   // [N] of d_type (f32, bf16 or f16), added after the scales; or null
+    // Grouped GEMM (groups > 0): a and d hold the groups' rows packed along M
+    // (M = the packed row count), b one [N][ldb] operand per group, b_batch
+    // bytes apart; grid tile row t is tile t - (tiles of the groups before) of
+    // its group. grp_sizes / grp_offsets: rows and first row of each group.
+    const int* grp_sizes;
+    const int* grp_offsets;
+    int groups;
 };
 
 // ------------------------------------------------------------------ helpers
@@ -322,6 +329,47 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int t
     tn = v / gsz;
 }
 
+// Grouped GEMM: grid tile row tm -> its group g (groups take ceil(rows / BM)
+// tile rows each, in order) and the tile row within it. Moves a and d to the
+// tile's first packed row and b to the group's operand, sets M to the tile's
+// valid rows and tm to 0. Rows are clamped to the packed buffer, so group
+// sizes and offsets that do not add up never read or write outside it. Every
+// wave computes this (a wave-wide prefix over 64 groups at a time); false
+// when the tile has no rows.
+template <int BM>
+__device__ __forceinline__ bool group_tile(GemmArgs& p, int& tm) {
+    const int lane = threadIdx.x & 63;
+    int64_t before = 0;  // tile rows of the groups before the current 64
+    for (int g0 = 0; g0 < p.groups; g0 += 64) {
+        const int g = g0 + lane;
+        const int64_t rows = g < p.groups ? min(max((int64_t)p.grp_sizes[g], (int64_t)0), (int64_t)p.M) : 0;
+        const int64_t own = (rows + BM - 1) / BM;
+        int64_t incl = own;  // inclusive prefix of the tile rows over the wave
+        for (int d = 1; d < 64; d <<= 1) {
+            const int64_t v = __shfl_up(incl, d);
+            if (lane >= d) incl += v;
+        }
+        const unsigned long long hit = __ballot(before + incl > tm);
+        if (hit) {
+            const int gl = __ffsll((long long)hit) - 1;
+            const int gsel = __builtin_amdgcn_readfirstlane(g0 + gl);
+            const int t = __builtin_amdgcn_readfirstlane((int)(tm - before - __shfl(incl - own, gl)));  // within the group
+            const int64_t row0 = (int64_t)p.grp_offsets[gsel] + (int64_t)t * BM;
+            const int64_t valid = min(min((int64_t)BM, (int64_t)p.grp_sizes[gsel] - (int64_t)t * BM), (int64_t)p.M - row0);
+            if (row0 < 0 || valid <= 0) return false;
+            const int es = p.d_type == T_F32 ? 4 : ((p.d_type == T_BF16 || p.d_type == T_F16) ? 2 : 1);
+            p.a += row0 * p.lda;
+            p.d = (uint8_t*)p.d + row0 * p.ldd * es;
+            p.b += (int64_t)gsel * p.b_batch;
+            p.M = (int)valid;
+            tm = 0;
+            return true;
+        }
+        before += __shfl(incl, 63);
+    }
+    return false;
+}
+
 // ------------------------------------------------------------------ tiled kernel
 //
 // Workgroup tile BM x BN computed by WM x WN waves, each wave a
@@ -402,6 +450,10 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     const int wm = gw / WN, wn = gw % WN;
     int l, tm, tn;
     tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, 8, l, tm, tn);
+    if (p.groups > 0) {
+        if (!group_tile<BM>(p, tm)) return;  // the whole workgroup leaves: a tile past the groups' rows
+        l = 0;
+    }
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = p.K;
     const int KT = (K + kBK - 1) / kBK;

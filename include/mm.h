@@ -189,6 +189,43 @@ mm_status mm_scaled_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K,
                                  void* stream);
 
 /*
+ * mm_scaled_gemm_grouped -- grouped FP8 GEMM: one GEMM per group, the groups'
+ * rows packed along M, as "TileOPs: Linear Algebra Operators",
+ * tileops.gemm.GroupedGemmFwdOp defines it in its default NT layout
+ * (forward(a, b, batch_sizes, batch_offsets)), with FP8 operands scaled as
+ * tileops.gemm.BmmFP8FwdOp's: one fp32 scale for a and one for b.
+ *
+ *  a        [batch_sum][lda] FP8 codes: the rows of every group; group g owns
+ *           rows batch_offsets[g] .. batch_offsets[g] + batch_sizes[g] - 1.
+ *  b        [G][N][ldb] FP8 codes (K innermost, the page's NT), group g's
+ *           operand at b + g * stride_b bytes.
+ *  batch_sizes, batch_offsets  int32 [G], DEVICE pointers: rows and first row
+ *           of each group. As on the page they are not checked (that would
+ *           synchronise): the sizes must add up to batch_sum and the offsets be
+ *           their exclusive prefix sum. Values that do not give unspecified
+ *           rows, never an access outside a, b, d or the two arrays: each
+ *           group's rows are clamped to [0, batch_sum).
+ *  d        [batch_sum][ldd] of d_type: row r of group g is
+ *           d[r, n] = (a[r,:] . b[g][n,:]) * scale_a * scale_b, cast as in
+ *           mm_scaled_gemm (scale_result for FP8 outputs, fast or slow
+ *           accumulation). Rows no group covers are not written.
+ *
+ * Sizes: batch_sum, N, K and G in [0, 2^31), (ceil(batch_sum/64) + G) *
+ * ceil(N/64) < 2^31. G, batch_sum or N == 0: nothing is launched. Alignment as
+ * mm_scaled_gemm (stride_b a multiple of 16 when G > 1); batch_sizes and
+ * batch_offsets 4-byte aligned. Errors as mm_scaled_gemm.
+ */
+mm_status mm_scaled_gemm_grouped(int64_t batch_sum, int64_t N, int64_t K, int64_t G,
+                                 const void* a, int a_type, int64_t lda,
+                                 const void* b, int b_type, int64_t ldb, int64_t stride_b,
+                                 const int32_t* batch_sizes, const int32_t* batch_offsets,
+                                 const float* scale_a, const float* scale_b,
+                                 const float* scale_result,
+                                 void* d, int d_type, int64_t ldd,
+                                 int use_fast_accum,
+                                 void* stream);
+
+/*
  * mm_blockscaled_gemm_amax -- batched block-scaled GEMM with a global amax.
  *
  * Defined by "cuDNN frontend: GEMM + Amax (SM100)", Overview, Shapes and

@@ -227,3 +227,23 @@ def workload_fp4(L=8, M=2048, N=2048, K=8192, sf=32, config=8):
     b = rng(config, 1).integers(0, 256, size=(L, N, K // 2), dtype=np.uint8)
     return dict(a=a, b=b, ab_fmt=5, sfa=e8m0_atom_codes(rng(config, 2), M, K, L, sf),
                 sfb=e8m0_atom_codes(rng(config, 3), N, K, L, sf), sf_vec=sf, K=K)
+
+
+def group_sizes(g, G, batch_sum, empty=0):
+    """Ragged group sizes adding up to batch_sum: multinomial counts with Dirichlet(1) proportions, the first
+    `empty` groups (after a seeded shuffle) forced to 0 rows."""
+    p = g.dirichlet(np.ones(G))
+    dead = g.permutation(G)[:empty]
+    p[dead] = 0.0
+    p = p / p.sum()
+    return g.multinomial(batch_sum, p).astype(np.int32)
+
+
+def workload_grouped(G=8, batch_sum=8192, N=4096, K=4096, empty=0, config=9):
+    """Grouped set (TileOPs GroupedGemmFwdOp, NT): a [batch_sum, K] and b [G, N, K] Gaussian codes as
+    workload 3, ragged group sizes, one scale per operand."""
+    sizes = group_sizes(rng(config, 3), G, batch_sum, empty)
+    offsets = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.int32)
+    a = gauss_codes(rng(config, 0), (batch_sum, K), 64.0)
+    b = gauss_codes(rng(config, 1), (G, N, K), 64.0)
+    return dict(a=a, b=b, sizes=sizes, offsets=offsets, K=K, scale_a=np.float32(0.5), scale_b=np.float32(0.25))

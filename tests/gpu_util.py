@@ -85,6 +85,27 @@ def blockscaled_gemm_amax_atom(a, b, fmt, sfa, sfb, c_type, with_amax=True, with
             int(tix.item()) if with_index else None)
 
 
+def scaled_gemm_grouped(a, a_fmt, b, b_fmt, sizes, offsets, sa, sb, d_type, scale_result=None, fast=False):
+    """a [batch_sum, K], b [G, N, K] uint8 codes; int32 sizes / offsets; returns d bits [batch_sum, N]
+    (rows of no group keep the fill pattern 0x5A)."""
+    batch_sum, K = a.shape
+    G, N, _ = b.shape
+    ta, tb = dev_u8(a), dev_u8(b)
+    ts = torch.from_numpy(np.ascontiguousarray(sizes, dtype=np.int32)).to(DEV)
+    to = torch.from_numpy(np.ascontiguousarray(offsets, dtype=np.int32)).to(DEV)
+    tsa, tsb = dev_f32([sa]), dev_f32([sb])
+    tsr = dev_f32([scale_result]) if scale_result is not None else None
+    es = np.dtype(BITS_NP[d_type]).itemsize
+    td = torch.full((max(batch_sum * N, 1) * es,), 0x5A, dtype=torch.uint8, device=DEV)
+    st = mm.mm_scaled_gemm_grouped(batch_sum, N, K, G, ta.data_ptr(), a_fmt, K, tb.data_ptr(), b_fmt, K, N * K,
+                                   ts.data_ptr(), to.data_ptr(), tsa.data_ptr(), tsb.data_ptr(),
+                                   tsr.data_ptr() if tsr is not None else 0, td.data_ptr(), d_type, N, int(fast),
+                                   stream())
+    assert st == mm.MM_OK, (st, mm.mm_last_error())
+    torch.cuda.synchronize()
+    return np.ascontiguousarray(td.cpu().numpy().view(BITS_NP[d_type])[: batch_sum * N].reshape(batch_sum, N))
+
+
 def debug_convert(x: np.ndarray, dtype: int) -> np.ndarray:
     tx = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
     es = np.dtype(BITS_NP[dtype]).itemsize

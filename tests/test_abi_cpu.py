@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) == {"mm_scaled_gemm", "mm_scaled_gemm_bias", "mm_scaled_gemm_batched",
+    assert set(names) == {"mm_scaled_gemm", "mm_scaled_gemm_bias", "mm_scaled_gemm_batched", "mm_scaled_gemm_grouped",
                           "mm_blockscaled_gemm_amax", "mm_blockscaled_gemm_amax_atom", "mm_last_error",
                           "mm_version", "mm_debug_convert"}
     lib = ctypes.CDLL(mm.LIB_PATH)
@@ -138,6 +138,38 @@ def test_scaled_gemm_batched_zero_sizes_launch_nothing():
     assert bmm(L=1, M=0, stride_a=8, d=0) == mm.MM_OK
 
 
+def grouped(**kw):
+    args = dict(batch_sum=300, N=64, K=256, G=4, a=P, a_type=0, lda=256, b=P, b_type=0, ldb=256, stride_b=64 * 256,
+                batch_sizes=P, batch_offsets=P, scale_a=P, scale_b=P, scale_result=0, d=P, d_type=3, ldd=64,
+                use_fast_accum=0, stream=0)
+    args.update(kw)
+    return mm.mm_scaled_gemm_grouped(**args)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(G=-1), mm.MM_ERR_INVALID_ARGUMENT, "group count"),
+    (dict(G=1 << 31), mm.MM_ERR_UNSUPPORTED, "too many groups"),
+    (dict(batch_sizes=0), mm.MM_ERR_INVALID_ARGUMENT, "batch_sizes or batch_offsets is NULL"),
+    (dict(batch_offsets=P + 2), mm.MM_ERR_MISALIGNED, "4-byte"),
+    (dict(stride_b=64 * 256 + 8), mm.MM_ERR_MISALIGNED, "multiples of 16"),
+    (dict(stride_b=-16), mm.MM_ERR_INVALID_ARGUMENT, "strides must be >= 0"),
+    (dict(a_type=2), mm.MM_ERR_INVALID_ARGUMENT, "a_type and b_type"),
+    (dict(ldb=128), mm.MM_ERR_INVALID_ARGUMENT, "lda and ldb must be >= K"),
+    (dict(d=0), mm.MM_ERR_INVALID_ARGUMENT, "d is NULL"),
+])
+def test_grouped_validation(kw, status, msg):
+    assert grouped(**kw) == status
+    assert msg in mm.mm_last_error()
+
+
+def test_grouped_nothing_to_do_launches_nothing():
+    assert grouped(G=0, batch_sizes=0, batch_offsets=0) == mm.MM_OK
+    assert grouped(batch_sum=0, d=0) == mm.MM_OK
+    assert grouped(N=0, d=0) == mm.MM_OK
+    # no groups: the stride is not used
+    assert grouped(G=0, stride_b=8) == mm.MM_OK
+
+
 def amax_call(**kw):
     args = dict(M=64, N=64, K=256, L=2, a=P, b=P, ab_type=0, sfa=P, sfb=P, sf_vec_size=32, c=P, c_type=2,
                 amax=P, amax_index=P, stream=0)
@@ -230,6 +262,7 @@ def test_forced_launch_failure(monkeypatch):
     assert atom_call() == mm.MM_ERR_DEVICE
     assert gemm_bias() == mm.MM_ERR_DEVICE
     assert bmm() == mm.MM_ERR_DEVICE
+    assert grouped() == mm.MM_ERR_DEVICE
     assert mm.mm_debug_convert(P, P, 2, 16, 0) == mm.MM_ERR_DEVICE
 
 

@@ -394,6 +394,64 @@ def test_atom_workload4_full_size():
     assert amax == a2 and idx == i2
 
 
+# ------------------------------------------------------------------ grouped GEMM (GroupedGemmFwdOp, NT, FP8)
+
+def check_grouped(w, d_type, fast=False, scale_result=None, rows=None, fmt=(E4M3FN, E4M3FN)):
+    gpu = gu.scaled_gemm_grouped(w["a"], fmt[0], w["b"], fmt[1], w["sizes"], w["offsets"], w["scale_a"],
+                                 w["scale_b"], d_type, scale_result=scale_result, fast=fast)
+    value, sabs, bits = oracle.grouped_gemm(w["a"], fmt[0], w["b"], fmt[1], w["sizes"], w["offsets"], w["scale_a"],
+                                            w["scale_b"], d_type, scale_result=scale_result)
+    r = np.arange(w["a"].shape[0]) if rows is None else rows
+    compare.check(gpu[r], value[r], sabs[r], bits[r], d_type, "grouped gemm")
+    return gpu
+
+
+@pytest.mark.parametrize("G,batch_sum,N,K,empty,fast,d_type", [
+    (5, 300, 136, 256, 1, False, BF16),     # ragged groups, one empty, partial tiles (64x64 tiles)
+    (3, 1000, 200, 1040, 0, True, F32),     # K tail
+    (100, 1500, 64, 128, 20, False, F16),   # more than 64 groups (two rounds of the wave scan), many empty
+    (8, 4096, 1024, 512, 2, False, BF16),   # 128x128 tiles, one per CU (two K groups)
+    (8, 8192, 2048, 512, 0, True, E4M3FN),  # 128x128 tiles, two per CU; FP8 out
+])
+def test_grouped_against_oracle(G, batch_sum, N, K, empty, fast, d_type):
+    w = datagen.workload_grouped(G, batch_sum, N, K, empty, config=10 + G)
+    sr = 1.0 / 16 if d_type == E4M3FN else None
+    rows = None if batch_sum <= 1500 else sample_rows(batch_sum, 16, seed=G)
+    check_grouped(w, d_type, fast=fast, scale_result=sr, rows=rows)
+
+
+def test_grouped_e5m2_and_single_group():
+    w = datagen.workload_grouped(1, 257, 96, 384, 0, config=21)
+    w["a"] = datagen.gauss_codes(datagen.rng(21, 4), w["a"].shape, 64.0, E5M2)
+    check_grouped(w, F32, fmt=(E5M2, E4M3FN))
+
+
+def test_grouped_rows_of_no_group_are_not_written():
+    # sizes that cover only part of the rows (the page makes this the caller's error): the covered rows are
+    # right and the others keep their previous contents
+    w = datagen.workload_grouped(4, 400, 72, 256, 0, config=22)
+    w["sizes"] = np.array([50, 0, 30, 100], np.int32)
+    w["offsets"] = np.array([0, 60, 60, 250], np.int32)
+    gpu = gu.scaled_gemm_grouped(w["a"], E4M3FN, w["b"], E4M3FN, w["sizes"], w["offsets"], w["scale_a"],
+                                 w["scale_b"], BF16)
+    for g, (sz, of) in enumerate(zip(w["sizes"], w["offsets"])):
+        if sz == 0:
+            continue
+        value, sabs, bits = oracle.scaled_gemm(w["a"][of:of + sz], E4M3FN, w["b"][g], E4M3FN, w["scale_a"], 0,
+                                               w["scale_b"], 0, BF16)
+        compare.check(gpu[of:of + sz], value, sabs, bits, BF16, f"group {g}")
+    covered = np.zeros(400, bool)
+    for sz, of in zip(w["sizes"], w["offsets"]):
+        covered[of:of + sz] = True
+    assert np.all(gpu[~covered] == 0x5A5A)
+
+
+def test_grouped_full_size():
+    """The grouped bench workload: 8 groups, 8192 packed rows, N = K = 4096, slow, bf16 out; sampled rows."""
+    w = datagen.workload_grouped()
+    check_grouped(w, BF16, rows=sample_rows(8192, 16, seed=3))
+
+
 # ------------------------------------------------------------------ FP4 (E2M1) operands, page-native factors
 
 def check_fp4_case(w, c_type, rows=None):
