@@ -303,7 +303,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     if args.workload:
-        run_other(args.workload, args.steps if args.steps != 200 else 20, args.warmup if args.warmup != 20 else 3)
+        # the first launches after the inputs are uploaded run up to 20% slower: 50 warm-up launches by default
+        run_other(args.workload, args.steps if args.steps != 200 else 100, args.warmup if args.warmup != 20 else 50)
         return
 
     import torch
