@@ -138,6 +138,8 @@ OTHER = {
                "K=8192, f32 C + amax + index",
     "mx_fp4": "batched FP4 (E2M1) GEMM with E8M0 factors per 32 K in the page-native atom layout, L=8, "
               "M=N=2048, K=8192, f32 C + amax + index",
+    "mx_nvfp4": "batched FP4 (E2M1) GEMM with E4M3 factors per 16 K in the page-native atom layout, L=8, "
+                "M=N=2048, K=8192, f32 C + amax + index",
     "grouped": "grouped per-tensor E4M3 GEMM (NT), 8 groups of ragged sizes packing 8192 rows, N=K=4096, slow, "
                "bf16 out",
 }
@@ -220,11 +222,12 @@ def run_other(name, steps, warmup):
                                              sb.data_ptr(), 0, out.data_ptr(), mm.MM_BF16, N, 0, stream)
         # every group's b is read: G N K bytes in place of N K
         scale_bytes = 8 + 8 * G + (G - 1) * N * K
-    elif name in ("mx_atom", "mx_fp4"):
-        d = datagen.workload4_atom() if name == "mx_atom" else datagen.workload_fp4()
+    elif name in ("mx_atom", "mx_fp4", "mx_nvfp4"):
+        d = {"mx_atom": datagen.workload4_atom, "mx_fp4": datagen.workload_fp4, "mx_nvfp4": datagen.workload_nvfp4}[name]()
         L, M, K = d["a"].shape; N = d["b"].shape[1]
         ab_type = mm.MM_F8_E4M3FN if name == "mx_atom" else mm.MM_F4_E2M1
         K = K if name == "mx_atom" else 2 * K
+        sf_type, sf_vec = (mm.MM_SF_E4M3FN, 16) if name == "mx_nvfp4" else (mm.MM_SF_E8M0, 32)
         a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
         sfa = torch.from_numpy(d["sfa"]).to(dev); sfb = torch.from_numpy(d["sfb"]).to(dev)
         c = torch.empty((L, M, N), dtype=torch.float32, device=dev)
@@ -234,7 +237,7 @@ def run_other(name, steps, warmup):
 
         def launch():
             return mm.mm_blockscaled_gemm_amax_atom(M, N, K, L, a.data_ptr(), b.data_ptr(), ab_type,
-                                                    sfa.data_ptr(), sfb.data_ptr(), mm.MM_SF_E8M0, 32, c.data_ptr(),
+                                                    sfa.data_ptr(), sfb.data_ptr(), sf_type, sf_vec, c.data_ptr(),
                                                     mm.MM_F32, amax.data_ptr(), idx.data_ptr(), stream)
         scale_bytes = sfa.numel() + sfb.numel() + 12
     else:
@@ -269,7 +272,7 @@ def run_other(name, steps, warmup):
     us = 1e3 * e0.elapsed_time(e1) / steps
     flops = 2.0 * L * M * N * K
     tf = flops / us / 1e6
-    op_bytes = 0.5 if name == "mx_fp4" else 1.0  # operand bytes per element (FP4: two per byte)
+    op_bytes = 0.5 if name in ("mx_fp4", "mx_nvfp4") else 1.0  # operand bytes per element (FP4: two per byte)
     nbytes = L * ((M + N) * K * op_bytes + M * N * out_bytes) + scale_bytes
     result = {
         "metric": f"{OTHER[name]}: TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,

@@ -304,7 +304,8 @@ def blockscaled_gemm_amax(a, b, sfa, sfb, c_dtype=None, sf_vec_size=32, with_ind
     [L, N, K/2]. The scale factors are either float32 powers of two (FP8
     only), sfa [L, M, ceil(K/32)] and sfb [L, N, ceil(K/32)], or the cuDNN
     page's own tensors: E8M0 bytes (float8_e8m0fnu, uint8 or int8) of storage
-    shape (L, ceil(MN/128), ceil(K/(4 sf)), 32, 4, 4). Returns
+    shape (L, ceil(MN/128), ceil(K/(4 sf)), 32, 4, 4), or E4M3 bytes (float8_e4m3fn) of that shape with FP4
+    operands and sf_vec_size=16. Returns
     (c [L, M, N], amax [1]) or (c, amax, amax_index [1]) with with_index.
     """
     torch = _torch()
@@ -325,8 +326,9 @@ def blockscaled_gemm_amax(a, b, sfa, sfb, c_dtype=None, sf_vec_size=32, with_ind
             if t.numel() != L * -(-rows // 128) * -(-K // (4 * sf_vec_size)) * 512:
                 raise ValueError("E8M0 scale factors must have the storage shape "
                                  "(L, ceil(MN/128), ceil(K/(4 sf)), 32, 4, 4)")
+        sf_type = MM_SF_E4M3FN if sfa.dtype == torch.float8_e4m3fn else MM_SF_E8M0
         st = mm_blockscaled_gemm_amax_atom(M, N, K, L, a.data_ptr(), b.data_ptr(), ab_type,
-                                           sfa.data_ptr(), sfb.data_ptr(), MM_SF_E8M0, sf_vec_size, c.data_ptr(),
+                                           sfa.data_ptr(), sfb.data_ptr(), sf_type, sf_vec_size, c.data_ptr(),
                                            dtype_code(c_dtype), amax.data_ptr(), idx.data_ptr() if with_index else 0,
                                            _stream())
     else:

@@ -262,7 +262,8 @@ namespace {
 // page-native E8M0 bytes (FP8 or FP4 operands) over fp32 factors (FP8).
 mm_status blockscaled_amax(const char* who, int64_t M, int64_t N, int64_t K, int64_t L, const void* a,
                            const void* b, int ab_type, const void* sfa, const void* sfb, bool atom, int sf_vec_size,
-                           void* c, int c_type, float* amax, int64_t* amax_index, void* stream) {
+                           void* c, int c_type, float* amax, int64_t* amax_index, void* stream,
+                           bool e4m3_factors = false) {
     if (M < 0 || N < 0 || K < 0 || L < 0)
         return fail(MM_ERR_INVALID_ARGUMENT, "M, N, K and L must be >= 0");
     if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim || L >= kMaxDim)
@@ -279,6 +280,8 @@ mm_status blockscaled_amax(const char* who, int64_t M, int64_t N, int64_t K, int
         return fail(MM_ERR_UNSUPPORTED, "sf_vec_size 16 is not supported with FP8 operands; use 32");
     if (sf_vec_size != 32 && sf_vec_size != 16)
         return fail(MM_ERR_INVALID_ARGUMENT, "sf_vec_size must be 32%s (got %d)", fp4 ? " or 16" : "", sf_vec_size);
+    if (e4m3_factors && (!fp4 || sf_vec_size != 16))
+        return fail(MM_ERR_UNSUPPORTED, "E4M3 scale factors need FP4 operands and sf_vec_size 16");
     if (is_fp8(c_type) && !fp4) return fail(MM_ERR_UNSUPPORTED, "FP8 C with FP8 operands is not supported");
     if (c_type == MM_F4_E2M1) return fail(MM_ERR_UNSUPPORTED, "FP4 C is not provided");
     if (!is_dtype(c_type)) return fail(MM_ERR_INVALID_ARGUMENT, "unknown c_type %d", c_type);
@@ -345,7 +348,10 @@ mm_status blockscaled_amax(const char* who, int64_t M, int64_t N, int64_t K, int
         p.tiles_n = (int)cdiv(N, mmfp8::kCfgBN[cfg]);
         const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * L;
         if (grid >= kMaxDim) return fail(MM_ERR_UNSUPPORTED, "too many output tiles");
-        const int layout = !atom ? mmfp8::SF_F32 : sf_vec_size == 16 ? mmfp8::SF_ATOM_E8M0_16 : mmfp8::SF_ATOM_E8M0;
+        const int layout = !atom                ? mmfp8::SF_F32
+                           : e4m3_factors       ? mmfp8::SF_ATOM_E4M3_16
+                           : sf_vec_size == 16  ? mmfp8::SF_ATOM_E8M0_16
+                                                : mmfp8::SF_ATOM_E8M0;
         const hipError_t e = fp4 ? mmfp8::launch_tile_fp4(cfg, layout, p, (int)grid, s)
                                  : mmfp8::launch_tile_sf32(cfg, layout, ab_type == MM_F8_E5M2 ? 1 : 0, p, (int)grid, s);
         mm_status st = device_status(e, who);
@@ -382,11 +388,10 @@ mm_status mm_blockscaled_gemm_amax_atom(int64_t M, int64_t N, int64_t K, int64_t
                                         int sf_vec_size, void* c, int c_type, float* amax, int64_t* amax_index,
                                         void* stream) {
     g_error.clear();
-    if (sf_type == MM_SF_E4M3FN)
-        return fail(MM_ERR_UNSUPPORTED, "E4M3 scale factors (the page's FP4 with sf_vec_size 16) are not provided");
-    if (sf_type != MM_SF_E8M0) return fail(MM_ERR_INVALID_ARGUMENT, "unknown sf_type %d", sf_type);
+    if (sf_type != MM_SF_E8M0 && sf_type != MM_SF_E4M3FN)
+        return fail(MM_ERR_INVALID_ARGUMENT, "unknown sf_type %d", sf_type);
     return blockscaled_amax("mm_blockscaled_gemm_amax_atom launch", M, N, K, L, a, b, ab_type, sfa, sfb, true,
-                            sf_vec_size, c, c_type, amax, amax_index, stream);
+                            sf_vec_size, c, c_type, amax, amax_index, stream, sf_type == MM_SF_E4M3FN);
 }
 
 mm_status mm_debug_convert(const float* x, void* y, int dtype, int64_t n, void* stream) {

@@ -43,6 +43,8 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -57,7 +59,9 @@ enum : int { SB_1x128 = 0, SB_128x128 = 1 };
 // with groups of 32 or 16 K, where for every 128 rows and 4 groups the 512
 // bytes hold row r's 4 groups as one dword at byte 16 (r % 32) + 4 (r / 32),
 // blocks ordered [L][MN/128][ceil(groups/4)].
-enum : int { SF_F32 = 0, SF_ATOM_E8M0 = 1, SF_ATOM_E8M0_16 = 2 };
+// SF_ATOM_E4M3_16: the same layout holding E4M3 factors, one per 16 values
+// (FP4 operands only).
+enum : int { SF_F32 = 0, SF_ATOM_E8M0 = 1, SF_ATOM_E8M0_16 = 2, SF_ATOM_E4M3_16 = 3 };
 
 constexpr int kBK = 128;                 // K per main-loop step = one MFMA = one 128-element chunk
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 buffer descriptor dword 3 (raw, 32-bit format)
@@ -109,6 +113,9 @@ __device__ __forceinline__ uint32_t operand_extent(int rows, int64_t ld, int K) 
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& first, const bf16x8& second, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(first, second, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma_f16(const f16x8& first, const f16x8& second, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(first, second, c, 0, 0, 0);
+}
 
 // Two FP8 codes (bytes 2 hi, 2 hi + 1 of w) to two bf16 values times `scale`.
 // F = 0: E4M3, F = 1: E5M2. Exact: every FP8 value is a bf16 value and the
@@ -150,6 +157,22 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const i32x4& f, int q, float scale) 
     const uint32_t w0 = (uint32_t)f[2 * q], w1 = (uint32_t)f[2 * q + 1];
     const bf16x2 p0 = cvt2<F, false>(w0, scale), p1 = cvt2<F, true>(w0, scale);
     const bf16x2 p2 = cvt2<F, false>(w1, scale), p3 = cvt2<F, true>(w1, scale);
+    const auto lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+    const auto hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Dword q of a 16-byte FP4 chunk as one f16 MFMA operand, each value times the
+// E4M3 factor s (a packed f16 multiply). Exact: an E2M1 value times an E4M3
+// value has at most 6 significant bits and lies in [2^-10, 2688], inside f16's
+// normal range. (The scaled conversions take only a power of two.)
+__device__ __forceinline__ f16x8 fp4_to_f16x8(const i32x4& f, int q, _Float16 s) {
+    const uint32_t w = (uint32_t)f[q];
+    const f16x2 ss = {s, s};
+    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
     const auto lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
     const auto hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -427,7 +450,9 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     // its main loop then fits in 256 VGPRs, where with one issue the compiler
     // spills 38 of them, which measured 17% slower.
     constexpr bool kAtom = MODE == MODE_SF32 && SBM != SF_F32;
-    constexpr int SFV = SBM == SF_ATOM_E8M0_16 ? 16 : 32;  // values per scale group
+    constexpr bool kE4M3 = kAtom && SBM == SF_ATOM_E4M3_16;  // E4M3 factors (FP4 only): f16 operands
+    static_assert(!kE4M3 || kFp4, "E4M3 factors go with FP4 operands");
+    constexpr int SFV = (SBM == SF_ATOM_E8M0_16 || SBM == SF_ATOM_E4M3_16) ? 16 : 32;  // values per scale group
     constexpr int GPS = (kFp4 ? 2 * kBK : kBK) / SFV;      // scale groups per step
     constexpr int NKB = kAtom ? GPS / 4 : 1;
     constexpr int kAtomRep = kAtom && !kFp4 && BM == 256 && BN == 256 ? 4 : 1;
@@ -699,10 +724,14 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
         const bool gv = kt * GPS + g < p.sa_ld;  // groups past ceil(K/sf) hold zero data
         const uint8_t* eA = stage + (BM + BN) * kBK + (g >> 2) * BM * 4 + (g & 3);
         const uint8_t* eB = stage + (BM + BN) * kBK + SC_A_INS * 256 + (g >> 2) * BN * 4 + (g & 3);
+        auto factor = [&](uint32_t code) {
+            if constexpr (kE4M3) return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);  // exact, NaN for 0x7F / 0xFF
+            else return e8m0_code_scale(code);
+        };
 #pragma unroll
-        for (int i = 0; i < FM; ++i) c_a[i] = gv ? e8m0_code_scale(eA[(wm * WTM + i * 16 + fr) * 4]) : 1.0f;
+        for (int i = 0; i < FM; ++i) c_a[i] = gv ? factor(eA[(wm * WTM + i * 16 + fr) * 4]) : 1.0f;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) c_b[j] = gv ? e8m0_code_scale(eB[(wn * WTN + j * 16 + fr) * 4]) : 1.0f;
+        for (int j = 0; j < FN; ++j) c_b[j] = gv ? factor(eB[(wn * WTN + j * 16 + fr) * 4]) : 1.0f;
     };
     auto mma_half4 = [&](const Frag& f, int kt, const uint8_t* stage, int h) {
         constexpr int QPS = SFV == 32 ? 4 : 2;  // k-slices per scale group
@@ -713,14 +742,26 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
 #pragma unroll
             for (int qq = 0; qq < QPS; ++qq) {
                 const int q = qp * QPS + qq;
-                bf16x8 ab[FM];
+                if constexpr (kE4M3) {
+                    f16x8 ab[FM];
 #pragma unroll
-                for (int i = 0; i < FM; ++i) ab[i] = fp4_to_bf16x8(f.a[i], q, c_a[i]);
+                    for (int i = 0; i < FM; ++i) ab[i] = fp4_to_f16x8(f.a[i], q, (_Float16)c_a[i]);
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const bf16x8 bb = fp4_to_bf16x8(f.b[j], q, c_b[j]);
+                    for (int j = 0; j < FN; ++j) {
+                        const f16x8 bb = fp4_to_f16x8(f.b[j], q, (_Float16)c_b[j]);
 #pragma unroll
-                    for (int i = 0; i < FM; ++i) acc[j][i] = mfma_bf16(bb, ab[i], acc[j][i]);
+                        for (int i = 0; i < FM; ++i) acc[j][i] = mfma_f16(bb, ab[i], acc[j][i]);
+                    }
+                } else {
+                    bf16x8 ab[FM];
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) ab[i] = fp4_to_bf16x8(f.a[i], q, c_a[i]);
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const bf16x8 bb = fp4_to_bf16x8(f.b[j], q, c_b[j]);
+#pragma unroll
+                        for (int i = 0; i < FM; ++i) acc[j][i] = mfma_bf16(bb, ab[i], acc[j][i]);
+                    }
                 }
             }
         }

@@ -300,9 +300,11 @@ mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L,
  *           padded shape must be readable; bytes of rows past M or groups past
  *           ceil(K/sf) are never used.
  *  sfb      the same for B with N rows.
- *  sf_type  MM_SF_E8M0 (int8 tensors included). MM_SF_E4M3FN (the page's FP4
- *           with sf_vec_size 16) -> MM_ERR_UNSUPPORTED; other values ->
- *           MM_ERR_INVALID_ARGUMENT.
+ *  sf_type  MM_SF_E8M0 (int8 tensors included), or MM_SF_E4M3FN with FP4
+ *           operands and sf_vec_size 16, the one combination the page allows
+ *           for E4M3 factors (others -> MM_ERR_UNSUPPORTED); other values ->
+ *           MM_ERR_INVALID_ARGUMENT. An E4M3 factor is any E4M3 value (signed,
+ *           subnormal, NaN codes give NaN).
  *  c_type   F32, BF16 or F16; with FP4 operands also MM_F8_E4M3FN or
  *           MM_F8_E5M2 (rounded to nearest even, saturating, as
  *           mm_scaled_gemm's FP8 outputs with scale_result 1). FP8 C with FP8
@@ -312,7 +314,9 @@ mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L,
  * and errors) is as mm_blockscaled_gemm_amax; in addition each batch item's
  * factor tensor must stay below 2^31 bytes (else MM_ERR_UNSUPPORTED). Every
  * E2M1 value times a factor 2^e is a bf16 value for e <= 125, so FP4 operands
- * are converted exactly with every E8M0 factor but 2^126 and 2^127.
+ * are converted exactly with every E8M0 factor but 2^126 and 2^127; times an
+ * E4M3 factor it is an f16 value (those operands are contracted in f16), so
+ * E4M3 factors are exact throughout.
  */
 mm_status mm_blockscaled_gemm_amax_atom(int64_t M, int64_t N, int64_t K, int64_t L,
                                         const void* a, const void* b, int ab_type,

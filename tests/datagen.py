@@ -247,3 +247,20 @@ def workload_grouped(G=8, batch_sum=8192, N=4096, K=4096, empty=0, config=9):
     a = gauss_codes(rng(config, 0), (batch_sum, K), 64.0)
     b = gauss_codes(rng(config, 1), (G, N, K), 64.0)
     return dict(a=a, b=b, sizes=sizes, offsets=offsets, K=K, scale_a=np.float32(0.5), scale_b=np.float32(0.25))
+
+
+def e4m3_atom_codes(g, MN, K, L, sf=16):
+    """E4M3 scale-factor codes for every byte of the page's scale tensor (storage shape as e8m0_atom_codes):
+    positive normal values (1 + m/8) 2^(e-7), e ~ U{3..11}, m ~ U{0..7}, i.e. factors in [2^-4, 30]."""
+    shape = (L, -(-MN // 128), -(-K // (4 * sf)), 32, 4, 4)
+    e = g.integers(3, 12, size=shape)
+    m = g.integers(0, 8, size=shape)
+    return ((e << 3) | m).astype(np.uint8)
+
+
+def workload_nvfp4(L=8, M=2048, N=2048, K=8192, config=11):
+    """FP4 operands (uniform random bytes) with E4M3 factors per 16 values in the page's layout."""
+    a = rng(config, 0).integers(0, 256, size=(L, M, K // 2), dtype=np.uint8)
+    b = rng(config, 1).integers(0, 256, size=(L, N, K // 2), dtype=np.uint8)
+    return dict(a=a, b=b, ab_fmt=5, sfa=e4m3_atom_codes(rng(config, 2), M, K, L),
+                sfb=e4m3_atom_codes(rng(config, 3), N, K, L), sf_vec=16, K=K)

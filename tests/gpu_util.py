@@ -63,7 +63,8 @@ def blockscaled_gemm_amax(a, b, fmt, sfa, sfb, c_type, with_amax=True, with_inde
             int(tix.item()) if with_index else None)
 
 
-def blockscaled_gemm_amax_atom(a, b, fmt, sfa, sfb, c_type, with_amax=True, with_index=True, sf=32):
+def blockscaled_gemm_amax_atom(a, b, fmt, sfa, sfb, c_type, with_amax=True, with_index=True, sf=32,
+                               sf_type=None):
     """As blockscaled_gemm_amax with E8M0 scale bytes in the page's storage shape (fmt 5: FP4 pairs)."""
     L, M, K = a.shape
     N = b.shape[1]
@@ -75,7 +76,8 @@ def blockscaled_gemm_amax_atom(a, b, fmt, sfa, sfb, c_type, with_amax=True, with
     tam = torch.full((1,), 123.0, dtype=torch.float32, device=DEV)
     tix = torch.full((1,), 777, dtype=torch.int64, device=DEV)
     st = mm.mm_blockscaled_gemm_amax_atom(M, N, K, L, ta.data_ptr(), tb.data_ptr(), fmt, tsa.data_ptr(),
-                                          tsb.data_ptr(), mm.MM_SF_E8M0, sf, tc.data_ptr(), c_type,
+                                          tsb.data_ptr(), mm.MM_SF_E8M0 if sf_type is None else sf_type, sf,
+                                          tc.data_ptr(), c_type,
                                           tam.data_ptr() if with_amax else 0, tix.data_ptr() if with_index else 0,
                                           stream())
     assert st == mm.MM_OK, (st, mm.mm_last_error())

@@ -210,7 +210,8 @@ def atom_call(**kw):
 
 
 @pytest.mark.parametrize("kw,status,msg", [
-    (dict(sf_type=mm.MM_SF_E4M3FN), mm.MM_ERR_UNSUPPORTED, "E4M3 scale factors"),
+    (dict(sf_type=mm.MM_SF_E4M3FN), mm.MM_ERR_UNSUPPORTED, "E4M3 scale factors"),  # FP8 operands
+    (dict(sf_type=mm.MM_SF_E4M3FN, ab_type=mm.MM_F4_E2M1), mm.MM_ERR_UNSUPPORTED, "sf_vec_size 16"),
     (dict(sf_type=5), mm.MM_ERR_INVALID_ARGUMENT, "unknown sf_type"),
     (dict(L=-1), mm.MM_ERR_INVALID_ARGUMENT, "must be >= 0"),
     (dict(ab_type=2), mm.MM_ERR_INVALID_ARGUMENT, "ab_type"),
@@ -241,7 +242,8 @@ def test_fp4_needs_the_atom_entry():
 
 @pytest.mark.parametrize("kw", [dict(ab_type=mm.MM_F4_E2M1), dict(ab_type=mm.MM_F4_E2M1, sf_vec_size=16),
                                 dict(ab_type=mm.MM_F4_E2M1, c_type=mm.MM_F8_E4M3FN, K=32),
-                                dict(ab_type=mm.MM_F4_E2M1, c_type=mm.MM_F8_E5M2, sf_vec_size=16, K=4096)])
+                                dict(ab_type=mm.MM_F4_E2M1, c_type=mm.MM_F8_E5M2, sf_vec_size=16, K=4096),
+                                dict(ab_type=mm.MM_F4_E2M1, sf_type=mm.MM_SF_E4M3FN, sf_vec_size=16)])
 def test_fp4_calls_pass_validation(kw, monkeypatch):
     # a launch failure forced after validation shows the call was accepted
     monkeypatch.setenv("MM_TEST_FORCE_FAIL", "launch")

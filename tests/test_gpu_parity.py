@@ -394,6 +394,59 @@ def test_atom_workload4_full_size():
     assert amax == a2 and idx == i2
 
 
+# ------------------------------------------------------------------ FP4 with E4M3 factors per 16 (the page's NVFP4)
+
+def check_nvfp4_case(w, c_type, rows=None):
+    c, amax, idx = gu.blockscaled_gemm_amax_atom(w["a"], w["b"], 5, w["sfa"], w["sfb"], c_type, sf=16,
+                                                 sf_type=gu.mm.MM_SF_E4M3FN)
+    value, sabs, bits, _, _ = oracle.blockscaled_gemm_amax_atom(w["a"], w["b"], oracle.E2M1, w["sfa"], w["sfb"],
+                                                                oracle.SF_E4M3FN, 16, c_type, rows=rows)
+    cg = c if rows is None else c[:, rows]
+    compare.check(cg, value, sabs, bits, c_type, "fp4 gemm, E4M3 factors")
+    return c, amax, idx, value, sabs
+
+
+@pytest.mark.parametrize("L,M,N,K,c_type", [
+    (3, 200, 136, 1024, F32), (2, 96, 200, 512, BF16), (1, 130, 70, 992, F16), (2, 257, 129, 800, E4M3FN),
+    (1, 40, 48, 32, F32)])
+def test_nvfp4_against_oracle(L, M, N, K, c_type):
+    w = datagen.workload_nvfp4(L, M, N, K, config=30 + L)
+    c, amax, idx, value, sabs = check_nvfp4_case(w, c_type)
+    v = np.abs(value.reshape(-1))
+    assert abs(amax - v.max()) <= 2.0 ** -20 * sabs.reshape(-1)[np.argmax(v)]
+    if c_type == F32:
+        cf = np.abs(c.view(np.float32).astype(np.float64).reshape(-1))
+        assert amax == float(cf.max()) and idx == int(np.argmax(cf))
+
+
+def test_nvfp4_signed_subnormal_and_nan_factors():
+    L, M, N, K = 1, 72, 80, 256
+    w = datagen.workload_nvfp4(L, M, N, K, config=35)
+    g = np.random.default_rng(35)
+    codes = np.array([0x01, 0x07, 0x81, 0xB8, 0x7E, 0xFE], np.uint8)  # subnormals, negative, largest
+    w["sfa"] = w["sfa"].copy()
+    w["sfa"].reshape(-1)[g.choice(w["sfa"].size, 200, replace=False)] = g.choice(codes, 200)
+    w["sfb"] = w["sfb"].copy()
+    w["sfb"][0, 0, 0, 9, 0, 1] = 0x7F  # NaN factor: row 9, group 1 of B
+    c, amax, idx, value, sabs = check_nvfp4_case(w, F32)
+    cf = c.view(np.float32)
+    assert np.isnan(cf[0, :, 9]).all() and np.isnan(amax) and idx == 9
+
+
+@pytest.mark.parametrize("L", [2, 1], ids=["128x256", "128x128"])
+def test_nvfp4_production_tiles(L):
+    w = datagen.workload_nvfp4(L, 2048, 2048, 1024, config=36)
+    rows = sample_rows(2048, 4)
+    c, amax, idx, value, sabs = check_nvfp4_case(w, F32, rows=rows)
+    cf = np.abs(c.view(np.float32).reshape(-1))
+    assert amax == float(cf.max()) and idx == int(np.argmax(cf))
+
+
+def test_nvfp4_full_size():
+    w = datagen.workload_nvfp4()
+    check_nvfp4_case(w, F32, rows=sample_rows(2048, 4))
+
+
 # ------------------------------------------------------------------ grouped GEMM (GroupedGemmFwdOp, NT, FP8)
 
 def check_grouped(w, d_type, fast=False, scale_result=None, rows=None, fmt=(E4M3FN, E4M3FN)):
