@@ -58,8 +58,8 @@ MUTANTS = {
     "group_b_operand": ("b + g * stride_b, b_fmt", "b + (g / 2) * stride_b, b_fmt"),
     "group_a_rows": ("a + r0 * lda, a_fmt", "a + (r0 / 2) * lda, a_fmt"),
     "group_output_rows": ("value ? value + r0 * N : nullptr", "value ? value + (r0 / 2) * N : nullptr"),
-    "group_prefix_unchecked": ("if (sizes[g] < 0 || offsets[g] != next) return ORC_ERR_ARG;",
-                               "if (sizes[g] < 0) return ORC_ERR_ARG;"),
+    "group_row_count_unchecked": ("    if (next != batch_sum) return ORC_ERR_ARG;\n    const int width",
+                                  "    if (false) return ORC_ERR_ARG;\n    const int width"),
     "zero_chain_negative": ("double S = +0.0, T = 0.0;\n                    for (int64_t k = 0; k < K; ++k) {\n                        const double t = Am[k] * Bn[k];\n                        S += t;",
                             "double S = -0.0, T = 0.0;\n                    for (int64_t k = 0; k < K; ++k) {\n                        const double t = Am[k] * Bn[k];\n                        S += t;"),
 }
