@@ -78,7 +78,7 @@ def log(*a):
 
 
 def make_sets(M, torch, dev, datagen):
-    d = datagen.workload2_gauss(M, N, K)
+    d = datagen.set_gauss_n4096(M, N, K)
     a0 = torch.from_numpy(d["a"]).to(dev)
     b0 = torch.from_numpy(d["b"]).to(dev)
     sa = torch.tensor([d["scale_a"]], dtype=torch.float32, device=dev)
@@ -112,7 +112,7 @@ def cpu_baseline():
     threads = os.cpu_count() or 1
     flops, secs = 0.0, 0.0
     for M in MS:
-        d = datagen.workload2_gauss(M, N, K)
+        d = datagen.set_gauss_n4096(M, N, K)
         t = time.perf_counter()
         oracle.scaled_gemm(d["a"], 0, d["b"], 0, d["scale_a"], 0, d["scale_b"], 0, oracle.BF16,
                            accum=oracle.ACC_EXACT, threads=threads)
@@ -155,7 +155,7 @@ def run_other(name, steps, warmup):
     stream = torch.cuda.current_stream().cuda_stream
     t0 = time.time()
     if name in ("block", "block_bias"):
-        d = datagen.workload3()
+        d = datagen.set_block_scaled_4096x14336x4096()
         M, K = d["a"].shape; N = d["b"].shape[0]; L = 1
         a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
         sa = torch.from_numpy(d["scale_a"]).to(dev); sb = torch.from_numpy(d["scale_b"]).to(dev)
@@ -178,7 +178,7 @@ def run_other(name, steps, warmup):
                                               stream)
             scale_bytes = 4 * (sa.numel() + sb.numel()) + 2 * N
     elif name == "bmm":
-        d = datagen.workload_bmm()
+        d = datagen.set_bmm_l8_2048x2048x4096()
         L, M, K = d["a"].shape; N = d["b"].shape[1]
         a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
         sa = torch.tensor([float(d["scale_a"])], dtype=torch.float32, device=dev)
@@ -192,7 +192,7 @@ def run_other(name, steps, warmup):
                                              out.data_ptr(), mm.MM_BF16, N, M * N, 0, stream)
         scale_bytes = 8
     elif name == "mx_amax":
-        d = datagen.workload4()
+        d = datagen.set_mx_l8_2048x2048x8192()
         L, M, K = d["a"].shape; N = d["b"].shape[1]
         a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
         sfa = torch.from_numpy(d["sfa"]).to(dev); sfb = torch.from_numpy(d["sfb"]).to(dev)
@@ -207,7 +207,7 @@ def run_other(name, steps, warmup):
                                                amax.data_ptr(), idx.data_ptr(), stream)
         scale_bytes = 4 * (sfa.numel() + sfb.numel()) + 12
     elif name == "grouped":
-        d = datagen.workload_grouped()
+        d = datagen.set_grouped_8x8192x4096x4096()
         M, K = d["a"].shape; N = d["b"].shape[1]; L = 1; G = d["b"].shape[0]
         a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
         gs = torch.from_numpy(d["sizes"]).to(dev); go = torch.from_numpy(d["offsets"]).to(dev)
@@ -223,7 +223,7 @@ def run_other(name, steps, warmup):
         # every group's b is read: G N K bytes in place of N K
         scale_bytes = 8 + 8 * G + (G - 1) * N * K
     elif name in ("mx_atom", "mx_fp4", "mx_nvfp4"):
-        d = {"mx_atom": datagen.workload4_atom, "mx_fp4": datagen.workload_fp4, "mx_nvfp4": datagen.workload_nvfp4}[name]()
+        d = {"mx_atom": datagen.set_mx_atom_l8_2048x2048x8192, "mx_fp4": datagen.set_fp4_l8_2048x2048x8192, "mx_nvfp4": datagen.set_nvfp4_l8_2048x2048x8192}[name]()
         L, M, K = d["a"].shape; N = d["b"].shape[1]
         ab_type = mm.MM_F8_E4M3FN if name == "mx_atom" else mm.MM_F4_E2M1
         K = K if name == "mx_atom" else 2 * K
@@ -241,7 +241,7 @@ def run_other(name, steps, warmup):
                                                     mm.MM_F32, amax.data_ptr(), idx.data_ptr(), stream)
         scale_bytes = sfa.numel() + sfb.numel() + 12
     else:
-        d = datagen.workload5a() if name == "e4m3_out" else datagen.workload5b()
+        d = datagen.set_e4m3_out_8192x28672x8200() if name == "e4m3_out" else datagen.set_e5m2_f16_8192x28672x8200()
         M, K = d["a"].shape; N = d["b"].shape[0]; L = 1
         fa = mm.MM_F8_E4M3FN if name == "e4m3_out" else mm.MM_F8_E5M2
         a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)

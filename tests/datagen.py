@@ -1,30 +1,33 @@
-"""Seeded synthetic inputs for the FP8 scaled GEMM workloads.
+"""Seeded synthetic inputs for the FP8 scaled GEMM sets.
 
 This module is shared by the oracle tests, the GPU parity tests and the
 benchmark. It holds none of the GEMM's arithmetic: it draws random numbers
-(numpy PCG64, seed = 1000 * workload + stream, stream 0 = A, 1 = B,
-2 = scales, 3 = adversarial codes) and turns synthetic real values into FP8
-codes with torch's CPU float8 casts after clamping to the format's range.
+(numpy PCG64, seed = 1000 * set id + stream, stream 0 = A, 1 = B,
+2 = scales, 3 = adversarial codes; the set ids are fixed integers) and turns
+synthetic real values into FP8 codes with torch's CPU float8 casts after
+clamping to the format's range.
 
-Workloads (the shapes and value recipes of the pages' LLM-layer GEMMs; where
-the pages leave a value open, the recipe below is this repository's choice):
+Sets (the shapes and value recipes of the pages' LLM-layer GEMMs; where the
+pages leave a value open, the recipe below is this repository's choice):
 
- 1. 256^3, E4M3 from N(0,1)*64 clamped to +-448, per-tensor scales 0.5 / 0.25,
-    fast accumulation, fp32 output.
- 2. per-tensor E4M3, N = K = 4096, M in {16, 64, 256, 1024, 2048, 8192},
-    slow accumulation, bf16 output. Gaussian set: z ~ N(0,1) per tensor,
-    x = z * 240 / max|z|, scale = max|z| / 240. Adversarial set: i.i.d. codes
-    (25% +-448, 25% random-sign subnormals, 10% +-0, 40% uniform finite codes)
-    with structured rows, scales 1.
- 3. M = 4096, N = 14336, K = 4096, E4M3 from N(0,1)*64, scale_a per 1x128
-    [M, K/128], scale_b per 128x128 [N/128, K/128], fp32 values 2^u with
-    u ~ U(-8, 4) (log-uniform in [2^-8, 2^4]), bf16 output.
- 4. L = 8, M = N = 2048, K = 8192, E4M3 from N(0,1)*64, power-of-two scale
-    factors 2^e, e ~ U{-8..4}, per 32 K elements per row; fp32 C and amax.
- 5. M = 8192, N = 28672, K = 8200; (a) E4M3 from N(0,1)*32 with 1% outliers at
-    +-448, scales 2^-3, scale_result 1/16, E4M3 output, slow accumulation;
-    (b) E5M2 from N(0,1)*32 with 1% outliers at +-57344, scales 2^-10, f16
-    output, slow accumulation.
+ - 256^3 (set id 1): E4M3 from N(0,1)*64 clamped to +-448, per-tensor scales
+   0.5 / 0.25, fast accumulation, fp32 output.
+ - per-tensor, N = K = 4096 (set id 2), M in {16, 64, 256, 1024, 2048, 8192},
+   slow accumulation, bf16 output. Gaussian set: z ~ N(0,1) per tensor,
+   x = z * 240 / max|z|, scale = max|z| / 240. Adversarial set: i.i.d. codes
+   (25% +-448, 25% random-sign subnormals, 10% +-0, 40% uniform finite codes)
+   with structured rows, scales 1.
+ - block-scaled 4096 x 14336 x 4096 (set id 3): E4M3 from N(0,1)*64, scale_a
+   per 1x128 [M, K/128], scale_b per 128x128 [N/128, K/128], fp32 values 2^u
+   with u ~ U(-8, 4) (log-uniform in [2^-8, 2^4]), bf16 output.
+ - MX, L = 8, 2048 x 2048 x 8192 (set id 4): E4M3 from N(0,1)*64, power-of-two
+   scale factors 2^e, e ~ U{-8..4}, per 32 K elements per row; fp32 C and amax.
+ - K tail, 8192 x 28672 x 8200 (set id 5): (a) E4M3 from N(0,1)*32 with 1%
+   outliers at +-448, scales 2^-3, scale_result 1/16, E4M3 output, slow
+   accumulation; (b) E5M2 from N(0,1)*32 with 1% outliers at +-57344, scales
+   2^-10, f16 output, slow accumulation.
+ - batched, page-native MX factors, FP4, grouped, FP4 with E4M3 factors: see
+   their functions below.
 """
 from __future__ import annotations
 
@@ -35,11 +38,11 @@ E4M3FN, E5M2 = 0, 1
 FMT_MAX = {E4M3FN: 448.0, E5M2: 57344.0}
 _TORCH_FP8 = {E4M3FN: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
 
-GEMM2_MS = (16, 64, 256, 1024, 2048, 8192)
+BENCH_MS = (16, 64, 256, 1024, 2048, 8192)
 
 
-def rng(workload: int, stream: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(1000 * workload + stream))
+def rng(set_id: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(1000 * set_id + stream))
 
 
 def to_codes(x: np.ndarray, fmt: int) -> np.ndarray:
@@ -94,14 +97,14 @@ def adversarial_codes(g: np.random.Generator, shape, fmt: int = E4M3FN) -> np.nd
     return out.reshape(shape)
 
 
-def adversarial_pair(M: int, N: int, K: int, workload: int = 2, fmt: int = E4M3FN):
+def adversarial_pair(M: int, N: int, K: int, set_id: int = 2, fmt: int = E4M3FN):
     """Adversarial A [M,K], B [N,K] with structured rows.
 
     Row 0 of A and of B is all +max; row 1 of A alternates +max / -max against
     B row 1 all +max (the sum cancels to 0); row 2 of A and B is all the
     smallest subnormal; row 3 of A is all -0.
     """
-    g = rng(workload, 3)
+    g = rng(set_id, 3)
     a = adversarial_codes(g, (M, K), fmt)
     b = adversarial_codes(g, (N, K), fmt)
     maxcode = 0x7E if fmt == E4M3FN else 0x7B
@@ -132,17 +135,17 @@ def pow2_scales(g: np.random.Generator, shape, lo: int = -8, hi: int = 4):
     return np.ldexp(np.ones(shape, dtype=np.float32), e).astype(np.float32)
 
 
-# ----------------------------------------------------------------- workloads
+# ----------------------------------------------------------------- sets
 
-def workload1(M=256, N=256, K=256):
+def set_256_cubed(M=256, N=256, K=256):
     a = gauss_codes(rng(1, 0), (M, K), 64.0)
     b = gauss_codes(rng(1, 1), (N, K), 64.0)
     return dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN,
                 scale_a=np.float32(0.5), scale_b=np.float32(0.25))
 
 
-def workload2_gauss(M: int, N: int = 4096, K: int = 4096, seed_offset: int = 0):
-    """Gaussian set of workload 2; seed_offset selects an independent copy."""
+def set_gauss_n4096(M: int, N: int = 4096, K: int = 4096, seed_offset: int = 0):
+    """Per-tensor Gaussian set (M x 4096 x 4096 by default); seed_offset selects an independent copy."""
     ga = rng(2, 0 + 10 * seed_offset)
     gb = rng(2, 1 + 10 * seed_offset)
     a, sa = normalized_codes(ga, (M, K))
@@ -150,13 +153,13 @@ def workload2_gauss(M: int, N: int = 4096, K: int = 4096, seed_offset: int = 0):
     return dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN, scale_a=sa, scale_b=sb)
 
 
-def workload2_adversarial(M: int, N: int = 4096, K: int = 4096):
+def set_adversarial_n4096(M: int, N: int = 4096, K: int = 4096):
     a, b = adversarial_pair(M, N, K, 2)
     return dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN,
                 scale_a=np.float32(1.0), scale_b=np.float32(1.0))
 
 
-def workload3(M=4096, N=14336, K=4096):
+def set_block_scaled_4096x14336x4096(M=4096, N=14336, K=4096):
     a = gauss_codes(rng(3, 0), (M, K), 64.0)
     b = gauss_codes(rng(3, 1), (N, K), 64.0)
     kb = -(-K // 128)
@@ -166,7 +169,7 @@ def workload3(M=4096, N=14336, K=4096):
     return dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN, scale_a=sa, scale_b=sb)
 
 
-def workload4(L=8, M=2048, N=2048, K=8192, sf=32):
+def set_mx_l8_2048x2048x8192(L=8, M=2048, N=2048, K=8192, sf=32):
     a = gauss_codes(rng(4, 0), (L, M, K), 64.0)
     b = gauss_codes(rng(4, 1), (L, N, K), 64.0)
     ks = -(-K // sf)
@@ -176,7 +179,7 @@ def workload4(L=8, M=2048, N=2048, K=8192, sf=32):
     return dict(a=a, b=b, ab_fmt=E4M3FN, sfa=sfa, sfb=sfb, sf_vec=sf)
 
 
-def workload5a(M=8192, N=28672, K=8200):
+def set_e4m3_out_8192x28672x8200(M=8192, N=28672, K=8200):
     a = gauss_codes(rng(5, 0), (M, K), 32.0, E4M3FN, 0.01)
     b = gauss_codes(rng(5, 1), (N, K), 32.0, E4M3FN, 0.01)
     return dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN,
@@ -184,15 +187,15 @@ def workload5a(M=8192, N=28672, K=8200):
                 scale_result=np.float32(1.0 / 16))
 
 
-def workload5b(M=8192, N=28672, K=8200):
+def set_e5m2_f16_8192x28672x8200(M=8192, N=28672, K=8200):
     a = gauss_codes(rng(6, 0), (M, K), 32.0, E5M2, 0.01)
     b = gauss_codes(rng(6, 1), (N, K), 32.0, E5M2, 0.01)
     return dict(a=a, b=b, K=K, a_fmt=E5M2, b_fmt=E5M2,
                 scale_a=np.float32(2.0 ** -10), scale_b=np.float32(2.0 ** -10))
 
 
-def workload_bmm(L=8, M=2048, N=2048, K=4096):
-    """Batched per-tensor set (TileOPs BmmFP8FwdOp): Gaussian codes as workload 3, one scale per operand."""
+def set_bmm_l8_2048x2048x4096(L=8, M=2048, N=2048, K=4096):
+    """Batched per-tensor set (TileOPs BmmFP8FwdOp): Gaussian codes as the block-scaled set, one scale per operand."""
     a = gauss_codes(rng(7, 0), (L, M, K), 64.0)
     b = gauss_codes(rng(7, 1), (L, N, K), 64.0)
     return dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN,
@@ -212,15 +215,16 @@ def e8m0_atom_codes(g, MN, K, L, sf=32, lo=-8, hi=4):
     return (127 + g.integers(lo, hi + 1, size=shape)).astype(np.uint8)
 
 
-def workload4_atom(L=8, M=2048, N=2048, K=8192):
-    """Workload 4 with the page's own scale format: the same codes, E8M0 factors in the atom layout."""
+def set_mx_atom_l8_2048x2048x8192(L=8, M=2048, N=2048, K=8192):
+    """The MX set (L=8, 2048 x 2048 x 8192) with the page's own scale format: the same codes, E8M0 factors in
+    the atom layout."""
     a = gauss_codes(rng(4, 0), (L, M, K), 64.0)
     b = gauss_codes(rng(4, 1), (L, N, K), 64.0)
     return dict(a=a, b=b, ab_fmt=E4M3FN, sfa=e8m0_atom_codes(rng(4, 5), M, K, L),
                 sfb=e8m0_atom_codes(rng(4, 6), N, K, L), sf_vec=32)
 
 
-def workload_fp4(L=8, M=2048, N=2048, K=8192, sf=32, config=8):
+def set_fp4_l8_2048x2048x8192(L=8, M=2048, N=2048, K=8192, sf=32, config=8):
     """FP4 set: uniform random bytes (each two E2M1 codes, all 16 codes equally likely) as a
     [L, M, K/2] and b [L, N, K/2]; E8M0 factors 2^U{-8..4} in the page's storage shape."""
     a = rng(config, 0).integers(0, 256, size=(L, M, K // 2), dtype=np.uint8)
@@ -239,9 +243,9 @@ def group_sizes(g, G, batch_sum, empty=0):
     return g.multinomial(batch_sum, p).astype(np.int32)
 
 
-def workload_grouped(G=8, batch_sum=8192, N=4096, K=4096, empty=0, config=9):
+def set_grouped_8x8192x4096x4096(G=8, batch_sum=8192, N=4096, K=4096, empty=0, config=9):
     """Grouped set (TileOPs GroupedGemmFwdOp, NT): a [batch_sum, K] and b [G, N, K] Gaussian codes as
-    workload 3, ragged group sizes, one scale per operand."""
+    the block-scaled set, ragged group sizes, one scale per operand."""
     sizes = group_sizes(rng(config, 3), G, batch_sum, empty)
     offsets = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.int32)
     a = gauss_codes(rng(config, 0), (batch_sum, K), 64.0)
@@ -258,7 +262,7 @@ def e4m3_atom_codes(g, MN, K, L, sf=16):
     return ((e << 3) | m).astype(np.uint8)
 
 
-def workload_nvfp4(L=8, M=2048, N=2048, K=8192, config=11):
+def set_nvfp4_l8_2048x2048x8192(L=8, M=2048, N=2048, K=8192, config=11):
     """FP4 operands (uniform random bytes) with E4M3 factors per 16 values in the page's layout."""
     a = rng(config, 0).integers(0, 256, size=(L, M, K // 2), dtype=np.uint8)
     b = rng(config, 1).integers(0, 256, size=(L, N, K // 2), dtype=np.uint8)

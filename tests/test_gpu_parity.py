@@ -68,7 +68,7 @@ def test_epilogue_conversion_bit_exact(dtype):
 
 
 def test_adversarial_structured_rows_bit_exact():
-    d = datagen.workload2_adversarial(64, 4096, 4096)
+    d = datagen.set_adversarial_n4096(64, 4096, 4096)
     gpu = gu.scaled_gemm(d["a"], 0, d["b"], 0, 4096, 1.0, 0, 1.0, 0, BF16, fast=False)
     _, _, bits = oracle.scaled_gemm(d["a"], 0, d["b"], 0, np.float32(1), 0, np.float32(1), 0, BF16, rows=[0, 1, 2, 3])
     assert gpu[0, 0] == bits[0, 0] and gpu[0, 0] != 0          # K * 448^2, exact in bf16
@@ -77,33 +77,33 @@ def test_adversarial_structured_rows_bit_exact():
     assert np.all(gpu[3] == 0x0000)                            # all -0 codes: +0 everywhere
 
 
-# ------------------------------------------------------------------ workload 1
+# ------------------------------------------------------------------ 256 x 256 x 256, scales 0.5 / 0.25, f32 out
 
 @pytest.mark.parametrize("fast", [True, False])
-def test_workload1_256_cubed(fast):
-    d = datagen.workload1()
+def test_gemm_256_cubed(fast):
+    d = datagen.set_256_cubed()
     check_gemm(d, 0, 0, F32, fast, what="256^3")
 
 
-# ------------------------------------------------------------------ workload 2 (the benchmark shapes)
+# ------------------------------------------------------------------ per-tensor, N = K = 4096, M = 16 .. 8192 (the benchmark shapes)
 
-@pytest.mark.parametrize("M", datagen.GEMM2_MS)
-def test_workload2_gauss_full_size(M):
-    d = datagen.workload2_gauss(M)
+@pytest.mark.parametrize("M", datagen.BENCH_MS)
+def test_gauss_n4096_full_size(M):
+    d = datagen.set_gauss_n4096(M)
     rows = None if M <= 64 else sample_rows(M)
-    check_gemm(d, 0, 0, BF16, fast=False, rows=rows, what=f"workload2 gauss M={M}")
+    check_gemm(d, 0, 0, BF16, fast=False, rows=rows, what=f"gauss N=K=4096 M={M}")
 
 
 @pytest.mark.parametrize("M", [16, 64, 256, 2048])
-def test_workload2_adversarial_full_size(M):
-    d = datagen.workload2_adversarial(M)
+def test_adversarial_n4096_full_size(M):
+    d = datagen.set_adversarial_n4096(M)
     rows = None if M <= 64 else sample_rows(M)
-    check_gemm(d, 0, 0, BF16, fast=False, rows=rows, what=f"workload2 adversarial M={M}")
+    check_gemm(d, 0, 0, BF16, fast=False, rows=rows, what=f"adversarial N=K=4096 M={M}")
 
 
 @pytest.mark.parametrize("M", [16, 2048])
-def test_workload2_fast_accumulation(M):
-    d = datagen.workload2_gauss(M)
+def test_gauss_n4096_fast_accumulation(M):
+    d = datagen.set_gauss_n4096(M)
     check_gemm(d, 0, 0, BF16, fast=True, rows=None if M <= 64 else sample_rows(M), what=f"fast M={M}")
 
 
@@ -139,7 +139,7 @@ def test_zero_k_gives_scaled_zero():
 
 
 def test_nan_and_inf_inputs():
-    d = datagen.workload1(64, 80, 384)
+    d = datagen.set_256_cubed(64, 80, 384)
     a = d["a"].copy(); b = d["b"].copy()
     a[5, 17] = 0x7F                          # E4M3 NaN code: row 5 is NaN everywhere
     b_e5 = datagen.gauss_codes(np.random.default_rng(3), (80, 384), 4.0, E5M2)
@@ -198,7 +198,7 @@ def test_production_tiles_block_scaled(M, sb_mode):
     check_gemm(d, 1, sb_mode, BF16, False, rows=sample_rows(M, 8), what=f"block {M}x{N}x{K} sb={sb_mode}")
 
 
-# ------------------------------------------------------------------ workload 3: block scales
+# ------------------------------------------------------------------ block scales: 1x128 / 128x128, 4096 x 14336 x 4096
 
 @pytest.mark.parametrize("sb_mode", [1, 2], ids=["1x128", "128x128"])
 @pytest.mark.parametrize("M,N,K", [(300, 400, 1000), (64, 256, 512), (260, 130, 4096)])
@@ -215,12 +215,12 @@ def test_block_scales_small(M, N, K, sb_mode):
         check_gemm(d, 1, sb_mode, dt, False, what=f"block {M}x{N}x{K} sb={sb_mode} {DT_NAME[dt]}")
 
 
-def test_workload3_full_size():
-    d = datagen.workload3()
-    check_gemm(d, 1, 2, BF16, False, rows=sample_rows(4096, 8), what="workload3 4096x14336x4096")
+def test_block_scaled_full_size():
+    d = datagen.set_block_scaled_4096x14336x4096()
+    check_gemm(d, 1, 2, BF16, False, rows=sample_rows(4096, 8), what="block-scaled 4096x14336x4096")
 
 
-# ------------------------------------------------------------------ workload 4: sf32 + amax
+# ------------------------------------------------------------------ MX factors per 32 + amax: L = 8, 2048 x 2048 x 8192
 
 def check_amax_case(w, c_type, rows=None):
     c, amax, idx = gu.blockscaled_gemm_amax(w["a"], w["b"], w["ab_fmt"], w["sfa"], w["sfb"], c_type)
@@ -232,7 +232,7 @@ def check_amax_case(w, c_type, rows=None):
 
 
 def test_sf32_amax_small_with_oracle():
-    w = datagen.workload4(3, 200, 136, 1024)
+    w = datagen.set_mx_l8_2048x2048x8192(3, 200, 136, 1024)
     c, amax, idx, value, sabs = check_amax_case(w, F32)
     cf = c.view(np.float32).astype(np.float64).reshape(-1)
     # amax and its index are bit-exact against the GPU's own C
@@ -244,7 +244,7 @@ def test_sf32_amax_small_with_oracle():
 
 @pytest.mark.parametrize("c_type", [BF16, F16])
 def test_sf32_low_precision_outputs(c_type):
-    w = datagen.workload4(2, 96, 200, 512)
+    w = datagen.set_mx_l8_2048x2048x8192(2, 96, 200, 512)
     c, amax, idx, value, sabs = check_amax_case(w, c_type)
     # amax is taken before the cast: within the fp32 bound of the oracle's max |C|
     v = np.abs(value.reshape(-1))
@@ -252,7 +252,7 @@ def test_sf32_low_precision_outputs(c_type):
 
 
 def test_sf32_batch_equals_separate_calls():
-    w = datagen.workload4(3, 72, 80, 256)
+    w = datagen.set_mx_l8_2048x2048x8192(3, 72, 80, 256)
     c, amax, idx = gu.blockscaled_gemm_amax(w["a"], w["b"], 0, w["sfa"], w["sfb"], F32)
     best = None
     for l in range(3):
@@ -265,7 +265,7 @@ def test_sf32_batch_equals_separate_calls():
 
 
 def test_sf32_nan_and_empty():
-    w = datagen.workload4(2, 40, 48, 128)
+    w = datagen.set_mx_l8_2048x2048x8192(2, 40, 48, 128)
     a = w["a"].copy(); a[1, 7, 3] = 0x7F
     c, amax, idx = gu.blockscaled_gemm_amax(a, w["b"], 0, w["sfa"], w["sfb"], F32)
     assert np.isnan(amax) and idx == 1 * 40 * 48 + 7 * 48 + 0
@@ -276,7 +276,7 @@ def test_sf32_nan_and_empty():
 
 
 def test_sf32_amax_without_index():
-    w = datagen.workload4(2, 100, 60, 256)
+    w = datagen.set_mx_l8_2048x2048x8192(2, 100, 60, 256)
     c, amax, _ = gu.blockscaled_gemm_amax(w["a"], w["b"], 0, w["sfa"], w["sfb"], F32, with_index=False)
     assert amax == float(np.max(np.abs(c.view(np.float32))))
 
@@ -294,15 +294,15 @@ def test_sf32_e5m2_unit_scales_is_plain_gemm():
 def test_production_tiles_sf32(L):
     """MX-scaled GEMM + amax at sizes that select the 128x256 and the
     (pipelined) 128x128 tile; the full-size workload below selects 256x256."""
-    w = datagen.workload4(L, 2048, 2048, 1040)
+    w = datagen.set_mx_l8_2048x2048x8192(L, 2048, 2048, 1040)
     rows = sample_rows(2048, 4)
     c, amax, idx, value, sabs = check_amax_case(w, F32, rows=rows)
     cf = np.abs(c.view(np.float32).reshape(-1))
     assert amax == float(cf.max()) and idx == int(np.argmax(cf))
 
 
-def test_workload4_full_size():
-    w = datagen.workload4()
+def test_mx_full_size():
+    w = datagen.set_mx_l8_2048x2048x8192()
     rows = sample_rows(2048, 4)
     c, amax, idx, value, sabs = check_amax_case(w, F32, rows=rows)
     cf = np.abs(c.view(np.float32).reshape(-1))
@@ -332,7 +332,7 @@ def atom_padding_mask(MN, K, L, sf=32):
 @pytest.mark.parametrize("L,M,N,K,c_type", [(3, 200, 136, 1024, F32), (2, 96, 200, 512, BF16),
                                             (1, 130, 70, 1008, F16), (2, 257, 129, 96, F32)])
 def test_atom_against_oracle(L, M, N, K, c_type):
-    w = datagen.workload4_atom(L, M, N, K)
+    w = datagen.set_mx_atom_l8_2048x2048x8192(L, M, N, K)
     c, amax, idx, value, sabs = check_atom_case(w, c_type)
     v = np.abs(value.reshape(-1))
     assert abs(amax - v.max()) <= 2.0 ** -20 * sabs.reshape(-1)[np.argmax(v)]
@@ -346,7 +346,7 @@ def test_atom_against_oracle(L, M, N, K, c_type):
 def test_atom_equals_fp32_factor_entry(L, M, N, K):
     """The same factors as fp32 powers of two through mm_blockscaled_gemm_amax: bitwise the same C,
     amax and index (the two entries differ only in how the factors are read)."""
-    w = datagen.workload4_atom(L, M, N, K)
+    w = datagen.set_mx_atom_l8_2048x2048x8192(L, M, N, K)
     c1, a1, i1 = gu.blockscaled_gemm_amax_atom(w["a"], w["b"], 0, w["sfa"], w["sfb"], F32)
     fa = oracle.sf_atom_unpack(w["sfa"], oracle.SF_E8M0, M, K, L, 32)
     fb = oracle.sf_atom_unpack(w["sfb"], oracle.SF_E8M0, N, K, L, 32)
@@ -357,7 +357,7 @@ def test_atom_equals_fp32_factor_entry(L, M, N, K):
 
 def test_atom_padding_is_not_read():
     L, M, N, K = 2, 100, 72, 208  # 28 / 56 padding rows, group 7 of the second 4-group block unused
-    w = datagen.workload4_atom(L, M, N, K)
+    w = datagen.set_mx_atom_l8_2048x2048x8192(L, M, N, K)
     c1, a1, i1 = gu.blockscaled_gemm_amax_atom(w["a"], w["b"], 0, w["sfa"], w["sfb"], F32)
     sfa, sfb = w["sfa"].copy(), w["sfb"].copy()
     sfa[atom_padding_mask(M, K, L)] = 0xFF  # NaN factors
@@ -370,7 +370,7 @@ def test_atom_padding_is_not_read():
 
 def test_atom_nan_factor_poisons_one_row():
     L, M, N, K = 2, 72, 80, 256
-    w = datagen.workload4_atom(L, M, N, K)
+    w = datagen.set_mx_atom_l8_2048x2048x8192(L, M, N, K)
     # row 5, group 2 of item 1 (storage [l][m/128][g/4][m%32][(m/32)%4][g%4])
     w["sfa"][1, 0, 0, 5, 0, 2] = 0xFF
     c, amax, idx, value, sabs = check_atom_case(w, F32)
@@ -379,10 +379,10 @@ def test_atom_nan_factor_poisons_one_row():
     assert np.isnan(amax) and idx == 1 * M * N + 5 * N
 
 
-def test_atom_workload4_full_size():
-    """Workload 4 (L=8, 2048 x 2048 x 8192) with E8M0 atom factors, on the 256x256 tile: sampled rows
+def test_atom_mx_full_size():
+    """The MX set (L=8, 2048 x 2048 x 8192) with E8M0 atom factors, on the 256x256 tile: sampled rows
     against the oracle, the whole C bitwise against the fp32-factor entry."""
-    w = datagen.workload4_atom()
+    w = datagen.set_mx_atom_l8_2048x2048x8192()
     rows = sample_rows(2048, 4)
     c, amax, idx, value, sabs = check_atom_case(w, F32, rows=rows)
     cf = np.abs(c.view(np.float32).reshape(-1))
@@ -410,7 +410,7 @@ def check_nvfp4_case(w, c_type, rows=None):
     (3, 200, 136, 1024, F32), (2, 96, 200, 512, BF16), (1, 130, 70, 992, F16), (2, 257, 129, 800, E4M3FN),
     (1, 40, 48, 32, F32)])
 def test_nvfp4_against_oracle(L, M, N, K, c_type):
-    w = datagen.workload_nvfp4(L, M, N, K, config=30 + L)
+    w = datagen.set_nvfp4_l8_2048x2048x8192(L, M, N, K, config=30 + L)
     c, amax, idx, value, sabs = check_nvfp4_case(w, c_type)
     v = np.abs(value.reshape(-1))
     assert abs(amax - v.max()) <= 2.0 ** -20 * sabs.reshape(-1)[np.argmax(v)]
@@ -421,7 +421,7 @@ def test_nvfp4_against_oracle(L, M, N, K, c_type):
 
 def test_nvfp4_signed_subnormal_and_nan_factors():
     L, M, N, K = 1, 72, 80, 256
-    w = datagen.workload_nvfp4(L, M, N, K, config=35)
+    w = datagen.set_nvfp4_l8_2048x2048x8192(L, M, N, K, config=35)
     g = np.random.default_rng(35)
     codes = np.array([0x01, 0x07, 0x81, 0xB8, 0x7E, 0xFE], np.uint8)  # subnormals, negative, largest
     w["sfa"] = w["sfa"].copy()
@@ -435,7 +435,7 @@ def test_nvfp4_signed_subnormal_and_nan_factors():
 
 @pytest.mark.parametrize("L", [2, 1], ids=["128x256", "128x128"])
 def test_nvfp4_production_tiles(L):
-    w = datagen.workload_nvfp4(L, 2048, 2048, 1024, config=36)
+    w = datagen.set_nvfp4_l8_2048x2048x8192(L, 2048, 2048, 1024, config=36)
     rows = sample_rows(2048, 4)
     c, amax, idx, value, sabs = check_nvfp4_case(w, F32, rows=rows)
     cf = np.abs(c.view(np.float32).reshape(-1))
@@ -443,7 +443,7 @@ def test_nvfp4_production_tiles(L):
 
 
 def test_nvfp4_full_size():
-    w = datagen.workload_nvfp4()
+    w = datagen.set_nvfp4_l8_2048x2048x8192()
     check_nvfp4_case(w, F32, rows=sample_rows(2048, 4))
 
 
@@ -467,14 +467,14 @@ def check_grouped(w, d_type, fast=False, scale_result=None, rows=None, fmt=(E4M3
     (8, 8192, 2048, 512, 0, True, E4M3FN),  # 128x128 tiles, two per CU; FP8 out
 ])
 def test_grouped_against_oracle(G, batch_sum, N, K, empty, fast, d_type):
-    w = datagen.workload_grouped(G, batch_sum, N, K, empty, config=10 + G)
+    w = datagen.set_grouped_8x8192x4096x4096(G, batch_sum, N, K, empty, config=10 + G)
     sr = 1.0 / 16 if d_type == E4M3FN else None
     rows = None if batch_sum <= 1500 else sample_rows(batch_sum, 16, seed=G)
     check_grouped(w, d_type, fast=fast, scale_result=sr, rows=rows)
 
 
 def test_grouped_e5m2_and_single_group():
-    w = datagen.workload_grouped(1, 257, 96, 384, 0, config=21)
+    w = datagen.set_grouped_8x8192x4096x4096(1, 257, 96, 384, 0, config=21)
     w["a"] = datagen.gauss_codes(datagen.rng(21, 4), w["a"].shape, 64.0, E5M2)
     check_grouped(w, F32, fmt=(E5M2, E4M3FN))
 
@@ -482,7 +482,7 @@ def test_grouped_e5m2_and_single_group():
 def test_grouped_rows_of_no_group_are_not_written():
     # sizes that cover only part of the rows (the page makes this the caller's error): the covered rows are
     # right and the others keep their previous contents
-    w = datagen.workload_grouped(4, 400, 72, 256, 0, config=22)
+    w = datagen.set_grouped_8x8192x4096x4096(4, 400, 72, 256, 0, config=22)
     w["sizes"] = np.array([50, 0, 30, 100], np.int32)
     w["offsets"] = np.array([0, 60, 60, 250], np.int32)
     gpu = gu.scaled_gemm_grouped(w["a"], E4M3FN, w["b"], E4M3FN, w["sizes"], w["offsets"], w["scale_a"],
@@ -501,7 +501,7 @@ def test_grouped_rows_of_no_group_are_not_written():
 
 def test_grouped_full_size():
     """The grouped bench workload: 8 groups, 8192 packed rows, N = K = 4096, slow, bf16 out; sampled rows."""
-    w = datagen.workload_grouped()
+    w = datagen.set_grouped_8x8192x4096x4096()
     check_grouped(w, BF16, rows=sample_rows(8192, 16, seed=3))
 
 
@@ -521,7 +521,7 @@ def check_fp4_case(w, c_type, rows=None):
     (2, 257, 129, 800, 32, F32),  # the last step's second factor block lies past the tensor's
     (1, 100, 72, 256, 32, E4M3FN), (2, 64, 96, 1056, 16, E5M2), (1, 40, 48, 32, 16, F32)])
 def test_fp4_against_oracle(L, M, N, K, sf, c_type):
-    w = datagen.workload_fp4(L, M, N, K, sf)
+    w = datagen.set_fp4_l8_2048x2048x8192(L, M, N, K, sf)
     c, amax, idx, value, sabs = check_fp4_case(w, c_type)
     v = np.abs(value.reshape(-1))
     assert abs(amax - v.max()) <= 2.0 ** -20 * sabs.reshape(-1)[np.argmax(v)]
@@ -532,7 +532,7 @@ def test_fp4_against_oracle(L, M, N, K, sf, c_type):
 
 @pytest.mark.parametrize("L,sf", [(2, 32), (1, 16)], ids=["128x256", "128x128"])
 def test_fp4_production_tiles(L, sf):
-    w = datagen.workload_fp4(L, 2048, 2048, 1024, sf)
+    w = datagen.set_fp4_l8_2048x2048x8192(L, 2048, 2048, 1024, sf)
     rows = sample_rows(2048, 4)
     c, amax, idx, value, sabs = check_fp4_case(w, F32, rows=rows)
     cf = np.abs(c.view(np.float32).reshape(-1))
@@ -541,7 +541,7 @@ def test_fp4_production_tiles(L, sf):
 
 def test_fp4_padding_is_not_read():
     L, M, N, K, sf = 2, 100, 72, 224, 16  # 14 groups: two unused in the last 4-group block
-    w = datagen.workload_fp4(L, M, N, K, sf)
+    w = datagen.set_fp4_l8_2048x2048x8192(L, M, N, K, sf)
     c1, a1, i1 = gu.blockscaled_gemm_amax_atom(w["a"], w["b"], 5, w["sfa"], w["sfb"], F32, sf=sf)
     sfa, sfb = w["sfa"].copy(), w["sfb"].copy()
     sfa[atom_padding_mask(M, K, L, sf)] = 0xFF
@@ -553,36 +553,36 @@ def test_fp4_padding_is_not_read():
 
 def test_fp4_full_size():
     """L=8, 2048 x 2048 x 8192 FP4 with factors per 32 (the FP4 bench workload): sampled rows."""
-    w = datagen.workload_fp4()
+    w = datagen.set_fp4_l8_2048x2048x8192()
     rows = sample_rows(2048, 4)
     c, amax, idx, value, sabs = check_fp4_case(w, F32, rows=rows)
     cf = np.abs(c.view(np.float32).reshape(-1))
     assert amax == float(cf.max()) and idx == int(np.argmax(cf))
 
 
-# ------------------------------------------------------------------ workload 5: K tail, FP8 / f16 out
+# ------------------------------------------------------------------ K tail (K = 8200), FP8 / f16 out: 8192 x 28672 x 8200
 
-def test_workload5_small():
-    for d, dt, sr in ((datagen.workload5a(200, 300, 8200), E4M3FN, np.float32(1 / 16)),
-                      (datagen.workload5b(200, 300, 8200), F16, None)):
-        check_gemm(d, 0, 0, dt, False, scale_result=sr, what=f"workload5 small {DT_NAME[dt]}")
+def test_k_tail_small():
+    for d, dt, sr in ((datagen.set_e4m3_out_8192x28672x8200(200, 300, 8200), E4M3FN, np.float32(1 / 16)),
+                      (datagen.set_e5m2_f16_8192x28672x8200(200, 300, 8200), F16, None)):
+        check_gemm(d, 0, 0, dt, False, scale_result=sr, what=f"K tail small {DT_NAME[dt]}")
 
 
-def test_workload5a_saturation_edge():
-    d = datagen.workload5a(96, 160, 8200)
+def test_e4m3_out_saturation_edge():
+    d = datagen.set_e4m3_out_8192x28672x8200(96, 160, 8200)
     d["scale_a"] = np.float32(1.0); d["scale_b"] = np.float32(1.0)
     _, gpu, value, _ = check_gemm(d, 0, 0, E4M3FN, False, scale_result=np.float32(1 / 16), what="saturation")
     assert np.mean((gpu & 0x7F) == 0x7E) > 0.9       # almost every output saturates
 
 
 @pytest.mark.parametrize("which", ["5a", "5b"])
-def test_workload5_full_size(which):
+def test_k_tail_full_size(which):
     if which == "5a":
-        d, dt, sr = datagen.workload5a(), E4M3FN, np.float32(1 / 16)
+        d, dt, sr = datagen.set_e4m3_out_8192x28672x8200(), E4M3FN, np.float32(1 / 16)
     else:
-        d, dt, sr = datagen.workload5b(), F16, None
+        d, dt, sr = datagen.set_e5m2_f16_8192x28672x8200(), F16, None
     rows = np.array([0, 1, 2, 4095, 8190, 8191])
-    check_gemm(d, 0, 0, dt, False, rows=rows, scale_result=sr, what=f"workload5{which} full size")
+    check_gemm(d, 0, 0, dt, False, rows=rows, scale_result=sr, what=f"K tail 8192x28672x8200 ({which}) full size")
 
 
 # ------------------------------------------------------------------ bias (TileOPs GemmFP8FwdOp, forward)

@@ -95,7 +95,7 @@ def test_sum_abs_is_sum_of_term_magnitudes():
 def test_e4m3_exact_equals_numpy_matmul(M, N, K):
     """Every partial sum of E4M3 products is exact in float64, so any summation
     order (BLAS's included) gives the same bits."""
-    d = datagen.workload1(M, N, K)
+    d = datagen.set_256_cubed(M, N, K)
     value, _, _ = oracle.scaled_gemm(d["a"], E4M3FN, d["b"], E4M3FN, d["scale_a"], 0, d["scale_b"], 0, F32)
     A, B = tdecode(d["a"], E4M3FN), tdecode(d["b"], E4M3FN)
     want = (A @ B.T) * np.float64(d["scale_a"]) * np.float64(d["scale_b"])
@@ -103,7 +103,7 @@ def test_e4m3_exact_equals_numpy_matmul(M, N, K):
 
 
 def test_output_bits_are_value_rounded_once():
-    d = datagen.workload1(16, 24, 512)
+    d = datagen.set_256_cubed(16, 24, 512)
     for dt in (F32, BF16, F16, E4M3FN, E5M2):
         value, _, bits = oracle.scaled_gemm(d["a"], E4M3FN, d["b"], E4M3FN, d["scale_a"], 0, d["scale_b"], 0, dt,
                                             scale_result=np.float32(0.01))
@@ -111,7 +111,7 @@ def test_output_bits_are_value_rounded_once():
 
 
 def test_scale_result_only_for_fp8_outputs():
-    d = datagen.workload1(8, 8, 256)
+    d = datagen.set_256_cubed(8, 8, 256)
     v32, _, _ = oracle.scaled_gemm(d["a"], 0, d["b"], 0, d["scale_a"], 0, d["scale_b"], 0, F32, scale_result=np.float32(0.0625))
     v8, _, _ = oracle.scaled_gemm(d["a"], 0, d["b"], 0, d["scale_a"], 0, d["scale_b"], 0, E4M3FN, scale_result=np.float32(0.0625))
     vn, _, _ = oracle.scaled_gemm(d["a"], 0, d["b"], 0, d["scale_a"], 0, d["scale_b"], 0, E4M3FN, scale_result=None)
@@ -162,14 +162,14 @@ def test_zero_k_and_zero_sign():
 
 
 def test_power_of_two_scale_change_is_exact():
-    d = datagen.workload1(20, 20, 700)
+    d = datagen.set_256_cubed(20, 20, 700)
     v1, _, _ = oracle.scaled_gemm(d["a"], 0, d["b"], 0, np.float32(0.75), 0, np.float32(3), 0, F32)
     v2, _, _ = oracle.scaled_gemm(d["a"], 0, d["b"], 0, np.float32(1.5), 0, np.float32(3), 0, F32)
     assert np.array_equal(v2, 2 * v1)
 
 
 def test_unit_block_scales_equal_per_tensor():
-    d = datagen.workload1(10, 140, 300)
+    d = datagen.set_256_cubed(10, 140, 300)
     kb = 3
     v_t, _, _ = oracle.scaled_gemm(d["a"], 0, d["b"], 0, np.float32(1), 0, np.float32(1), 0, F32)
     v_b, _, _ = oracle.scaled_gemm(d["a"], 0, d["b"], 0, np.ones((10, kb), np.float32), 1,
@@ -180,7 +180,7 @@ def test_unit_block_scales_equal_per_tensor():
 def test_block_scale_on_one_block_scales_that_block_only():
     """Scaling sa[m, kb] by 2 equals doubling the decoded a[m, k] of that block:
     the result moves by exactly that block's contribution."""
-    d = datagen.workload1(6, 5, 384)
+    d = datagen.set_256_cubed(6, 5, 384)
     sa = np.ones((6, 3), np.float32)
     sb = np.ones((1, 3), np.float32)
     v0, _, _ = oracle.scaled_gemm(d["a"], 0, d["b"], 0, sa, 1, sb, 2, F32)
@@ -232,9 +232,9 @@ def test_chunk_mode_matches_numpy_float32(kind):
     # the adversarial codes (subnormals beside +-448) give chunk sums wider than
     # 24 bits, so the rounding of each chunk partial is visible
     if kind == "gauss":
-        d = datagen.workload2_gauss(12, 9, 1000)
+        d = datagen.set_gauss_n4096(12, 9, 1000)
     else:
-        d = datagen.workload2_adversarial(12, 9, 1000)
+        d = datagen.set_adversarial_n4096(12, 9, 1000)
     A, B = tdecode(d["a"], E4M3FN), tdecode(d["b"], E4M3FN)
     alpha = np.float32(np.float32(d["scale_a"]) * np.float32(d["scale_b"]))
     want = _chunks_numpy_f32(A, B, 1000, alpha)
@@ -243,7 +243,7 @@ def test_chunk_mode_matches_numpy_float32(kind):
 
 
 def test_chunk_mode_single_chunk_equals_rounded_exact():
-    d = datagen.workload1(10, 10, 128)
+    d = datagen.set_256_cubed(10, 10, 128)
     ve, _, be = oracle.scaled_gemm(d["a"], 0, d["b"], 0, np.float32(1), 0, np.float32(1), 0, F32)
     vc, _, bc = oracle.scaled_gemm(d["a"], 0, d["b"], 0, np.float32(1), 0, np.float32(1), 0, F32, accum=ACC_F32_CHUNKS)
     assert np.array_equal(be, bc)
@@ -265,17 +265,17 @@ def test_chunk_mode_meets_tolerance_on_workload_data(name):
     met by an fp32 accumulator."""
     rows = None
     if name == "w1":
-        d = datagen.workload1(32, 64, 256); sam = sbm = 0
+        d = datagen.set_256_cubed(32, 64, 256); sam = sbm = 0
     elif name == "w2g":
-        d = datagen.workload2_gauss(16, 64, 4096); sam = sbm = 0
+        d = datagen.set_gauss_n4096(16, 64, 4096); sam = sbm = 0
     elif name == "w2a":
-        d = datagen.workload2_adversarial(16, 64, 4096); sam = sbm = 0
+        d = datagen.set_adversarial_n4096(16, 64, 4096); sam = sbm = 0
     elif name == "w3":
-        d = datagen.workload3(16, 256, 4096); sam, sbm = 1, 2
+        d = datagen.set_block_scaled_4096x14336x4096(16, 256, 4096); sam, sbm = 1, 2
     elif name == "w5a":
-        d = datagen.workload5a(8, 32, 8200); sam = sbm = 0
+        d = datagen.set_e4m3_out_8192x28672x8200(8, 32, 8200); sam = sbm = 0
     else:
-        d = datagen.workload5b(8, 32, 8200); sam = sbm = 0
+        d = datagen.set_e5m2_f16_8192x28672x8200(8, 32, 8200); sam = sbm = 0
     fa, fb = d["a_fmt"], d["b_fmt"]
     ve, sabs, _ = oracle.scaled_gemm(d["a"], fa, d["b"], fb, d["scale_a"], sam, d["scale_b"], sbm, F32)
     vc, _, _ = oracle.scaled_gemm(d["a"], fa, d["b"], fb, d["scale_a"], sam, d["scale_b"], sbm, F32, accum=ACC_F32_CHUNKS)
@@ -319,7 +319,7 @@ def test_amax_unit_scales_equal_plain_gemm():
 
 
 def test_amax_batch_equals_separate_calls():
-    d = datagen.workload4(3, 20, 24, 200)
+    d = datagen.set_mx_l8_2048x2048x8192(3, 20, 24, 200)
     v, _, bits, amax, idx = oracle.blockscaled_gemm_amax(d["a"], d["b"], 0, d["sfa"], d["sfb"], 32, BF16)
     maxes = []
     for l in range(3):
@@ -347,7 +347,7 @@ def test_amax_nan_empty_and_ties():
 
 
 def test_row_subset_matches_full():
-    d = datagen.workload1(40, 30, 300)
+    d = datagen.set_256_cubed(40, 30, 300)
     vf, sf_, bf = oracle.scaled_gemm(d["a"], 0, d["b"], 0, d["scale_a"], 0, d["scale_b"], 0, BF16)
     rows = np.array([39, 0, 17, 17])
     vr, sr, br = oracle.scaled_gemm(d["a"], 0, d["b"], 0, d["scale_a"], 0, d["scale_b"], 0, BF16, rows=rows)
@@ -356,7 +356,7 @@ def test_row_subset_matches_full():
 
 def test_row_pitch_is_respected():
     """Bytes between K and the row pitch never contribute (filled with NaN codes)."""
-    d = datagen.workload1(9, 7, 100)
+    d = datagen.set_256_cubed(9, 7, 100)
     a = np.full((9, 112), 0x7F, np.uint8); a[:, :100] = d["a"]
     b = np.full((7, 104), 0x7F, np.uint8); b[:, :100] = d["b"]
     v1, _, _ = oracle.scaled_gemm_k(a, 0, b, 0, 100, np.float32(1), 0, np.float32(1), 0, F32)
