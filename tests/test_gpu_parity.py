@@ -222,6 +222,19 @@ def test_block_scaled_full_size():
 
 # ------------------------------------------------------------------ MX factors per 32 + amax: L = 8, 2048 x 2048 x 8192
 
+def check_amax_index_against_oracle(idx, value, sabs):
+    """The GPU's amax index is the oracle's, unless the runner-up |C| lies within twice the fp32 bound of the
+    maximum (then either may be the maximum after rounding); `value` / `sabs` cover every output."""
+    v = np.abs(value.reshape(-1))
+    if np.isnan(v).any():
+        return
+    order = np.argsort(-v, kind="stable")
+    top, second = order[0], order[1]
+    bound = 2.0 ** -20 * (sabs.reshape(-1)[top] + sabs.reshape(-1)[second])
+    if v[top] - v[second] > 2 * bound:
+        assert idx == int(top), (idx, int(top))
+
+
 def check_amax_case(w, c_type, rows=None):
     c, amax, idx = gu.blockscaled_gemm_amax(w["a"], w["b"], w["ab_fmt"], w["sfa"], w["sfb"], c_type)
     value, sabs, bits, _, _ = oracle.blockscaled_gemm_amax(w["a"], w["b"], w["ab_fmt"], w["sfa"], w["sfb"], 32,
@@ -234,6 +247,7 @@ def check_amax_case(w, c_type, rows=None):
 def test_sf32_amax_small_with_oracle():
     w = datagen.set_mx_l8_2048x2048x8192(3, 200, 136, 1024)
     c, amax, idx, value, sabs = check_amax_case(w, F32)
+    check_amax_index_against_oracle(idx, value, sabs)
     cf = c.view(np.float32).astype(np.float64).reshape(-1)
     # amax and its index are bit-exact against the GPU's own C
     assert amax == float(np.max(np.abs(cf))) and idx == int(np.argmax(np.abs(cf)))
@@ -334,6 +348,7 @@ def atom_padding_mask(MN, K, L, sf=32):
 def test_atom_against_oracle(L, M, N, K, c_type):
     w = datagen.set_mx_atom_l8_2048x2048x8192(L, M, N, K)
     c, amax, idx, value, sabs = check_atom_case(w, c_type)
+    check_amax_index_against_oracle(idx, value, sabs)
     v = np.abs(value.reshape(-1))
     assert abs(amax - v.max()) <= 2.0 ** -20 * sabs.reshape(-1)[np.argmax(v)]
     if c_type == F32:  # bit-exact against the GPU's own C
@@ -412,6 +427,7 @@ def check_nvfp4_case(w, c_type, rows=None):
 def test_nvfp4_against_oracle(L, M, N, K, c_type):
     w = datagen.set_nvfp4_l8_2048x2048x8192(L, M, N, K, config=30 + L)
     c, amax, idx, value, sabs = check_nvfp4_case(w, c_type)
+    check_amax_index_against_oracle(idx, value, sabs)
     v = np.abs(value.reshape(-1))
     assert abs(amax - v.max()) <= 2.0 ** -20 * sabs.reshape(-1)[np.argmax(v)]
     if c_type == F32:
@@ -523,6 +539,7 @@ def check_fp4_case(w, c_type, rows=None):
 def test_fp4_against_oracle(L, M, N, K, sf, c_type):
     w = datagen.set_fp4_l8_2048x2048x8192(L, M, N, K, sf)
     c, amax, idx, value, sabs = check_fp4_case(w, c_type)
+    check_amax_index_against_oracle(idx, value, sabs)
     v = np.abs(value.reshape(-1))
     assert abs(amax - v.max()) <= 2.0 ** -20 * sabs.reshape(-1)[np.argmax(v)]
     if c_type == F32:
