@@ -370,6 +370,16 @@ def test_atom_equals_fp32_factor_entry(L, M, N, K):
     assert a1 == a2 and i1 == i2
 
 
+def test_atom_e5m2_operands():
+    L, M, N, K = 2, 150, 90, 416
+    w = datagen.set_mx_atom_l8_2048x2048x8192(L, M, N, K)
+    w["a"] = datagen.gauss_codes(datagen.rng(47, 0), (L, M, K), 64.0, E5M2)
+    w["b"] = datagen.gauss_codes(datagen.rng(47, 1), (L, N, K), 64.0, E5M2)
+    w["ab_fmt"] = E5M2
+    c, amax, idx, value, sabs = check_atom_case(w, F32)
+    check_amax_index_against_oracle(idx, value, sabs)
+
+
 def test_atom_padding_is_not_read():
     L, M, N, K = 2, 100, 72, 208  # 28 / 56 padding rows, group 7 of the second 4-group block unused
     w = datagen.set_mx_atom_l8_2048x2048x8192(L, M, N, K)
