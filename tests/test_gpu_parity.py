@@ -689,3 +689,45 @@ def test_batched_per_item_against_oracle(L, M, N, K, fast, d_type, fmt):
         value, sabs, bits = oracle.scaled_gemm(a[l], fmt, b[l], fmt, np.float32(0.5), 0, np.float32(0.25), 0,
                                                d_type, scale_result=sr, rows=rows)
         compare.check(gpu[l][rows], value, sabs, bits, d_type, f"batched item {l} of {L}: {M}x{N}x{K}")
+
+
+# ------------------------------------------------------------------ seeded random shapes, newer entries
+
+def random_shape(seed, k_mult):
+    g = np.random.default_rng(1000 + seed)
+    L = int(g.integers(1, 4))
+    M, N = (int(x) for x in g.integers(1, 300, size=2))
+    K = int(g.integers(1, 24)) * k_mult
+    return L, M, N, K
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shapes_page_native_factors(seed):
+    L, M, N, K = random_shape(seed, 16)
+    w = datagen.set_mx_atom_l8_2048x2048x8192(L, M, N, K)
+    c, amax, idx, value, sabs = check_atom_case(w, (F32, BF16, F16)[seed % 3])
+    check_amax_index_against_oracle(idx, value, sabs)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shapes_fp4(seed):
+    L, M, N, K = random_shape(seed + 10, 32)
+    if seed % 2:
+        w = datagen.set_nvfp4_l8_2048x2048x8192(L, M, N, K, config=50 + seed)
+        c, amax, idx, value, sabs = check_nvfp4_case(w, (F32, BF16, E4M3FN)[seed % 3])
+    else:
+        w = datagen.set_fp4_l8_2048x2048x8192(L, M, N, K, 16 if seed % 4 else 32, config=50 + seed)
+        c, amax, idx, value, sabs = check_fp4_case(w, (F32, F16, E5M2)[seed % 3])
+    check_amax_index_against_oracle(idx, value, sabs)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shapes_grouped(seed):
+    g = np.random.default_rng(2000 + seed)
+    G = int(g.integers(1, 20))
+    batch_sum = int(g.integers(1, 600))
+    N, K = int(g.integers(1, 300)), int(g.integers(1, 38)) * 16  # group strides N K bytes 16-byte aligned
+    w = datagen.set_grouped_8x8192x4096x4096(G, batch_sum, N, K, empty=min(G - 1, int(g.integers(0, 3))),
+                                             config=60 + seed)
+    check_grouped(w, (BF16, F32, E4M3FN, F16, E5M2, BF16)[seed], fast=bool(seed % 2),
+                  scale_result=0.0625 if seed in (2, 4) else None)
