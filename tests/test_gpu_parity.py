@@ -731,3 +731,35 @@ def test_random_shapes_grouped(seed):
                                              config=60 + seed)
     check_grouped(w, (BF16, F32, E4M3FN, F16, E5M2, BF16)[seed], fast=bool(seed % 2),
                   scale_result=0.0625 if seed in (2, 4) else None)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes_scaled_gemm(seed):
+    """mm_scaled_gemm on seeded random M, N, K with padded pitches, every scale mode, output type and
+    accumulation; M up to 1500 so that the skinny, K-split and tile kernels all take part."""
+    g = np.random.default_rng(3000 + seed)
+    M = int(g.choice([int(g.integers(1, 65)), int(g.integers(65, 400)), int(g.integers(400, 1500))]))
+    N = int(g.integers(1, 700))
+    K = int(g.integers(1, 900))
+    lda = (K + 7) // 8 * 8 + 8 * int(g.integers(0, 3))
+    ldb = (K + 7) // 8 * 8 + 8 * int(g.integers(0, 3))
+    fa, fb = (E4M3FN, E4M3FN) if seed % 3 else (E5M2, E4M3FN)
+    a = np.full((M, lda), 0x7F, np.uint8)  # NaN codes in the padding: never read
+    b = np.full((N, ldb), 0x7F, np.uint8)
+    a[:, :K] = datagen.gauss_codes(g, (M, K), 64.0, fa)
+    b[:, :K] = datagen.gauss_codes(g, (N, K), 64.0, fb)
+    d_type = (F32, BF16, F16, E4M3FN, E5M2, BF16, F32, F16)[seed]
+    sr = 1.0 / 64 if d_type in (E4M3FN, E5M2) else None
+    kb = -(-K // 128)
+    if seed % 4 == 3:  # block scales: 1x128 a, 1x128 or 128x128 b
+        sa_mode, sb_mode = 1, (1 if seed % 8 == 3 else 2)
+        sa = datagen.pow2_scales(g, (M, kb))
+        sb = datagen.pow2_scales(g, (N if sb_mode == 1 else -(-N // 128), kb))
+        sr = None if d_type not in (E4M3FN, E5M2) else sr
+    else:
+        sa_mode = sb_mode = 0
+        sa, sb = np.float32(2.0 ** -5), np.float32(0.75)
+    d = dict(a=a, b=b, K=K, a_fmt=fa, b_fmt=fb, scale_a=sa, scale_b=sb)
+    rows = None if M <= 400 else sample_rows(M, 16, seed=seed)
+    check_gemm(d, sa_mode, sb_mode, d_type, bool(seed % 2), rows=rows, scale_result=sr,
+               what=f"random M={M} N={N} K={K} lda={lda} ldb={ldb}", ldd=N + 4 * (seed % 3))
