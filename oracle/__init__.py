@@ -37,7 +37,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _LIB_OVERRIDE = os.environ.get("ORACLE_LIB_PATH")
 _lib = None
 
-_BITS_DTYPE = {E4M3FN: np.uint8, E5M2: np.uint8, F32: np.uint32, BF16: np.uint16, F16: np.uint16}
+_BITS_DTYPE = {E4M3FN: np.uint8, E5M2: np.uint8, F32: np.uint32, BF16: np.uint16, F16: np.uint16, 5: np.uint8}
 
 
 def build(force: bool = True) -> str:
@@ -113,7 +113,8 @@ def decode_fp4(codes: np.ndarray) -> np.ndarray:
 
 
 def round_to(x: np.ndarray, dtype: int) -> np.ndarray:
-    """Round float64 values to dtype with the oracle's output rules; returns bit patterns."""
+    """Round float64 values to dtype with the oracle's output rules; returns bit patterns (E2M1: one code per
+    byte)."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     out = np.empty(x.shape, dtype=_BITS_DTYPE[dtype])
     _check(_load().orc_round(_ptr(x), x.size, dtype, _ptr(out)))
@@ -204,7 +205,8 @@ def blockscaled_gemm_amax(a, b, ab_fmt, sfa, sfb, sf_vec, c_type, rows=None, thr
     R = M if r is None else r.size
     value = np.empty((L, R, N), dtype=np.float64)
     sabs = np.empty((L, R, N), dtype=np.float64)
-    bits = np.empty((L, R, N), dtype=_BITS_DTYPE[c_type])
+    # E2M1 C: packed, [L, R, ceil(N/2)] bytes
+    bits = np.empty((L, R, (N + 1) // 2 if c_type == E2M1 else N), dtype=_BITS_DTYPE[c_type])
     amax = np.zeros(1, dtype=np.float32)
     idx = np.zeros(1, dtype=np.int64)
     _check(_load().orc_blockscaled_gemm_amax(M, N, K, L, _ptr(a), _ptr(b), ab_fmt, _ptr(sfa),

@@ -164,6 +164,9 @@ Format format_of(int t) {
         case ORC_E4M3FN: return {3, 7, 8, 448.0, false, true, 0x7Fu};
         case ORC_E5M2:   return {2, 15, 8, 57344.0, true, true, 0x7Fu};
         case ORC_F16:    return {10, 15, 16, 65504.0, true, false, 0x7FFFu};
+        /* E2M1 output: saturating like the FP8 outputs; the format has no NaN code, so NaN takes the largest
+         * value's code 0x7 (a reading: the page gives FP4 C a shape but no conversion rule) */
+        case ORC_E2M1:   return {1, 1, 4, 6.0, false, true, 0x7u};
         case ORC_BF16:   return {7, 127, 16, std::ldexp(255.0, 120), true, false, 0x7FFFu};
         default:         return {23, 127, 32, std::ldexp(16777215.0, 104), true, false, 0x7FFFFFFFu};
     }
@@ -220,7 +223,7 @@ uint32_t encode(double r, const Format& f) {
 }
 
 void store_bits(void* out, int64_t i, uint32_t bits, int width) {
-    if (width == 8) ((uint8_t*)out)[i] = (uint8_t)bits;
+    if (width <= 8) ((uint8_t*)out)[i] = (uint8_t)bits; /* E2M1 codes here are one per byte */
     else if (width == 16) ((uint16_t*)out)[i] = (uint16_t)bits;
     else ((uint32_t*)out)[i] = bits;
 }
@@ -276,7 +279,7 @@ int orc_decode_fp4(const uint8_t* codes, int64_t n, double* out) {
 }
 
 int orc_round(const double* x, int64_t n, int dtype, void* out_bits) {
-    if (dtype < ORC_E4M3FN || dtype > ORC_F16) return ORC_ERR_ARG;
+    if (dtype < ORC_E4M3FN || dtype > ORC_E2M1) return ORC_ERR_ARG; /* E2M1: one code per byte */
     const Format f = format_of(dtype);
     for (int64_t i = 0; i < n; ++i) store_bits(out_bits, i, encode(round_to(x[i], f), f), f.bits);
     return ORC_OK;
@@ -451,8 +454,11 @@ int orc_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L,
                               float* amax, int64_t* amax_index, int threads) {
     if (fpenv_flushes()) return ORC_ERR_FPENV;
     if (M < 0 || N < 0 || K < 0 || L < 0 || sf_vec <= 0) return ORC_ERR_ARG;
-    if (c_type < ORC_E4M3FN || c_type > ORC_F16) return ORC_ERR_ARG;
+    if (c_type < ORC_E4M3FN || c_type > ORC_E2M1) return ORC_ERR_ARG;
     if (ab_fmt != ORC_E4M3FN && ab_fmt != ORC_E5M2 && ab_fmt != ORC_E2M1) return ORC_ERR_ARG;
+    /* E2M1 C is packed like the FP4 operands: rows of ceil(N/2) bytes, element 2i in the low nibble; an odd
+     * N leaves the last byte's high nibble 0 */
+    const int64_t c_row_bytes = (N + 1) / 2;
     if (ab_fmt == ORC_E2M1 && (K & 1)) return ORC_ERR_ARG;
     const int64_t pitch = ab_fmt == ORC_E2M1 ? K / 2 : K; /* bytes per operand row */
     if (!rows) n_rows = M;
@@ -489,7 +495,13 @@ int orc_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L,
                 vals[o] = S;
                 if (value) value[o] = S;
                 if (sum_abs) sum_abs[o] = T;
-                if (c_bits) store_bits(c_bits, (int64_t)o, encode(round_to(S, out_f), out_f), out_f.bits);
+                if (c_bits && c_type == ORC_E2M1) {
+                    uint8_t* cb = (uint8_t*)c_bits + ((size_t)l * n_rows + i) * c_row_bytes + n / 2;
+                    const uint8_t code = (uint8_t)encode(round_to(S, out_f), out_f);
+                    *cb = (n & 1) ? (uint8_t)((*cb & 0x0F) | (code << 4)) : code;
+                } else if (c_bits) {
+                    store_bits(c_bits, (int64_t)o, encode(round_to(S, out_f), out_f), out_f.bits);
+                }
             }
         });
     }

@@ -70,3 +70,37 @@ def test_fp4_closed_forms():
     alt[..., 1::2] = 7 | 8  # -6 at odd k
     v, *_ = oracle.blockscaled_gemm_amax(pack(alt), pack(six), oracle.E2M1, ones, ones, 32, oracle.F32)
     assert np.all(v == 0.0) and not np.any(np.signbit(v))
+
+
+# ------------------------------------------------------------------ E2M1 output (FP4 C)
+
+def test_e2m1_output_rounding():
+    vals = oracle.decode_fp4(np.arange(8))  # 0, 0.5, 1, 1.5, 2, 3, 4, 6 (pinned above)
+    # every value is its own code, both signs
+    np.testing.assert_array_equal(oracle.round_to(vals, oracle.E2M1), np.arange(8))
+    np.testing.assert_array_equal(oracle.round_to(-vals[1:], oracle.E2M1), np.arange(9, 16))
+    # midpoints go to the even code, anything off the midpoint to the nearer value
+    for c in range(7):
+        mid = (vals[c] + vals[c + 1]) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.round_to(np.array([mid]), oracle.E2M1)[0] == even
+        assert oracle.round_to(np.array([np.nextafter(mid, 0)]), oracle.E2M1)[0] == c
+        assert oracle.round_to(np.array([np.nextafter(mid, 9)]), oracle.E2M1)[0] == c + 1
+    # saturation (no infinities in E2M1), NaN takes the largest value's code (a reading), -0 keeps its sign
+    got = oracle.round_to(np.array([6.5, 1e30, np.inf, -7.0, -np.inf, np.nan, -0.0]), oracle.E2M1)
+    np.testing.assert_array_equal(got, [7, 7, 7, 15, 15, 7, 8])
+
+
+@pytest.mark.parametrize("N", [6, 7])
+def test_e2m1_c_is_packed_low_nibble_first(N):
+    # C rows of ceil(N/2) bytes, element 2i in the low nibble; an odd N leaves the last high nibble 0
+    g = np.random.default_rng(N)
+    L, M, K = 2, 3, 64
+    a = g.integers(0, 256, size=(L, M, K // 2), dtype=np.uint8)
+    b = g.integers(0, 256, size=(L, N, K // 2), dtype=np.uint8)
+    ones = np.ones((L, M, 2), np.float32), np.ones((L, N, 2), np.float32)
+    value, _, packed, _, _ = oracle.blockscaled_gemm_amax(a, b, oracle.E2M1, ones[0], ones[1], 32, oracle.E2M1)
+    codes = oracle.round_to(value.reshape(-1), oracle.E2M1).reshape(L, M, N)
+    if N % 2:
+        codes = np.concatenate([codes, np.zeros((L, M, 1), codes.dtype)], axis=2)
+    np.testing.assert_array_equal(packed, codes[..., 0::2] | (codes[..., 1::2] << 4))

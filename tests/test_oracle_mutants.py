@@ -60,6 +60,9 @@ MUTANTS = {
     "group_output_rows": ("value ? value + r0 * N : nullptr", "value ? value + (r0 / 2) * N : nullptr"),
     "group_row_count_unchecked": ("    if (next != batch_sum) return ORC_ERR_ARG;\n    const int width",
                                   "    if (false) return ORC_ERR_ARG;\n    const int width"),
+    "e2m1_out_max": ("{1, 1, 4, 6.0, false, true, 0x7u}", "{1, 1, 4, 4.0, false, true, 0x7u}"),
+    "e2m1_c_high_nibble_first": ("*cb = (n & 1) ? (uint8_t)((*cb & 0x0F) | (code << 4)) : code;",
+                                 "*cb = (n & 1) ? (uint8_t)((*cb & 0xF0) | code) : (uint8_t)(code << 4);"),
     "zero_chain_negative": ("double S = +0.0, T = 0.0;\n                    for (int64_t k = 0; k < K; ++k) {\n                        const double t = Am[k] * Bn[k];\n                        S += t;",
                             "double S = -0.0, T = 0.0;\n                    for (int64_t k = 0; k < K; ++k) {\n                        const double t = Am[k] * Bn[k];\n                        S += t;"),
 }
