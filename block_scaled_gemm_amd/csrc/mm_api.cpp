@@ -283,8 +283,8 @@ mm_status blockscaled_amax(const char* who, int64_t M, int64_t N, int64_t K, int
     if (e4m3_factors && (!fp4 || sf_vec_size != 16))
         return fail(MM_ERR_UNSUPPORTED, "E4M3 scale factors need FP4 operands and sf_vec_size 16");
     if (is_fp8(c_type) && !fp4) return fail(MM_ERR_UNSUPPORTED, "FP8 C with FP8 operands is not supported");
-    if (c_type == MM_F4_E2M1) return fail(MM_ERR_UNSUPPORTED, "FP4 C is not provided");
-    if (!is_dtype(c_type)) return fail(MM_ERR_INVALID_ARGUMENT, "unknown c_type %d", c_type);
+    if (c_type == MM_F4_E2M1 && !fp4) return fail(MM_ERR_UNSUPPORTED, "FP4 C needs FP4 operands");
+    if (!is_dtype(c_type) && c_type != MM_F4_E2M1) return fail(MM_ERR_INVALID_ARGUMENT, "unknown c_type %d", c_type);
     if (K > kMaxPitch) return fail(MM_ERR_UNSUPPORTED, "K must be at most 2^22");
     const int64_t outs = L * M * N;
     if (amax_index && outs >= ((int64_t)1 << 33))
@@ -337,10 +337,11 @@ mm_status blockscaled_amax(const char* who, int64_t M, int64_t N, int64_t K, int
             p.sb_batch = N * groups;
         }
         p.d = c;
-        p.ldd = N;
-        p.d_batch = M * N;
+        // FP4 C: rows of ceil(N/2) bytes, so the pitch in elements is N rounded up to even
+        p.ldd = c_type == MM_F4_E2M1 ? N + (N & 1) : N;
+        p.d_batch = M * p.ldd;
         p.d_type = c_type;
-        p.vec_store = (N % 4 == 0);
+        p.vec_store = (p.ldd % 4 == 0);
         p.amax_bits = amax_bits;
         p.amax_key = key;
         const int cfg = choose_cfg(M, N, L, cu_count(), mmfp8::min_cfg(mmfp8::MODE_SF32, 0, ab_type));

@@ -218,12 +218,24 @@ __device__ __forceinline__ uint32_t cvt_e5m2(float v) {
     return __builtin_isnan(v) ? 0x7Fu : code;
 }
 
+// E2M1 (FP4) outputs: round to nearest even over 0, 0.5, 1, 1.5, 2, 3, 4, 6
+// and saturate; each midpoint (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) goes to the
+// neighbour with the even code, so the count of thresholds passed is the code.
+// E2M1 has no NaN: NaN gives the largest value's code 0x7.
+__device__ __forceinline__ uint32_t cvt_e2m1(float v) {
+    const float a = __builtin_fabsf(v);
+    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+    return __builtin_isnan(v) ? 0x7u : (c | ((__float_as_uint(v) >> 28) & 8u));
+}
+
 template <int T>
 __device__ __forceinline__ uint32_t convert_t(float v) {
     if constexpr (T == T_F32) return cvt_f32(v);
     else if constexpr (T == T_BF16) return cvt_bf16(v);
     else if constexpr (T == T_F16) return cvt_f16(v);
     else if constexpr (T == T_E4M3) return cvt_e4m3(v);
+    else if constexpr (T == T_E2M1) return cvt_e2m1(v);
     else return cvt_e5m2(v);
 }
 __device__ __forceinline__ uint32_t convert(float v, int t) {
@@ -279,6 +291,16 @@ __device__ __forceinline__ void store4(void* d, int64_t e, const uint32_t v[4], 
             return;
         }
         for (int r = 0; r < valid; ++r) p[r] = (uint16_t)v[r];
+    } else if constexpr (T == T_E2M1) {
+        // packed two per byte, low nibble first; e (in elements) is even: rows
+        // of an even number of elements, 4 consecutive ones per lane. A lone
+        // last element leaves its byte's high nibble 0.
+        uint8_t* p = (uint8_t*)d + (e >> 1);
+        const uint32_t lo = v[0] | ((valid > 1 ? v[1] : 0u) << 4);
+        const uint32_t hi = (valid > 2 ? v[2] : 0u) | ((valid > 3 ? v[3] : 0u) << 4);
+        if (vec && valid == 4) { *(uint16_t*)p = (uint16_t)(lo | (hi << 8)); return; }
+        if (valid > 0) p[0] = (uint8_t)lo;
+        if (valid > 2) p[1] = (uint8_t)hi;
     } else {
         uint8_t* p = (uint8_t*)d + e;
         if (vec && valid == 4) { *(uint32_t*)p = v[0] | (v[1] << 8) | (v[2] << 16) | (v[3] << 24); return; }
@@ -1044,7 +1066,7 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
         else epilogue(ot, am, IC<0>{}, bi);
     };
     if constexpr (MODE == MODE_SF32) {
-        // the MX entries write f32, bf16 or f16, and FP8 with FP4 operands
+        // the MX entries write f32, bf16 or f16, and FP8 or FP4 (E2M1) with FP4 operands
         auto with_amax = [&](auto ot) {
             if (p.amax_key) epilogue_g(ot, IC<2>{}, IC<0>{});
             else if (p.amax_bits) epilogue_g(ot, IC<1>{}, IC<0>{});
@@ -1055,7 +1077,8 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
         else if (p.d_type == T_F32 || !kFp4) with_amax(IC<T_F32>{});
         else if constexpr (kFp4) {
             if (p.d_type == T_E4M3) with_amax(IC<T_E4M3>{});
-            else with_amax(IC<T_E5M2>{});
+            else if (p.d_type == T_E5M2) with_amax(IC<T_E5M2>{});
+            else with_amax(IC<T_E2M1>{});
         }
     } else {
         // a bias (f32, bf16 and f16 outputs) is another compile-time variant

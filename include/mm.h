@@ -307,8 +307,12 @@ mm_status mm_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L,
  *           subnormal, NaN codes give NaN).
  *  c_type   F32, BF16 or F16; with FP4 operands also MM_F8_E4M3FN or
  *           MM_F8_E5M2 (rounded to nearest even, saturating, as
- *           mm_scaled_gemm's FP8 outputs with scale_result 1). FP8 C with FP8
- *           operands and FP4 C -> MM_ERR_UNSUPPORTED.
+ *           mm_scaled_gemm's FP8 outputs with scale_result 1) and MM_F4_E2M1:
+ *           c is then [L][M][ceil(N/2)] bytes, two values each (low nibble
+ *           first, an odd N's last high nibble 0), rounded to nearest even,
+ *           saturating at +-6, NaN written as the code of +6 (E2M1 has no
+ *           NaN; the page gives no rule). FP8 or FP4 C with FP8 operands ->
+ *           MM_ERR_UNSUPPORTED.
  *
  * Everything else (amax, amax_index, stream, the arithmetic, sizes, alignment
  * and errors) is as mm_blockscaled_gemm_amax; in addition each batch item's

@@ -15,11 +15,15 @@ from __future__ import annotations
 
 import numpy as np
 
-E4M3FN, E5M2, F32, BF16, F16 = 0, 1, 2, 3, 4
+E4M3FN, E5M2, F32, BF16, F16, E2M1 = 0, 1, 2, 3, 4, 5
 CANON_NAN = {F32: 0x7FFFFFFF, BF16: 0x7FFF, F16: 0x7FFF, E4M3FN: 0x7F, E5M2: 0x7F}
-WIDTH = {F32: 32, BF16: 16, F16: 16, E4M3FN: 8, E5M2: 8}
-MANT = {F32: 23, BF16: 7, F16: 10, E4M3FN: 3, E5M2: 2}
-EMIN = {F32: -126, BF16: -126, F16: -14, E4M3FN: -6, E5M2: -14}
+WIDTH = {F32: 32, BF16: 16, F16: 16, E4M3FN: 8, E5M2: 8, E2M1: 4}
+MANT = {F32: 23, BF16: 7, F16: 10, E4M3FN: 3, E5M2: 2, E2M1: 1}
+EMIN = {F32: -126, BF16: -126, F16: -14, E4M3FN: -6, E5M2: -14, E2M1: 0}
+# E2M1 (FP4) codes, one per array element: sign bit 3, magnitudes of the OCP format
+E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+# E2M1 has no NaN: a NaN output is written as the code of +6 (the library's and the oracle's reading)
+E2M1_NAN_CODE = 0x7
 TOL = 2.0 ** -20
 
 
@@ -34,6 +38,9 @@ def bits_to_float(bits: np.ndarray, fmt: int) -> np.ndarray:
     if fmt == BF16:
         t = torch.from_numpy(np.ascontiguousarray(bits.astype(np.uint16)).view(np.int16))
         return t.view(torch.bfloat16).to(torch.float64).numpy()
+    if fmt == E2M1:
+        b = bits.astype(np.int64) & 15
+        return np.where(b & 8, -1.0, 1.0) * E2M1_MAG[b & 7]
     t = torch.from_numpy(np.ascontiguousarray(bits.astype(np.uint8)))
     if fmt == E4M3FN:
         return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
@@ -78,8 +85,11 @@ def check(gpu_bits: np.ndarray, value: np.ndarray, sum_abs: np.ndarray, oracle_b
     v_nan = np.isnan(v)
     g_nan = np.isnan(g)
     ok = np.zeros(v.shape, dtype=bool)
-    # NaN: both NaN and the GPU's encoding canonical
-    ok |= v_nan & g_nan & (gb == CANON_NAN[fmt])
+    if fmt == E2M1:
+        ok |= v_nan & (gb == E2M1_NAN_CODE)
+    else:
+        # NaN: both NaN and the GPU's encoding canonical
+        ok |= v_nan & g_nan & (gb == CANON_NAN[fmt])
     # infinities and saturated values: exact bit match of the rounded result
     fin = ~v_nan & ~g_nan
     exact_bits = fin & (gb == ob)

@@ -226,7 +226,7 @@ def atom_call(**kw):
     # FP4 operands
     (dict(ab_type=mm.MM_F4_E2M1, K=272), mm.MM_ERR_MISALIGNED, "multiple of 32"),
     (dict(ab_type=mm.MM_F4_E2M1, sf_vec_size=64), mm.MM_ERR_INVALID_ARGUMENT, "32 or 16"),
-    (dict(ab_type=mm.MM_F4_E2M1, c_type=mm.MM_F4_E2M1), mm.MM_ERR_UNSUPPORTED, "FP4 C"),
+    (dict(c_type=mm.MM_F4_E2M1), mm.MM_ERR_UNSUPPORTED, "FP4 C needs FP4 operands"),
     (dict(ab_type=mm.MM_F4_E2M1, c_type=7), mm.MM_ERR_INVALID_ARGUMENT, "unknown c_type"),
     (dict(ab_type=6), mm.MM_ERR_INVALID_ARGUMENT, "MM_F4_E2M1"),
 ])
@@ -243,7 +243,8 @@ def test_fp4_needs_the_atom_entry():
 @pytest.mark.parametrize("kw", [dict(ab_type=mm.MM_F4_E2M1), dict(ab_type=mm.MM_F4_E2M1, sf_vec_size=16),
                                 dict(ab_type=mm.MM_F4_E2M1, c_type=mm.MM_F8_E4M3FN, K=32),
                                 dict(ab_type=mm.MM_F4_E2M1, c_type=mm.MM_F8_E5M2, sf_vec_size=16, K=4096),
-                                dict(ab_type=mm.MM_F4_E2M1, sf_type=mm.MM_SF_E4M3FN, sf_vec_size=16)])
+                                dict(ab_type=mm.MM_F4_E2M1, sf_type=mm.MM_SF_E4M3FN, sf_vec_size=16),
+                                dict(ab_type=mm.MM_F4_E2M1, c_type=mm.MM_F4_E2M1, N=63)])
 def test_fp4_calls_pass_validation(kw, monkeypatch):
     # a launch failure forced after validation shows the call was accepted
     monkeypatch.setenv("MM_TEST_FORCE_FAIL", "launch")

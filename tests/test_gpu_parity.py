@@ -473,6 +473,54 @@ def test_nvfp4_full_size():
     check_nvfp4_case(w, F32, rows=sample_rows(2048, 4))
 
 
+# ------------------------------------------------------------------ FP4 (E2M1) C with FP4 operands
+
+def unpack_e2m1(packed, N):
+    """[..., ceil(N/2)] bytes -> [..., N] codes, low nibble first."""
+    p = np.asarray(packed, np.uint8)
+    codes = np.stack([p & 15, p >> 4], axis=-1).reshape(*p.shape[:-1], 2 * p.shape[-1])
+    return codes[..., :N]
+
+
+@pytest.mark.parametrize("L,M,N,K,sf,e4m3", [
+    (2, 96, 136, 512, 32, False),   # N % 4 == 0: 2-byte stores
+    (1, 130, 71, 992, 16, False),   # odd N: the last byte's high nibble
+    (2, 64, 99, 256, 16, True),     # N % 4 == 3 with E4M3 factors
+    (1, 200, 2, 64, 32, False),     # two columns: one byte per row
+])
+def test_fp4_c_output(L, M, N, K, sf, e4m3):
+    w = (datagen.set_nvfp4_l8_2048x2048x8192(L, M, N, K, config=70) if e4m3 else
+         datagen.set_fp4_l8_2048x2048x8192(L, M, N, K, sf, config=70))
+    sft = oracle.SF_E4M3FN if e4m3 else oracle.SF_E8M0
+    # A's factors lowered so that the outputs spread over the whole E2M1 range, saturation included
+    s = w["sfa"].astype(np.int64)
+    if e4m3:  # exponent field - 6 (at least 1)
+        w["sfa"] = ((np.maximum((s >> 3) - 6, 1) << 3) | (s & 7)).astype(np.uint8)
+    else:  # factor / 2^9
+        w["sfa"] = np.clip(s - 9, 1, 254).astype(np.uint8)
+    es = -(-N // 2)
+    ta, tb = gu.dev_u8(w["a"]), gu.dev_u8(w["b"])
+    tsa, tsb = gu.dev_u8(w["sfa"]), gu.dev_u8(w["sfb"])
+    tc = gu.torch.full((L * M * es,), 0x5A, dtype=gu.torch.uint8, device=gu.DEV)
+    tam = gu.torch.zeros((1,), dtype=gu.torch.float32, device=gu.DEV)
+    st = gu.mm.mm_blockscaled_gemm_amax_atom(M, N, K, L, ta.data_ptr(), tb.data_ptr(), gu.mm.MM_F4_E2M1,
+                                             tsa.data_ptr(), tsb.data_ptr(),
+                                             gu.mm.MM_SF_E4M3FN if e4m3 else gu.mm.MM_SF_E8M0, 16 if e4m3 else sf,
+                                             tc.data_ptr(), gu.mm.MM_F4_E2M1, tam.data_ptr(), 0, gu.stream())
+    assert st == gu.mm.MM_OK, (st, gu.mm.mm_last_error())
+    gu.torch.cuda.synchronize()
+    packed = tc.cpu().numpy().reshape(L, M, es)
+    if N % 2:
+        assert np.all(packed[..., -1] >> 4 == 0)  # the pad nibble
+    value, sabs, bits, _, _ = oracle.blockscaled_gemm_amax_atom(w["a"], w["b"], oracle.E2M1, w["sfa"], w["sfb"],
+                                                                sft, 16 if e4m3 else sf, 5)
+    g = unpack_e2m1(packed, N)
+    assert np.any(g & 7 == 7) and np.any(g & 7 == 1)  # saturated and small values both present
+    compare.check(g, value, sabs, unpack_e2m1(bits, N), 5, "fp4 C")
+    v = np.abs(value.reshape(-1))
+    assert abs(float(tam.item()) - v.max()) <= 2.0 ** -20 * sabs.reshape(-1)[np.argmax(v)]
+
+
 # ------------------------------------------------------------------ grouped GEMM (GroupedGemmFwdOp, NT, FP8)
 
 def check_grouped(w, d_type, fast=False, scale_result=None, rows=None, fmt=(E4M3FN, E4M3FN)):
