@@ -187,6 +187,54 @@ def grouped_gemm(a, a_fmt, b, b_fmt, sizes, offsets, scale_a, scale_b, d_type, s
     return value, sabs, bits
 
 
+
+def grouped_gemm_layout(a, a_fmt, b, b_fmt, sizes, offsets, scale_a, scale_b, d_type, transpose_a, transpose_b,
+                        scale_result=None, accum=ACC_EXACT, threads=None):
+    """TileOPs GroupedGemmFwdOp in all four (transpose_a, transpose_b) layouts ("Linear Algebra Operators",
+    GroupedGemmFwdOp: the layout table and the forward's argument shapes), with FP8 codes and one scale per
+    operand as the NT grouped_gemm.
+
+    Without transpose_a the groups split the rows of a [batch_sum, K]: group g's rows times b[g]^T (NT, b
+    [G, N, K]) or times b[g] (NN, b [G, K, N]); returns (value, sum_abs, d_bits), each [batch_sum, N].
+    With transpose_a the groups split the contraction: a is [batch_sum, N], b is [batch_sum, K] (TN) or
+    [K, batch_sum] (TT), and group g gives the [N, K] product A_g^T @ B_g of its rows (an empty group gives
+    zeros); returns the three arrays, each [G, N, K]. Each group's product is the plain scaled GEMM over its
+    own contraction (slow chunks of 128 counted from the group's first row).
+    """
+    a = np.asarray(a, dtype=np.uint8)
+    b = np.asarray(b, dtype=np.uint8)
+    sz = np.ascontiguousarray(sizes, dtype=np.int32).reshape(-1)
+    of = np.ascontiguousarray(offsets, dtype=np.int32).reshape(-1)
+    G = sz.size
+    if of.size != G:
+        raise ValueError("sizes and offsets need one entry per group")
+    if (sz < 0).any() or (of != np.concatenate([[0], np.cumsum(sz)[:-1]]).astype(np.int64)[:G]).any():
+        raise ValueError("sizes must be >= 0 and offsets their exclusive prefix sum")
+    if not transpose_a:
+        if a.shape[0] != int(sz.sum()):
+            raise ValueError("sizes must add up to a's rows")
+        # NN: group g's operand b[g] is [K, N]; its transpose is the NT operand
+        bt = b if transpose_b else np.transpose(b, (0, 2, 1))
+        return grouped_gemm(a, a_fmt, bt, b_fmt, sz, of, scale_a, scale_b, d_type, scale_result, accum, threads)
+    batch_sum, N = a.shape
+    # TN: b [batch_sum, K] -> the group's B_g is its rows; TT: b [K, batch_sum] -> B_g^T is its columns
+    K = b.shape[0] if transpose_b else b.shape[1]
+    if (b.shape[1] if transpose_b else b.shape[0]) != batch_sum or int(sz.sum()) != batch_sum:
+        raise ValueError("sizes must add up to the packed contraction of a and b")
+    value = np.zeros((G, N, K))
+    sabs = np.zeros((G, N, K))
+    bits = np.zeros((G, N, K), dtype=_BITS_DTYPE[d_type])
+    for g in range(G):
+        r0, s = int(of[g]), int(sz[g])
+        if s == 0:
+            # the product over an empty contraction: +0, whose code is 0 in every output type
+            continue
+        at = np.ascontiguousarray(a[r0:r0 + s, :].T)                       # A_g^T   [N, s]
+        bt = np.ascontiguousarray(b[:, r0:r0 + s] if transpose_b else b[r0:r0 + s, :].T)  # B_g^T [K, s]
+        value[g], sabs[g], bits[g] = scaled_gemm(at, a_fmt, bt, b_fmt, scale_a, SCALE_TENSOR, scale_b,
+                                                 SCALE_TENSOR, d_type, scale_result, accum, threads=threads)
+    return value, sabs, bits
+
 def blockscaled_gemm_amax(a, b, ab_fmt, sfa, sfb, sf_vec, c_type, rows=None, threads=None):
     """C[l,m,n] = sum_k A^ B^ with A^ = A*SFA[l,m,k//sf]; a [L,M,K], b [L,N,K] uint8
     (E2M1: [L,M,K/2] and [L,N,K/2] bytes, two elements each).

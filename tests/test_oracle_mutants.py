@@ -21,7 +21,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.cpp")
 PINS = [os.path.join(ROOT, "tests", "test_oracle_fp8.py"), os.path.join(ROOT, "tests", "test_oracle_gemm.py"),
         os.path.join(ROOT, "tests", "test_oracle_atom.py"), os.path.join(ROOT, "tests", "test_oracle_fp4.py"),
-        os.path.join(ROOT, "tests", "test_oracle_grouped.py")]
+        os.path.join(ROOT, "tests", "test_oracle_grouped.py"),
+        os.path.join(ROOT, "tests", "test_oracle_grouped_layouts.py")]
 
 # name -> (old text, new text); old text must occur exactly once
 MUTANTS = {
