@@ -7,6 +7,7 @@ this directory and raises if it is missing: there is no fallback path.
 
 Raw C-ABI wrappers (same names as the C functions, integer pointers):
 ``mm_scaled_gemm``, ``mm_scaled_gemm_bias``, ``mm_scaled_gemm_batched``, ``mm_scaled_gemm_grouped``,
+``mm_scaled_gemm_grouped_layout``, ``mm_grouped_workspace_bytes``, ``mm_transpose_u8``,
 ``mm_blockscaled_gemm_amax``, ``mm_blockscaled_gemm_amax_atom``,
 ``mm_debug_convert``, ``mm_last_error``, ``mm_version``. Tensor-level helpers:
 ``scaled_gemm`` (with an optional bias), ``scaled_bmm``, ``scaled_grouped_mm`` and
@@ -57,12 +58,20 @@ _lib.mm_blockscaled_gemm_amax.restype = _I
 _lib.mm_blockscaled_gemm_amax_atom.argtypes = [_I64, _I64, _I64, _I64, _P, _P, _I, _P, _P, _I, _I, _P, _I, _P, _P,
                                                _P]
 _lib.mm_blockscaled_gemm_amax_atom.restype = _I
+_lib.mm_transpose_u8.argtypes = [_I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P]
+_lib.mm_transpose_u8.restype = _I
+_lib.mm_grouped_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I, _I, ctypes.POINTER(ctypes.c_uint64)]
+_lib.mm_grouped_workspace_bytes.restype = _I
+_lib.mm_scaled_gemm_grouped_layout.argtypes = [_I64, _I64, _I64, _I64, _I, _I, _P, _I, _I64, _P, _I, _I64, _I64,
+                                               _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _P, ctypes.c_uint64, _I, _P]
+_lib.mm_scaled_gemm_grouped_layout.restype = _I
 _lib.mm_debug_convert.argtypes = [_P, _P, _I, _I64, _P]
 _lib.mm_debug_convert.restype = _I
 _lib.mm_last_error.restype = ctypes.c_char_p
 _lib.mm_version.restype = ctypes.c_char_p
 
 EXPORTED = ("mm_scaled_gemm", "mm_scaled_gemm_bias", "mm_scaled_gemm_batched", "mm_scaled_gemm_grouped",
+            "mm_scaled_gemm_grouped_layout", "mm_grouped_workspace_bytes", "mm_transpose_u8",
             "mm_blockscaled_gemm_amax",
             "mm_blockscaled_gemm_amax_atom", "mm_last_error", "mm_version", "mm_debug_convert")
 
@@ -113,6 +122,31 @@ def mm_scaled_gemm_grouped(batch_sum, N, K, G, a, a_type, lda, b, b_type, ldb, s
                                        batch_sizes or None, batch_offsets or None, scale_a or None, scale_b or None,
                                        scale_result or None, d or None, d_type, ldd, int(use_fast_accum),
                                        stream or None)
+
+
+def mm_transpose_u8(L, R, C, src, ld_src, stride_src, dst, ld_dst, stride_dst, stream) -> int:
+    """Raw call of the C function; pointers and the stream are integers (0 = NULL). Returns the status."""
+    return _lib.mm_transpose_u8(L, R, C, src or None, ld_src, stride_src, dst or None, ld_dst, stride_dst,
+                                stream or None)
+
+
+def mm_grouped_workspace_bytes(batch_sum, N, K, G, transpose_a, transpose_b):
+    """Raw call of the C function. Returns (status, bytes)."""
+    n = ctypes.c_uint64(0)
+    st = _lib.mm_grouped_workspace_bytes(batch_sum, N, K, G, int(transpose_a), int(transpose_b), ctypes.byref(n))
+    return st, n.value
+
+
+def mm_scaled_gemm_grouped_layout(batch_sum, N, K, G, transpose_a, transpose_b, a, a_type, lda, b, b_type, ldb,
+                                  stride_b, batch_sizes, batch_offsets, scale_a, scale_b, scale_result, d, d_type,
+                                  ldd, stride_d, workspace, workspace_bytes, use_fast_accum, stream) -> int:
+    """Raw call of the C function; pointers and the stream are integers (0 = NULL). Returns the status."""
+    return _lib.mm_scaled_gemm_grouped_layout(batch_sum, N, K, G, int(transpose_a), int(transpose_b), a or None,
+                                              a_type, lda, b or None, b_type, ldb, stride_b, batch_sizes or None,
+                                              batch_offsets or None, scale_a or None, scale_b or None,
+                                              scale_result or None, d or None, d_type, ldd, stride_d,
+                                              workspace or None, workspace_bytes, int(use_fast_accum),
+                                              stream or None)
 
 
 def mm_blockscaled_gemm_amax(M, N, K, L, a, b, ab_type, sfa, sfb, sf_vec_size, c, c_type, amax, amax_index,
@@ -237,21 +271,35 @@ def scaled_gemm(a, b, scale_a, scale_b, out_dtype, scale_result=None, use_fast_a
 
 
 def scaled_bmm(a, b, scale_a, scale_b, out_dtype, scale_result=None, use_fast_accum=False, out=None,
-               a_format=None, b_format=None):
-    """d[l] = (a[l] * scale_a) @ (b[l] * scale_b)^T for every l, on the current stream.
+               a_format=None, b_format=None, trans_b=True):
+    """d[l] = (a[l] * scale_a) @ B[l] * scale_b for every l, on the current stream.
 
-    a: [L, M, K] and b: [L, N, K] FP8 (K innermost, contiguous rows; a b held as
-    [L, K, N] must be transposed by the caller first). scale_a / scale_b: one
-    fp32 element each, shared by the batch. Returns d [L, M, N] of out_dtype.
+    a: [L, M, K] FP8 with K innermost. b: [L, N, K] (trans_b, B[l] = b[l]^T) or
+    torch.bmm's [L, K, N] (trans_b False, B[l] = b[l]). As for BmmFP8FwdOp, b's
+    strides decide whether it is copied: a b whose K axis is not innermost is
+    first transposed into a new [L, N, K] buffer (mm_transpose_u8, one extra
+    read and write of b). scale_a / scale_b: one fp32 element each, shared by
+    the batch. Returns d [L, M, N] of out_dtype.
     """
     torch = _torch()
+    if b.dim() == 3 and not trans_b:
+        b = b.transpose(1, 2)  # the [L, N, K] view of b [L, K, N]
     if a.dim() != 3 or b.dim() != 3 or a.shape[0] != b.shape[0] or a.shape[2] != b.shape[2]:
-        raise ValueError(f"expected a [L, M, K] and b [L, N, K], got {tuple(a.shape)} and {tuple(b.shape)}")
+        raise ValueError(f"expected a [L, M, K] and b [L, N, K] (or [L, K, N]), got {tuple(a.shape)} and "
+                         f"{tuple(b.shape)}")
     L, M, K = a.shape
     N = b.shape[1]
-    for t in (a, b):
-        if t.shape[2] > 1 and t.stride(2) != 1:
-            raise ValueError("operands need K innermost (b as [L, N, K]); transpose b first")
+    if a.shape[2] > 1 and a.stride(2) != 1:
+        raise ValueError("a needs K innermost")
+    if K > 1 and b.stride(2) != 1:
+        if N > 1 and b.stride(1) != 1:
+            raise ValueError("b needs K or N innermost")
+        kp = -(-K // 16) * 16
+        bt = torch.empty((L, N, kp), dtype=torch.uint8, device=b.device)
+        _check(mm_transpose_u8(L, K, N, b.data_ptr(), b.stride(2), b.stride(0), bt.data_ptr(), kp, N * kp,
+                               _stream()))
+        b_format = _fp8_code(b, b_format)
+        b = bt[:, :, :K]
     for s in (scale_a, scale_b):
         if s.dtype != torch.float32 or s.numel() != 1:
             raise TypeError("scale_a and scale_b must be one-element float32 tensors")
@@ -272,26 +320,55 @@ def scaled_bmm(a, b, scale_a, scale_b, out_dtype, scale_result=None, use_fast_ac
 
 
 def scaled_grouped_mm(a, b, batch_sizes, batch_offsets, scale_a, scale_b, out_dtype, scale_result=None,
-                      use_fast_accum=False, out=None, ab_formats=None):
-    """Grouped FP8 GEMM (NT): a [batch_sum, K] with the groups' rows packed, b [G, N, K] (K innermost),
-    batch_sizes / batch_offsets int32 [G] on the device; returns d [batch_sum, N] with group g's rows
-    a[rows] @ b[g]^T * scale_a * scale_b."""
+                      use_fast_accum=False, out=None, ab_formats=None, transpose_a=False, transpose_b=True):
+    """Grouped FP8 GEMM in GroupedGemmFwdOp's four layouts, batch_sizes / batch_offsets int32 [G] on the device.
+
+    NT (default): a [batch_sum, K], b [G, N, K]; NN: b [G, K, N]. Both return d [batch_sum, N] with group g's
+    rows a[rows] @ B_g * scale_a * scale_b. TN (transpose_a): a [batch_sum, N], b [batch_sum, K]; TT: b
+    [K, batch_sum]; both return d [G, N, K], group g's block A_g^T @ B_g over its rows. Layouts other than NT
+    pack their operands into a workspace allocated here (mm_scaled_gemm_grouped_layout).
+    """
     torch = _torch()
-    if a.dim() != 2 or b.dim() != 3 or a.stride(1) != 1 or b.stride(2) != 1 or b.stride(1) < b.shape[2]:
-        raise ValueError("a must be [batch_sum, K] and b [G, N, K], both K innermost")
     for t in (batch_sizes, batch_offsets):
-        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != b.shape[0]:
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.dim() != 1 or t.numel() != batch_sizes.numel():
             raise ValueError("batch_sizes and batch_offsets must be contiguous int32 [G]")
-    batch_sum, K = a.shape
-    G, N = b.shape[0], b.shape[1]
+    G = batch_sizes.numel()
+    if a.dim() != 2 or b.dim() != (2 if transpose_a else 3) or (a.shape[1] > 1 and a.stride(1) != 1) or \
+            (b.shape[-1] > 1 and b.stride(-1) != 1):
+        raise ValueError("a must be 2-D and b 3-D (2-D with transpose_a), both with contiguous rows")
+    if transpose_a:
+        batch_sum, N = a.shape
+        K = b.shape[0] if transpose_b else b.shape[1]
+        if (b.shape[1] if transpose_b else b.shape[0]) != batch_sum:
+            raise ValueError(f"b {tuple(b.shape)} does not match batch_sum {batch_sum}")
+        shape = (G, N, K)
+    else:
+        batch_sum, K = a.shape
+        if b.shape[0] != G:
+            raise ValueError("b needs one operand per group")
+        N = b.shape[1] if transpose_b else b.shape[2]
+        if (b.shape[2] if transpose_b else b.shape[1]) != K:
+            raise ValueError(f"b {tuple(b.shape)} does not match K {K}")
+        shape = (batch_sum, N)
     if out is None:
-        out = torch.empty((batch_sum, N), dtype=out_dtype, device=a.device)
+        out = torch.empty(shape, dtype=out_dtype, device=a.device)
+    if tuple(out.shape) != shape or (out.shape[-1] > 1 and out.stride(-1) != 1):
+        raise ValueError(f"out must be {shape} with contiguous rows")
     fa = _fp8_code(a, ab_formats[0] if ab_formats else None)
     fb = _fp8_code(b, ab_formats[1] if ab_formats else None)
-    st = mm_scaled_gemm_grouped(batch_sum, N, K, G, a.data_ptr(), fa, a.stride(0), b.data_ptr(), fb, b.stride(1),
-                                b.stride(0), batch_sizes.data_ptr(), batch_offsets.data_ptr(), scale_a.data_ptr(),
-                                scale_b.data_ptr(), scale_result.data_ptr() if scale_result is not None else 0,
-                                out.data_ptr(), dtype_code(out_dtype), out.stride(0), use_fast_accum, _stream())
+    st, nbytes = mm_grouped_workspace_bytes(batch_sum, N, K, G, transpose_a, transpose_b)
+    _check(st)
+    ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=a.device)
+    lda = a.stride(0) if a.shape[0] > 1 else a.shape[1]
+    ldb = b.stride(-2) if b.shape[-2] > 1 else b.shape[-1]
+    ldd = out.stride(-2) if out.shape[-2] > 1 else out.shape[-1]
+    st = mm_scaled_gemm_grouped_layout(batch_sum, N, K, G, transpose_a, transpose_b, a.data_ptr(), fa, lda,
+                                       b.data_ptr(), fb, ldb, b.stride(0) if not transpose_a else 0,
+                                       batch_sizes.data_ptr(), batch_offsets.data_ptr(), scale_a.data_ptr(),
+                                       scale_b.data_ptr(), scale_result.data_ptr() if scale_result is not None else 0,
+                                       out.data_ptr(), dtype_code(out_dtype), ldd,
+                                       out.stride(0) if transpose_a else 0, ws.data_ptr(), nbytes, use_fast_accum,
+                                       _stream())
     _check(st)
     return out
 

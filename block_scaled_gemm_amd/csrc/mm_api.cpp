@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <string>
 
@@ -99,7 +100,8 @@ mm_status scaled_gemm(const char* who, int64_t L, int64_t M, int64_t N, int64_t 
                       const float* scale_a, int sa_mode, const float* scale_b, int sb_mode, const float* scale_result,
                       const void* bias, void* d, int d_type, int64_t ldd, int64_t stride_d, int use_fast_accum,
                       void* stream, bool grouped = false, int64_t G = 0, const int32_t* gsizes = nullptr,
-                      const int32_t* goffsets = nullptr) {
+                      const int32_t* goffsets = nullptr,
+                      const std::function<hipError_t(hipStream_t)>& pre = {}) {
     g_error.clear();
     if (L < 0 || M < 0 || N < 0 || K < 0)
         return fail(MM_ERR_INVALID_ARGUMENT, "L, M, N and K must be >= 0 (got %lld, %lld, %lld, %lld)", (long long)L,
@@ -151,6 +153,10 @@ mm_status scaled_gemm(const char* who, int64_t L, int64_t M, int64_t N, int64_t 
     if (forced_launch_failure()) return fail(MM_ERR_DEVICE, "launch failure forced by MM_TEST_FORCE_FAIL");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (pre) {  // operand packing that the validated call needs first
+        const hipError_t e = pre(s);
+        if (e != hipSuccess) return device_status(e, who);
+    }
     mmfp8::GemmArgs p{};
     p.a = static_cast<const uint8_t*>(a);
     p.b = static_cast<const uint8_t*>(b);
@@ -406,6 +412,197 @@ mm_status mm_debug_convert(const float* x, void* y, int dtype, int64_t n, void* 
     if (forced_launch_failure()) return fail(MM_ERR_DEVICE, "launch failure forced by MM_TEST_FORCE_FAIL");
     return device_status(mmfp8::launch_debug_convert(x, y, dtype, n, static_cast<hipStream_t>(stream)),
                          "mm_debug_convert launch");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ layouts with packing
+//
+// "TileOPs: Linear Algebra Operators": BmmFP8FwdOp accepts b as [B, K, N] and
+// GroupedGemmFwdOp has the NN, TN and TT layouts besides NT. The kernels read
+// the contraction innermost; other operands are packed first (mm_pack.hip).
+
+namespace {
+
+int64_t round16(int64_t x) { return (x + 15) & ~(int64_t)15; }
+
+// The packing grid: ceil(R/64) x ceil(C/64) x L workgroups of 256 lanes.
+bool pack_fits(int64_t L, int64_t R, int64_t C) {
+    return L < 65536 && cdiv(C, 64) < 65536 && R < ((int64_t)1 << 30);
+}
+
+// Pitch of the packed operands when groups split the contraction: every
+// group's start rounded up to 16 bytes fits in it whatever the sizes.
+int64_t kgroup_pitch(int64_t batch_sum, int64_t G) { return round16(batch_sum) + 16 * G; }
+
+struct KGroupWs {
+    size_t start, shift, a, b, total;
+};
+
+KGroupWs kgroup_ws(int64_t batch_sum, int64_t N, int64_t K, int64_t G) {
+    const auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t P = (size_t)kgroup_pitch(batch_sum, G);
+    KGroupWs w{};
+    w.start = 0;
+    w.shift = up(8 * (size_t)G);
+    w.a = w.shift + up(8 * (size_t)G);
+    w.b = w.a + up((size_t)N * P);
+    w.total = w.b + (size_t)K * P;
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+mm_status mm_transpose_u8(int64_t L, int64_t R, int64_t C, const void* src, int64_t ld_src, int64_t stride_src,
+                          void* dst, int64_t ld_dst, int64_t stride_dst, void* stream) {
+    g_error.clear();
+    if (L < 0 || R < 0 || C < 0) return fail(MM_ERR_INVALID_ARGUMENT, "L, R and C must be >= 0");
+    if (ld_src < C || ld_dst < R) return fail(MM_ERR_INVALID_ARGUMENT, "ld_src must be >= C and ld_dst >= R");
+    if (stride_src < 0 || stride_dst < 0) return fail(MM_ERR_INVALID_ARGUMENT, "batch strides must be >= 0");
+    if (!pack_fits(L, R, C))
+        return fail(MM_ERR_UNSUPPORTED, "L must be below 2^16, C below 2^22 and R below 2^30");
+    if (L == 0 || R == 0 || C == 0) return MM_OK;
+    if (!src || !dst) return fail(MM_ERR_INVALID_ARGUMENT, "src or dst is NULL");
+    if (forced_launch_failure()) return fail(MM_ERR_DEVICE, "launch failure forced by MM_TEST_FORCE_FAIL");
+    return device_status(mmfp8::launch_pack(true, static_cast<const uint8_t*>(src), L, R, C, ld_src, stride_src,
+                                            static_cast<uint8_t*>(dst), ld_dst, stride_dst, ld_dst, nullptr,
+                                            nullptr, 0, static_cast<hipStream_t>(stream)),
+                         "mm_transpose_u8 launch");
+}
+
+mm_status mm_grouped_workspace_bytes(int64_t batch_sum, int64_t N, int64_t K, int64_t G, int transpose_a,
+                                     int transpose_b, uint64_t* bytes) {
+    g_error.clear();
+    if (!bytes) return fail(MM_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (batch_sum < 0 || N < 0 || K < 0 || G < 0)
+        return fail(MM_ERR_INVALID_ARGUMENT, "batch_sum, N, K and G must be >= 0");
+    if (batch_sum >= kMaxDim || N >= kMaxDim || K >= kMaxDim || G >= kMaxDim)
+        return fail(MM_ERR_UNSUPPORTED, "batch_sum, N, K and G must be below 2^31");
+    if (transpose_a) *bytes = (G == 0 || N == 0 || K == 0) ? 0 : kgroup_ws(batch_sum, N, K, G).total;
+    else *bytes = transpose_b ? 0 : (uint64_t)G * (uint64_t)N * (uint64_t)round16(K);
+    return MM_OK;
+}
+
+mm_status mm_scaled_gemm_grouped_layout(int64_t batch_sum, int64_t N, int64_t K, int64_t G, int transpose_a,
+                                        int transpose_b, const void* a, int a_type, int64_t lda, const void* b,
+                                        int b_type, int64_t ldb, int64_t stride_b, const int32_t* batch_sizes,
+                                        const int32_t* batch_offsets, const float* scale_a, const float* scale_b,
+                                        const float* scale_result, void* d, int d_type, int64_t ldd,
+                                        int64_t stride_d, void* workspace, uint64_t workspace_bytes,
+                                        int use_fast_accum, void* stream) {
+    g_error.clear();
+    if ((transpose_a != 0 && transpose_a != 1) || (transpose_b != 0 && transpose_b != 1))
+        return fail(MM_ERR_INVALID_ARGUMENT, "transpose_a and transpose_b must be 0 or 1");
+    if (!transpose_a && transpose_b)  // NT: the operands are already contraction-innermost
+        return mm_scaled_gemm_grouped(batch_sum, N, K, G, a, a_type, lda, b, b_type, ldb, stride_b, batch_sizes,
+                                      batch_offsets, scale_a, scale_b, scale_result, d, d_type, ldd,
+                                      use_fast_accum, stream);
+    uint64_t need = 0;
+    if (const mm_status st = mm_grouped_workspace_bytes(batch_sum, N, K, G, transpose_a, transpose_b, &need))
+        return st;
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(MM_ERR_INVALID_ARGUMENT, "the workspace needs %llu bytes (got %llu%s)", (unsigned long long)need,
+                    (unsigned long long)workspace_bytes, workspace ? "" : ", NULL");
+    if (!aligned(workspace, 16)) return fail(MM_ERR_MISALIGNED, "the workspace must be 16-byte aligned");
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+
+    if (!transpose_a) {
+        // NN: b [G][K][ldb] (N used) packed to [G][N][round16(K)], then the NT grouped GEMM
+        if (ldb < N) return fail(MM_ERR_INVALID_ARGUMENT, "ldb must be >= N (b is [G][K][ldb] under NN)");
+        if (stride_b < 0) return fail(MM_ERR_INVALID_ARGUMENT, "stride_b must be >= 0");
+        if (!pack_fits(G, K, N))
+            return fail(MM_ERR_UNSUPPORTED, "NN packing: G must be below 2^16, N below 2^22 and K below 2^30");
+        const int64_t kp = round16(K);
+        if (kp > kMaxPitch) return fail(MM_ERR_UNSUPPORTED, "NN packing: K must be at most 2^22 bytes");
+        if (G > 0 && N > 0 && K > 0 && !b) return fail(MM_ERR_INVALID_ARGUMENT, "b is NULL");
+        const auto pack = [=](hipStream_t s) {
+            return mmfp8::launch_pack(true, static_cast<const uint8_t*>(b), G, K, N, ldb, stride_b, ws, kp, N * kp,
+                                      kp, nullptr, nullptr, 0, s);
+        };
+        return scaled_gemm("mm_scaled_gemm_grouped_layout launch", 1, batch_sum, N, K, a, a_type, lda, 0,
+                           (G > 0 && N > 0 && K > 0) ? ws : b, b_type, kp, N * kp, scale_a, MM_SCALE_TENSOR,
+                           scale_b, MM_SCALE_TENSOR, scale_result, nullptr, d, d_type, ldd, 0, use_fast_accum,
+                           stream, true, G, batch_sizes, batch_offsets,
+                           (G > 0 && N > 0 && K > 0) ? std::function<hipError_t(hipStream_t)>(pack)
+                                                     : std::function<hipError_t(hipStream_t)>());
+    }
+
+    // TN / TT: the groups split the contraction; group g's [N][K] block is A_g^T B_g over its rows
+    if (!is_fp8(a_type) || !is_fp8(b_type))
+        return fail(MM_ERR_INVALID_ARGUMENT, "a_type and b_type must be MM_F8_E4M3FN or MM_F8_E5M2 (got %d, %d)",
+                    a_type, b_type);
+    if (!is_dtype(d_type)) return fail(MM_ERR_INVALID_ARGUMENT, "unknown d_type %d", d_type);
+    if (lda < N) return fail(MM_ERR_INVALID_ARGUMENT, "lda must be >= N (a is [batch_sum][lda] with transpose_a)");
+    if (transpose_b ? ldb < batch_sum : ldb < K)
+        return fail(MM_ERR_INVALID_ARGUMENT, "ldb must be >= %s (b is %s)", transpose_b ? "batch_sum" : "K",
+                    transpose_b ? "[K][ldb] under TT" : "[batch_sum][ldb] under TN");
+    if (ldd < K) return fail(MM_ERR_INVALID_ARGUMENT, "ldd must be >= K (each group's block is [N][ldd])");
+    if (stride_d < 0) return fail(MM_ERR_INVALID_ARGUMENT, "stride_d must be >= 0");
+    const int64_t P = kgroup_pitch(batch_sum, G);
+    if (P > kMaxPitch) return fail(MM_ERR_UNSUPPORTED, "batch_sum + 16 G must stay below 2^22");
+    if (!pack_fits(1, batch_sum, N) || !pack_fits(1, batch_sum, K))
+        return fail(MM_ERR_UNSUPPORTED, "N and K must be below 2^22");
+    if (G > 0 && cdiv(N, 64) * cdiv(K, 64) >= kMaxDim / G) return fail(MM_ERR_UNSUPPORTED, "too many output tiles");
+    if (G == 0 || N == 0 || K == 0) return MM_OK;
+    if (!batch_sizes || !batch_offsets) return fail(MM_ERR_INVALID_ARGUMENT, "batch_sizes or batch_offsets is NULL");
+    if (!aligned(batch_sizes, 4) || !aligned(batch_offsets, 4))
+        return fail(MM_ERR_MISALIGNED, "batch_sizes and batch_offsets must be 4-byte aligned");
+    if (!d) return fail(MM_ERR_INVALID_ARGUMENT, "d is NULL");
+    if (batch_sum > 0 && (!a || !b)) return fail(MM_ERR_INVALID_ARGUMENT, "a or b is NULL");
+    if (!scale_a || !scale_b) return fail(MM_ERR_INVALID_ARGUMENT, "scale_a or scale_b is NULL");
+    if (!aligned(d, elem_size(d_type))) return fail(MM_ERR_MISALIGNED, "d must be aligned to its element size");
+    if (!aligned(scale_a, 4) || !aligned(scale_b, 4) || !aligned(scale_result, 4))
+        return fail(MM_ERR_MISALIGNED, "scale pointers must be 4-byte aligned");
+    if (forced_launch_failure()) return fail(MM_ERR_DEVICE, "launch failure forced by MM_TEST_FORCE_FAIL");
+
+    const char* who = "mm_scaled_gemm_grouped_layout launch";
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const KGroupWs w = kgroup_ws(batch_sum, N, K, G);
+    int64_t* start = reinterpret_cast<int64_t*>(ws + w.start);
+    int64_t* shift = reinterpret_cast<int64_t*>(ws + w.shift);
+    uint8_t* at = ws + w.a;
+    uint8_t* bt = ws + w.b;
+    hipError_t e = mmfp8::launch_group_starts(batch_sizes, batch_offsets, (int)G, start, shift, s);
+    if (e != hipSuccess) return device_status(e, who);
+    if (batch_sum > 0) {
+        e = mmfp8::launch_pack(true, static_cast<const uint8_t*>(a), 1, batch_sum, N, lda, 0, at, P, 0, P,
+                               batch_offsets, shift, (int)G, s);
+        if (e != hipSuccess) return device_status(e, who);
+        e = mmfp8::launch_pack(!transpose_b, static_cast<const uint8_t*>(b), 1, batch_sum, K, ldb, 0, bt, P, 0, P,
+                               batch_offsets, shift, (int)G, s);
+        if (e != hipSuccess) return device_status(e, who);
+    }
+    mmfp8::GemmArgs p{};
+    p.a = at;
+    p.b = bt;
+    p.lda = P;
+    p.ldb = P;
+    p.M = (int)N;
+    p.N = (int)K;
+    p.K = 0;  // per group, from batch_sizes
+    p.L = (int)G;
+    p.sa = scale_a;
+    p.sb = scale_b;
+    p.scale_result = scale_result;
+    p.d = d;
+    p.ldd = ldd;
+    p.d_batch = stride_d;
+    p.d_type = d_type;
+    p.vec_store = (ldd % 4 == 0) && (stride_d % 4 == 0) && aligned(d, 4 * elem_size(d_type));
+    p.grp_sizes = batch_sizes;
+    p.kgrp_start = start;
+    const int mode = use_fast_accum ? mmfp8::MODE_FAST : mmfp8::MODE_SLOW;
+    const int cfg = choose_cfg(N, K, G, cu_count(), mmfp8::min_cfg(mode, 0));
+    p.tiles_m = (int)cdiv(N, mmfp8::kCfgBM[cfg]);
+    p.tiles_n = (int)cdiv(K, mmfp8::kCfgBN[cfg]);
+    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * G;
+    const int fa = a_type == MM_F8_E5M2 ? 1 : 0;
+    const int fb = b_type == MM_F8_E5M2 ? 1 : 0;
+    e = use_fast_accum ? mmfp8::launch_tile_fast(cfg, fa, fb, p, (int)grid, s)
+                       : mmfp8::launch_tile_slow(cfg, fa, fb, p, (int)grid, s);
+    return device_status(e, who);
 }
 
 }  // extern "C"

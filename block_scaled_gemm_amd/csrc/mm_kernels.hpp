@@ -93,6 +93,11 @@ struct GemmArgs {
     const int* grp_sizes;
     const int* grp_offsets;
     int groups;
+    // Groups that split the contraction (kgrp_start non-null, tile kernel):
+    // batch item l is group l, whose operands are columns kgrp_start[l] ..
+    // + grp_sizes[l] - 1 of a and b (both [rows][lda] with lda == ldb), so its
+    // K is grp_sizes[l] (0 gives a zero block).
+    const int64_t* kgrp_start;
 };
 
 // ------------------------------------------------------------------ helpers
@@ -500,6 +505,14 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     if (p.groups > 0) {
         if (!group_tile<BM>(p, tm)) return;  // the whole workgroup leaves: a tile past the groups' rows
         l = 0;
+    }
+    if (p.kgrp_start) {
+        // clamped so that a slice never leaves the rows, whatever the metadata
+        const int64_t c0 = min(max(p.kgrp_start[l], (int64_t)0), p.lda);
+        const int64_t kk = min(max((int64_t)p.grp_sizes[l], (int64_t)0), p.lda - c0);
+        p.a += c0;
+        p.b += c0;
+        p.K = __builtin_amdgcn_readfirstlane((int)kk);
     }
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = p.K;

@@ -164,7 +164,7 @@ mm_status mm_scaled_gemm_bias(int64_t M, int64_t N, int64_t K,
  * (batched FP8 GEMM, one per-tensor scale for a and one for b shared by the
  * whole batch). b is taken with K innermost, the page's trans_b layout
  * [B, N, K], which the page names as the layout that needs no transposed
- * copy; a caller holding b as [B, K, N] transposes it first.
+ * copy; a caller holding b as [B, K, N] transposes it first (mm_transpose_u8).
  *
  *  L        batch count, in [0, 2^31); L == 0 returns MM_OK, nothing enqueued.
  *  a        item l at a + l * stride_a bytes: [M, K], row pitch lda bytes.
@@ -224,6 +224,82 @@ mm_status mm_scaled_gemm_grouped(int64_t batch_sum, int64_t N, int64_t K, int64_
                                  void* d, int d_type, int64_t ldd,
                                  int use_fast_accum,
                                  void* stream);
+
+/*
+ * mm_transpose_u8 -- byte transpose, dst[l][c][r] = src[l][r][c]: the copy
+ * that "TileOPs: Linear Algebra Operators", tileops.gemm.BmmFP8FwdOp makes of
+ * a b that arrives as [B, K, N] (N innermost), since the GEMM reads b with K
+ * innermost. One extra read and write of the operand.
+ *
+ *  L, R, C  items, rows and columns of src, each >= 0; L < 2^16, C < 2^22,
+ *           R < 2^30 (MM_ERR_UNSUPPORTED otherwise). Any of them 0: MM_OK,
+ *           nothing enqueued.
+ *  src      item l at src + l * stride_src bytes: [R][ld_src], ld_src >= C.
+ *  dst      item l at dst + l * stride_dst bytes: [C][ld_dst], ld_dst >= R.
+ *           Bytes of dst past R in a row are not written. src and dst must
+ *           not overlap. Both are DEVICE pointers owned by the caller.
+ * No alignment is required. Errors as mm_scaled_gemm.
+ */
+mm_status mm_transpose_u8(int64_t L, int64_t R, int64_t C,
+                          const void* src, int64_t ld_src, int64_t stride_src,
+                          void* dst, int64_t ld_dst, int64_t stride_dst,
+                          void* stream);
+
+/*
+ * mm_grouped_workspace_bytes -- bytes of device workspace that
+ * mm_scaled_gemm_grouped_layout needs for these sizes and layout (written to
+ * *bytes; 0 for NT and when G, N or K is 0). Needs no GPU. Negative sizes: MM_ERR_INVALID_ARGUMENT.
+ */
+mm_status mm_grouped_workspace_bytes(int64_t batch_sum, int64_t N, int64_t K, int64_t G,
+                                     int transpose_a, int transpose_b, uint64_t* bytes);
+
+/*
+ * mm_scaled_gemm_grouped_layout -- the grouped FP8 GEMM in the four layouts of
+ * "TileOPs: Linear Algebra Operators", tileops.gemm.GroupedGemmFwdOp (its
+ * layout table and forward's argument shapes), selected by (transpose_a,
+ * transpose_b), with one fp32 scale for a and one for b as in
+ * mm_scaled_gemm_grouped. The metadata rules are that function's.
+ *
+ * Without transpose_a the groups split the rows of a [batch_sum][lda] (K
+ * used), d is [batch_sum][ldd] (stride_d is ignored):
+ *  NT (0, 1)  b [G][N][ldb], K used: exactly mm_scaled_gemm_grouped (no
+ *             workspace).
+ *  NN (0, 0)  b [G][K][ldb], N used, group g's at b + g * stride_b bytes:
+ *             d[r, n] = sum_k a[r, k] b[g][k, n] * scale_a * scale_b.
+ * With transpose_a the groups split the contraction; a is [batch_sum][lda]
+ * (N used) and group g yields the [N][K] block
+ *   d[g][n, k] = sum over g's rows r of a[r, n] * B(r, k) * scale_a * scale_b
+ * at d + g * stride_d ELEMENTS, rows of ldd (>= K) elements; an empty group
+ * gives +0. (N and K name the block's extents as on the page.)
+ *  TN (1, 0)  b [batch_sum][ldb], K used: B(r, k) = b[r, k].
+ *  TT (1, 1)  b [K][ldb], batch_sum used: B(r, k) = b[k, r].
+ * Each group's product is mm_scaled_gemm's (the slow mode's 128-element
+ * chunks counted from the group's first row), cast to d_type as there.
+ *
+ *  workspace  DEVICE memory of at least mm_grouped_workspace_bytes bytes,
+ *           16-byte aligned, owned by the caller, used by this call's kernels
+ *           on `stream` until they finish: the operands repacked with the
+ *           contraction innermost, each group starting on a 16-byte boundary.
+ *           Its previous contents never matter. NULL is accepted when 0 bytes
+ *           are needed.
+ * Limits (MM_ERR_UNSUPPORTED): NN: G < 2^16, N < 2^22, round16(K) <= 2^22;
+ * TN / TT: round16(batch_sum) + 16 G <= 2^22, N and K < 2^22,
+ * G ceil(N/64) ceil(K/64) < 2^31. G, N or K == 0 with transpose_a: MM_OK,
+ * nothing enqueued. Errors as mm_scaled_gemm; a workspace that is too small
+ * is MM_ERR_INVALID_ARGUMENT. Bad metadata gives unspecified values, never an
+ * access outside the arguments.
+ */
+mm_status mm_scaled_gemm_grouped_layout(int64_t batch_sum, int64_t N, int64_t K, int64_t G,
+                                        int transpose_a, int transpose_b,
+                                        const void* a, int a_type, int64_t lda,
+                                        const void* b, int b_type, int64_t ldb, int64_t stride_b,
+                                        const int32_t* batch_sizes, const int32_t* batch_offsets,
+                                        const float* scale_a, const float* scale_b,
+                                        const float* scale_result,
+                                        void* d, int d_type, int64_t ldd, int64_t stride_d,
+                                        void* workspace, uint64_t workspace_bytes,
+                                        int use_fast_accum,
+                                        void* stream);
 
 /*
  * mm_blockscaled_gemm_amax -- batched block-scaled GEMM with a global amax.

@@ -268,3 +268,18 @@ def set_nvfp4_l8_2048x2048x8192(L=8, M=2048, N=2048, K=8192, config=11):
     b = rng(config, 1).integers(0, 256, size=(L, N, K // 2), dtype=np.uint8)
     return dict(a=a, b=b, ab_fmt=5, sfa=e4m3_atom_codes(rng(config, 2), M, K, L),
                 sfb=e4m3_atom_codes(rng(config, 3), N, K, L), sf_vec=16, K=K)
+
+
+def set_grouped_layout(G, batch_sum, N, K, empty, transpose_a, transpose_b, config):
+    """Grouped set in one of GroupedGemmFwdOp's layouts: Gaussian codes as set_grouped_8x8192x4096x4096,
+    ragged group sizes, one scale per operand. a [batch_sum, K] (or [batch_sum, N] with transpose_a); b
+    [G, N, K] (NT), [G, K, N] (NN), [batch_sum, K] (TN) or [K, batch_sum] (TT)."""
+    sizes = group_sizes(rng(config, 3), G, batch_sum, empty)
+    offsets = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.int32)
+    a = gauss_codes(rng(config, 0), (batch_sum, N if transpose_a else K), 64.0)
+    if transpose_a:
+        bshape = (K, batch_sum) if transpose_b else (batch_sum, K)
+    else:
+        bshape = (G, N, K) if transpose_b else (G, K, N)
+    b = gauss_codes(rng(config, 1), bshape, 64.0)
+    return dict(a=a, b=b, sizes=sizes, offsets=offsets, scale_a=np.float32(0.5), scale_b=np.float32(0.25))

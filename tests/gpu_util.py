@@ -160,3 +160,56 @@ def scaled_gemm_batched(a, a_fmt, b, b_fmt, K, sa, sb, d_type, scale_result=None
     torch.cuda.synchronize()
     out = td.cpu().numpy().view(BITS_NP[d_type])[: L * stride_d].reshape(L, stride_d)[:, : M * N]
     return np.ascontiguousarray(out.reshape(L, M, N))
+
+
+def transpose_u8(src, ld_src=None, ld_dst=None, fill=0x5A):
+    """src [L, R, C] uint8 (numpy); rows padded to ld_src, dst rows of ld_dst; returns dst [L, C, ld_dst]."""
+    L, R, C = src.shape
+    ld_src = ld_src or C
+    ld_dst = ld_dst or R
+    s = np.full((L, R, ld_src), 0xA5, np.uint8)
+    s[:, :, :C] = src
+    ts = dev_u8(s)
+    td = torch.full((max(L * C * ld_dst, 1),), fill, dtype=torch.uint8, device=DEV)
+    st = mm.mm_transpose_u8(L, R, C, ts.data_ptr(), ld_src, R * ld_src, td.data_ptr(), ld_dst, C * ld_dst,
+                            stream())
+    assert st == mm.MM_OK, (st, mm.mm_last_error())
+    torch.cuda.synchronize()
+    return td.cpu().numpy()[: L * C * ld_dst].reshape(L, C, ld_dst)
+
+
+def scaled_gemm_grouped_layout(a, a_fmt, b, b_fmt, sizes, offsets, sa, sb, d_type, transpose_a, transpose_b,
+                               scale_result=None, fast=False, fill=0x5A):
+    """Any of the four layouts on uint8 codes (numpy, contiguous rows); returns d bits ([batch_sum, N], or
+    [G, N, K] with transpose_a; untouched elements keep the fill pattern)."""
+    G = len(sizes)
+    if transpose_a:
+        batch_sum, N = a.shape
+        K = b.shape[0] if transpose_b else b.shape[1]
+        shape = (G, N, K)
+    else:
+        batch_sum, K = a.shape
+        N = b.shape[1] if transpose_b else b.shape[2]
+        shape = (batch_sum, N)
+    ta, tb = dev_u8(a), dev_u8(b)
+    ts = torch.from_numpy(np.ascontiguousarray(sizes, dtype=np.int32)).to(DEV)
+    to = torch.from_numpy(np.ascontiguousarray(offsets, dtype=np.int32)).to(DEV)
+    tsa, tsb = dev_f32([sa]), dev_f32([sb])
+    tsr = dev_f32([scale_result]) if scale_result is not None else None
+    es = np.dtype(BITS_NP[d_type]).itemsize
+    n_out = int(np.prod(shape))
+    td = torch.full((max(n_out, 1) * es,), fill, dtype=torch.uint8, device=DEV)
+    st, nbytes = mm.mm_grouped_workspace_bytes(batch_sum, N, K, G, transpose_a, transpose_b)
+    assert st == mm.MM_OK
+    ws = torch.full((max(nbytes, 1),), 0xC3, dtype=torch.uint8, device=DEV)  # contents never matter
+    ldb = b.shape[-1]
+    stride_b = 0 if transpose_a else b.shape[1] * b.shape[2]
+    st = mm.mm_scaled_gemm_grouped_layout(batch_sum, N, K, G, transpose_a, transpose_b, ta.data_ptr(), a_fmt,
+                                          a.shape[1], tb.data_ptr(), b_fmt, ldb, stride_b, ts.data_ptr(),
+                                          to.data_ptr(), tsa.data_ptr(), tsb.data_ptr(),
+                                          tsr.data_ptr() if tsr is not None else 0, td.data_ptr(), d_type,
+                                          shape[-1], N * K if transpose_a else 0, ws.data_ptr(), nbytes, int(fast),
+                                          stream())
+    assert st == mm.MM_OK, (st, mm.mm_last_error())
+    torch.cuda.synchronize()
+    return np.ascontiguousarray(td.cpu().numpy().view(BITS_NP[d_type])[:n_out].reshape(shape))

@@ -28,6 +28,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"mm_scaled_gemm", "mm_scaled_gemm_bias", "mm_scaled_gemm_batched", "mm_scaled_gemm_grouped",
+                          "mm_scaled_gemm_grouped_layout", "mm_grouped_workspace_bytes", "mm_transpose_u8",
                           "mm_blockscaled_gemm_amax", "mm_blockscaled_gemm_amax_atom", "mm_last_error",
                           "mm_version", "mm_debug_convert"}
     lib = ctypes.CDLL(mm.LIB_PATH)
@@ -296,3 +297,93 @@ def test_single_hip_runtime_after_import():
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip() == "1", r.stdout
+
+
+def layout_call(**kw):
+    args = dict(batch_sum=300, N=64, K=96, G=3, transpose_a=1, transpose_b=0, a=P, a_type=0, lda=64, b=P, b_type=1,
+                ldb=96, stride_b=0, batch_sizes=P, batch_offsets=P, scale_a=P, scale_b=P, scale_result=0, d=P,
+                d_type=2, ldd=96, stride_d=64 * 96, workspace=P, workspace_bytes=1 << 30, use_fast_accum=0, stream=0)
+    args.update(kw)
+    return mm.mm_scaled_gemm_grouped_layout(**args)
+
+
+def test_grouped_workspace_bytes():
+    assert mm.mm_grouped_workspace_bytes(300, 64, 96, 3, 0, 1) == (mm.MM_OK, 0)      # NT: none
+    assert mm.mm_grouped_workspace_bytes(300, 64, 90, 3, 0, 0) == (mm.MM_OK, 3 * 64 * 96)  # NN: b as [G][N][K16]
+    st, n = mm.mm_grouped_workspace_bytes(300, 64, 96, 3, 1, 0)
+    # TN / TT: both operands at a pitch holding every group 16-aligned, plus two int64 [G] tables
+    assert st == mm.MM_OK and n >= (64 + 96) * (304 + 48) + 16 * 3
+    assert mm.mm_grouped_workspace_bytes(300, 64, 96, 3, 1, 1) == (st, n)
+    assert mm.mm_grouped_workspace_bytes(-1, 64, 96, 3, 1, 0)[0] == mm.MM_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(transpose_a=2), mm.MM_ERR_INVALID_ARGUMENT, "0 or 1"),
+    (dict(workspace_bytes=100), mm.MM_ERR_INVALID_ARGUMENT, "workspace needs"),
+    (dict(workspace=0), mm.MM_ERR_INVALID_ARGUMENT, "workspace needs"),
+    (dict(workspace=P + 8), mm.MM_ERR_MISALIGNED, "16-byte aligned"),
+    (dict(a_type=2), mm.MM_ERR_INVALID_ARGUMENT, "a_type"),
+    (dict(d_type=7), mm.MM_ERR_INVALID_ARGUMENT, "d_type"),
+    (dict(lda=63), mm.MM_ERR_INVALID_ARGUMENT, "lda must be >= N"),
+    (dict(ldb=95), mm.MM_ERR_INVALID_ARGUMENT, "ldb must be >= K"),
+    (dict(transpose_b=1, ldb=299), mm.MM_ERR_INVALID_ARGUMENT, "ldb must be >= batch_sum"),
+    (dict(ldd=95), mm.MM_ERR_INVALID_ARGUMENT, "ldd must be >= K"),
+    (dict(stride_d=-1), mm.MM_ERR_INVALID_ARGUMENT, "stride_d"),
+    (dict(batch_sum=1 << 22, ldb=1 << 22), mm.MM_ERR_UNSUPPORTED, "2^22"),
+    (dict(batch_sizes=0), mm.MM_ERR_INVALID_ARGUMENT, "NULL"),
+    (dict(batch_offsets=P + 2), mm.MM_ERR_MISALIGNED, "4-byte aligned"),
+    (dict(d=0), mm.MM_ERR_INVALID_ARGUMENT, "d is NULL"),
+    (dict(b=0), mm.MM_ERR_INVALID_ARGUMENT, "a or b is NULL"),
+    (dict(scale_b=0), mm.MM_ERR_INVALID_ARGUMENT, "scale_a or scale_b is NULL"),
+    (dict(d=P + 2), mm.MM_ERR_MISALIGNED, "aligned to its element size"),
+    # NN: b is [G][K][ldb]
+    (dict(transpose_a=0, lda=96, ldb=63, ldd=64), mm.MM_ERR_INVALID_ARGUMENT, "ldb must be >= N"),
+    (dict(transpose_a=0, lda=96, ldb=64, ldd=64, stride_b=-16), mm.MM_ERR_INVALID_ARGUMENT, "stride_b"),
+    (dict(transpose_a=0, lda=96, ldb=64, ldd=64, G=1 << 16), mm.MM_ERR_UNSUPPORTED, "NN packing"),
+    (dict(transpose_a=0, lda=96, ldb=64, ldd=64, b=0), mm.MM_ERR_INVALID_ARGUMENT, "b is NULL"),
+    (dict(transpose_a=0, lda=96, ldb=64, ldd=63), mm.MM_ERR_INVALID_ARGUMENT, "ldd must be >= N"),
+])
+def test_grouped_layout_validation(kw, status, msg):
+    assert layout_call(**kw) == status
+    assert msg in mm.mm_last_error()
+
+
+def test_grouped_layout_nothing_to_do_launches_nothing():
+    assert layout_call(G=0, batch_sizes=0, batch_offsets=0, workspace=0, workspace_bytes=0) == mm.MM_OK
+    assert layout_call(N=0, d=0) == mm.MM_OK
+    assert layout_call(K=0, d=0, ldd=0) == mm.MM_OK
+    # NT needs no workspace and is the plain grouped entry
+    assert layout_call(transpose_a=0, transpose_b=1, lda=96, ldb=96, ldd=64, workspace=0, workspace_bytes=0,
+                       batch_sum=0, d=0) == mm.MM_OK
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(transpose_b=1, ldb=300), dict(batch_sum=0, a=0, b=0, ldb=96),
+                                dict(transpose_a=0, lda=96, ldb=64, ldd=64, stride_b=96 * 64),
+                                dict(transpose_a=0, transpose_b=1, lda=96, ldb=96, ldd=64, stride_b=96 * 64,
+                                     workspace=0, workspace_bytes=0)],
+                         ids=["TN", "TT", "TN-empty", "NN", "NT"])
+def test_grouped_layout_calls_pass_validation(kw, monkeypatch):
+    monkeypatch.setenv("MM_TEST_FORCE_FAIL", "launch")
+    assert layout_call(**kw) == mm.MM_ERR_DEVICE
+    assert "forced" in mm.mm_last_error()
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((-1, 4, 4, P, 4, 0, P, 4, 0), mm.MM_ERR_INVALID_ARGUMENT, ">= 0"),
+    ((1, 4, 8, P, 7, 0, P, 4, 0), mm.MM_ERR_INVALID_ARGUMENT, "ld_src"),
+    ((1, 8, 4, P, 4, 0, P, 7, 0), mm.MM_ERR_INVALID_ARGUMENT, "ld_dst"),
+    ((1, 4, 4, P, 4, -1, P, 4, 0), mm.MM_ERR_INVALID_ARGUMENT, "strides"),
+    ((1 << 16, 4, 4, P, 4, 16, P, 4, 16), mm.MM_ERR_UNSUPPORTED, "2^16"),
+    ((1, 4, 1 << 22, P, 1 << 22, 0, P, 4, 0), mm.MM_ERR_UNSUPPORTED, "2^22"),
+    ((1, 4, 4, 0, 4, 0, P, 4, 0), mm.MM_ERR_INVALID_ARGUMENT, "NULL"),
+])
+def test_transpose_validation(args, status, msg):
+    assert mm.mm_transpose_u8(*args, 0) == status
+    assert msg in mm.mm_last_error()
+
+
+def test_transpose_zero_sizes_and_forced_failure(monkeypatch):
+    assert mm.mm_transpose_u8(0, 4, 4, 0, 4, 0, 0, 4, 0, 0) == mm.MM_OK
+    assert mm.mm_transpose_u8(2, 0, 4, 0, 4, 0, 0, 0, 0, 0) == mm.MM_OK
+    monkeypatch.setenv("MM_TEST_FORCE_FAIL", "launch")
+    assert mm.mm_transpose_u8(2, 4, 4, P, 4, 16, P, 4, 16, 0) == mm.MM_ERR_DEVICE

@@ -128,10 +128,10 @@ def test_helper_errors_raise_before_launch():
     with pytest.raises(TypeError):  # scales must be float32
         mm.scaled_gemm(a, a, torch.ones(1, dtype=torch.float16, device=DEV), f32(1.0), torch.float32,
                        a_format=mm.MM_F8_E4M3FN, b_format=mm.MM_F8_E4M3FN)
-    with pytest.raises(ValueError):  # b held [L, K, N] is refused, not transposed
-        b = torch.zeros((2, 64, 128), dtype=torch.uint8, device=DEV)
-        mm.scaled_bmm(b, b.transpose(1, 2).contiguous().transpose(1, 2), f32(1.0), f32(1.0), torch.float32,
-                      a_format=0, b_format=0)
+    with pytest.raises(ValueError):  # a b with neither K nor N innermost is refused
+        b = torch.zeros((2, 64, 256), dtype=torch.uint8, device=DEV)
+        mm.scaled_bmm(b[:, :, :128].contiguous(), b[:, :, ::2], f32(1.0), f32(1.0), torch.float32, a_format=0,
+                      b_format=0)
     # E4M3 factors with 32 values per factor: refused by the library (the page allows them with 16 only)
     w = datagen.set_nvfp4_l8_2048x2048x8192(1, 64, 64, 256, config=46)
     u8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
