@@ -142,6 +142,10 @@ OTHER = {
                 "M=N=2048, K=8192, f32 C + amax + index",
     "grouped": "grouped per-tensor E4M3 GEMM (NT), 8 groups of ragged sizes packing 8192 rows, N=K=4096, slow, "
                "bf16 out",
+    "grouped_nn": "grouped per-tensor E4M3 GEMM (NN, b [G, K, N] packed per call), 8 groups of ragged sizes "
+                  "packing 8192 rows, N=K=4096, slow, bf16 out",
+    "grouped_tn": "grouped per-tensor E4M3 GEMM (TN, the groups split the contraction, both operands packed per "
+                  "call), 8 groups of ragged sizes packing 8192 rows, blocks [8, 4096, 4096], slow, bf16 out",
 }
 
 
@@ -222,6 +226,33 @@ def run_other(name, steps, warmup):
                                              sb.data_ptr(), 0, out.data_ptr(), mm.MM_BF16, N, 0, stream)
         # every group's b is read: G N K bytes in place of N K
         scale_bytes = 8 + 8 * G + (G - 1) * N * K
+    elif name in ("grouped_nn", "grouped_tn"):
+        tn = name == "grouped_tn"
+        d = datagen.set_grouped_layout(8, 8192, 4096, 4096, 0, tn, False, config=9)
+        S = d["a"].shape[0]; G = d["sizes"].size; N = K = N0 = K0 = 4096
+        a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
+        gs = torch.from_numpy(d["sizes"]).to(dev); go = torch.from_numpy(d["offsets"]).to(dev)
+        sa = torch.tensor([float(d["scale_a"])], dtype=torch.float32, device=dev)
+        sb = torch.tensor([float(d["scale_b"])], dtype=torch.float32, device=dev)
+        out = torch.empty((G, N, K) if tn else (S, N), dtype=torch.bfloat16, device=dev)
+        st, ws_bytes = mm.mm_grouped_workspace_bytes(S, N, K, G, int(tn), 0)
+        ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+        out_bytes = 2
+
+        def launch():
+            return mm.mm_scaled_gemm_grouped_layout(S, N0, K0, G, int(tn), 0, a.data_ptr(), mm.MM_F8_E4M3FN,
+                                                    d["a"].shape[1], b.data_ptr(), mm.MM_F8_E4M3FN, d["b"].shape[-1],
+                                                    0 if tn else K0 * N0, gs.data_ptr(), go.data_ptr(),
+                                                    sa.data_ptr(), sb.data_ptr(), 0, out.data_ptr(), mm.MM_BF16,
+                                                    K0 if tn else N0, N0 * K0 if tn else 0, ws.data_ptr(), ws_bytes,
+                                                    0, stream)
+        if tn:
+            # as one GEMM of [N, S] by [S, K] (flops 2 N K S) whose output is G blocks of [N, K]
+            L, M, N, K = 1, N, K, S
+            scale_bytes = 8 + 8 * G + (G - 1) * M * N * out_bytes
+        else:
+            L, M = 1, S
+            scale_bytes = 8 + 8 * G + (G - 1) * N * K  # every group's b is read
     elif name in ("mx_atom", "mx_fp4", "mx_nvfp4"):
         d = {"mx_atom": datagen.set_mx_atom_l8_2048x2048x8192, "mx_fp4": datagen.set_fp4_l8_2048x2048x8192, "mx_nvfp4": datagen.set_nvfp4_l8_2048x2048x8192}[name]()
         L, M, K = d["a"].shape; N = d["b"].shape[1]

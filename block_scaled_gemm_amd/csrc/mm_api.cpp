@@ -436,7 +436,7 @@ bool pack_fits(int64_t L, int64_t R, int64_t C) {
 int64_t kgroup_pitch(int64_t batch_sum, int64_t G) { return round16(batch_sum) + 16 * G; }
 
 struct KGroupWs {
-    size_t start, shift, a, b, total;
+    size_t start, a, b, total;
 };
 
 KGroupWs kgroup_ws(int64_t batch_sum, int64_t N, int64_t K, int64_t G) {
@@ -444,8 +444,7 @@ KGroupWs kgroup_ws(int64_t batch_sum, int64_t N, int64_t K, int64_t G) {
     const size_t P = (size_t)kgroup_pitch(batch_sum, G);
     KGroupWs w{};
     w.start = 0;
-    w.shift = up(8 * (size_t)G);
-    w.a = w.shift + up(8 * (size_t)G);
+    w.a = up(8 * (size_t)G);
     w.b = w.a + up((size_t)N * P);
     w.total = w.b + (size_t)K * P;
     return w;
@@ -466,9 +465,9 @@ mm_status mm_transpose_u8(int64_t L, int64_t R, int64_t C, const void* src, int6
     if (L == 0 || R == 0 || C == 0) return MM_OK;
     if (!src || !dst) return fail(MM_ERR_INVALID_ARGUMENT, "src or dst is NULL");
     if (forced_launch_failure()) return fail(MM_ERR_DEVICE, "launch failure forced by MM_TEST_FORCE_FAIL");
-    return device_status(mmfp8::launch_pack(true, static_cast<const uint8_t*>(src), L, R, C, ld_src, stride_src,
-                                            static_cast<uint8_t*>(dst), ld_dst, stride_dst, ld_dst, nullptr,
-                                            nullptr, 0, static_cast<hipStream_t>(stream)),
+    return device_status(mmfp8::launch_transpose(static_cast<const uint8_t*>(src), L, R, C, ld_src, stride_src,
+                                                 static_cast<uint8_t*>(dst), ld_dst, stride_dst,
+                                                 static_cast<hipStream_t>(stream)),
                          "mm_transpose_u8 launch");
 }
 
@@ -518,8 +517,7 @@ mm_status mm_scaled_gemm_grouped_layout(int64_t batch_sum, int64_t N, int64_t K,
         if (kp > kMaxPitch) return fail(MM_ERR_UNSUPPORTED, "NN packing: K must be at most 2^22 bytes");
         if (G > 0 && N > 0 && K > 0 && !b) return fail(MM_ERR_INVALID_ARGUMENT, "b is NULL");
         const auto pack = [=](hipStream_t s) {
-            return mmfp8::launch_pack(true, static_cast<const uint8_t*>(b), G, K, N, ldb, stride_b, ws, kp, N * kp,
-                                      kp, nullptr, nullptr, 0, s);
+            return mmfp8::launch_transpose(static_cast<const uint8_t*>(b), G, K, N, ldb, stride_b, ws, kp, N * kp, s);
         };
         return scaled_gemm("mm_scaled_gemm_grouped_layout launch", 1, batch_sum, N, K, a, a_type, lda, 0,
                            (G > 0 && N > 0 && K > 0) ? ws : b, b_type, kp, N * kp, scale_a, MM_SCALE_TENSOR,
@@ -561,17 +559,16 @@ mm_status mm_scaled_gemm_grouped_layout(int64_t batch_sum, int64_t N, int64_t K,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const KGroupWs w = kgroup_ws(batch_sum, N, K, G);
     int64_t* start = reinterpret_cast<int64_t*>(ws + w.start);
-    int64_t* shift = reinterpret_cast<int64_t*>(ws + w.shift);
     uint8_t* at = ws + w.a;
     uint8_t* bt = ws + w.b;
-    hipError_t e = mmfp8::launch_group_starts(batch_sizes, batch_offsets, (int)G, start, shift, s);
+    hipError_t e = mmfp8::launch_group_starts(batch_sizes, (int)G, start, s);
     if (e != hipSuccess) return device_status(e, who);
     if (batch_sum > 0) {
-        e = mmfp8::launch_pack(true, static_cast<const uint8_t*>(a), 1, batch_sum, N, lda, 0, at, P, 0, P,
-                               batch_offsets, shift, (int)G, s);
+        e = mmfp8::launch_group_pack(true, static_cast<const uint8_t*>(a), batch_sum, N, lda, at, P, batch_sizes,
+                                     batch_offsets, start, (int)G, s);
         if (e != hipSuccess) return device_status(e, who);
-        e = mmfp8::launch_pack(!transpose_b, static_cast<const uint8_t*>(b), 1, batch_sum, K, ldb, 0, bt, P, 0, P,
-                               batch_offsets, shift, (int)G, s);
+        e = mmfp8::launch_group_pack(!transpose_b, static_cast<const uint8_t*>(b), batch_sum, K, ldb, bt, P,
+                                     batch_sizes, batch_offsets, start, (int)G, s);
         if (e != hipSuccess) return device_status(e, who);
     }
     mmfp8::GemmArgs p{};

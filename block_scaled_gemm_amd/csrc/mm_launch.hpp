@@ -52,12 +52,13 @@ hipError_t launch_ksplit(int ks, int mode, int fa, int fb, const GemmArgs& p, in
 hipError_t launch_amax_init(uint32_t* bits, unsigned long long* key, hipStream_t s);
 hipError_t launch_amax_finalize(float* amax, unsigned long long* key, hipStream_t s);
 hipError_t launch_debug_convert(const float* x, void* y, int t, int64_t n, hipStream_t s);
-// Operand packing (mm_pack.hip): dst[l][c][r + shift(r)] from src[l][r][c] (trans) or src[l][c][r].
-hipError_t launch_group_starts(const int* sizes, const int* offsets, int G, int64_t* start, int64_t* shift,
-                               hipStream_t s);
-hipError_t launch_pack(bool trans, const uint8_t* src, int64_t L, int64_t R, int64_t C, int64_t ld_src,
-                       int64_t src_batch, uint8_t* dst, int64_t ld_dst, int64_t dst_batch, int64_t dst_cols,
-                       const int* offsets, const int64_t* shift, int G, hipStream_t s);
+// Operand packing (mm_pack.hip).
+hipError_t launch_group_starts(const int* sizes, int G, int64_t* start, hipStream_t s);
+hipError_t launch_transpose(const uint8_t* src, int64_t L, int64_t R, int64_t C, int64_t ld_src, int64_t src_batch,
+                            uint8_t* dst, int64_t ld_dst, int64_t dst_batch, hipStream_t s);
+hipError_t launch_group_pack(bool trans, const uint8_t* src, int64_t R, int64_t C, int64_t ld_src, uint8_t* dst,
+                             int64_t dst_cols, const int* sizes, const int* offsets, const int64_t* start, int G,
+                             hipStream_t s);
 
 // Largest tile each mode is built for. The chained modes (fast, MX) keep 128
 // fp32 accumulators per lane and little else, so they take the 64x128 wave
