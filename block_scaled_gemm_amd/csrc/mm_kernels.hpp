@@ -361,15 +361,24 @@ __device__ __forceinline__ void amax_commit(const GemmArgs& p, uint32_t kb, unsi
 // Map the linear workgroup id to a tile. Workgroups are dispatched round-robin
 // over the 8 XCDs (each with its own L2); this gives every XCD a contiguous run
 // of tiles, walked in groups of `group_m` tile rows so that the tiles live on
-// one XCD at the same time share A rows and B columns.
+// one XCD at the same time share A rows and B columns. With l_fastest = L
+// the batch index varies fastest along the run instead, so that every XCD
+// gets an equal share of every item (items of unequal work: groups that split
+// the contraction).
 __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int group_m, int& l,
-                                        int& tm, int& tn) {
+                                        int& tm, int& tn, int l_fastest = 0) {
     const int per = nblocks / 8, rem = nblocks % 8;
     const int x = bid % 8, i = bid / 8;
     const int t = (x < rem) ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
     const int tiles = tiles_m * tiles_n;
-    l = t / tiles;
-    const int u = t - l * tiles;
+    int u;
+    if (l_fastest > 0) {
+        l = t % l_fastest;
+        u = t / l_fastest;
+    } else {
+        l = t / tiles;
+        u = t - l * tiles;
+    }
     const int width = group_m * tiles_n;
     const int grp = u / width;
     const int first = grp * group_m;
@@ -501,7 +510,7 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     const int gw = KG > 1 ? wave % NW : wave;                    // wave within its group
     const int wm = gw / WN, wn = gw % WN;
     int l, tm, tn;
-    tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, 8, l, tm, tn);
+    tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, 8, l, tm, tn, p.kgrp_start ? p.L : 0);
     if (p.groups > 0) {
         if (!group_tile<BM>(p, tm)) return;  // the whole workgroup leaves: a tile past the groups' rows
         l = 0;
