@@ -154,3 +154,30 @@ def test_grouped_contraction_split_full_size():
         value, sabs, obits = oracle.scaled_gemm(at, E4M3FN, bt, E4M3FN, w["scale_a"], 0, w["scale_b"], 0, BF16,
                                                 accum=oracle.ACC_F32_CHUNKS, rows=rows)
         compare.check(gpu[g][rows], value, sabs, obits, BF16, f"group {g}")
+
+
+@pytest.mark.parametrize("tb", [False, True], ids=["TN", "TT"])
+def test_contraction_split_uses_exactly_the_listed_rows(tb):
+    # metadata the page makes the caller's error (sizes not adding up, a gap between groups): every group's
+    # block is still the product over exactly its listed rows, within the buffers
+    S, N, K = 400, 72, 96
+    w = datagen.set_grouped_layout(4, S, N, K, 0, True, tb, config=92)
+    sizes = np.array([50, 0, 30, 100], np.int32)
+    offsets = np.array([0, 60, 60, 250], np.int32)
+    gpu = gu.scaled_gemm_grouped_layout(w["a"], E4M3FN, w["b"], E4M3FN, sizes, offsets, w["scale_a"], w["scale_b"],
+                                        F32, True, tb)
+    bt_all = w["b"] if tb else np.ascontiguousarray(w["b"].T)  # [K, S]
+    for g, (sz, of) in enumerate(zip(sizes, offsets)):
+        if sz == 0:
+            assert (gpu[g] == 0).all()
+            continue
+        value, sabs, obits = oracle.scaled_gemm(np.ascontiguousarray(w["a"][of:of + sz].T), E4M3FN,
+                                                np.ascontiguousarray(bt_all[:, of:of + sz]), E4M3FN, w["scale_a"],
+                                                0, w["scale_b"], 0, F32, accum=oracle.ACC_F32_CHUNKS)
+        compare.check(gpu[g], value, sabs, obits, F32, f"group {g}")
+
+
+def test_grouped_nn_e5m2_fast():
+    w = datagen.set_grouped_layout(6, 900, 136, 320, 1, False, False, config=93)
+    w["b"] = datagen.gauss_codes(datagen.rng(93, 7), w["b"].shape, 64.0, E5M2)
+    check_layout(w, BF16, False, False, fast=True, fmt=(E4M3FN, E5M2))
