@@ -134,6 +134,8 @@ OTHER = {
     "e5m2_f16": "E5M2 GEMM, M=8192, N=28672, K=8200 (lda 8200), slow, f16 out",
     "block_bias": "E4M3 1x128 / 128x128 block-scaled GEMM + bf16 bias [N], M=4096, N=14336, K=4096, bf16 out",
     "bmm": "batched per-tensor E4M3 GEMM, L=8, M=N=2048, K=4096, slow, bf16 out",
+    "bmm_kn": "batched per-tensor E4M3 GEMM with b as [L, K, N] (transposed per call), L=8, M=N=2048, K=4096, "
+              "slow, bf16 out",
     "mx_atom": "batched E4M3 GEMM with E8M0 factors per 32 K in the page-native atom layout, L=8, M=N=2048, "
                "K=8192, f32 C + amax + index",
     "mx_fp4": "batched FP4 (E2M1) GEMM with E8M0 factors per 32 K in the page-native atom layout, L=8, "
@@ -192,6 +194,25 @@ def run_other(name, steps, warmup):
 
         def launch():
             return mm.mm_scaled_gemm_batched(L, M, N, K, a.data_ptr(), mm.MM_F8_E4M3FN, K, M * K, b.data_ptr(),
+                                             mm.MM_F8_E4M3FN, K, N * K, sa.data_ptr(), sb.data_ptr(), 0,
+                                             out.data_ptr(), mm.MM_BF16, N, M * N, 0, stream)
+        scale_bytes = 8
+    elif name == "bmm_kn":
+        d = datagen.set_bmm_l8_2048x2048x4096()
+        L, M, K = d["a"].shape; N = d["b"].shape[1]
+        a = torch.from_numpy(d["a"]).to(dev)
+        b = torch.from_numpy(np.ascontiguousarray(d["b"].transpose(0, 2, 1))).to(dev)  # [L, K, N]
+        bt = torch.empty((L, N, K), dtype=torch.uint8, device=dev)
+        sa = torch.tensor([float(d["scale_a"])], dtype=torch.float32, device=dev)
+        sb = torch.tensor([float(d["scale_b"])], dtype=torch.float32, device=dev)
+        out = torch.empty((L, M, N), dtype=torch.bfloat16, device=dev)
+        out_bytes = 2
+
+        def launch():
+            st = mm.mm_transpose_u8(L, K, N, b.data_ptr(), N, K * N, bt.data_ptr(), K, N * K, stream)
+            if st != mm.MM_OK:
+                return st
+            return mm.mm_scaled_gemm_batched(L, M, N, K, a.data_ptr(), mm.MM_F8_E4M3FN, K, M * K, bt.data_ptr(),
                                              mm.MM_F8_E4M3FN, K, N * K, sa.data_ptr(), sb.data_ptr(), 0,
                                              out.data_ptr(), mm.MM_BF16, N, M * N, 0, stream)
         scale_bytes = 8
