@@ -42,6 +42,8 @@ COUNTERS = os.path.join(ROOT, "profiles", "gemm_tile_M8192_N4096_K4096_slow_coun
 KERNEL_SOURCES = [os.path.join(ROOT, "block_scaled_gemm_amd", "csrc", f) for f in ("mm_kernels.hpp", "mm_launch.hpp")]
 ROTATION_BYTES = 512 << 20    # 2x the Infinity Cache
 METRIC = "FP8 scaled-GEMM TFLOP/s and % of MI355X FP8 MFMA peak, M=16..8192"
+# kernel the library dispatches for each M of the benchmark (N = K = 4096, per-tensor)
+KERNEL_AT = {16: "gemm_skinny", 64: "gemm_skinny", 256: "gemm_ksplit"}
 
 
 def gemm_bytes(M):
@@ -457,7 +459,7 @@ def main():
                      "traffic": measured_traffic() if dominant == 8192 else None,
                      "peak_unit_note": "dense bf16 MFMA (FP8 operands converted exactly in registers)",
                      "frac_of_fp8_peak": round(achieved / PEAK_FP8_TFLOPS, 4),
-                     "kernel": f"gemm_tile M={dominant} N=K=4096", "kernel_us": round(dom_us, 3)},
+                     "kernel": f"{KERNEL_AT.get(dominant, 'gemm_tile')} M={dominant} N=K=4096", "kernel_us": round(dom_us, 3)},
         "per_m": per_m,
     }
     if not args.no_cpu_baseline and not args.only_m:
