@@ -17,8 +17,20 @@ accumulation is not accurate enough for the required 2^-20 sum|a b| bound), so
 the roofline peak is the dense bf16 MFMA rate; the per-M lines also give the
 fraction of the FP8 MFMA peak that the metric names. `traffic` is the HBM bytes
 per launch of that kernel from committed rocprofv3 counters, reported only while
-the kernel sources are the ones the counters were taken on. `cpu_baseline`
-times the CPU oracle on one full step of the same workload.
+the kernel sources are the ones the counters were taken on.
+
+Method (after "mmaemu backends", Benchmarks, Method):
+ - exactness gate before timing: every M's output on the first buffer set is
+   compared with the CPU oracle on rows 0 .. min(M, 64) - 1 plus 64 seeded rows,
+   all columns; any output outside the tolerance stops the run (exit 1) after
+   printing the first bad elements. The oracle's time on those rows is the
+   `cpu_baseline` (all host cores, and one thread);
+ - warm-up: the requested untimed steps, then more untimed steps until at least
+   1.5 s have passed (`warmup_s`), so that the clock has settled;
+ - the requested K steps are timed (`value`); then interleaved windows of at
+   least 1.0 s each run the same step loop, and their median is reported with
+   the GPU clock sampled every 200 ms meanwhile (`method`), as a rate per clock
+   (flop per clock per CU) and as a fraction of the bf16 MFMA peak at that clock.
 """
 from __future__ import annotations
 
@@ -104,25 +116,111 @@ def launch(mm, M, s, S, stream):
         raise RuntimeError(f"mm_scaled_gemm failed: {mm.mm_last_error()}")
 
 
-def cpu_baseline():
-    """The oracle, untuned, on the host cores, over one full step of the same
-    workload: the six GEMMs M = 16 .. 8192 (N = K = 4096, all rows, exact
-    float64 sums), on the same seeded inputs as the GPU's first buffer set."""
+def gate_rows(M):
+    """Rows the exactness gate checks: 0 .. min(M, 64) - 1 plus 64 seeded rows of the rest."""
     import numpy as np
+    first = np.arange(min(M, 64))
+    if M <= 64:
+        return first
+    rest = np.random.default_rng(1000 + M).choice(np.arange(64, M), size=min(64, M - 64), replace=False)
+    return np.unique(np.concatenate([first, rest]))
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline_and_gate(outputs, ms):
+    """The CPU oracle leg. For every M it computes the oracle (exact float64 sums, untuned) on the gate rows
+    of the first buffer set, timed on all host cores and again on one thread, and compares the GPU's output of
+    that buffer set with it element by element (tests/compare.py tolerances). Returns (cpu_baseline, gate);
+    gate["passed"] is False at the first M with an output out of tolerance, whose message names it."""
+    import numpy as np
+    import compare
     import datagen
     import oracle
-    threads = os.cpu_count() or 1
-    flops, secs = 0.0, 0.0
-    for M in MS:
+    threads = host_cores()
+    flops, secs, secs1, checked = 0.0, 0.0, 0.0, 0
+    gate = {"passed": True, "rows": "0..min(M,64)-1 plus 64 seeded rows, all columns", "outputs_checked": 0}
+    for M in ms:
         d = datagen.set_gauss_n4096(M, N, K)
+        rows = gate_rows(M)
+        args = (d["a"], 0, d["b"], 0, d["scale_a"], 0, d["scale_b"], 0, oracle.BF16)
         t = time.perf_counter()
-        oracle.scaled_gemm(d["a"], 0, d["b"], 0, d["scale_a"], 0, d["scale_b"], 0, oracle.BF16,
-                           accum=oracle.ACC_EXACT, threads=threads)
+        value, sabs, bits = oracle.scaled_gemm(*args, accum=oracle.ACC_EXACT, rows=rows, threads=threads)
         secs += time.perf_counter() - t
-        flops += gemm_flops(M)
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full step: M in {list(MS)}, N=K=4096, every row ({flops:.3g} flop, float64), "
-                      f"{secs:.1f} s"}
+        t = time.perf_counter()
+        oracle.scaled_gemm(*args, accum=oracle.ACC_EXACT, rows=rows, threads=1)
+        secs1 += time.perf_counter() - t
+        flops += 2.0 * rows.size * N * K
+        gpu = outputs[M][rows]
+        try:
+            compare.check(gpu, value, sabs, bits, compare.BF16, f"exactness gate M={M}")
+        except AssertionError as e:
+            gate["passed"] = False
+            gate["message"] = str(e)
+            break
+        checked += gpu.size
+    gate["outputs_checked"] = checked
+    base = {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"the exactness gate's rows of the benchmark step: M in {list(ms)}, N=K=4096, "
+                      f"rows 0..min(M,64)-1 plus 64 seeded rows of each M ({flops:.3g} flop, exact float64 "
+                      f"sums), {secs:.2f} s on {threads} threads",
+            "value_1thread": flops / secs1 / 1e12, "seconds_1thread": round(secs1, 2),
+            "cpu_model": cpu_model()}
+    return base, gate
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock every 200 ms in a background thread through the amdsmi library (the
+    library behind amd-smi); `mean_mhz()` is None when no sample could be taken."""
+
+    def __init__(self, period=0.2):
+        import threading
+        self.period = period
+        self.samples = []
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+            while not self._stop.is_set():
+                clk = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX).get("clk")
+                if isinstance(clk, (int, float)) and clk > 0:
+                    self.samples.append(float(clk))
+                self._stop.wait(self.period)
+            amdsmi.amdsmi_shut_down()
+        except Exception as e:  # no library, no permission, no device: report no clock
+            self.error = f"{type(e).__name__}: {e}"
+
+    def start(self):
+        self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        self._thread.join(timeout=5)
+
+    def mean_mhz(self):
+        return sum(self.samples) / len(self.samples) if self.samples else None
 
 
 # ------------------------------------------------------------------ other workloads
@@ -153,7 +251,7 @@ OTHER = {
 }
 
 
-def run_other(name, steps, warmup):
+def run_other(name, steps, warmup, settle_s=1.5):
     import torch
     import block_scaled_gemm_amd as mm
     import datagen
@@ -317,6 +415,7 @@ def run_other(name, steps, warmup):
         if launch() != mm.MM_OK:
             raise RuntimeError(mm.mm_last_error())
     torch.cuda.synchronize()
+    settle_steps, settle_secs = settle(lambda i: launch(), settle_s) if settle_s > 0 else (0, 0.0)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
@@ -330,7 +429,8 @@ def run_other(name, steps, warmup):
     nbytes = L * ((M + N) * K * op_bytes + M * N * out_bytes) + scale_bytes
     result = {
         "metric": f"{OTHER[name]}: TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": steps, "warmup": warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": True,
+        "steps": steps, "warmup": warmup, "warmup_s": round(settle_secs, 3), "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "data": "synthetic",
         "config": {"workload": OTHER[name], "L": L, "M": M, "N": N, "K": K},
         "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -341,14 +441,44 @@ def run_other(name, steps, warmup):
     print(json.dumps(result), flush=True)
 
 
+def counter_clock_ghz():
+    """The clock the committed counter run measured for the M = 8192 kernel (GRBM_GUI_ACTIVE over the kernel
+    time), or None."""
+    import re
+    try:
+        text = open(COUNTERS).read()
+    except OSError:
+        return None
+    m = re.search(r"counter_clock_ghz: ([0-9.]+)", text)
+    return float(m.group(1)) if m else None
+
+
+def settle(step, min_s):
+    """Untimed steps until at least min_s seconds have passed; returns (steps, seconds)."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        step(n)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= min_s:
+                return n, time.perf_counter() - t0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # 100 untimed steps (~40 ms): the chip's clock and the first-touch costs settle (about 1% over 20 steps)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100, help="untimed steps before the settling phase")
+    ap.add_argument("--settle-s", type=float, default=1.5,
+                    help="untimed steps after --warmup until this many seconds have passed (the clock settles)")
+    ap.add_argument("--windows", type=int, default=5, help="timed windows of the pages' method (median)")
+    ap.add_argument("--window-s", type=float, default=1.0, help="minimum length of each window")
     ap.add_argument("--only-m", type=int, default=0, help="run only this M (for profiler runs)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle leg, and with it the exactness gate (profiler runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device (reads and writes that many bytes) so that "
                          "profiler byte counters can be scaled against a kernel of known traffic")
@@ -361,8 +491,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     if args.workload:
-        # the first launches after the inputs are uploaded run up to 20% slower: 50 warm-up launches by default
-        run_other(args.workload, args.steps if args.steps != 200 else 100, args.warmup if args.warmup != 100 else 50)
+        run_other(args.workload, args.steps if args.steps != 200 else 100, args.warmup if args.warmup != 100 else 50,
+                  args.settle_s)
         return
 
     import torch
@@ -388,6 +518,26 @@ def main():
     dominant = max(ms)
     flops_step = sum(gemm_flops(M) for M in ms)
 
+    # exactness gate (and the CPU oracle leg) before any timing
+    base = gate = None
+    if not args.no_cpu_baseline and not args.only_m:
+        outputs = {}
+        for M in ms:
+            S = data[M]
+            launch(mm, M, S["sets"][0], S, stream)
+        torch.cuda.synchronize()
+        for M in ms:
+            outputs[M] = data[M]["sets"][0][2].view(torch.int16).cpu().numpy().view("uint16")
+        log("exactness gate: oracle on the gate rows of every M ...")
+        base, gate = cpu_baseline_and_gate(outputs, ms)
+        if not gate["passed"]:
+            log(gate["message"])
+            print(json.dumps({"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "gate": gate}),
+                  flush=True)
+            sys.exit(1)
+        log(f"exactness gate passed: {gate['outputs_checked']} outputs; oracle {base['value']:.4f} TFLOP/s on "
+            f"{base['cores']} threads, {base['value_1thread']:.5f} on one")
+
     def step(i, ev=None):
         for M in ms:
             S = data[M]
@@ -402,6 +552,8 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    settle_steps, settle_s = settle(lambda i: step(args.warmup + i), args.settle_s) if args.settle_s > 0 else (0, 0.0)
+    log(f"settled: {args.warmup} warm-up steps, then {settle_steps} more over {settle_s:.2f} s")
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -413,6 +565,39 @@ def main():
     ms_step = start.elapsed_time(stop) / args.steps
     dom_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / args.steps
     log(f"timed {args.steps} steps: {ms_step:.4f} ms/step; M={dominant} kernel {dom_us:.2f} us")
+
+    # the pages' windows: interleaved windows of at least window_s seconds of the same step loop, median,
+    # with the graphics clock sampled meanwhile
+    windows = []
+    sampler = ClockSampler().start()
+    for w in range(args.windows):
+        n = max(1, int(args.window_s / max(ms_step * 1e-3, 1e-6)))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        while True:
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(n):
+                step(i)
+            e1.record()
+            torch.cuda.synchronize()
+            el = e0.elapsed_time(e1) * 1e-3
+            if el >= args.window_s:
+                break
+            n = int(n * args.window_s / max(el, 1e-6) * 1.1) + 1
+        windows.append(flops_step * n / el / 1e12)
+    sampler.stop()
+    med = sorted(windows)[len(windows) // 2] if windows else None
+    clk = sampler.mean_mhz()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    method = {"windows_tflops": [round(w, 1) for w in windows], "median_tflops": round(med, 2) if med else None,
+              "window_s": args.window_s, "clock_mhz_mean": round(clk, 1) if clk else None,
+              "clock_samples": len(sampler.samples), "cus": cus}
+    if clk:
+        method["flop_per_clk_per_cu"] = round(med * 1e12 / (clk * 1e6 * cus), 1)
+        method["frac_bf16_peak_at_clock"] = round(med * 1e12 / (clk * 1e6 * cus * 4096), 4)
+    if sampler.error:
+        method["clock_error"] = sampler.error
+    log(f"windows: {method['windows_tflops']} TFLOP/s, median {method['median_tflops']}; clock {clk} MHz")
 
     # per-M breakdown (each M alone, same rotation)
     per_m = {}
@@ -433,7 +618,8 @@ def main():
         gbs = gemm_bytes(M) / us / 1e3
         per_m[str(M)] = {"us": round(us, 3), "tflops": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
                          "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "hbm_gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+                         "hbm_gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                         "kernel": KERNEL_AT.get(M, "gemm_tile")}
         log(f"M={M}: {us:.2f} us, {tf:.1f} TFLOP/s ({100 * tf / PEAK_FP8_TFLOPS:.1f}% of FP8 peak, "
             f"{100 * tf / PEAK_BF16_TFLOPS:.1f}% of bf16 peak), {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% HBM)")
 
@@ -445,6 +631,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_s": round(settle_s, 3),
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -459,12 +646,15 @@ def main():
                      "traffic": measured_traffic() if dominant == 8192 else None,
                      "peak_unit_note": "dense bf16 MFMA (FP8 operands converted exactly in registers)",
                      "frac_of_fp8_peak": round(achieved / PEAK_FP8_TFLOPS, 4),
-                     "kernel": f"{KERNEL_AT.get(dominant, 'gemm_tile')} M={dominant} N=K=4096", "kernel_us": round(dom_us, 3)},
+                     "kernel": f"{KERNEL_AT.get(dominant, 'gemm_tile')} M={dominant} N=K=4096",
+                     "kernel_us": round(dom_us, 3),
+                     "clock_ghz_counters": counter_clock_ghz() if dominant == 8192 else None},
+        "method": method,
         "per_m": per_m,
     }
-    if not args.no_cpu_baseline and not args.only_m:
-        log("cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline()
+    if gate is not None:
+        result["gate"] = gate
+        result["cpu_baseline"] = base
     print(json.dumps(result), flush=True)
 
 

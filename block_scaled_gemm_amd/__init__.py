@@ -225,8 +225,9 @@ def scaled_gemm(a, b, scale_a, scale_b, out_dtype, scale_result=None, use_fast_a
        after the scales (mm_scaled_gemm_bias).
     """
     torch = _torch()
-    if b.dim() == 2 and a.dim() == 2 and b.shape[0] == a.shape[1] and b.stride(0) == 1 and b.shape[1] != a.shape[1]:
-        b = b.t()  # scaled_mm's column-major mat2 [K, N] -> its [N, K] rows
+    if b.dim() == 2 and a.dim() == 2 and b.shape[0] == a.shape[1] and b.shape[1] > 1 and b.stride(0) == 1 and \
+            b.stride(1) >= b.shape[0]:
+        b = b.t()  # scaled_mm's column-major mat2 [K, N] (told by its strides alone) -> its [N, K] rows
     M, K = a.shape
     N = b.shape[0]
     if b.shape[1] != K:
@@ -383,7 +384,8 @@ def blockscaled_gemm_amax(a, b, sfa, sfb, c_dtype=None, sf_vec_size=32, with_ind
     page's own tensors: E8M0 bytes (float8_e8m0fnu, uint8 or int8) of storage
     shape (L, ceil(MN/128), ceil(K/(4 sf)), 32, 4, 4), or E4M3 bytes (float8_e4m3fn) of that shape with FP4
     operands and sf_vec_size=16. Returns
-    (c [L, M, N], amax [1]) or (c, amax, amax_index [1]) with with_index.
+    (c [L, M, N], amax [1]) or (c, amax, amax_index [1]) with with_index; an FP4 C (c_dtype
+    float4_e2m1fn_x2, FP4 operands only) is [L, M, ceil(N/2)], two values per byte, low nibble first.
     """
     torch = _torch()
     c_dtype = c_dtype or torch.float32
@@ -395,7 +397,9 @@ def blockscaled_gemm_amax(a, b, sfa, sfb, c_dtype=None, sf_vec_size=32, with_ind
     for t in (a, b, sfa, sfb):
         if not t.is_contiguous():
             raise ValueError("operands must be contiguous")
-    c = torch.empty((L, M, N), dtype=c_dtype, device=a.device)
+    c_type = dtype_code(c_dtype)
+    # FP4 C holds two values per byte: rows of ceil(N/2) bytes, the page's (M, ceil(N/2), L) n-major tensor
+    c = torch.empty((L, M, -(-N // 2) if c_type == MM_F4_E2M1 else N), dtype=c_dtype, device=a.device)
     amax = torch.empty((1,), dtype=torch.float32, device=a.device)
     idx = torch.empty((1,), dtype=torch.int64, device=a.device) if with_index else None
     if sfa.element_size() == 1 and sfb.element_size() == 1:
@@ -406,13 +410,13 @@ def blockscaled_gemm_amax(a, b, sfa, sfb, c_dtype=None, sf_vec_size=32, with_ind
         sf_type = MM_SF_E4M3FN if sfa.dtype == torch.float8_e4m3fn else MM_SF_E8M0
         st = mm_blockscaled_gemm_amax_atom(M, N, K, L, a.data_ptr(), b.data_ptr(), ab_type,
                                            sfa.data_ptr(), sfb.data_ptr(), sf_type, sf_vec_size, c.data_ptr(),
-                                           dtype_code(c_dtype), amax.data_ptr(), idx.data_ptr() if with_index else 0,
+                                           c_type, amax.data_ptr(), idx.data_ptr() if with_index else 0,
                                            _stream())
     else:
         if sfa.dtype != torch.float32 or sfb.dtype != torch.float32:
             raise ValueError("scale factors must be float32, or E8M0 bytes for both operands")
         st = mm_blockscaled_gemm_amax(M, N, K, L, a.data_ptr(), b.data_ptr(), ab_type,
-                                      sfa.data_ptr(), sfb.data_ptr(), sf_vec_size, c.data_ptr(), dtype_code(c_dtype),
+                                      sfa.data_ptr(), sfb.data_ptr(), sf_vec_size, c.data_ptr(), c_type,
                                       amax.data_ptr(), idx.data_ptr() if with_index else 0, _stream())
     _check(st)
     return (c, amax, idx) if with_index else (c, amax)

@@ -135,6 +135,78 @@ def pow2_scales(g: np.random.Generator, shape, lo: int = -8, hi: int = 4):
     return np.ldexp(np.ones(shape, dtype=np.float32), e).astype(np.float32)
 
 
+def set_smoke_random_16x8x64(fmt: int = E4M3FN, set_id: int = 40):
+    """The first case of the "mmaemu backends" smoke gate: 16 x 8 x 64 uniformly random codes (all 256 codes,
+    NaN and Inf codes included), scales 1."""
+    g = rng(set_id, fmt)
+    a = g.integers(0, 256, size=(16, 64)).astype(np.uint8)
+    b = g.integers(0, 256, size=(8, 64)).astype(np.uint8)
+    return dict(a=a, b=b, K=64, a_fmt=fmt, b_fmt=fmt, scale_a=np.float32(1.0), scale_b=np.float32(1.0))
+
+
+# the row kinds of the 64 x 64 x 256 adversarial smoke case, row r of A and of B taking kind r % 8
+SMOKE_KINDS = ("every_finite", "one_exponent", "cancel", "subnormal_zero", "max", "minus_zero", "mixed",
+               "one_exponent")
+
+
+def set_smoke_adversarial_64x64x256(fmt: int = E4M3FN, set_id: int = 41):
+    """The second case of the "mmaemu backends" smoke gate: 64 x 64 x 256 adversarial codes. Row r of A and of
+    B is of kind SMOKE_KINDS[r % 8]:
+
+     - every_finite: every finite code of the format once, in a seeded order (the rest of the row +0);
+     - one_exponent: each 16-element block draws its codes from one exponent field (random per block; random
+       sign and mantissa);
+     - cancel: each 16-element block holds 8 random finite codes and their negations, in a shuffled order
+       (the block's values sum to zero);
+     - subnormal_zero: subnormal codes of random sign and +-0;
+     - max: +-max (random sign);
+     - minus_zero: -0 everywhere;
+     - mixed: i.i.d. adversarial codes (adversarial_codes).
+    Scales 1.
+    """
+    g = rng(set_id, fmt)
+    K = 256
+    fin = finite_codes(fmt)
+    mbits = 3 if fmt == E4M3FN else 2
+    top_exp = 15 if fmt == E4M3FN else 30       # largest exponent field of a finite code
+    sub_hi = 7 if fmt == E4M3FN else 3
+    maxcode = 0x7E if fmt == E4M3FN else 0x7B
+
+    def row(kind):
+        if kind == "every_finite":
+            r = np.zeros(K, np.uint8)
+            r[: fin.size] = g.permutation(fin)
+            return r
+        if kind == "one_exponent":
+            blocks = []
+            for _ in range(K // 16):
+                e = int(g.integers(0, top_exp + 1))
+                m = g.integers(0, 1 << mbits, size=16)
+                if fmt == E4M3FN and e == 15:
+                    m = np.minimum(m, 6)          # mantissa 7 with exponent 15 is the NaN code
+                sign = (g.random(16) < 0.5).astype(np.int64) << 7
+                blocks.append(((e << mbits) | m | sign).astype(np.uint8))
+            return np.concatenate(blocks)
+        if kind == "cancel":
+            blocks = []
+            for _ in range(K // 16):
+                half = fin[g.integers(0, fin.size, size=8)]
+                blocks.append(g.permutation(np.concatenate([half, half ^ 0x80])).astype(np.uint8))
+            return np.concatenate(blocks)
+        if kind == "subnormal_zero":
+            code = g.integers(0, sub_hi + 1, size=K)
+            return (code | ((g.random(K) < 0.5).astype(np.int64) << 7)).astype(np.uint8)
+        if kind == "max":
+            return (maxcode | ((g.random(K) < 0.5).astype(np.int64) << 7)).astype(np.uint8)
+        if kind == "minus_zero":
+            return np.full(K, 0x80, np.uint8)
+        return adversarial_codes(g, (K,), fmt)
+
+    a = np.stack([row(SMOKE_KINDS[r % 8]) for r in range(64)])
+    b = np.stack([row(SMOKE_KINDS[r % 8]) for r in range(64)])
+    return dict(a=a, b=b, K=K, a_fmt=fmt, b_fmt=fmt, scale_a=np.float32(1.0), scale_b=np.float32(1.0))
+
+
 # ----------------------------------------------------------------- sets
 
 def set_256_cubed(M=256, N=256, K=256):

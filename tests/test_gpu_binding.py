@@ -144,3 +144,38 @@ def test_helper_errors_raise_before_launch():
 
 def mm_atom_bytes(MN, K, L, sf):
     return L * -(-MN // 128) * -(-K // (4 * sf)) * 512
+
+
+def test_square_column_major_mat2_matches_raw_abi():
+    """A square weight's .t() (scaled_mm's column-major mat2 [K, N] with N == K) is read as its
+    [N, K] transpose, told by its strides alone."""
+    M, N, K = 96, 512, 512
+    g = datagen.rng(47, 0)
+    a = datagen.gauss_codes(g, (M, K), 64.0)
+    w = datagen.gauss_codes(g, (N, K), 64.0)
+    out = mm.scaled_gemm(fp8(a), fp8(w).t(), f32(0.5), f32(0.25), torch.bfloat16)
+    raw = gu.scaled_gemm(a, E4M3FN, w, E4M3FN, K, 0.5, 0, 0.25, 0, BF16)
+    np.testing.assert_array_equal(bits(out), raw)
+
+
+@pytest.mark.parametrize("N", [71, 72])
+def test_blockscaled_helper_fp4_c_matches_raw_abi(N):
+    """FP4 C through the helper: [L, M, ceil(N/2)] bytes, bitwise the raw call's (odd N included)."""
+    L, M, K, sf = 2, 96, 256, 32
+    w = datagen.set_fp4_l8_2048x2048x8192(L, M, N, K, sf, config=48)
+    u8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    c, amax = mm.blockscaled_gemm_amax(u8(w["a"]), u8(w["b"]), u8(w["sfa"]), u8(w["sfb"]), torch.float4_e2m1fn_x2,
+                                       sf_vec_size=sf, ab_format=mm.MM_F4_E2M1)
+    torch.cuda.synchronize()
+    assert tuple(c.shape) == (L, M, -(-N // 2))
+    es = -(-N // 2)
+    tc = torch.full((L * M * es,), 0x5A, dtype=torch.uint8, device=DEV)
+    tam = torch.zeros((1,), dtype=torch.float32, device=DEV)
+    ta, tb, tsa, tsb = u8(w["a"]), u8(w["b"]), u8(w["sfa"]), u8(w["sfb"])
+    st = mm.mm_blockscaled_gemm_amax_atom(M, N, K, L, ta.data_ptr(), tb.data_ptr(), mm.MM_F4_E2M1, tsa.data_ptr(),
+                                          tsb.data_ptr(), mm.MM_SF_E8M0, sf, tc.data_ptr(), mm.MM_F4_E2M1,
+                                          tam.data_ptr(), 0, gu.stream())
+    assert st == mm.MM_OK, mm.mm_last_error()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(c.view(torch.uint8).cpu().numpy().reshape(-1), tc.cpu().numpy())
+    assert float(amax.item()) == float(tam.item())

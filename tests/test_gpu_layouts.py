@@ -71,7 +71,7 @@ def test_bmm_with_b_as_k_by_n(L, M, N, K, d_type, fast):
     for l in range(L):
         value, sabs, obits = oracle.scaled_gemm(a[l], E4M3FN, np.ascontiguousarray(b_kn[l].T), E5M2, 0.5, 0, 0.125,
                                                 0, d_type, scale_result=sr,
-                                                accum=oracle.ACC_EXACT if fast else oracle.ACC_F32_CHUNKS)
+                                                accum=oracle.ACC_EXACT)
         compare.check(got[l], value, sabs, obits, d_type, f"bmm item {l}")
 
 
@@ -95,7 +95,7 @@ def check_layout(w, d_type, ta, tb, fast=False, scale_result=None, fmt=(E4M3FN, 
     value, sabs, obits = oracle.grouped_gemm_layout(w["a"], fmt[0], w["b"], fmt[1], w["sizes"], w["offsets"],
                                                     w["scale_a"], w["scale_b"], d_type, ta, tb,
                                                     scale_result=scale_result,
-                                                    accum=oracle.ACC_EXACT if fast else oracle.ACC_F32_CHUNKS)
+                                                    accum=oracle.ACC_EXACT)
     if ta:
         compare.check(gpu.reshape(-1, gpu.shape[-1]), value.reshape(-1, value.shape[-1]),
                       sabs.reshape(-1, sabs.shape[-1]), obits.reshape(-1, obits.shape[-1]), d_type, "grouped TN/TT")
@@ -146,13 +146,14 @@ def test_grouped_contraction_split_full_size():
     w = datagen.set_grouped_layout(G, S, N, K, 0, True, False, config=9)
     gpu = gu.scaled_gemm_grouped_layout(w["a"], E4M3FN, w["b"], E4M3FN, w["sizes"], w["offsets"], w["scale_a"],
                                         w["scale_b"], BF16, True, False)
-    rows = np.sort(datagen.rng(91, 0).choice(N, 16, replace=False))
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(0, N, 64) + datagen.rng(91, 0).integers(0, 64, N // 64),
+                                     np.arange(N - 16, N)]))  # a row in every 64-row band of the block
     for g in range(G):
         r0, s = int(w["offsets"][g]), int(w["sizes"][g])
         at = np.ascontiguousarray(w["a"][r0:r0 + s].T)
         bt = np.ascontiguousarray(w["b"][r0:r0 + s].T)
         value, sabs, obits = oracle.scaled_gemm(at, E4M3FN, bt, E4M3FN, w["scale_a"], 0, w["scale_b"], 0, BF16,
-                                                accum=oracle.ACC_F32_CHUNKS, rows=rows)
+                                                accum=oracle.ACC_EXACT, rows=rows)
         compare.check(gpu[g][rows], value, sabs, obits, BF16, f"group {g}")
 
 
@@ -173,7 +174,7 @@ def test_contraction_split_uses_exactly_the_listed_rows(tb):
             continue
         value, sabs, obits = oracle.scaled_gemm(np.ascontiguousarray(w["a"][of:of + sz].T), E4M3FN,
                                                 np.ascontiguousarray(bt_all[:, of:of + sz]), E4M3FN, w["scale_a"],
-                                                0, w["scale_b"], 0, F32, accum=oracle.ACC_F32_CHUNKS)
+                                                0, w["scale_b"], 0, F32, accum=oracle.ACC_EXACT)
         compare.check(gpu[g], value, sabs, obits, F32, f"group {g}")
 
 

@@ -21,11 +21,22 @@ DT_NAME = {F32: "f32", BF16: "bf16", F16: "f16", E4M3FN: "e4m3", E5M2: "e5m2"}
 
 
 def sample_rows(M, n_each=16, seed=0):
-    if M <= 3 * n_each:
+    """Rows checked at sizes where every row would take the oracle too long: tile_rows with `n_each` rows at
+    each edge."""
+    return tile_rows(M, band=64, edge=n_each, seed=seed)
+
+
+def tile_rows(M, band=64, edge=16, seed=0):
+    """The first and last `edge` rows and one seeded row in every `band`-row band: every workgroup tile row of
+    every kernel (tiles are 64 to 256 rows high, all aligned to 64) has at least one checked row, over all
+    columns."""
+    if M <= 2 * edge + band:
         return np.arange(M)
     rng = np.random.default_rng(seed)
-    mid = rng.choice(np.arange(n_each, M - n_each), size=n_each, replace=False)
-    return np.unique(np.concatenate([np.arange(n_each), mid, np.arange(M - n_each, M)]))
+    starts = np.arange(0, M, band)
+    pick = starts + rng.integers(0, band, size=starts.size)
+    pick = pick[pick < M]
+    return np.unique(np.concatenate([np.arange(edge), pick, np.arange(M - edge, M)]))
 
 
 def check_gemm(d, sa_mode, sb_mode, d_type, fast, rows=None, scale_result=None, what="", ldd=None):
@@ -90,21 +101,21 @@ def test_gemm_256_cubed(fast):
 @pytest.mark.parametrize("M", datagen.BENCH_MS)
 def test_gauss_n4096_full_size(M):
     d = datagen.set_gauss_n4096(M)
-    rows = None if M <= 64 else sample_rows(M)
+    rows = None if M <= 256 else tile_rows(M, seed=M)
     check_gemm(d, 0, 0, BF16, fast=False, rows=rows, what=f"gauss N=K=4096 M={M}")
 
 
-@pytest.mark.parametrize("M", [16, 64, 256, 2048])
+@pytest.mark.parametrize("M", datagen.BENCH_MS)
 def test_adversarial_n4096_full_size(M):
     d = datagen.set_adversarial_n4096(M)
-    rows = None if M <= 64 else sample_rows(M)
+    rows = None if M <= 256 else tile_rows(M, seed=M + 1)
     check_gemm(d, 0, 0, BF16, fast=False, rows=rows, what=f"adversarial N=K=4096 M={M}")
 
 
-@pytest.mark.parametrize("M", [16, 2048])
+@pytest.mark.parametrize("M", [16, 64, 256, 2048])
 def test_gauss_n4096_fast_accumulation(M):
     d = datagen.set_gauss_n4096(M)
-    check_gemm(d, 0, 0, BF16, fast=True, rows=None if M <= 64 else sample_rows(M), what=f"fast M={M}")
+    check_gemm(d, 0, 0, BF16, fast=True, rows=None if M <= 256 else tile_rows(M, seed=2), what=f"fast M={M}")
 
 
 # ------------------------------------------------------------------ ragged shapes, padding, all output types
@@ -217,7 +228,7 @@ def test_block_scales_small(M, N, K, sb_mode):
 
 def test_block_scaled_full_size():
     d = datagen.set_block_scaled_4096x14336x4096()
-    check_gemm(d, 1, 2, BF16, False, rows=sample_rows(4096, 8), what="block-scaled 4096x14336x4096")
+    check_gemm(d, 1, 2, BF16, False, rows=tile_rows(4096, seed=3), what="block-scaled 4096x14336x4096")
 
 
 # ------------------------------------------------------------------ MX factors per 32 + amax: L = 8, 2048 x 2048 x 8192
@@ -295,6 +306,47 @@ def test_sf32_amax_without_index():
     assert amax == float(np.max(np.abs(c.view(np.float32))))
 
 
+def factors_as_read(f):
+    """The factor each fp32 scale factor acts as in mm_blockscaled_gemm_amax (its contract in include/mm.h):
+    only the exponent field e is read, as an E8M0 code, so x acts as 2^(e - 127): 2^floor(log2|x|) for a
+    normal x whatever its sign and mantissa, 2^-127 for zero and fp32 subnormals (e = 0), and NaN for Inf and
+    NaN (e = 255)."""
+    e = (np.asarray(f, np.float32).view(np.uint32) >> 23) & 0xFF
+    out = np.ldexp(1.0, e.astype(np.int64) - 127)
+    out[e == 255] = np.nan
+    return out.astype(np.float32)
+
+
+def test_sf32_factors_read_by_their_exponent_field():
+    """Non-power-of-two, negative, zero, subnormal, Inf and NaN fp32 factors: the GPU result equals the
+    oracle's on the factors as read (2^floor(log2|x|), 2^-127 for zero, NaN for Inf / NaN), element by
+    element; the factors' own values would differ by up to 2x."""
+    L, M, N, K = 2, 96, 136, 512
+    w = datagen.set_mx_l8_2048x2048x8192(L, M, N, K)
+    g = np.random.default_rng(77)
+    for key in ("sfa", "sfb"):
+        f = w[key] * g.uniform(1.0, 2.0, size=w[key].shape).astype(np.float32)  # mantissas other than 1
+        f = np.where(g.random(f.shape) < 0.3, -f, f).astype(np.float32)          # negative factors
+        zero = g.random(f.shape) < 0.02
+        f[zero] = 0.0
+        f.reshape(-1)[g.choice(f.size, 5, replace=False)] = np.float32(1e-40)   # fp32 subnormals
+        w[key] = f
+    w["sfa"][1, 7, 3] = np.float32(np.inf)   # row 7 of item 1: NaN
+    w["sfb"][0, 11, 0] = np.float32(np.nan)  # column 11 of item 0: NaN
+    assert np.any(w["sfa"] < 0) and np.any(w["sfa"] == 0)
+    c, amax, idx = gu.blockscaled_gemm_amax(w["a"], w["b"], 0, w["sfa"], w["sfb"], F32)
+    value, sabs, bits, _, _ = oracle.blockscaled_gemm_amax(w["a"], w["b"], 0, factors_as_read(w["sfa"]),
+                                                           factors_as_read(w["sfb"]), 32, F32)
+    compare.check(c, value, sabs, bits, F32, "fp32 factors as read")
+    cf = c.view(np.float32)
+    assert np.isnan(cf[1, 7]).all() and np.isnan(cf[0, :, 11]).all() and np.isnan(amax)
+    # and the factors taken at face value would not pass: the reading is what the kernel does
+    v_face, s_face, _, _, _ = oracle.blockscaled_gemm_amax(w["a"], w["b"], 0, np.abs(np.nan_to_num(w["sfa"])),
+                                                           np.abs(np.nan_to_num(w["sfb"])), 32, F32)
+    fin = np.isfinite(cf)
+    assert (np.abs(cf[fin] - v_face[fin]) > 2.0 ** -20 * s_face[fin]).mean() > 0.5
+
+
 def test_sf32_e5m2_unit_scales_is_plain_gemm():
     """The cuDNN example shape (m, n, k = 512, 256, 256, sf 32, E5M2, all-ones scales)."""
     g = np.random.default_rng(0)
@@ -316,9 +368,13 @@ def test_production_tiles_sf32(L):
 
 
 def test_mx_full_size():
+    """L = 8, 2048 x 2048 x 8192 with fp32 factors: every output of every batch item against the oracle, the
+    amax and its index against the oracle's (and bit-exact against the GPU's own C)."""
     w = datagen.set_mx_l8_2048x2048x8192()
-    rows = sample_rows(2048, 4)
-    c, amax, idx, value, sabs = check_amax_case(w, F32, rows=rows)
+    c, amax, idx, value, sabs = check_amax_case(w, F32)
+    check_amax_index_against_oracle(idx, value, sabs)
+    v = np.abs(value.reshape(-1))
+    assert abs(amax - v.max()) <= 2.0 ** -20 * sabs.reshape(-1)[np.argmax(v)]
     cf = np.abs(c.view(np.float32).reshape(-1))
     assert amax == float(cf.max()) and idx == int(np.argmax(cf))
 
@@ -408,7 +464,7 @@ def test_atom_mx_full_size():
     """The MX set (L=8, 2048 x 2048 x 8192) with E8M0 atom factors, on the 256x256 tile: sampled rows
     against the oracle, the whole C bitwise against the fp32-factor entry."""
     w = datagen.set_mx_atom_l8_2048x2048x8192()
-    rows = sample_rows(2048, 4)
+    rows = tile_rows(2048, seed=4)
     c, amax, idx, value, sabs = check_atom_case(w, F32, rows=rows)
     cf = np.abs(c.view(np.float32).reshape(-1))
     assert amax == float(cf.max()) and idx == int(np.argmax(cf))
@@ -470,7 +526,7 @@ def test_nvfp4_production_tiles(L):
 
 def test_nvfp4_full_size():
     w = datagen.set_nvfp4_l8_2048x2048x8192()
-    check_nvfp4_case(w, F32, rows=sample_rows(2048, 4))
+    check_nvfp4_case(w, F32, rows=tile_rows(2048, seed=5))
 
 
 # ------------------------------------------------------------------ FP4 (E2M1) C with FP4 operands
@@ -576,7 +632,7 @@ def test_grouped_rows_of_no_group_are_not_written():
 def test_grouped_full_size():
     """The grouped bench workload: 8 groups, 8192 packed rows, N = K = 4096, slow, bf16 out; sampled rows."""
     w = datagen.set_grouped_8x8192x4096x4096()
-    check_grouped(w, BF16, rows=sample_rows(8192, 16, seed=3))
+    check_grouped(w, BF16, rows=tile_rows(8192, seed=6))
 
 
 # ------------------------------------------------------------------ FP4 (E2M1) operands, page-native factors
@@ -629,7 +685,7 @@ def test_fp4_padding_is_not_read():
 def test_fp4_full_size():
     """L=8, 2048 x 2048 x 8192 FP4 with factors per 32 (the FP4 bench workload): sampled rows."""
     w = datagen.set_fp4_l8_2048x2048x8192()
-    rows = sample_rows(2048, 4)
+    rows = tile_rows(2048, seed=7)
     c, amax, idx, value, sabs = check_fp4_case(w, F32, rows=rows)
     cf = np.abs(c.view(np.float32).reshape(-1))
     assert amax == float(cf.max()) and idx == int(np.argmax(cf))
@@ -656,7 +712,7 @@ def test_k_tail_full_size(which):
         d, dt, sr = datagen.set_e4m3_out_8192x28672x8200(), E4M3FN, np.float32(1 / 16)
     else:
         d, dt, sr = datagen.set_e5m2_f16_8192x28672x8200(), F16, None
-    rows = np.array([0, 1, 2, 4095, 8190, 8191])
+    rows = tile_rows(8192, seed=8 if which == "5a" else 9)
     check_gemm(d, 0, 0, dt, False, rows=rows, scale_result=sr, what=f"K tail 8192x28672x8200 ({which}) full size")
 
 
