@@ -1,5 +1,6 @@
 // Skinny-M instantiations (M <= 64, per-tensor scales) and the small helper kernels.
 #include "mm_launch.hpp"
+#include "mm_skinny_k.hpp"
 
 namespace mmfp8 {
 
@@ -46,9 +47,19 @@ static hipError_t skinny_mode(int mt, int fa, int fb, const GemmArgs& p, int gri
     else if (fa == 1 && fb == 1) MMFP8_SK(MT, 1, 1);          \
     else if (fa == 0 && fb == 1) MMFP8_SK(MT, 0, 1);          \
     else MMFP8_SK(MT, 1, 0);
+#define MMFP8_SKK(A, B)                                                                                      \
+    hipLaunchKernelGGL((gemm_skinny_k<4, 1, MODE, A, B, 16, 2>), dim3(grid), dim3(16 * 64), 0, s, p)
     if (mt == 1) { MMFP8_SKF(1) }
     else if (mt == 2) { MMFP8_SKF(2) }
-    else { MMFP8_SKF(4) }
+    else if ((p.K + kBK - 1) / kBK > 32) { MMFP8_SKF(4) }
+    else {
+        // M = 33 .. 64, K <= 32 steps: sixteen waves with two steps each in flight (gemm_skinny_k)
+        if (fa == 0 && fb == 0) MMFP8_SKK(0, 0);
+        else if (fa == 1 && fb == 1) MMFP8_SKK(1, 1);
+        else if (fa == 0 && fb == 1) MMFP8_SKK(0, 1);
+        else MMFP8_SKK(1, 0);
+    }
+#undef MMFP8_SKK
 #undef MMFP8_SKF
 #undef MMFP8_SK
     return hipGetLastError();

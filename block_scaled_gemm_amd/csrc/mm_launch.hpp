@@ -28,9 +28,11 @@ constexpr int cfg_pipe(int cfg, int mode, int fmt) {
 }
 
 // gemm_skinny: waves per workgroup and K steps in flight per wave, by MT
-// (M <= 16 MT). Sixteen waves with two steps each put a K = 4096 B tile in
-// flight at once; with MT = 4 the A fragments need more registers than 16
-// waves per CU leave, so that case runs 8 waves with one step each.
+// (M <= 16 MT; MT = 1, 2). Sixteen waves with two steps each put a K = 4096 B
+// tile in flight at once. M = 33 .. 64 (MT = 4) with K <= 4096 runs
+// gemm_skinny_k, whose sixteen waves also keep two steps each in flight (with
+// gemm_skinny at MT = 4 the A fragments need more registers than 16 waves per
+// CU leave); a longer K runs gemm_skinny<4> with 8 waves of one step.
 constexpr int skinny_waves(int mt) { return mt == 4 ? 8 : 16; }
 constexpr int skinny_steps(int mt) { return mt == 4 ? 1 : 2; }
 

@@ -195,6 +195,23 @@ def test_production_tiles_per_tensor(M, N, K, fast):
     check_gemm(d, 0, 0, BF16, fast, rows=sample_rows(M, 8), what=f"{M}x{N}x{K} fast={fast}")
 
 
+# M = 33 .. 64 with K <= 4096 runs the skinny kernel with sixteen waves and two K steps each in flight (K = 4096,
+# a ragged K = 4040 whose last chunk straddles a 16-byte boundary, K = 136), a longer K the eight-wave one
+# (K = 8200)
+@pytest.mark.parametrize("M,N,K,fast,d_type", [(64, 4096, 4096, False, BF16), (33, 1000, 4040, True, F32),
+                                               (48, 777, 8200, False, E4M3FN), (64, 130, 8200, True, F16),
+                                               (40, 4100, 136, False, E5M2)])
+def test_skinny_m33_to_64(M, N, K, fast, d_type):
+    g = np.random.default_rng(M * 31 + K)
+    lda, ldb = (K + 7) // 8 * 8 + 8, (K + 7) // 8 * 8
+    a = np.full((M, lda), 0x7F, np.uint8); a[:, :K] = datagen.gauss_codes(g, (M, K), 64.0)
+    b = np.full((N, ldb), 0x7F, np.uint8); b[:, :K] = datagen.gauss_codes(g, (N, K), 64.0, E5M2 if fast else E4M3FN)
+    d = dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E5M2 if fast else E4M3FN, scale_a=np.float32(0.5),
+             scale_b=np.float32(2.0 ** -7))
+    sr = np.float32(1 / 8) if d_type in (E4M3FN, E5M2) else None
+    check_gemm(d, 0, 0, d_type, fast, scale_result=sr, what=f"skinny {M}x{N}x{K}", ldd=N + 3)
+
+
 @pytest.mark.parametrize("sb_mode", [1, 2], ids=["1x128", "128x128"])
 @pytest.mark.parametrize("M", [2048, 1024, 200], ids=["128x128", "128x128-kgroups", "64x64"])
 def test_production_tiles_block_scaled(M, sb_mode):
@@ -737,6 +754,7 @@ def _bias_values(bits, d_type):
 
 @pytest.mark.parametrize("d_type", [BF16, F16, F32], ids=["bf16", "f16", "f32"])
 @pytest.mark.parametrize("M,N,K,fast", [(16, 4100, 1032, False),    # skinny
+                                        (64, 4100, 1032, True),      # skinny, sixteen waves of two steps
                                         (200, 4096, 1032, True),     # K split
                                         (1000, 1030, 1032, False),   # 128x128 tiles, ragged N and K
                                         (2048, 2048, 520, True)])    # 256x256 / 128x256 tiles
