@@ -25,6 +25,7 @@ MM_OK, MM_ERR_INVALID_ARGUMENT, MM_ERR_UNSUPPORTED, MM_ERR_MISALIGNED, MM_ERR_DE
 MM_F8_E4M3FN, MM_F8_E5M2, MM_F32, MM_BF16, MM_F16, MM_F4_E2M1 = 0, 1, 2, 3, 4, 5
 MM_SCALE_TENSOR, MM_SCALE_1x128, MM_SCALE_128x128 = 0, 1, 2
 MM_SF_E8M0, MM_SF_E4M3FN = 0, 1
+MM_NOALLOC_SCRATCH_BYTES = 160 << 20  # the scratch array of mm_scaled_gemm_grouped_layout_noalloc
 
 # One HIP runtime per process. PyTorch ships its own HIP runtime with the same
 # soname as the system one libmmfp8 is linked against; loaded first, it also
@@ -65,13 +66,17 @@ _lib.mm_grouped_workspace_bytes.restype = _I
 _lib.mm_scaled_gemm_grouped_layout.argtypes = [_I64, _I64, _I64, _I64, _I, _I, _P, _I, _I64, _P, _I, _I64, _I64,
                                                _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _P, ctypes.c_uint64, _I, _P]
 _lib.mm_scaled_gemm_grouped_layout.restype = _I
+_lib.mm_scaled_gemm_grouped_layout_noalloc.argtypes = [_I64, _I64, _I64, _I64, _I, _I, _P, _I, _I64, _P, _I, _I64,
+                                                       _I64, _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I, _P]
+_lib.mm_scaled_gemm_grouped_layout_noalloc.restype = _I
 _lib.mm_debug_convert.argtypes = [_P, _P, _I, _I64, _P]
 _lib.mm_debug_convert.restype = _I
 _lib.mm_last_error.restype = ctypes.c_char_p
 _lib.mm_version.restype = ctypes.c_char_p
 
 EXPORTED = ("mm_scaled_gemm", "mm_scaled_gemm_bias", "mm_scaled_gemm_batched", "mm_scaled_gemm_grouped",
-            "mm_scaled_gemm_grouped_layout", "mm_grouped_workspace_bytes", "mm_transpose_u8",
+            "mm_scaled_gemm_grouped_layout", "mm_scaled_gemm_grouped_layout_noalloc", "mm_grouped_workspace_bytes",
+            "mm_transpose_u8",
             "mm_blockscaled_gemm_amax",
             "mm_blockscaled_gemm_amax_atom", "mm_last_error", "mm_version", "mm_debug_convert")
 
@@ -147,6 +152,18 @@ def mm_scaled_gemm_grouped_layout(batch_sum, N, K, G, transpose_a, transpose_b, 
                                               scale_result or None, d or None, d_type, ldd, stride_d,
                                               workspace or None, workspace_bytes, int(use_fast_accum),
                                               stream or None)
+
+
+def mm_scaled_gemm_grouped_layout_noalloc(batch_sum, N, K, G, transpose_a, transpose_b, a, a_type, lda, b, b_type,
+                                          ldb, stride_b, batch_sizes, batch_offsets, scale_a, scale_b, scale_result, d,
+                                          d_type, ldd, stride_d, use_fast_accum, stream) -> int:
+    """Raw call of the C function (the library's own scratch array in place of a workspace); pointers and the
+    stream are integers (0 = NULL). Returns the status."""
+    return _lib.mm_scaled_gemm_grouped_layout_noalloc(batch_sum, N, K, G, int(transpose_a), int(transpose_b),
+                                                      a or None, a_type, lda, b or None, b_type, ldb, stride_b,
+                                                      batch_sizes or None, batch_offsets or None, scale_a or None,
+                                                      scale_b or None, scale_result or None, d or None, d_type, ldd,
+                                                      stride_d, int(use_fast_accum), stream or None)
 
 
 def mm_blockscaled_gemm_amax(M, N, K, L, a, b, ab_type, sfa, sfb, sf_vec_size, c, c_type, amax, amax_index,

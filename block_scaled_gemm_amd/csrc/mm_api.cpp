@@ -603,3 +603,70 @@ mm_status mm_scaled_gemm_grouped_layout(int64_t batch_sum, int64_t N, int64_t K,
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ no-allocation variant
+//
+// mm_scaled_gemm_grouped_layout_noalloc: the same call with the library's own
+// device scratch array in place of the caller's workspace. The array is a
+// file-scope __device__ object, so every GPU the library runs on holds one copy
+// of it from the code object's load until the process ends, and nothing is
+// allocated per call. In host code its name is a host-side stand-in: the
+// device address comes from hipGetSymbolAddress, once per device with that
+// device current, and only that address reaches kernels.
+
+static __device__ __attribute__((aligned(256))) uint8_t scratch[MM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[64] = {};
+
+mm_status scratch_address(uint8_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(MM_ERR_UNSUPPORTED, "device index %d is beyond 63", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return device_status(e, "hipGetSymbolAddress of the scratch array");
+        g_scratch_ptr[dev] = static_cast<uint8_t*>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
+    return MM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mm_status mm_scaled_gemm_grouped_layout_noalloc(int64_t batch_sum, int64_t N, int64_t K, int64_t G, int transpose_a,
+                                                int transpose_b, const void* a, int a_type, int64_t lda,
+                                                const void* b, int b_type, int64_t ldb, int64_t stride_b,
+                                                const int32_t* batch_sizes, const int32_t* batch_offsets,
+                                                const float* scale_a, const float* scale_b,
+                                                const float* scale_result, void* d, int d_type, int64_t ldd,
+                                                int64_t stride_d, int use_fast_accum, void* stream) {
+    g_error.clear();
+    if ((transpose_a != 0 && transpose_a != 1) || (transpose_b != 0 && transpose_b != 1))
+        return fail(MM_ERR_INVALID_ARGUMENT, "transpose_a and transpose_b must be 0 or 1");
+    uint64_t need = 0;
+    if (const mm_status st = mm_grouped_workspace_bytes(batch_sum, N, K, G, transpose_a, transpose_b, &need))
+        return st;
+    if (need > (uint64_t)MM_NOALLOC_SCRATCH_BYTES)
+        return fail(MM_ERR_UNSUPPORTED,
+                    "this layout and size need %llu bytes of workspace, more than the library's %llu-byte scratch "
+                    "array; use mm_scaled_gemm_grouped_layout with a workspace",
+                    (unsigned long long)need, (unsigned long long)MM_NOALLOC_SCRATCH_BYTES);
+    uint8_t* ws = nullptr;
+    if (need > 0) {
+        if (const mm_status st = scratch_address(&ws)) return st;
+    }
+    return mm_scaled_gemm_grouped_layout(batch_sum, N, K, G, transpose_a, transpose_b, a, a_type, lda, b, b_type, ldb,
+                                         stride_b, batch_sizes, batch_offsets, scale_a, scale_b, scale_result, d,
+                                         d_type, ldd, stride_d, ws, need > 0 ? (uint64_t)MM_NOALLOC_SCRATCH_BYTES : 0,
+                                         use_fast_accum, stream);
+}
+
+}  // extern "C"

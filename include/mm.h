@@ -405,6 +405,42 @@ mm_status mm_blockscaled_gemm_amax_atom(int64_t M, int64_t N, int64_t K, int64_t
                                         float* amax, int64_t* amax_index,
                                         void* stream);
 
+/*
+ * mm_scaled_gemm_grouped_layout_noalloc -- mm_scaled_gemm_grouped_layout for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same arguments
+ * and result without the workspace, whose role a scratch array of the
+ * library takes. Nothing is allocated or freed by the call.
+ *
+ *  The scratch array is MM_NOALLOC_SCRATCH_BYTES bytes of device memory in
+ *  the library's code object: every GPU the library is used on holds one copy
+ *  from the library's load until the process ends. A layout and size whose
+ *  mm_grouped_workspace_bytes exceeds it -> MM_ERR_UNSUPPORTED (nothing
+ *  enqueued). The NT layout needs none. Nothing in the array needs clearing:
+ *  the packing kernels write every byte the GEMM reads.
+ *  All calls on one GPU share its array (it keeps the last call's contents):
+ *  calls that overlap on one GPU (on different streams, or from different
+ *  threads) race and give unspecified results. Calls on one stream are ordered
+ *  and safe.
+ *  The first call on a device that needs the array resolves its device
+ *  address (hipGetSymbolAddress, with the device current; a HIP query, no
+ *  work enqueued) before the remaining arguments are validated; a failure
+ *  there is MM_ERR_DEVICE.
+ * Everything else (arguments, layouts, limits, errors) is
+ * mm_scaled_gemm_grouped_layout's.
+ */
+#define MM_NOALLOC_SCRATCH_BYTES (160ull << 20)
+mm_status mm_scaled_gemm_grouped_layout_noalloc(int64_t batch_sum, int64_t N, int64_t K, int64_t G,
+                                                int transpose_a, int transpose_b,
+                                                const void* a, int a_type, int64_t lda,
+                                                const void* b, int b_type, int64_t ldb, int64_t stride_b,
+                                                const int32_t* batch_sizes, const int32_t* batch_offsets,
+                                                const float* scale_a, const float* scale_b,
+                                                const float* scale_result,
+                                                void* d, int d_type, int64_t ldd, int64_t stride_d,
+                                                int use_fast_accum,
+                                                void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if
  * none). The pointer stays valid until the thread's next mm_* call. */
 const char* mm_last_error(void);

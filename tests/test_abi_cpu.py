@@ -28,7 +28,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"mm_scaled_gemm", "mm_scaled_gemm_bias", "mm_scaled_gemm_batched", "mm_scaled_gemm_grouped",
-                          "mm_scaled_gemm_grouped_layout", "mm_grouped_workspace_bytes", "mm_transpose_u8",
+                          "mm_scaled_gemm_grouped_layout", "mm_scaled_gemm_grouped_layout_noalloc",
+                          "mm_grouped_workspace_bytes", "mm_transpose_u8",
                           "mm_blockscaled_gemm_amax", "mm_blockscaled_gemm_amax_atom", "mm_last_error",
                           "mm_version", "mm_debug_convert"}
     lib = ctypes.CDLL(mm.LIB_PATH)
@@ -387,3 +388,37 @@ def test_transpose_zero_sizes_and_forced_failure(monkeypatch):
     assert mm.mm_transpose_u8(2, 0, 4, 0, 4, 0, 0, 0, 0, 0) == mm.MM_OK
     monkeypatch.setenv("MM_TEST_FORCE_FAIL", "launch")
     assert mm.mm_transpose_u8(2, 4, 4, P, 4, 16, P, 4, 16, 0) == mm.MM_ERR_DEVICE
+
+
+def noalloc(**kw):
+    args = dict(batch_sum=600, N=136, K=520, G=5, transpose_a=0, transpose_b=0, a=P, a_type=0, lda=520, b=P,
+                b_type=0, ldb=136, stride_b=520 * 136, batch_sizes=P, batch_offsets=P, scale_a=P, scale_b=P,
+                scale_result=0, d=P, d_type=3, ldd=136, stride_d=0, use_fast_accum=0, stream=0)
+    args.update(kw)
+    return mm.mm_scaled_gemm_grouped_layout_noalloc(**args)
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MM_NOALLOC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == mm.MM_NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(transpose_a=2), mm.MM_ERR_INVALID_ARGUMENT, "must be 0 or 1"),
+    (dict(batch_sum=-1), mm.MM_ERR_INVALID_ARGUMENT, "must be >= 0"),
+    # NN with G N K above the scratch array: refused before any HIP call
+    (dict(G=64, N=2048, K=2048, ldb=2048, stride_b=2048 * 2048), mm.MM_ERR_UNSUPPORTED, "scratch array"),
+    (dict(transpose_a=1, batch_sum=1 << 21, N=4096, K=4096, lda=4096, ldb=4096, G=2), mm.MM_ERR_UNSUPPORTED,
+     "scratch array"),
+])
+def test_noalloc_rejects_before_any_hip_call(kw, status, msg):
+    assert noalloc(**kw) == status
+    assert msg in mm.mm_last_error()
+
+
+def test_noalloc_nt_layout_needs_no_scratch(monkeypatch):
+    # NT packs nothing: the call goes straight to the grouped GEMM's validation (forced failure after it)
+    monkeypatch.setenv("MM_TEST_FORCE_FAIL", "launch")
+    assert noalloc(transpose_b=1, ldb=520) == mm.MM_ERR_DEVICE
+    assert "forced" in mm.mm_last_error()
