@@ -71,6 +71,8 @@ _lib.mm_scaled_gemm_grouped_layout_noalloc.argtypes = [_I64, _I64, _I64, _I64, _
 _lib.mm_scaled_gemm_grouped_layout_noalloc.restype = _I
 _lib.mm_debug_convert.argtypes = [_P, _P, _I, _I64, _P]
 _lib.mm_debug_convert.restype = _I
+_lib.mm_debug_mfma_gemm.argtypes = [_I64, _I64, _I64, _P, _P, _I, _P, _P, _P, _P]
+_lib.mm_debug_mfma_gemm.restype = _I
 _lib.mm_last_error.restype = ctypes.c_char_p
 _lib.mm_version.restype = ctypes.c_char_p
 
@@ -78,7 +80,7 @@ EXPORTED = ("mm_scaled_gemm", "mm_scaled_gemm_bias", "mm_scaled_gemm_batched", "
             "mm_scaled_gemm_grouped_layout", "mm_scaled_gemm_grouped_layout_noalloc", "mm_grouped_workspace_bytes",
             "mm_transpose_u8",
             "mm_blockscaled_gemm_amax",
-            "mm_blockscaled_gemm_amax_atom", "mm_last_error", "mm_version", "mm_debug_convert")
+            "mm_blockscaled_gemm_amax_atom", "mm_last_error", "mm_version", "mm_debug_convert", "mm_debug_mfma_gemm")
 
 
 class MMError(RuntimeError):
@@ -164,6 +166,12 @@ def mm_scaled_gemm_grouped_layout_noalloc(batch_sum, N, K, G, transpose_a, trans
                                                       batch_sizes or None, batch_offsets or None, scale_a or None,
                                                       scale_b or None, scale_result or None, d or None, d_type, ldd,
                                                       stride_d, int(use_fast_accum), stream or None)
+
+
+def mm_debug_mfma_gemm(M, N, K, a, b, ab_type, sfa, sfb, d, stream) -> int:
+    """Test hook (raw call): a GEMM summed by the scaled FP8 / FP4 MFMA, for measuring its precision."""
+    return _lib.mm_debug_mfma_gemm(M, N, K, a or None, b or None, ab_type, sfa or None, sfb or None, d or None,
+                                   stream or None)
 
 
 def mm_blockscaled_gemm_amax(M, N, K, L, a, b, ab_type, sfa, sfb, sf_vec_size, c, c_type, amax, amax_index,

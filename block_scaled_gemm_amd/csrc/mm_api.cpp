@@ -350,15 +350,15 @@ mm_status blockscaled_amax(const char* who, int64_t M, int64_t N, int64_t K, int
         p.vec_store = (p.ldd % 4 == 0);
         p.amax_bits = amax_bits;
         p.amax_key = key;
-        const int cfg = choose_cfg(M, N, L, cu_count(), mmfp8::min_cfg(mmfp8::MODE_SF32, 0, ab_type));
-        p.tiles_m = (int)cdiv(M, mmfp8::kCfgBM[cfg]);
-        p.tiles_n = (int)cdiv(N, mmfp8::kCfgBN[cfg]);
-        const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * L;
-        if (grid >= kMaxDim) return fail(MM_ERR_UNSUPPORTED, "too many output tiles");
         const int layout = !atom                ? mmfp8::SF_F32
                            : e4m3_factors       ? mmfp8::SF_ATOM_E4M3_16
                            : sf_vec_size == 16  ? mmfp8::SF_ATOM_E8M0_16
                                                 : mmfp8::SF_ATOM_E8M0;
+        const int cfg = choose_cfg(M, N, L, cu_count(), mmfp8::min_cfg(mmfp8::MODE_SF32, layout, ab_type));
+        p.tiles_m = (int)cdiv(M, mmfp8::kCfgBM[cfg]);
+        p.tiles_n = (int)cdiv(N, mmfp8::kCfgBN[cfg]);
+        const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * L;
+        if (grid >= kMaxDim) return fail(MM_ERR_UNSUPPORTED, "too many output tiles");
         const hipError_t e = fp4 ? mmfp8::launch_tile_fp4(cfg, layout, p, (int)grid, s)
                                  : mmfp8::launch_tile_sf32(cfg, layout, ab_type == MM_F8_E5M2 ? 1 : 0, p, (int)grid, s);
         mm_status st = device_status(e, who);
@@ -412,6 +412,24 @@ mm_status mm_debug_convert(const float* x, void* y, int dtype, int64_t n, void* 
     if (forced_launch_failure()) return fail(MM_ERR_DEVICE, "launch failure forced by MM_TEST_FORCE_FAIL");
     return device_status(mmfp8::launch_debug_convert(x, y, dtype, n, static_cast<hipStream_t>(stream)),
                          "mm_debug_convert launch");
+}
+
+mm_status mm_debug_mfma_gemm(int64_t M, int64_t N, int64_t K, const void* a, const void* b, int ab_type,
+                             const void* sfa, const void* sfb, float* d, void* stream) {
+    g_error.clear();
+    if (M < 0 || N < 0 || K < 0) return fail(MM_ERR_INVALID_ARGUMENT, "M, N and K must be >= 0");
+    if (!is_fp8(ab_type) && ab_type != MM_F4_E2M1) return fail(MM_ERR_INVALID_ARGUMENT, "unknown ab_type %d", ab_type);
+    if (M % 16 || N % 16 || K % 128) return fail(MM_ERR_UNSUPPORTED, "M and N must be multiples of 16, K of 128");
+    if (M >= (1 << 20) || N >= (1 << 20) || K >= (1 << 22)) return fail(MM_ERR_UNSUPPORTED, "M, N or K too large");
+    if (M == 0 || N == 0) return MM_OK;
+    if (!d || (K > 0 && (!a || !b))) return fail(MM_ERR_INVALID_ARGUMENT, "a, b or d is NULL");
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 4)) return fail(MM_ERR_MISALIGNED, "a and b must be 16-byte aligned");
+    if (forced_launch_failure()) return fail(MM_ERR_DEVICE, "launch failure forced by MM_TEST_FORCE_FAIL");
+    const int fmt = ab_type == MM_F8_E4M3FN ? 0 : (ab_type == MM_F8_E5M2 ? 1 : 4);
+    return device_status(mmfp8::launch_debug_mfma_gemm(fmt, static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(b),
+                                                       static_cast<const uint8_t*>(sfa), static_cast<const uint8_t*>(sfb),
+                                                       d, (int)M, (int)N, (int)K, static_cast<hipStream_t>(stream)),
+                         "mm_debug_mfma_gemm launch");
 }
 
 }  // extern "C"

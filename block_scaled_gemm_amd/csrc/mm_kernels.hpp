@@ -487,6 +487,11 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     // spills 38 of them, which measured 17% slower.
     constexpr bool kAtom = MODE == MODE_SF32 && SBM != SF_F32;
     constexpr bool kE4M3 = kAtom && SBM == SF_ATOM_E4M3_16;  // E4M3 factors (FP4 only): f16 operands
+    // FP4 with E8M0 factors per 32 values: the scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4) takes the
+    // E2M1 codes and the factors as they are; it sums E2M1 products exactly enough (measured against the
+    // exact sums: at most 2^-22.6 sum|t| for factors 2^-8 .. 2^4 at K = 8192, with factors 2^24 apart inside
+    // one instruction as well), where on FP8 data it does not.
+    constexpr bool kFp4Mfma = kFp4 && SBM == SF_ATOM_E8M0;
     static_assert(!kE4M3 || kFp4, "E4M3 factors go with FP4 operands");
     constexpr int SFV = (SBM == SF_ATOM_E8M0_16 || SBM == SF_ATOM_E4M3_16) ? 16 : 32;  // values per scale group
     constexpr int GPS = (kFp4 ? 2 * kBK : kBK) / SFV;      // scale groups per step
@@ -681,8 +686,10 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     // k = 32g .. 32g + 31 of the step: one 32-element scale group per lane.
     const int fr = lane & 15, fg = lane >> 4;
     const int fsw = (fr & 7) ^ (fr >> 3);  // swz of the fragment's row (fragments start at multiples of 16)
-    const int foff0 = fr * kBK + (((2 * fg) ^ fsw) << 4);
-    const int foff1 = fr * kBK + (((2 * fg + 1) ^ fsw) << 4);
+    // With the scaled FP4 MFMA, half h of a step is one instruction's K = 128 values: lane (r, g) takes chunk
+    // 4 h + g of row r, the 32 values of scale group 4 h + g.
+    const int foff0 = fr * kBK + (((kFp4Mfma ? fg : 2 * fg) ^ fsw) << 4);
+    const int foff1 = fr * kBK + (((kFp4Mfma ? 4 + fg : 2 * fg + 1) ^ fsw) << 4);
 
     f32x4 acc[FN][FM];
 #pragma unroll
@@ -810,6 +817,28 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
             }
         }
     };
+    // FP4 on the scaled MFMA: half h of the step is one K = 128 instruction per 16 x 16 block; lane (r, g)
+    // passes its group's E8M0 code (byte g of LDS dword [h][row], the step's groups 4 h .. 4 h + 3), 127 (a
+    // factor of 1) for groups past ceil(K/32), whose data is zero.
+    auto mma_fp4_scaled = [&](const Frag& f, int kt, const uint8_t* stage, int h) {
+        if constexpr (kFp4Mfma) {
+            const bool gv = kt * GPS + 4 * h + fg < p.sa_ld;
+            const uint32_t* wA = (const uint32_t*)(stage + (BM + BN) * kBK) + h * BM;
+            const uint32_t* wB = (const uint32_t*)(stage + (BM + BN) * kBK + SC_A_INS * 256) + h * BN;
+            int sa[FM], sb[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) sa[i] = gv ? (int)((wA[wm * WTM + i * 16 + fr] >> (8 * fg)) & 0xFFu) : 127;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) sb[j] = gv ? (int)((wB[wn * WTN + j * 16 + fr] >> (8 * fg)) & 0xFFu) : 127;
+            const i32x4 z = {0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cat(f.b[j], z), cat(f.a[i], z),
+                                                                                 acc[j][i], 4, 4, 0, sb[j], 0, sa[i]);
+        }
+    };
     // The scales of step kt: s_a / s_b fold a block-scaled partial into the
     // accumulator, c_a / c_b ride in the FP8 -> bf16 conversion (MX groups).
     // They are read from the step's stage before the barrier that frees it.
@@ -931,7 +960,8 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
                     if (h) __builtin_amdgcn_sched_barrier(0);
                     Frag f;
                     read_frag(cs, h, f);
-                    if constexpr (kFp4) mma_half4(f, kt, cs, h);
+                    if constexpr (kFp4Mfma) mma_fp4_scaled(f, kt, cs, h);
+                    else if constexpr (kFp4) mma_half4(f, kt, cs, h);
                     else mma_half(f, c_a, c_b);
                 }
                 promote(s_a, s_b);

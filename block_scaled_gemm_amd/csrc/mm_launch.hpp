@@ -54,6 +54,8 @@ hipError_t launch_ksplit(int ks, int mode, int fa, int fb, const GemmArgs& p, in
 hipError_t launch_amax_init(uint32_t* bits, unsigned long long* key, hipStream_t s);
 hipError_t launch_amax_finalize(float* amax, unsigned long long* key, hipStream_t s);
 hipError_t launch_debug_convert(const float* x, void* y, int t, int64_t n, hipStream_t s);
+hipError_t launch_debug_mfma_gemm(int fmt, const uint8_t* a, const uint8_t* b, const uint8_t* sfa, const uint8_t* sfb,
+                                  float* d, int M, int N, int K, hipStream_t s);
 // Operand packing (mm_pack.hip).
 hipError_t launch_group_starts(const int* sizes, int G, int64_t* start, hipStream_t s);
 hipError_t launch_transpose(const uint8_t* src, int64_t L, int64_t R, int64_t C, int64_t ld_src, int64_t src_batch,
@@ -69,8 +71,8 @@ hipError_t launch_group_pack(bool trans, const uint8_t* src, int64_t R, int64_t 
 // which measured faster than 128x256 at one (eight waves that all meet at
 // every step's barrier, where the older wave of each SIMD pair finishes first
 // and the younger then runs alone). FP4 operands on the 64x128 wave tile
-// spill over a hundred registers (their scale factors change within a step),
-// so they start at 128x256.
+// spill over a hundred registers (their scale factors change within a step;
+// on the scaled FP4 MFMA too: 242), so they start at 128x256.
 constexpr int min_cfg(int mode, int sbm, int fmt = 0) {
     (void)sbm;
     if (fmt == T_E2M1) return CFG_128x256;

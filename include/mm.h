@@ -457,6 +457,23 @@ const char* mm_version(void);
  */
 mm_status mm_debug_convert(const float* x, void* y, int dtype, int64_t n, void* stream);
 
+/*
+ * mm_debug_mfma_gemm -- test hook, not part of the GEMM contract: a plain
+ * GEMM whose products are summed by the gfx950 scaled FP8 / FP4 MFMA
+ * (v_mfma_scale_f32_16x16x128_f8f6f4, one fp32 chain over K), to measure how
+ * exactly that instruction sums ("mmaemu API reference (v0.1)", instruction
+ * model, is the pages' account of such limited tensor-core sums).
+ * d[m][n] = sum_k A[m][k] B[n][k] 2^(sfa[m][k/32] - 127) 2^(sfb[n][k/32] - 127).
+ *  a, b     [M][K] / [N][K] codes of ab_type (MM_F8_E4M3FN, MM_F8_E5M2, or
+ *           MM_F4_E2M1 two per byte, rows of K/2 bytes), 16-byte aligned.
+ *  sfa, sfb [M][K/32] / [N][K/32] E8M0 bytes, or NULL (all 127, i.e. 1).
+ *  d        [M][N] fp32.
+ * M and N multiples of 16, K of 128 (else MM_ERR_UNSUPPORTED). Device
+ * pointers; asynchronous on stream.
+ */
+mm_status mm_debug_mfma_gemm(int64_t M, int64_t N, int64_t K, const void* a, const void* b, int ab_type,
+                             const void* sfa, const void* sfb, float* d, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

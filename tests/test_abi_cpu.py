@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
                           "mm_scaled_gemm_grouped_layout", "mm_scaled_gemm_grouped_layout_noalloc",
                           "mm_grouped_workspace_bytes", "mm_transpose_u8",
                           "mm_blockscaled_gemm_amax", "mm_blockscaled_gemm_amax_atom", "mm_last_error",
-                          "mm_version", "mm_debug_convert"}
+                          "mm_version", "mm_debug_convert", "mm_debug_mfma_gemm"}
     lib = ctypes.CDLL(mm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

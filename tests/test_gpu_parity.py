@@ -687,6 +687,34 @@ def test_fp4_production_tiles(L, sf):
     assert amax == float(cf.max()) and idx == int(np.argmax(cf))
 
 
+def test_fp4_worst_case_factor_spread():
+    """Factors 2^-8 and 2^4 alternating per group of 32 on both operands (products 2^24 apart inside one
+    scaled MFMA instruction), sf 32, every output against the oracle."""
+    L, M, N, K = 2, 200, 136, 2048
+    w = datagen.set_fp4_l8_2048x2048x8192(L, M, N, K, 32, config=71)
+    for key in ("sfa", "sfb"):
+        sf = w[key].copy()
+        sf[..., 0::2] = 127 - 8  # storage [l][mn/128][g/4][mn%32][(mn/32)%4][g%4]: g even at j0 = 0, 2
+        sf[..., 1::2] = 127 + 4
+        w[key] = sf
+    c, amax, idx, value, sabs = check_fp4_case(w, F32)
+    check_amax_index_against_oracle(idx, value, sabs)
+
+
+def test_fp4_nan_and_extreme_factors():
+    """E8M0 NaN (0xFF) poisons its row; factors at 2^-127 and 2^64 elsewhere stay within the bound."""
+    L, M, N, K = 1, 96, 80, 512
+    w = datagen.set_fp4_l8_2048x2048x8192(L, M, N, K, 32, config=72)
+    w["sfa"] = w["sfa"].copy()
+    w["sfa"][0, 0, 0, 7, 0, 1] = 0xFF  # row 7, group 1: NaN
+    w["sfb"] = w["sfb"].copy()
+    w["sfb"][0, 0, 1, 3, 0, 2] = 0x00  # column 3, group 6: 2^-127
+    w["sfb"][0, 0, 0, 9, 0, 0] = 127 + 64  # column 9, group 0: 2^64
+    c, amax, idx, value, sabs = check_fp4_case(w, F32)
+    cf = c.view(np.float32)
+    assert np.isnan(cf[0, 7]).all() and np.isnan(amax)
+
+
 def test_fp4_padding_is_not_read():
     L, M, N, K, sf = 2, 100, 72, 224, 16  # 14 groups: two unused in the last 4-group block
     w = datagen.set_fp4_l8_2048x2048x8192(L, M, N, K, sf)
