@@ -56,7 +56,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "block_scaled_gemm_amd", "csrc", f) for f i
 ROTATION_BYTES = 512 << 20    # 2x the Infinity Cache
 METRIC = "FP8 scaled-GEMM TFLOP/s and % of MI355X FP8 MFMA peak, M=16..8192"
 # kernel the library dispatches for each M of the benchmark (N = K = 4096, per-tensor)
-KERNEL_AT = {16: "gemm_skinny", 64: "gemm_skinny", 256: "gemm_ksplit"}
+KERNEL_AT = {16: "gemm_skinny", 64: "gemm_skinny_k", 256: "gemm_ksplit"}
 
 
 def gemm_bytes(M):
