@@ -68,9 +68,9 @@ def gemm_flops(M):
     return 2.0 * M * N * K
 
 
-def measured_traffic():
-    """HBM bytes per launch of the M = 8192 kernel from the committed counter
-    summary, or None when the kernel sources changed since it was taken."""
+def counters_profile():
+    """The committed counter summary of the M = 8192 kernel, or None when the
+    kernel sources changed since it was taken (its figures no longer apply)."""
     import hashlib
     import re
     try:
@@ -82,10 +82,18 @@ def measured_traffic():
         with open(f, "rb") as fh:
             h.update(fh.read())
     digest = re.search(r"kernel_sources_sha256: ([0-9a-f]{64})", text)
-    traffic = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    if not digest or not traffic or digest.group(1) != h.hexdigest():
+    if not digest or digest.group(1) != h.hexdigest():
         return None
-    return int(traffic.group(1))
+    return text
+
+
+def measured_traffic():
+    """HBM bytes per launch of the M = 8192 kernel from the committed counter
+    summary, or None."""
+    import re
+    text = counters_profile()
+    traffic = re.search(r"traffic_bytes_per_launch: (\d+)", text) if text else None
+    return int(traffic.group(1)) if traffic else None
 
 
 def log(*a):
@@ -450,11 +458,8 @@ def counter_clock_ghz():
     """The clock the committed counter run measured for the M = 8192 kernel (GRBM_GUI_ACTIVE over the kernel
     time), or None."""
     import re
-    try:
-        text = open(COUNTERS).read()
-    except OSError:
-        return None
-    m = re.search(r"counter_clock_ghz: ([0-9.]+)", text)
+    text = counters_profile()
+    m = re.search(r"counter_clock_ghz: ([0-9.]+)", text) if text else None
     return float(m.group(1)) if m else None
 
 
