@@ -442,6 +442,95 @@ __device__ __forceinline__ void sched_row() {
     }
 }
 
+// One 128-K step of a wave's 16 NF x 16 NF tile whose fragments lie in LDS
+// (A rows at As, B rows at Bs, 128-byte rows with the XOR swizzle; lane (r, g)
+// reads its row's chunk 2 g + h at fo_h). The step is four sub-steps of K = 32
+// (u = 2 h + q), each a row-by-row pass over the fragments (row j: the MFMAs of
+// B fragment j with every A fragment). Next to row j's MFMAs of sub-step u go
+// the conversions of B and A fragment j for sub-step u + 1 and, in sub-step 0,
+// the reads of the second half's fragment j (into the registers the first
+// half's fragment j just left), so that one wave keeps the matrix core and the
+// vector ALU busy at once. CHAIN: the MFMAs accumulate into acc. Otherwise each
+// step's 128-chunk sums into a fresh fp32 partial that is then added to acc
+// (slow accumulation), row j's addition going between row j + 1's MFMAs of the
+// last sub-step. c_a / c_b scale the conversions of A / B fragment j.
+template <int FA, int FB, int NF, bool CHAIN>
+__device__ __forceinline__ void ilv_step(const uint8_t* As, const uint8_t* Bs, int fo0, int fo1, const float* c_a,
+                                         const float* c_b, f32x4 (&acc)[NF][NF], f32x4 (&part)[NF][NF]) {
+    auto row = [&](int j, const bf16x8 (&xa)[NF], const bf16x8& xbj) {
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            if constexpr (CHAIN) acc[j][i] = mfma_bf16(xbj, xa[i], acc[j][i]);
+            else part[j][i] = mfma_bf16(xbj, xa[i], part[j][i]);
+        }
+    };
+    auto promote_row = [&](int j) {
+        if constexpr (!CHAIN) {
+#pragma unroll
+            for (int i = 0; i < NF; ++i) acc[j][i] += part[j][i];
+        }
+    };
+    if constexpr (!CHAIN) {
+#pragma unroll
+        for (int j = 0; j < NF; ++j)
+#pragma unroll
+            for (int i = 0; i < NF; ++i) part[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    i32x4 ra[NF], rb[NF];  // raw fragments: the first half, then the second
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+        ra[j] = *(const i32x4*)(As + j * 16 * kBK + fo0);
+        rb[j] = *(const i32x4*)(Bs + j * 16 * kBK + fo0);
+    }
+    bf16x8 xa0[NF], xa1[NF], xb[NF];
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+        xa0[j] = to_bf16x8<FA>(ra[j], 0, c_a[j]);
+        xb[j] = to_bf16x8<FB>(rb[j], 0, c_b[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // sub-step 0: MFMAs of (xa0, xb); sub-step 1's operands from the first half; second-half reads
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+        row(j, xa0, xb[j]);
+        xb[j] = to_bf16x8<FB>(rb[j], 1, c_b[j]);
+        xa1[j] = to_bf16x8<FA>(ra[j], 1, c_a[j]);
+        ra[j] = *(const i32x4*)(As + j * 16 * kBK + fo1);
+        rb[j] = *(const i32x4*)(Bs + j * 16 * kBK + fo1);
+        sched_row<8, 2, NF>();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // sub-step 1: MFMAs of (xa1, xb); sub-step 2's operands from the second half
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+        row(j, xa1, xb[j]);
+        xb[j] = to_bf16x8<FB>(rb[j], 0, c_b[j]);
+        xa0[j] = to_bf16x8<FA>(ra[j], 0, c_a[j]);
+        sched_row<8, 0, NF>();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // sub-step 2: MFMAs of (xa0, xb); sub-step 3's operands
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+        row(j, xa0, xb[j]);
+        xb[j] = to_bf16x8<FB>(rb[j], 1, c_b[j]);
+        xa1[j] = to_bf16x8<FA>(ra[j], 1, c_a[j]);
+        sched_row<8, 0, NF>();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // sub-step 3: MFMAs of (xa1, xb), each row with the promotion of the row before
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+        row(j, xa1, xb[j]);
+        if (j > 0) promote_row(j - 1);
+        if constexpr (!CHAIN) {
+            if (j > 0) sched_row<4 * NF, 0, NF>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    promote_row(NF - 1);
+}
+
 // ------------------------------------------------------------------ tiled kernel
 //
 // Workgroup tile BM x BN computed by WM x WN waves, each wave a
@@ -928,6 +1017,7 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     // block scaling: its step scales (s_a, s_b) on top of the second operand set
     // push that loop past the register file
     constexpr bool kIlv = !PIPE && !kFp4 && FM == FN && MODE != MODE_BLOCK;
+
     if constexpr (PIPE) {
         Frag f0, f1;
         auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
@@ -954,104 +1044,20 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
             }
         }
     } else if constexpr (kIlv) {
-        // Interleaved: a step is four sub-steps of K = 32 (u = 2 h + q), each a
-        // row-by-row pass over the wave's fragments (row j: the MFMAs of B
-        // fragment j with every A fragment). Next to row j's MFMAs of sub-step u
-        // go the conversions of B and A fragment j for sub-step u + 1 and, in
-        // sub-step 0, the reads of the second half's fragment j (into the
-        // registers the first half's fragment j just left), so that one wave keeps
-        // the matrix core and the vector ALU busy at once. In slow mode row j of
-        // the last sub-step goes with the promotion of row j - 1's partials.
-        constexpr int NF = FM;
-        auto row = [&](int j, const bf16x8 (&xa)[NF], const bf16x8& xbj) {
-#pragma unroll
-            for (int i = 0; i < NF; ++i) {
-                if constexpr (chain) acc[j][i] = mfma_bf16(xbj, xa[i], acc[j][i]);
-                else part[j][i] = mfma_bf16(xbj, xa[i], part[j][i]);
-            }
-        };
-        auto promote_row = [&](int j, const float* s_a, const float (*s_b)[4]) {
-            if constexpr (!chain) {
-#pragma unroll
-                for (int i = 0; i < NF; ++i) {
-                    if (MODE == MODE_SLOW) {
-                        acc[j][i] += part[j][i];
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[j][i][r] = __builtin_fmaf(part[j][i][r], s_a[i] * s_b[j][r], acc[j][i][r]);
-                    }
-                }
-            }
-        };
+        // the interleaved step of ilv_step (slow mode promotes per step)
+        static_assert(MODE != MODE_BLOCK, "block scaling promotes with its step scales");
         auto step = [&](int s, uint8_t* cur, uint8_t* nxt) {
             const int kt = s * KG + kg;
             uint8_t* cs = cur + kg * STAGE;
             stage_ready(kt, cs);
             float s_a[FM], s_b[FN][4], c_a[FM], c_b[FN];
-            if (kt < KT) {
-                step_scales(kt, cs, s_a, s_b, c_a, c_b);
-                if (kSbMem) sc_cur = load_scales(kt + KG);
-            }
+            if (kt < KT) step_scales(kt, cs, s_a, s_b, c_a, c_b);
             issue(kt + KG, nxt + kg * STAGE);
             if (kt < KT) {
-                zero_part();
-                const int fo0 = foff0, fo1 = foff1;
                 const uint8_t* As = cs + wm * WTM * kBK;
                 const uint8_t* Bs = cs + BM * kBK + wn * WTN * kBK;
-                i32x4 ra[NF], rb[NF];  // raw fragments: the first half, then the second
-#pragma unroll
-                for (int j = 0; j < NF; ++j) {
-                    ra[j] = *(const i32x4*)(As + j * 16 * kBK + fo0);
-                    rb[j] = *(const i32x4*)(Bs + j * 16 * kBK + fo0);
-                }
-                bf16x8 xa0[NF], xa1[NF], xb[NF];
-#pragma unroll
-                for (int j = 0; j < NF; ++j) {
-                    xa0[j] = to_bf16x8<FA>(ra[j], 0, c_a[j]);
-                    xb[j] = to_bf16x8<FB>(rb[j], 0, c_b[j]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                // sub-step 0: MFMAs of (xa0, xb); sub-step 1's operands from the first half; second-half reads
-#pragma unroll
-                for (int j = 0; j < NF; ++j) {
-                    row(j, xa0, xb[j]);
-                    xb[j] = to_bf16x8<FB>(rb[j], 1, c_b[j]);
-                    xa1[j] = to_bf16x8<FA>(ra[j], 1, c_a[j]);
-                    ra[j] = *(const i32x4*)(As + j * 16 * kBK + fo1);
-                    rb[j] = *(const i32x4*)(Bs + j * 16 * kBK + fo1);
-                    sched_row<8, 2, NF>();
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                // sub-step 1: MFMAs of (xa1, xb); sub-step 2's operands from the second half
-#pragma unroll
-                for (int j = 0; j < NF; ++j) {
-                    row(j, xa1, xb[j]);
-                    xb[j] = to_bf16x8<FB>(rb[j], 0, c_b[j]);
-                    xa0[j] = to_bf16x8<FA>(ra[j], 0, c_a[j]);
-                    sched_row<8, 0, NF>();
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                // sub-step 2: MFMAs of (xa0, xb); sub-step 3's operands
-#pragma unroll
-                for (int j = 0; j < NF; ++j) {
-                    row(j, xa0, xb[j]);
-                    xb[j] = to_bf16x8<FB>(rb[j], 1, c_b[j]);
-                    xa1[j] = to_bf16x8<FA>(ra[j], 1, c_a[j]);
-                    sched_row<8, 0, NF>();
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                // sub-step 3: MFMAs of (xa1, xb), each row with the promotion of the row before
-#pragma unroll
-                for (int j = 0; j < NF; ++j) {
-                    row(j, xa1, xb[j]);
-                    if (j > 0) promote_row(j - 1, s_a, s_b);
-                    if constexpr (!chain) {
-                        if (j > 0) sched_row<4 * NF, 0, NF>();
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                promote_row(NF - 1, s_a, s_b);
+                if constexpr (chain) ilv_step<FA, FB, FM, true>(As, Bs, foff0, foff1, c_a, c_b, acc, acc);
+                else ilv_step<FA, FB, FM, false>(As, Bs, foff0, foff1, c_a, c_b, acc, part);
             }
         };
         issue(kg, smem0 + kg * STAGE);
@@ -1574,6 +1580,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_ksplit(GemmArgs p) {
         // Fast: one chain into the accumulators. Slow: a fresh fp32 partial per
         // 128-chunk (this step), promoted into the accumulator after.
         constexpr bool chain = MODE == MODE_FAST;
+
         f32x4 part[chain ? 1 : MT][chain ? 1 : NT];
         if constexpr (!chain) {
 #pragma unroll
