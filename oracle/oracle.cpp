@@ -333,9 +333,9 @@ int orc_scaled_gemm(int64_t M, int64_t N, int64_t K,
 
     parallel_rows(n_rows, threads, [&](int64_t i) {
         const int64_t m = rows ? rows[i] : i;
-        const double* Am = &A[(size_t)i * K];
+        const double* Am = A.data() + (size_t)i * K;
         for (int64_t n = 0; n < N; ++n) {
-            const double* Bn = &B[(size_t)n * K];
+            const double* Bn = B.data() + (size_t)n * K;
             double v, sabs = 0.0;
             if (accum == ORC_ACC_EXACT) {
                 if (!block) {
@@ -482,9 +482,9 @@ int orc_blockscaled_gemm_amax(int64_t M, int64_t N, int64_t K, int64_t L,
                 Bh[(size_t)n * K + k] = element(&b[(l * N + n) * pitch], k, ab_fmt) *
                                         (double)sfb[(l * N + n) * KS + k / sf_vec];
         parallel_rows(n_rows, threads, [&](int64_t i) {
-            const double* Am = &Ah[(size_t)i * K];
+            const double* Am = Ah.data() + (size_t)i * K;
             for (int64_t n = 0; n < N; ++n) {
-                const double* Bn = &Bh[(size_t)n * K];
+                const double* Bn = Bh.data() + (size_t)n * K;
                 double S = +0.0, T = 0.0;
                 for (int64_t k = 0; k < K; ++k) {
                     const double t = Am[k] * Bn[k];
