@@ -453,10 +453,15 @@ __device__ __forceinline__ void sched_row() {
 // vector ALU busy at once. CHAIN: the MFMAs accumulate into acc. Otherwise each
 // step's 128-chunk sums into a fresh fp32 partial that is then added to acc
 // (slow accumulation), row j's addition going between row j + 1's MFMAs of the
-// last sub-step. c_a / c_b scale the conversions of A / B fragment j.
-template <int FA, int FB, int NF, bool CHAIN>
+// last sub-step; with SCALED the partial is folded in as acc = fma(part,
+// s_a * s_b, acc) (block scaling: s_a of A fragment i's row, read from LDS at
+// sa_col[16 i] just before the last sub-step, and the step's one s_b). c_a /
+// c_b scale the conversions of A / B fragment j.
+template <int FA, int FB, int NF, bool CHAIN, bool SCALED = false>
 __device__ __forceinline__ void ilv_step(const uint8_t* As, const uint8_t* Bs, int fo0, int fo1, const float* c_a,
-                                         const float* c_b, f32x4 (&acc)[NF][NF], f32x4 (&part)[NF][NF]) {
+                                         const float* c_b, f32x4 (&acc)[NF][NF], f32x4 (&part)[NF][NF],
+                                         const float* sa_col = nullptr, float sb = 1.0f) {
+    float sab[NF];
     auto row = [&](int j, const bf16x8 (&xa)[NF], const bf16x8& xbj) {
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
@@ -467,7 +472,14 @@ __device__ __forceinline__ void ilv_step(const uint8_t* As, const uint8_t* Bs, i
     auto promote_row = [&](int j) {
         if constexpr (!CHAIN) {
 #pragma unroll
-            for (int i = 0; i < NF; ++i) acc[j][i] += part[j][i];
+            for (int i = 0; i < NF; ++i) {
+                if constexpr (SCALED) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[j][i][r] = __builtin_fmaf(part[j][i][r], sab[i], acc[j][i][r]);
+                } else {
+                    acc[j][i] += part[j][i];
+                }
+            }
         }
     };
     if constexpr (!CHAIN) {
@@ -519,6 +531,10 @@ __device__ __forceinline__ void ilv_step(const uint8_t* As, const uint8_t* Bs, i
         __builtin_amdgcn_sched_barrier(0);
     }
     // sub-step 3: MFMAs of (xa1, xb), each row with the promotion of the row before
+    if constexpr (SCALED) {
+#pragma unroll
+        for (int i = 0; i < NF; ++i) sab[i] = sa_col[16 * i] * sb;
+    }
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
         row(j, xa1, xb[j]);
@@ -647,16 +663,17 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     auto ld_chunk = [&](int ins) { return (lane & 7) ^ ld_row ^ (ins & 1); };
     const bool k_tail = (K % kBK) != 0;
     uint32_t aoff[A_INS], boff[B_INS];
-    int achunk[A_INS], bchunk[B_INS];
+    // (the chunks are recomputed where the tail step needs them: kept from here,
+    // they would hold registers across the whole main loop)
+    auto achunk = [&](int q) { return ld_chunk(gw * A_INS + q); };
+    auto bchunk = [&](int q) { return ld_chunk(gw * B_INS + q); };
 #pragma unroll
     for (int q = 0; q < A_INS; ++q) {
-        achunk[q] = ld_chunk(gw * A_INS + q);
-        aoff[q] = (uint32_t)(((gw * A_INS + q) * 8 + ld_row) * p.lda + achunk[q] * 16);
+        aoff[q] = (uint32_t)(((gw * A_INS + q) * 8 + ld_row) * p.lda + achunk(q) * 16);
     }
 #pragma unroll
     for (int q = 0; q < B_INS; ++q) {
-        bchunk[q] = ld_chunk(gw * B_INS + q);
-        boff[q] = (uint32_t)(((gw * B_INS + q) * 8 + ld_row) * p.ldb + bchunk[q] * 16);
+        boff[q] = (uint32_t)(((gw * B_INS + q) * 8 + ld_row) * p.ldb + bchunk(q) * 16);
     }
 
     const float* sa_l = p.sa + (int64_t)l * p.sa_batch;
@@ -700,14 +717,14 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
 #pragma unroll
             for (int q = 0; q < A_INS; ++q) {
                 uint32_t off = aoff[q];
-                if constexpr (TAIL) off = (int)kb + achunk[q] * 16 >= K ? kOOB : off + kb;
+                if constexpr (TAIL) off = (int)kb + achunk(q) * 16 >= K ? kOOB : off + kb;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sbase + (gw * A_INS + q) * 1024), 16, off,
                                                          soff, 0, 0);
             }
 #pragma unroll
             for (int q = 0; q < B_INS; ++q) {
                 uint32_t off = boff[q];
-                if constexpr (TAIL) off = (int)kb + bchunk[q] * 16 >= K ? kOOB : off + kb;
+                if constexpr (TAIL) off = (int)kb + bchunk(q) * 16 >= K ? kOOB : off + kb;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sbase + BM * kBK + (gw * B_INS + q) * 1024),
                                                          16, off, soff, 0, 0);
             }
@@ -779,9 +796,9 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
             *(i32x4*)slot = v;
         };
 #pragma unroll
-        for (int q = 0; q < A_INS; ++q) fix(sbase + (gw * A_INS + q) * 1024 + lane * 16, achunk[q]);
+        for (int q = 0; q < A_INS; ++q) fix(sbase + (gw * A_INS + q) * 1024 + lane * 16, achunk(q));
 #pragma unroll
-        for (int q = 0; q < B_INS; ++q) fix(sbase + BM * kBK + (gw * B_INS + q) * 1024 + lane * 16, bchunk[q]);
+        for (int q = 0; q < B_INS; ++q) fix(sbase + BM * kBK + (gw * B_INS + q) * 1024 + lane * 16, bchunk(q));
     };
 
     // Fragment reads: lane (r, g) takes chunks 2g and 2g + 1 of row r, i.e.
@@ -813,6 +830,8 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     // 128x128 scale_b of one step, loaded one step ahead of its use (the other
     // scales come through LDS with the tiles).
     constexpr bool kSbMem = MODE == MODE_BLOCK && SBM == SB_128x128;
+    // the wave's columns lie in one 128-column block of scale_b (WTN divides 128)
+    constexpr bool kSbOne = kSbMem && 128 % WTN == 0;
     struct StepScales {
         float b[FN];
     };
@@ -820,8 +839,12 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
         StepScales sc;
         if (KT == 0) return sc;  // K = 0: no step reads them (and the tables may be empty)
         kt = min(kt, KT - 1);    // the prefetch past the last step reads a valid entry
+        if constexpr (kSbOne) {
+            sc.b[0] = sb_l[(int64_t)srow_b[0] * p.sb_ld + kt];  // every fragment of the wave is in this block
+        } else {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) sc.b[j] = sb_l[(int64_t)srow_b[j] * p.sb_ld + kt];
+            for (int j = 0; j < FN; ++j) sc.b[j] = sb_l[(int64_t)srow_b[j] * p.sb_ld + kt];
+        }
         return sc;
     };
     StepScales sc_cur;
@@ -953,7 +976,8 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) s_b[j][r] = kSbMem ? sc_cur.b[j] : scB[wn * WTN + j * 16 + 4 * fg + r];
+                for (int r = 0; r < 4; ++r)
+                    s_b[j][r] = kSbMem ? sc_cur.b[kSbOne ? 0 : j] : scB[wn * WTN + j * 16 + 4 * fg + r];
         }
         if (MODE == MODE_SF32 && kAtom) {
             // the row's dword holds the step's 4 groups; byte fg is this lane's
@@ -1013,10 +1037,12 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
         __syncthreads();
     };
 
-    // FP8 operands on square wave tiles take the interleaved loop below, except
-    // block scaling: its step scales (s_a, s_b) on top of the second operand set
-    // push that loop past the register file
-    constexpr bool kIlv = !PIPE && !kFp4 && FM == FN && MODE != MODE_BLOCK;
+    // FP8 operands on square wave tiles take the interleaved loop below, block
+    // scaling only with a 128x128 scale_b whose 128-column blocks hold whole wave
+    // tiles (one s_b per wave and step): with a scale_b per column its step
+    // scales on top of the second operand set push that loop past the register
+    // file
+    constexpr bool kIlv = !PIPE && !kFp4 && FM == FN && (MODE != MODE_BLOCK || kSbOne);
 
     if constexpr (PIPE) {
         Frag f0, f1;
@@ -1044,19 +1070,35 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
             }
         }
     } else if constexpr (kIlv) {
-        // the interleaved step of ilv_step (slow mode promotes per step)
-        static_assert(MODE != MODE_BLOCK, "block scaling promotes with its step scales");
+        // the interleaved step of ilv_step (slow mode promotes per step, block
+        // scaling folds the partial in with s_a of the row times the step's s_b)
         auto step = [&](int s, uint8_t* cur, uint8_t* nxt) {
             const int kt = s * KG + kg;
             uint8_t* cs = cur + kg * STAGE;
             stage_ready(kt, cs);
-            float s_a[FM], s_b[FN][4], c_a[FM], c_b[FN];
-            if (kt < KT) step_scales(kt, cs, s_a, s_b, c_a, c_b);
+            float c_a[FM], c_b[FN];
+            float sb = 1.0f;
+            if (kt < KT) {
+                if constexpr (MODE == MODE_BLOCK) {
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) c_a[i] = 1.0f;
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) c_b[j] = 1.0f;
+                    sb = sc_cur.b[0];
+                    sc_cur = load_scales(kt + KG);
+                } else {
+                    float s_a[FM], s_b[FN][4];
+                    step_scales(kt, cs, s_a, s_b, c_a, c_b);
+                }
+            }
             issue(kt + KG, nxt + kg * STAGE);
             if (kt < KT) {
                 const uint8_t* As = cs + wm * WTM * kBK;
                 const uint8_t* Bs = cs + BM * kBK + wn * WTN * kBK;
                 if constexpr (chain) ilv_step<FA, FB, FM, true>(As, Bs, foff0, foff1, c_a, c_b, acc, acc);
+                else if constexpr (MODE == MODE_BLOCK)
+                    ilv_step<FA, FB, FM, false, true>(As, Bs, foff0, foff1, c_a, c_b, acc, part,
+                                                      (const float*)(cs + (BM + BN) * kBK) + wm * WTM + fr, sb);
                 else ilv_step<FA, FB, FM, false>(As, Bs, foff0, foff1, c_a, c_b, acc, part);
             }
         };
