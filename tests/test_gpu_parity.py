@@ -243,6 +243,26 @@ def test_block_scales_small(M, N, K, sb_mode):
         check_gemm(d, 1, sb_mode, dt, False, what=f"block {M}x{N}x{K} sb={sb_mode} {DT_NAME[dt]}")
 
 
+# block scaling on the production tiles: 128x128 with two K groups (one tile per CU) and with two workgroups per
+# CU, a ragged M, and a K whose last chunk straddles a 16-byte boundary; with a 128x128 scale_b these run the
+# interleaved main loop (one s_b per wave and step), with a 1x128 scale_b the plain one
+BLOCK_TILE_CASES = [(1024, 4096, 1032, 2), (2048, 4096, 1032, 2), (1000, 4096, 1032, 2),
+                    (1024, 4096, 1032, 1), (2048, 4096, 1032, 1)]
+
+
+@pytest.mark.parametrize("M,N,K,sb_mode", BLOCK_TILE_CASES)
+def test_production_tiles_block(M, N, K, sb_mode):
+    rng = np.random.default_rng(M * 7 + K + sb_mode)
+    a = datagen.gauss_codes(rng, (M, K), 64.0)
+    b = datagen.gauss_codes(rng, (N, K), 64.0)
+    kb = -(-K // 128)
+    sa = datagen.log_uniform_scales(rng, (M, kb))
+    sb = datagen.log_uniform_scales(rng, (N if sb_mode == 1 else -(-N // 128), kb))
+    d = dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN, scale_a=sa, scale_b=sb)
+    check_gemm(d, 1, sb_mode, BF16, False, rows=tile_rows(M, seed=M + sb_mode),
+               what=f"block tiles {M}x{N}x{K} sb={sb_mode}")
+
+
 def test_block_scaled_full_size():
     d = datagen.set_block_scaled_4096x14336x4096()
     check_gemm(d, 1, 2, BF16, False, rows=tile_rows(4096, seed=3), what="block-scaled 4096x14336x4096")
