@@ -241,6 +241,10 @@ OTHER = {
     "mx_amax": "batched E4M3 GEMM with power-of-two scales per 32 K, L=8, M=N=2048, K=8192, f32 C + amax + index",
     "e4m3_out": "E4M3 GEMM, M=8192, N=28672, K=8200 (lda 8200), slow, E4M3 out via scale_result=1/16",
     "e5m2_f16": "E5M2 GEMM, M=8192, N=28672, K=8200 (lda 8200), slow, f16 out",
+    "shard_e4m3_out": "one GPU's share of the E4M3-out GEMM split over 8 GPUs by columns: M=8192, N=3584, K=8200 "
+                      "(lda 8200), slow, E4M3 out via scale_result=1/16",
+    "shard_mx_l1": "one GPU's share of the batched MX GEMM + amax split over 8 GPUs by batch item: L=1, M=N=2048, "
+                   "K=8192, power-of-two scales per 32 K, f32 C + amax + index",
     "block_bias": "E4M3 1x128 / 128x128 block-scaled GEMM + bf16 bias [N], M=4096, N=14336, K=4096, bf16 out",
     "bmm": "batched per-tensor E4M3 GEMM, L=8, M=N=2048, K=4096, slow, bf16 out",
     "bmm_kn": "batched per-tensor E4M3 GEMM with b as [L, K, N] (transposed per call), L=8, M=N=2048, K=4096, "
@@ -325,11 +329,15 @@ def run_other(name, steps, warmup, settle_s=1.5):
                                              mm.MM_F8_E4M3FN, K, N * K, sa.data_ptr(), sb.data_ptr(), 0,
                                              out.data_ptr(), mm.MM_BF16, N, M * N, 0, stream)
         scale_bytes = 8
-    elif name == "mx_amax":
+    elif name in ("mx_amax", "shard_mx_l1"):
         d = datagen.set_mx_l8_2048x2048x8192()
+        if name == "shard_mx_l1":  # batch item 0: what one of 8 GPUs computes when the batch is split
+            d = {k: (v[:1] if k in ("a", "b", "sfa", "sfb") else v) for k, v in d.items()}
         L, M, K = d["a"].shape; N = d["b"].shape[1]
-        a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
-        sfa = torch.from_numpy(d["sfa"]).to(dev); sfb = torch.from_numpy(d["sfb"]).to(dev)
+        a = torch.from_numpy(np.ascontiguousarray(d["a"])).to(dev)
+        b = torch.from_numpy(np.ascontiguousarray(d["b"])).to(dev)
+        sfa = torch.from_numpy(np.ascontiguousarray(d["sfa"])).to(dev)
+        sfb = torch.from_numpy(np.ascontiguousarray(d["sfb"])).to(dev)
         c = torch.empty((L, M, N), dtype=torch.float32, device=dev)
         amax = torch.empty((1,), dtype=torch.float32, device=dev)
         idx = torch.empty((1,), dtype=torch.int64, device=dev)
@@ -402,21 +410,24 @@ def run_other(name, steps, warmup, settle_s=1.5):
                                                     mm.MM_F32, amax.data_ptr(), idx.data_ptr(), stream)
         scale_bytes = sfa.numel() + sfb.numel() + 12
     else:
-        d = datagen.set_e4m3_out_8192x28672x8200() if name == "e4m3_out" else datagen.set_e5m2_f16_8192x28672x8200()
+        e4 = name in ("e4m3_out", "shard_e4m3_out")
+        d = datagen.set_e4m3_out_8192x28672x8200() if e4 else datagen.set_e5m2_f16_8192x28672x8200()
+        if name == "shard_e4m3_out":  # the first 3584 columns: what one of 8 GPUs computes when N is split
+            d = dict(d, b=np.ascontiguousarray(d["b"][:3584]))
         M, K = d["a"].shape; N = d["b"].shape[0]; L = 1
-        fa = mm.MM_F8_E4M3FN if name == "e4m3_out" else mm.MM_F8_E5M2
+        fa = mm.MM_F8_E4M3FN if e4 else mm.MM_F8_E5M2
         a = torch.from_numpy(d["a"]).to(dev); b = torch.from_numpy(d["b"]).to(dev)
         sa = torch.tensor([float(d["scale_a"])], dtype=torch.float32, device=dev)
         sb = torch.tensor([float(d["scale_b"])], dtype=torch.float32, device=dev)
         sr = torch.tensor([float(d.get("scale_result", 1.0))], dtype=torch.float32, device=dev)
-        dt = mm.MM_F8_E4M3FN if name == "e4m3_out" else mm.MM_F16
-        out_bytes = 1 if name == "e4m3_out" else 2
+        dt = mm.MM_F8_E4M3FN if e4 else mm.MM_F16
+        out_bytes = 1 if e4 else 2
         out = torch.empty((M * N * out_bytes,), dtype=torch.uint8, device=dev)
 
         def launch():
             return mm.mm_scaled_gemm(M, N, K, a.data_ptr(), fa, K, b.data_ptr(), fa, K, sa.data_ptr(),
                                      mm.MM_SCALE_TENSOR, sb.data_ptr(), mm.MM_SCALE_TENSOR,
-                                     sr.data_ptr() if name == "e4m3_out" else 0, out.data_ptr(), dt, N, 0, stream)
+                                     sr.data_ptr() if e4 else 0, out.data_ptr(), dt, N, 0, stream)
         scale_bytes = 12
     torch.cuda.synchronize()
     log(f"{name}: inputs ready in {time.time() - t0:.1f}s")

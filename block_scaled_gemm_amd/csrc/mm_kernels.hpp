@@ -18,7 +18,13 @@
 //    accumulates to ~2^-26 * sum|t|. Every FP8 value (E4M3 and E5M2) is exactly
 //    a bf16 value, so the kernels convert FP8 to bf16 in registers
 //    (v_cvt_scalef32_pk_bf16_fp8 / _bf8, with a power-of-two scale that is
-//    exact) and contract with the bf16 MFMA.
+//    exact) and contract with the bf16 MFMA. On FP4 (E2M1) operands the scaled
+//    MFMA stays within 2^-22 * sum|t| (E8M0 factors 2^-8 .. 2^4, also 2^24
+//    apart in one instruction), so FP4 with E8M0 factors per 32 runs on it.
+//  * Issue: every VALU instruction, the MFMA included, holds the SIMD's VALU
+//    issue for 4 cycles and a 16x16x32 bf16 MFMA runs 16; independent VALU
+//    work issued between a wave's MFMAs overlaps them (2 conversions and 1 add
+//    per MFMA: 22.5 cycles per MFMA at two waves per SIMD, 27 at one).
 //  * 16x16 MFMA results: D[i][j] (i from the first operand, j from the
 //    second) is in lane j + 16 (i / 4), register i % 4. Both operands use the
 //    same lane layout, so any assignment of k to (lane group, element) that is
@@ -564,10 +570,14 @@ __device__ __forceinline__ void ilv_step(const uint8_t* As, const uint8_t* Bs, i
 // k = 32g .. 32g+31 of row r (one MX group), converted to bf16 8 values at a
 // time for the four v_mfma_f32_16x16x32_bf16 of the step.
 //
-// PIPE selects the main loop: with it the fragment reads run a half-step ahead
-// of the MFMAs (the way to hide LDS latency with one wave per SIMD, at the cost
-// of a second set of fragment registers); without it each half-step reads and
-// then multiplies, and a second wave on the SIMD hides the latency.
+// The main loop is one of three. FP8 operands on square wave tiles (every
+// per-tensor and MX 128x128 / 64x64 tile, and block scaling with a 128x128
+// scale_b) run ilv_step, which interleaves the next K = 32 sub-step's
+// conversions and the second half's fragment reads with the current MFMAs.
+// Otherwise PIPE runs the fragment reads a half-step ahead of the MFMAs (the
+// way to hide LDS latency with one wave per SIMD, at the cost of a second set
+// of fragment registers), and the plain loop reads each half-step's fragments
+// and then multiplies, a second wave on the SIMD hiding the latency.
 //
 // KG = 2 splits the K steps of a tile between two groups of WM x WN waves (even
 // steps to group 0, odd steps to group 1), each with its own pair of stages;

@@ -84,12 +84,13 @@ int device_cus();
 
 // Launch gemm_tile<BM, BN, MODE, FA, FB, SBM> for a runtime cfg over `grid`
 // tiles. 128x128 tiles that are no more than the CUs (one per CU) run with two
-// K groups of four waves (eight waves per workgroup) in the modes that have
-// them: it measured 5-7% faster there than four waves with one wave per SIMD,
-// and slower as soon as two workgroups per CU are possible.
+// K groups of four waves (eight waves per workgroup), FP8 operands in every
+// mode: per-tensor slow it measured 5-7% faster there than four waves with one
+// wave per SIMD (and slower as soon as two workgroups per CU are possible), MX
+// 1.4x faster than the pipelined four-wave tile (L = 1, 2048 x 2048 x 8192).
 template <int MODE, int SBM, int FA, int FB>
 hipError_t tile_launch(int cfg, const GemmArgs& p, int grid, hipStream_t s) {
-    constexpr int kKG = MODE == MODE_SF32 ? 1 : 2;
+    constexpr int kKG = FA == T_E2M1 ? 1 : 2;
     const bool kgroups = kKG > 1 && cfg == CFG_128x128 && grid <= device_cus();
 #define MMFP8_TILE(C)                                                                                              \
     do {                                                                                                           \

@@ -393,10 +393,11 @@ def test_sf32_e5m2_unit_scales_is_plain_gemm():
     check_amax_case(w, F32)
 
 
-@pytest.mark.parametrize("L", [2, 1], ids=["128x256", "128x128"])
+@pytest.mark.parametrize("L", [2, 1], ids=["128x256", "128x128-kgroups"])
 def test_production_tiles_sf32(L):
-    """MX-scaled GEMM + amax at sizes that select the 128x256 and the
-    (pipelined) 128x128 tile; the full-size workload below selects 256x256."""
+    """MX-scaled GEMM + amax at sizes that select the 128x256 tile and the
+    128x128 tile with two K groups (one tile per CU: 256 of them); the
+    full-size workload below selects 256x256."""
     w = datagen.set_mx_l8_2048x2048x8192(L, 2048, 2048, 1040)
     rows = sample_rows(2048, 4)
     c, amax, idx, value, sabs = check_amax_case(w, F32, rows=rows)
@@ -450,7 +451,8 @@ def test_atom_against_oracle(L, M, N, K, c_type):
 
 
 @pytest.mark.parametrize("L,M,N,K", [(3, 200, 136, 1024), (1, 130, 70, 1008), (2, 2048, 2048, 1040),
-                                     (1, 2048, 2048, 1040)], ids=["64x64", "64x64-ragged", "128x256", "128x128"])
+                                     (1, 2048, 2048, 1040)], ids=["64x64", "64x64-ragged", "128x256",
+                                                                  "128x128-kgroups"])
 def test_atom_equals_fp32_factor_entry(L, M, N, K):
     """The same factors as fp32 powers of two through mm_blockscaled_gemm_amax: bitwise the same C,
     amax and index (the two entries differ only in how the factors are read)."""
