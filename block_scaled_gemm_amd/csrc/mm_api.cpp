@@ -209,7 +209,15 @@ mm_status scaled_gemm(const char* who, int64_t L, int64_t M, int64_t N, int64_t 
     }
     const int mode = per_tensor ? (use_fast_accum ? mmfp8::MODE_FAST : mmfp8::MODE_SLOW) : mmfp8::MODE_BLOCK;
     const int sbm = sb_mode == MM_SCALE_128x128 ? mmfp8::SB_128x128 : mmfp8::SB_1x128;
-    const int cfg = choose_cfg(M, N, L, cu_count(), mmfp8::min_cfg(mode, sbm));
+    int cfg = choose_cfg(M, N, L, cu_count(), mmfp8::min_cfg(mode, sbm));
+    if (mode == mmfp8::MODE_SLOW && K % 128 == 0 && cfg == mmfp8::CFG_128x128) {
+        // The 256x256 tile's row-chunk loop does about 13% more per clock than two 128x128 workgroups per
+        // CU, but runs one tile per CU: take it when its rounds cost less than the 128x128 tiles' rounds
+        // (a round of one 256x256 tile per CU counted 1, a round of two 128x128 tiles per CU 0.565).
+        const int64_t cus = cu_count();
+        const int64_t t256 = cdiv(M, 256) * cdiv(N, 256) * L, t128 = cdiv(M, 128) * cdiv(N, 128) * L;
+        if (t256 >= cus && cdiv(t256, cus) * 1000 < cdiv(t128, 2 * cus) * 565) cfg = mmfp8::CFG_256x256;
+    }
     if (per_tensor && L == 1 && cfg == mmfp8::CFG_64x64) {
         // too few 128x128 tiles to fill the chip: K split over the waves of 64x64 / 32x64 tiles
         const int ks = cdiv(M, 64) * cdiv(N, 64) >= cu_count() ? mmfp8::KS_64x64 : mmfp8::KS_32x64;

@@ -570,7 +570,9 @@ __device__ __forceinline__ void ilv_step(const uint8_t* As, const uint8_t* Bs, i
 // k = 32g .. 32g+31 of row r (one MX group), converted to bf16 8 values at a
 // time for the four v_mfma_f32_16x16x32_bf16 of the step.
 //
-// The main loop is one of three. FP8 operands on square wave tiles (every
+// The main loop is one of four. Slow accumulation on the 256x256 tile (64x128
+// wave tiles) runs the row-chunk loop (kRc), which keeps only one fragment
+// row's 128-chunk partials live. FP8 operands on square wave tiles (every
 // per-tensor and MX 128x128 / 64x64 tile, and block scaling with a 128x128
 // scale_b) run ilv_step, which interleaves the next K = 32 sub-step's
 // conversions and the second half's fragment reads with the current MFMAs.
@@ -591,6 +593,9 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     constexpr int NT = NW * KG * 64;  // threads of the workgroup
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
+    // Slow accumulation on 64x128 wave tiles (the row-chunk main loop below). Its launcher guarantees
+    // K % 128 == 0, so it carries no K-tail code (which would not fit its registers).
+    constexpr bool kRc = MODE == MODE_SLOW && !PIPE && KG == 1 && FA != T_E2M1 && FM == 4 && FN == 8;
     constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;  // 1 KB LDS-DMA writes per wave per step
     constexpr int INS = A_INS + B_INS;
     static_assert(A_INS * 8 * NW == BM && B_INS * 8 * NW == BN, "tile rows must split evenly over the waves");
@@ -671,7 +676,7 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     // The row of wave-instruction q is 8 q + ld_row, so swz(row) = ld_row ^ (q & 1).
     const int ld_row = lane >> 3;
     auto ld_chunk = [&](int ins) { return (lane & 7) ^ ld_row ^ (ins & 1); };
-    const bool k_tail = (K % kBK) != 0;
+    const bool k_tail = !kRc && (K % kBK) != 0;
     uint32_t aoff[A_INS], boff[B_INS];
     // (the chunks are recomputed where the tail step needs them: kept from here,
     // they would hold registers across the whole main loop)
@@ -685,6 +690,19 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     for (int q = 0; q < B_INS; ++q) {
         boff[q] = (uint32_t)(((gw * B_INS + q) * 8 + ld_row) * p.ldb + bchunk(q) * 16);
     }
+    // Slow 64x128 wave tiles keep only the two per-lane parts (the chunk depends on the instruction's
+    // parity) and add the instruction's row block at issue: registers
+    constexpr bool kRcOff = kRc && A_INS % 2 == 0 && B_INS % 2 == 0;
+    const uint32_t alane[2] = {(uint32_t)(ld_row * p.lda + ld_chunk(gw * A_INS) * 16),
+                               (uint32_t)(ld_row * p.lda + ld_chunk(gw * A_INS + 1) * 16)};
+    const uint32_t blane[2] = {(uint32_t)(ld_row * p.ldb + ld_chunk(gw * B_INS) * 16),
+                               (uint32_t)(ld_row * p.ldb + ld_chunk(gw * B_INS + 1) * 16)};
+    auto aoffq = [&](int q) -> uint32_t {
+        return kRcOff ? alane[q & 1] + (uint32_t)((gw * A_INS + q) * 8 * p.lda) : aoff[q];
+    };
+    auto boffq = [&](int q) -> uint32_t {
+        return kRcOff ? blane[q & 1] + (uint32_t)((gw * B_INS + q) * 8 * p.ldb) : boff[q];
+    };
 
     const float* sa_l = p.sa + (int64_t)l * p.sa_batch;
     const float* sb_l = p.sb + (int64_t)l * p.sb_batch;
@@ -723,18 +741,26 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
         // arithmetic; the tail path is taken (a uniform branch) once per tile.
         auto load_ab = [&](auto tail) {
             constexpr bool TAIL = decltype(tail)::value;
-            const int soff = TAIL ? 0 : (int)kb;
+            // (kRcOff: the step offset joins the per-lane sum at issue, which keeps the compiler from holding
+            // every instruction's offset in a register across the loop)
+            const int soff = (TAIL || kRcOff) ? 0 : (int)kb;
 #pragma unroll
             for (int q = 0; q < A_INS; ++q) {
-                uint32_t off = aoff[q];
-                if constexpr (TAIL) off = (int)kb + achunk(q) * 16 >= K ? kOOB : off + kb;
+                uint32_t off = kRcOff ? alane[q & 1] + (uint32_t)((gw * A_INS + q) * 8 * p.lda + (int)kb) : aoffq(q);
+                if constexpr (TAIL) {
+                    if ((int)kb + achunk(q) * 16 >= K) off = kOOB;
+                    else if (!kRcOff) off += kb;
+                }
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sbase + (gw * A_INS + q) * 1024), 16, off,
                                                          soff, 0, 0);
             }
 #pragma unroll
             for (int q = 0; q < B_INS; ++q) {
-                uint32_t off = boff[q];
-                if constexpr (TAIL) off = (int)kb + bchunk(q) * 16 >= K ? kOOB : off + kb;
+                uint32_t off = kRcOff ? blane[q & 1] + (uint32_t)((gw * B_INS + q) * 8 * p.ldb + (int)kb) : boffq(q);
+                if constexpr (TAIL) {
+                    if ((int)kb + bchunk(q) * 16 >= K) off = kOOB;
+                    else if (!kRcOff) off += kb;
+                }
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sbase + BM * kBK + (gw * B_INS + q) * 1024),
                                                          16, off, soff, 0, 0);
             }
@@ -1054,7 +1080,76 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     // file
     constexpr bool kIlv = !PIPE && !kFp4 && FM == FN && (MODE != MODE_BLOCK || kSbOne);
 
-    if constexpr (PIPE) {
+    if constexpr (kRc) {
+        // Each step converts the wave's A fragments for all four K = 32 sub-steps once (the first sub-step's
+        // before the first MFMA, the others between the first row's MFMAs), then walks the B fragment rows
+        // (a 128-chunk's partial sums keep the same order as in the other loops, so the results are the
+        // same bit for bit): row j's partials (one per A fragment) take
+        // their four MFMAs back to back, interleaved over the A fragments, and row j - 1's partials are added
+        // to the accumulators just before row j's first MFMAs overwrite them. Only FM partials are live, so
+        // the 64x128 tile of the chained modes fits the promoted mode too: 1.5 conversions per MFMA instead
+        // of 2. The next row's B fragment is read and converted between the current row's MFMAs.
+        auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
+            stage_ready(kt, cur);
+            issue(kt + 1, nxt);
+            const uint8_t* As = cur + wm * WTM * kBK;
+            const uint8_t* Bs = cur + BM * kBK + wn * WTN * kBK;
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            i32x4 ra[2][FM];
+            bf16x8 xa[4][FM];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) ra[0][i] = *(const i32x4*)(As + i * 16 * kBK + foff0);
+            i32x4 rb0 = *(const i32x4*)(Bs + foff0), rb1 = *(const i32x4*)(Bs + foff1);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) ra[1][i] = *(const i32x4*)(As + i * 16 * kBK + foff1);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) xa[0][i] = to_bf16x8<FA>(ra[0][i], 0, 1.0f);
+            bf16x8 xb = to_bf16x8<FB>(rb0, 0, 1.0f);
+            f32x4 pt[FM];
+            i32x4 nb0 = rb0, nb1 = rb1;
+            __builtin_amdgcn_sched_barrier(0);
+            // sub-step u of B fragment row j (compile-time j and u: the scheduling pattern depends on them)
+            auto sub = [&](auto jc, auto uc) {
+                constexpr int j = decltype(jc)::value, u = decltype(uc)::value;
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    if constexpr (u == 0 && j > 0) acc[j - 1][i] += pt[i];
+                    pt[i] = mfma_bf16(xb, xa[u][i], u == 0 ? z : pt[i]);
+                }
+                if constexpr (j == 0 && u < 3) {  // the A operands of the next sub-step
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) xa[u + 1][i] = to_bf16x8<FA>(ra[(u + 1) / 2][i], (u + 1) & 1, 1.0f);
+                }
+                if constexpr (u == 1 && j + 1 < FN) {
+                    nb0 = *(const i32x4*)(Bs + (j + 1) * 16 * kBK + foff0);
+                    nb1 = *(const i32x4*)(Bs + (j + 1) * 16 * kBK + foff1);
+                }
+                if constexpr (u < 3) xb = to_bf16x8<FB>(u + 1 < 2 ? rb0 : rb1, (u + 1) & 1, 1.0f);
+                else if constexpr (j + 1 < FN) xb = to_bf16x8<FB>(nb0, 0, 1.0f);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (u == 3) {
+                    rb0 = nb0;
+                    rb1 = nb1;
+                }
+            };
+            auto row = [&](auto jc) {
+                sub(jc, IC<0>{});
+                sub(jc, IC<1>{});
+                sub(jc, IC<2>{});
+                sub(jc, IC<3>{});
+            };
+            static_assert(FN == 8, "eight B fragment rows");
+            row(IC<0>{}); row(IC<1>{}); row(IC<2>{}); row(IC<3>{});
+            row(IC<4>{}); row(IC<5>{}); row(IC<6>{}); row(IC<7>{});
+#pragma unroll
+            for (int i = 0; i < FM; ++i) acc[FN - 1][i] += pt[i];
+        };
+        issue(0, smem0);
+        for (int kt = 0; kt < KT; kt += 2) {
+            step(kt, smem0, smem1);
+            if (kt + 1 < KT) step(kt + 1, smem1, smem0);
+        }
+    } else if constexpr (PIPE) {
         Frag f0, f1;
         auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
             float s_a[FM], s_b[FN][4], c_a[FM], c_b[FN];

@@ -70,9 +70,12 @@ hipError_t launch_group_pack(bool trans, const uint8_t* src, int64_t R, int64_t 
 // per accumulator; their largest tile is 128x128 at two workgroups per CU,
 // which measured faster than 128x256 at one (eight waves that all meet at
 // every step's barrier, where the older wave of each SIMD pair finishes first
-// and the younger then runs alone). FP4 operands on the 64x128 wave tile
-// spill over a hundred registers (their scale factors change within a step;
-// on the scaled FP4 MFMA too: 242), so they start at 128x256.
+// and the younger then runs alone). Slow accumulation also has the 256x256
+// tile with its row-chunk loop (only the partials of one fragment row live),
+// which the dense entry points pick by tile count and K (mm_api.cpp); it is
+// not a starting point of the largest-tile search. FP4 operands on the 64x128
+// wave tile spill over a hundred registers (their scale factors change within
+// a step; on the scaled FP4 MFMA too: 242), so they start at 128x256.
 constexpr int min_cfg(int mode, int sbm, int fmt = 0) {
     (void)sbm;
     if (fmt == T_E2M1) return CFG_128x256;
@@ -107,10 +110,13 @@ hipError_t tile_launch(int cfg, const GemmArgs& p, int grid, hipStream_t s) {
                                           FB, SBM>),                                                               \
                                dim3(grid), dim3(kCfgWM[C] * kCfgWN[C] * 64), 0, s, p);                             \
     } while (0)
-    if (cfg < min_cfg(MODE, SBM, FA)) cfg = min_cfg(MODE, SBM, FA);
+    // (slow accumulation takes the 256x256 tile only when the caller picked it, for K a multiple of 128)
+    const bool slow256 = MODE == MODE_SLOW && cfg == CFG_256x256 && p.K % 128 == 0;
+    if (cfg < min_cfg(MODE, SBM, FA) && !slow256) cfg = min_cfg(MODE, SBM, FA);
     switch (cfg) {
         case CFG_256x256:
-            if constexpr ((MODE == MODE_FAST || MODE == MODE_SF32) && FA != T_E2M1) MMFP8_TILE(CFG_256x256);
+            if constexpr ((MODE == MODE_FAST || MODE == MODE_SF32 || MODE == MODE_SLOW) && FA != T_E2M1)
+                MMFP8_TILE(CFG_256x256);
             break;
         case CFG_128x256:
             if constexpr (MODE == MODE_FAST || MODE == MODE_SF32) MMFP8_TILE(CFG_128x256);

@@ -195,6 +195,47 @@ def test_production_tiles_per_tensor(M, N, K, fast):
     check_gemm(d, 0, 0, BF16, fast, rows=sample_rows(M, 8), what=f"{M}x{N}x{K} fast={fast}")
 
 
+# Slow accumulation with K a multiple of 128 and at least one 256x256 tile per CU runs the 256x256 tile's
+# row-chunk loop: square, ragged M and N with mixed formats, FP8 out, and a batch of eight items
+@pytest.mark.parametrize("M,N,K,fa,fb,d_type", [(4096, 4096, 1024, E4M3FN, E4M3FN, BF16),
+                                                (4056, 4072, 512, E5M2, E4M3FN, F32),
+                                                (4096, 4096, 256, E4M3FN, E5M2, E4M3FN)])
+def test_production_tiles_slow_256(M, N, K, fa, fb, d_type):
+    g = np.random.default_rng(M + N + K)
+    a = datagen.gauss_codes(g, (M, K), 64.0, fa)
+    b = datagen.gauss_codes(g, (N, K), 64.0, fb)
+    d = dict(a=a, b=b, K=K, a_fmt=fa, b_fmt=fb, scale_a=np.float32(0.5), scale_b=np.float32(0.25))
+    sr = np.float32(1 / 16) if d_type in (E4M3FN, E5M2) else None
+    check_gemm(d, 0, 0, d_type, False, rows=sample_rows(M, 8), scale_result=sr, ldd=N + 3 if d_type == F32 else None,
+               what=f"slow 256x256 {M}x{N}x{K}")
+
+
+def test_slow_256_matches_128_bitwise():
+    """The row-chunk loop sums each 128-chunk in the same order as the 128x128 tiles' loop: the first 2048 rows of
+    a 4096 x 4096 x 1024 product (256x256 tiles) equal, bit for bit, the 2048 x 4096 x 1024 product of those rows
+    (128x128 tiles, two per CU)."""
+    M, N, K = 4096, 4096, 1024
+    g = np.random.default_rng(77)
+    a = datagen.gauss_codes(g, (M, K), 64.0)
+    b = datagen.gauss_codes(g, (N, K), 64.0)
+    big = gu.scaled_gemm(a, E4M3FN, b, E4M3FN, K, 0.5, 0, 0.25, 0, F32)
+    half = gu.scaled_gemm(np.ascontiguousarray(a[:2048]), E4M3FN, b, E4M3FN, K, 0.5, 0, 0.25, 0, F32)
+    compare.assert_bitwise_equal(big[:2048], half, "256x256 slow rows vs 128x128 slow")
+
+
+def test_bias_slow_256():
+    M, N, K = 4096, 4096, 1024
+    g = np.random.default_rng(91)
+    a = datagen.gauss_codes(g, (M, K), 64.0)
+    b = datagen.gauss_codes(g, (N, K), 64.0)
+    bias_bits = _bias_bits(g, N, BF16)
+    gpu = gu.scaled_gemm_bias(a, E4M3FN, b, E4M3FN, K, 0.5, 0, 0.25, 0, bias_bits, BF16)
+    rows = sample_rows(M, 8)
+    value, sabs, bits = oracle.scaled_gemm(a, E4M3FN, b, E4M3FN, np.float32(0.5), 0, np.float32(0.25), 0, BF16,
+                                           rows=rows, bias=_bias_values(bias_bits, BF16))
+    compare.check(gpu[rows], value, sabs, bits, BF16, f"bias slow 256x256 {M}x{N}x{K}")
+
+
 # M = 33 .. 64 with K <= 4096 runs the skinny kernel with sixteen waves and two K steps each in flight (K = 4096,
 # a ragged K = 4040 whose last chunk straddles a 16-byte boundary, K = 136), a longer K the eight-wave one
 # (K = 8200)
@@ -846,6 +887,7 @@ def test_bias_block_scaled(sb_mode):
     (4, 512, 1024, 1032, False, F16, E5M2),      # 128x128 tiles, two per CU, ragged K
     (2, 2048, 1024, 264, True, BF16, E4M3FN),    # 256x256 tiles
     (3, 70, 200, 136, False, E4M3FN, E4M3FN),    # FP8 out with scale_result
+    (8, 2048, 1024, 512, False, BF16, E4M3FN),   # slow, 256x256 tiles (row-chunk loop), padded rows
 ])
 def test_batched_per_item_against_oracle(L, M, N, K, fast, d_type, fmt):
     g = np.random.default_rng(L * 1000 + M)
