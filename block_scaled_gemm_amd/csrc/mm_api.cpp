@@ -210,7 +210,7 @@ mm_status scaled_gemm(const char* who, int64_t L, int64_t M, int64_t N, int64_t 
     const int mode = per_tensor ? (use_fast_accum ? mmfp8::MODE_FAST : mmfp8::MODE_SLOW) : mmfp8::MODE_BLOCK;
     const int sbm = sb_mode == MM_SCALE_128x128 ? mmfp8::SB_128x128 : mmfp8::SB_1x128;
     int cfg = choose_cfg(M, N, L, cu_count(), mmfp8::min_cfg(mode, sbm));
-    if (mode == mmfp8::MODE_SLOW && K % 128 == 0 && cfg == mmfp8::CFG_128x128) {
+    if (mode == mmfp8::MODE_SLOW && cfg == mmfp8::CFG_128x128) {
         // The 256x256 tile's row-chunk loop does about 13% more per clock than two 128x128 workgroups per
         // CU, but runs one tile per CU: take it when its rounds cost less than the 128x128 tiles' rounds
         // (a round of one 256x256 tile per CU counted 1, a round of two 128x128 tiles per CU 0.565).

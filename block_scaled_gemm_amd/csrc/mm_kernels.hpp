@@ -593,8 +593,9 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     constexpr int NT = NW * KG * 64;  // threads of the workgroup
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
-    // Slow accumulation on 64x128 wave tiles (the row-chunk main loop below). Its launcher guarantees
-    // K % 128 == 0, so it carries no K-tail code (which would not fit its registers).
+    // Slow accumulation on 64x128 wave tiles (the row-chunk main loop below). A ragged K's last step is
+    // loaded like the others (every offset is per lane there, so the range check covers it) and the
+    // chunks at or past K are zeroed in LDS: the tail load path would not fit its registers.
     constexpr bool kRc = MODE == MODE_SLOW && !PIPE && KG == 1 && FA != T_E2M1 && FM == 4 && FN == 8;
     constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;  // 1 KB LDS-DMA writes per wave per step
     constexpr int INS = A_INS + B_INS;
@@ -693,6 +694,7 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     // Slow 64x128 wave tiles keep only the two per-lane parts (the chunk depends on the instruction's
     // parity) and add the instruction's row block at issue: registers
     constexpr bool kRcOff = kRc && A_INS % 2 == 0 && B_INS % 2 == 0;
+    static_assert(kRcOff == kRc, "the row-chunk loop's ragged K relies on per-lane step offsets");
     const uint32_t alane[2] = {(uint32_t)(ld_row * p.lda + ld_chunk(gw * A_INS) * 16),
                                (uint32_t)(ld_row * p.lda + ld_chunk(gw * A_INS + 1) * 16)};
     const uint32_t blane[2] = {(uint32_t)(ld_row * p.ldb + ld_chunk(gw * B_INS) * 16),
@@ -816,11 +818,12 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     };
     // In the last step of a K that is not a multiple of 16, a chunk straddling K
     // holds bytes of the next row (or padding): zero them in this lane's own
-    // LDS slots once its loads have landed.
+    // LDS slots once its loads have landed. The row-chunk loop loads its ragged
+    // last step like the others, so there every chunk at or past K is zeroed too.
     auto mask_straddle = [&](int kt, uint8_t* sbase) {
         auto fix = [&](uint8_t* slot, int chunk) {
             const int k0 = kt * kBK + chunk * 16;
-            if (!(k0 < K && K < k0 + 16)) return;
+            if (kRc ? K >= k0 + 16 : !(k0 < K && K < k0 + 16)) return;
             const int valid = K - k0;
             i32x4 v = *(i32x4*)slot;
 #pragma unroll
@@ -1069,7 +1072,7 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     // issuing the loads untracked with a fence-free barrier measured no faster).
     auto stage_ready = [&](int kt, uint8_t* stage) {
         __builtin_amdgcn_s_waitcnt(0);
-        if (k_tail && kt == KT - 1 && (K & 15)) mask_straddle(kt, stage);
+        if (kRc ? (kt == KT - 1 && (K % kBK) != 0) : (k_tail && kt == KT - 1 && (K & 15))) mask_straddle(kt, stage);
         __syncthreads();
     };
 

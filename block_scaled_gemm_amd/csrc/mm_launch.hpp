@@ -110,8 +110,8 @@ hipError_t tile_launch(int cfg, const GemmArgs& p, int grid, hipStream_t s) {
                                           FB, SBM>),                                                               \
                                dim3(grid), dim3(kCfgWM[C] * kCfgWN[C] * 64), 0, s, p);                             \
     } while (0)
-    // (slow accumulation takes the 256x256 tile only when the caller picked it, for K a multiple of 128)
-    const bool slow256 = MODE == MODE_SLOW && cfg == CFG_256x256 && p.K % 128 == 0;
+    // (slow accumulation takes the 256x256 tile only when the caller picked it)
+    const bool slow256 = MODE == MODE_SLOW && cfg == CFG_256x256;
     if (cfg < min_cfg(MODE, SBM, FA) && !slow256) cfg = min_cfg(MODE, SBM, FA);
     switch (cfg) {
         case CFG_256x256:

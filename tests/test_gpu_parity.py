@@ -195,32 +195,43 @@ def test_production_tiles_per_tensor(M, N, K, fast):
     check_gemm(d, 0, 0, BF16, fast, rows=sample_rows(M, 8), what=f"{M}x{N}x{K} fast={fast}")
 
 
-# Slow accumulation with K a multiple of 128 and at least one 256x256 tile per CU runs the 256x256 tile's
-# row-chunk loop: square, ragged M and N with mixed formats, FP8 out, and a batch of eight items
+# Slow accumulation with at least one 256x256 tile per CU runs the 256x256 tile's row-chunk loop: square,
+# ragged M and N with mixed formats, FP8 out, ragged K (its last step's chunks at or past K zeroed in LDS; the
+# row pitches padded with NaN codes, which must not reach the sums), a K below one step, and a batch of eight
 @pytest.mark.parametrize("M,N,K,fa,fb,d_type", [(4096, 4096, 1024, E4M3FN, E4M3FN, BF16),
                                                 (4056, 4072, 512, E5M2, E4M3FN, F32),
-                                                (4096, 4096, 256, E4M3FN, E5M2, E4M3FN)])
+                                                (4096, 4096, 256, E4M3FN, E5M2, E4M3FN),
+                                                (4096, 4096, 1000, E4M3FN, E4M3FN, F32),
+                                                (4100, 4096, 1032, E5M2, E5M2, BF16),
+                                                (4096, 4096, 40, E4M3FN, E4M3FN, F32)])
 def test_production_tiles_slow_256(M, N, K, fa, fb, d_type):
     g = np.random.default_rng(M + N + K)
-    a = datagen.gauss_codes(g, (M, K), 64.0, fa)
-    b = datagen.gauss_codes(g, (N, K), 64.0, fb)
+    a, b = _nan_padded(g, M, K, fa, 24), _nan_padded(g, N, K, fb, 8)
     d = dict(a=a, b=b, K=K, a_fmt=fa, b_fmt=fb, scale_a=np.float32(0.5), scale_b=np.float32(0.25))
     sr = np.float32(1 / 16) if d_type in (E4M3FN, E5M2) else None
     check_gemm(d, 0, 0, d_type, False, rows=sample_rows(M, 8), scale_result=sr, ldd=N + 3 if d_type == F32 else None,
                what=f"slow 256x256 {M}x{N}x{K}")
 
 
-def test_slow_256_matches_128_bitwise():
+def _nan_padded(g, rows, K, fmt, pad):
+    """Gaussian codes [rows, K] in a row pitch of K + pad bytes whose padding holds NaN codes."""
+    x = np.full((rows, K + pad), 0x7F, np.uint8)
+    x[:, :K] = datagen.gauss_codes(g, (rows, K), 64.0, fmt)
+    return x
+
+
+@pytest.mark.parametrize("K", [1024, 1000])
+def test_slow_256_matches_128_bitwise(K):
     """The row-chunk loop sums each 128-chunk in the same order as the 128x128 tiles' loop: the first 2048 rows of
-    a 4096 x 4096 x 1024 product (256x256 tiles) equal, bit for bit, the 2048 x 4096 x 1024 product of those rows
-    (128x128 tiles, two per CU)."""
-    M, N, K = 4096, 4096, 1024
-    g = np.random.default_rng(77)
-    a = datagen.gauss_codes(g, (M, K), 64.0)
-    b = datagen.gauss_codes(g, (N, K), 64.0)
+    a 4096 x 4096 x K product (256x256 tiles) equal, bit for bit, the 2048 x 4096 x K product of those rows
+    (128x128 tiles, two per CU); with a ragged K in NaN-padded pitches too."""
+    M, N = 4096, 4096
+    g = np.random.default_rng(77 + K)
+    a, b = _nan_padded(g, M, K, E4M3FN, 16), _nan_padded(g, N, K, E4M3FN, 16)
     big = gu.scaled_gemm(a, E4M3FN, b, E4M3FN, K, 0.5, 0, 0.25, 0, F32)
     half = gu.scaled_gemm(np.ascontiguousarray(a[:2048]), E4M3FN, b, E4M3FN, K, 0.5, 0, 0.25, 0, F32)
-    compare.assert_bitwise_equal(big[:2048], half, "256x256 slow rows vs 128x128 slow")
+    assert np.all(np.isfinite(half.view(np.float32)))
+    compare.assert_bitwise_equal(big[:2048], half, f"256x256 slow rows vs 128x128 slow, K = {K}")
 
 
 def test_bias_slow_256():
