@@ -71,6 +71,27 @@ int choose_cfg(int64_t M, int64_t N, int64_t L, int cus, int first) {
     return mmfp8::CFG_64x64;
 }
 
+// Columns of the product that the 256x256 row-chunk tiles take (slow accumulation, or block scaling with a
+// 128x128 scale_b): 0 for none, N for all, or a multiple of 256 whose tiles fill whole rounds of the CUs, the
+// other columns then going to the usual tiles in a second launch. Each plan is priced in rounds: one 256x256
+// tile per CU counts 1000, two 128x128 tiles per CU 565 (their measured times per round; the row-chunk loop
+// does about 13% more per clock, but one tile per CU leaves a partial last round half idle), a second launch
+// 250.
+int64_t rc_columns(int64_t M, int64_t N, int64_t L, int64_t cus) {
+    const int64_t tm = cdiv(M, 256) * L;  // 256-row tiles over the batch
+    const int64_t t256 = tm * cdiv(N, 256);
+    if (t256 < cus) return 0;
+    auto r128 = [&](int64_t cols) { return cdiv(cdiv(M, 128) * cdiv(cols, 128) * L, 2 * cus) * 565; };
+    int64_t best = r128(N), cols = 0;
+    if (cdiv(t256, cus) * 1000 < best) {
+        best = cdiv(t256, cus) * 1000;
+        cols = N;
+    }
+    const int64_t c = t256 / cus * cus / tm;  // 256-column blocks that whole rounds cover
+    if (c > 0 && c * 256 < N && cdiv(tm * c, cus) * 1000 + 250 + r128(N - c * 256) < best) cols = c * 256;
+    return cols;
+}
+
 mm_status device_status(hipError_t e, const char* what) {
     if (e == hipSuccess) return MM_OK;
     return fail(MM_ERR_DEVICE, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
@@ -209,14 +230,34 @@ mm_status scaled_gemm(const char* who, int64_t L, int64_t M, int64_t N, int64_t 
     }
     const int mode = per_tensor ? (use_fast_accum ? mmfp8::MODE_FAST : mmfp8::MODE_SLOW) : mmfp8::MODE_BLOCK;
     const int sbm = sb_mode == MM_SCALE_128x128 ? mmfp8::SB_128x128 : mmfp8::SB_1x128;
+    auto launch_tiles = [&](int c, mmfp8::GemmArgs& q, int64_t n) {
+        q.tiles_m = (int)cdiv(M, mmfp8::kCfgBM[c]);
+        q.tiles_n = (int)cdiv(n, mmfp8::kCfgBN[c]);
+        const int grid = (int)((int64_t)q.tiles_m * q.tiles_n * L);
+        if (!per_tensor) return mmfp8::launch_tile_block(c, sbm, fa, fb, q, grid, s);
+        return use_fast_accum ? mmfp8::launch_tile_fast(c, fa, fb, q, grid, s)
+                              : mmfp8::launch_tile_slow(c, fa, fb, q, grid, s);
+    };
     int cfg = choose_cfg(M, N, L, cu_count(), mmfp8::min_cfg(mode, sbm));
-    if (mode == mmfp8::MODE_SLOW && cfg == mmfp8::CFG_128x128) {
-        // The 256x256 tile's row-chunk loop does about 13% more per clock than two 128x128 workgroups per
-        // CU, but runs one tile per CU: take it when its rounds cost less than the 128x128 tiles' rounds
-        // (a round of one 256x256 tile per CU counted 1, a round of two 128x128 tiles per CU 0.565).
-        const int64_t cus = cu_count();
-        const int64_t t256 = cdiv(M, 256) * cdiv(N, 256) * L, t128 = cdiv(M, 128) * cdiv(N, 128) * L;
-        if (t256 >= cus && cdiv(t256, cus) * 1000 < cdiv(t128, 2 * cus) * 565) cfg = mmfp8::CFG_256x256;
+    const bool rc = mode == mmfp8::MODE_SLOW || (mode == mmfp8::MODE_BLOCK && sbm == mmfp8::SB_128x128);
+    if (rc && cfg == mmfp8::CFG_128x128) {
+        const int64_t cols = rc_columns(M, N, L, cu_count());
+        if (cols == N) {
+            cfg = mmfp8::CFG_256x256;
+        } else if (cols > 0) {
+            // columns [0, cols) on 256x256 tiles, the rest on the tiles their own count gives
+            mmfp8::GemmArgs q = p;
+            q.N = (int)cols;
+            e = launch_tiles(mmfp8::CFG_256x256, q, cols);
+            if (e != hipSuccess) return device_status(e, who);
+            p.b += cols * ldb;
+            p.d = static_cast<uint8_t*>(d) + cols * es;
+            if (bias) p.bias = static_cast<const uint8_t*>(bias) + cols * es;
+            if (mode == mmfp8::MODE_BLOCK) p.sb += cols / 128 * p.sb_ld;
+            N -= cols;
+            p.N = (int)N;
+            cfg = choose_cfg(M, N, L, cu_count(), mmfp8::min_cfg(mode, sbm));
+        }
     }
     if (per_tensor && L == 1 && cfg == mmfp8::CFG_64x64) {
         // too few 128x128 tiles to fill the chip: K split over the waves of 64x64 / 32x64 tiles
@@ -227,15 +268,7 @@ mm_status scaled_gemm(const char* who, int64_t L, int64_t M, int64_t N, int64_t 
         e = mmfp8::launch_ksplit(ks, mode, fa, fb, p, (int)grid, s);
         return device_status(e, who);
     }
-    p.tiles_m = (int)cdiv(M, mmfp8::kCfgBM[cfg]);
-    p.tiles_n = (int)cdiv(N, mmfp8::kCfgBN[cfg]);
-    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * L;
-    if (per_tensor) {
-        e = use_fast_accum ? mmfp8::launch_tile_fast(cfg, fa, fb, p, (int)grid, s)
-                           : mmfp8::launch_tile_slow(cfg, fa, fb, p, (int)grid, s);
-    } else {
-        e = mmfp8::launch_tile_block(cfg, sbm, fa, fb, p, (int)grid, s);
-    }
+    e = launch_tiles(cfg, p, N);
     return device_status(e, who);
 }
 

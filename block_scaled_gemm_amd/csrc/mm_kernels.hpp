@@ -593,10 +593,12 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     constexpr int NT = NW * KG * 64;  // threads of the workgroup
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
-    // Slow accumulation on 64x128 wave tiles (the row-chunk main loop below). A ragged K's last step is
-    // loaded like the others (every offset is per lane there, so the range check covers it) and the
-    // chunks at or past K are zeroed in LDS: the tail load path would not fit its registers.
-    constexpr bool kRc = MODE == MODE_SLOW && !PIPE && KG == 1 && FA != T_E2M1 && FM == 4 && FN == 8;
+    // Slow accumulation on 64x128 wave tiles, and block scaling there with a 128x128 scale_b (one s_b per
+    // wave and step): the row-chunk main loop below. A ragged K's last step is loaded like the others
+    // (every offset is per lane there, so the range check covers it) and the chunks at or past K are
+    // zeroed in LDS: the tail load path would not fit its registers.
+    constexpr bool kRc = (MODE == MODE_SLOW || (MODE == MODE_BLOCK && SBM == SB_128x128 && 128 % WTN == 0)) &&
+                         !PIPE && KG == 1 && FA != T_E2M1 && FM == 4 && FN == 8;
     constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;  // 1 KB LDS-DMA writes per wave per step
     constexpr int INS = A_INS + B_INS;
     static_assert(A_INS * 8 * NW == BM && B_INS * 8 * NW == BN, "tile rows must split evenly over the waves");
@@ -821,8 +823,12 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     // LDS slots once its loads have landed. The row-chunk loop loads its ragged
     // last step like the others, so there every chunk at or past K is zeroed too.
     auto mask_straddle = [&](int kt, uint8_t* sbase) {
+        // (the step's K offset is made opaque to the compiler: known to be the last step's, it let the masks be
+        // computed before the main loop, where they held eight registers across it)
+        int kbase = kt * kBK;
+        asm volatile("" : "+s"(kbase));
         auto fix = [&](uint8_t* slot, int chunk) {
-            const int k0 = kt * kBK + chunk * 16;
+            const int k0 = kbase + chunk * 16;
             if (kRc ? K >= k0 + 16 : !(k0 < K && K < k0 + 16)) return;
             const int valid = K - k0;
             i32x4 v = *(i32x4*)slot;
@@ -1092,8 +1098,23 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
         // to the accumulators just before row j's first MFMAs overwrite them. Only FM partials are live, so
         // the 64x128 tile of the chained modes fits the promoted mode too: 1.5 conversions per MFMA instead
         // of 2. The next row's B fragment is read and converted between the current row's MFMAs.
+        // (block scaling: a row's partials are folded in as acc = fma(part, s_a * s_b, acc), s_a of each A
+        // fragment's row read from the stage's scale column and the step's one s_b, as the other loops do)
         auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
             stage_ready(kt, cur);
+            float sab[FM];
+            if constexpr (MODE == MODE_BLOCK) {
+                const float sb = sc_cur.b[0];
+                sc_cur = load_scales(kt + 1);
+                const float* sa_col = (const float*)(cur + (BM + BN) * kBK) + wm * WTM + fr;
+#pragma unroll
+                for (int i = 0; i < FM; ++i) sab[i] = sa_col[16 * i] * sb;
+            }
+            // (one vector fma per fragment: written per element, the fold pushed this loop past the register file)
+            auto fold = [&](f32x4& a, const f32x4& part, int i) {
+                if constexpr (MODE == MODE_BLOCK) a = __builtin_elementwise_fma(part, f32x4{sab[i], sab[i], sab[i], sab[i]}, a);
+                else a += part;
+            };
             issue(kt + 1, nxt);
             const uint8_t* As = cur + wm * WTM * kBK;
             const uint8_t* Bs = cur + BM * kBK + wn * WTN * kBK;
@@ -1116,19 +1137,19 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
                 constexpr int j = decltype(jc)::value, u = decltype(uc)::value;
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
-                    if constexpr (u == 0 && j > 0) acc[j - 1][i] += pt[i];
+                    if constexpr (u == 0 && j > 0) fold(acc[j - 1][i], pt[i], i);
                     pt[i] = mfma_bf16(xb, xa[u][i], u == 0 ? z : pt[i]);
                 }
                 if constexpr (j == 0 && u < 3) {  // the A operands of the next sub-step
 #pragma unroll
                     for (int i = 0; i < FM; ++i) xa[u + 1][i] = to_bf16x8<FA>(ra[(u + 1) / 2][i], (u + 1) & 1, 1.0f);
                 }
-                if constexpr (u == 1 && j + 1 < FN) {
-                    nb0 = *(const i32x4*)(Bs + (j + 1) * 16 * kBK + foff0);
-                    nb1 = *(const i32x4*)(Bs + (j + 1) * 16 * kBK + foff1);
-                }
+                // (the next row's halves are read once this row's have been converted for the last time, so
+                // that one half of each is live at a time)
+                if constexpr (u == 1 && j + 1 < FN) nb0 = *(const i32x4*)(Bs + (j + 1) * 16 * kBK + foff0);
                 if constexpr (u < 3) xb = to_bf16x8<FB>(u + 1 < 2 ? rb0 : rb1, (u + 1) & 1, 1.0f);
                 else if constexpr (j + 1 < FN) xb = to_bf16x8<FB>(nb0, 0, 1.0f);
+                if constexpr (u == 2 && j + 1 < FN) nb1 = *(const i32x4*)(Bs + (j + 1) * 16 * kBK + foff1);
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (u == 3) {
                     rb0 = nb0;
@@ -1145,7 +1166,7 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
             row(IC<0>{}); row(IC<1>{}); row(IC<2>{}); row(IC<3>{});
             row(IC<4>{}); row(IC<5>{}); row(IC<6>{}); row(IC<7>{});
 #pragma unroll
-            for (int i = 0; i < FM; ++i) acc[FN - 1][i] += pt[i];
+            for (int i = 0; i < FM; ++i) fold(acc[FN - 1][i], pt[i], i);
         };
         issue(0, smem0);
         for (int kt = 0; kt < KT; kt += 2) {

@@ -110,12 +110,15 @@ hipError_t tile_launch(int cfg, const GemmArgs& p, int grid, hipStream_t s) {
                                           FB, SBM>),                                                               \
                                dim3(grid), dim3(kCfgWM[C] * kCfgWN[C] * 64), 0, s, p);                             \
     } while (0)
-    // (slow accumulation takes the 256x256 tile only when the caller picked it)
-    const bool slow256 = MODE == MODE_SLOW && cfg == CFG_256x256;
+    // (slow accumulation, and block scaling with a 128x128 scale_b, take the 256x256 tile only when the
+    // caller picked it)
+    const bool slow256 = (MODE == MODE_SLOW || (MODE == MODE_BLOCK && SBM == SB_128x128)) && cfg == CFG_256x256;
     if (cfg < min_cfg(MODE, SBM, FA) && !slow256) cfg = min_cfg(MODE, SBM, FA);
     switch (cfg) {
         case CFG_256x256:
-            if constexpr ((MODE == MODE_FAST || MODE == MODE_SF32 || MODE == MODE_SLOW) && FA != T_E2M1)
+            if constexpr ((MODE == MODE_FAST || MODE == MODE_SF32 || MODE == MODE_SLOW ||
+                           (MODE == MODE_BLOCK && SBM == SB_128x128)) &&
+                          FA != T_E2M1)
                 MMFP8_TILE(CFG_256x256);
             break;
         case CFG_128x256:

@@ -202,7 +202,7 @@ def test_production_tiles_per_tensor(M, N, K, fast):
                                                 (4056, 4072, 512, E5M2, E4M3FN, F32),
                                                 (4096, 4096, 256, E4M3FN, E5M2, E4M3FN),
                                                 (4096, 4096, 1000, E4M3FN, E4M3FN, F32),
-                                                (4100, 4096, 1032, E5M2, E5M2, BF16),
+                                                (4000, 4096, 1032, E5M2, E5M2, BF16),
                                                 (4096, 4096, 40, E4M3FN, E4M3FN, F32)])
 def test_production_tiles_slow_256(M, N, K, fa, fb, d_type):
     g = np.random.default_rng(M + N + K)
@@ -234,9 +234,46 @@ def test_slow_256_matches_128_bitwise(K):
     compare.assert_bitwise_equal(big[:2048], half, f"256x256 slow rows vs 128x128 slow, K = {K}")
 
 
-def test_bias_slow_256():
-    M, N, K = 4096, 4096, 1024
-    g = np.random.default_rng(91)
+# M = 4096, N = 14336 takes 3.5 rounds of 256x256 tiles: the first 12288 columns run on them (three whole rounds),
+# the last 2048 on 128x128 tiles in a second launch (b, d, bias and scale_b moved to those columns)
+@pytest.mark.parametrize("K,sb_mode,d_type", [(1000, 0, BF16), (520, 2, BF16), (136, 2, F32), (256, 0, E4M3FN)],
+                         ids=["tensor-bf16", "block-bf16", "block-f32", "tensor-e4m3"])
+def test_split_256_and_128_columns(K, sb_mode, d_type):
+    M, N = 4096, 14336
+    g = np.random.default_rng(K + sb_mode)
+    a, b = _nan_padded(g, M, K, E4M3FN, 8), _nan_padded(g, N, K, E4M3FN, 24)
+    if sb_mode:
+        kb = -(-K // 128)
+        sa, sb, sa_mode = datagen.log_uniform_scales(g, (M, kb)), datagen.log_uniform_scales(g, (N // 128, kb)), 1
+    else:
+        sa, sb, sa_mode = np.float32(0.5), np.float32(0.25), 0
+    d = dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN, scale_a=sa, scale_b=sb)
+    sr = np.float32(1 / 16) if d_type == E4M3FN else None
+    rows = tile_rows(M, band=256, edge=8)
+    check_gemm(d, sa_mode, sb_mode, d_type, False, rows=rows, scale_result=sr, what=f"split {M}x{N}x{K} sb={sb_mode}")
+
+
+@pytest.mark.parametrize("sb_mode", [0, 2], ids=["tensor", "block"])
+def test_split_256_matches_128_bitwise(sb_mode):
+    """The split plan's rows equal, bit for bit, those of a 1024-row product on 128x128 tiles only."""
+    M, N, K = 4096, 14336, 1000
+    g = np.random.default_rng(5 + sb_mode)
+    a, b = _nan_padded(g, M, K, E4M3FN, 8), _nan_padded(g, N, K, E4M3FN, 8)
+    kb = -(-K // 128)
+    if sb_mode:
+        sa, sb, sa_mode = datagen.log_uniform_scales(g, (M, kb)), datagen.log_uniform_scales(g, (N // 128, kb)), 1
+    else:
+        sa, sb, sa_mode = 0.5, 0.25, 0
+    big = gu.scaled_gemm(a, E4M3FN, b, E4M3FN, K, sa, sa_mode, sb, sb_mode, F32)
+    part = gu.scaled_gemm(np.ascontiguousarray(a[:1024]), E4M3FN, b, E4M3FN, K, sa[:1024] if sb_mode else sa, sa_mode,
+                          sb, sb_mode, F32)
+    assert np.all(np.isfinite(part.view(np.float32)))
+    compare.assert_bitwise_equal(big[:1024], part, f"split plan rows vs 128x128 tiles, sb={sb_mode}")
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 1024), (4096, 14336, 256)], ids=["256x256", "split"])
+def test_bias_slow_256(M, N, K):
+    g = np.random.default_rng(91 + N)
     a = datagen.gauss_codes(g, (M, K), 64.0)
     b = datagen.gauss_codes(g, (N, K), 64.0)
     bias_bits = _bias_bits(g, N, BF16)
@@ -244,7 +281,7 @@ def test_bias_slow_256():
     rows = sample_rows(M, 8)
     value, sabs, bits = oracle.scaled_gemm(a, E4M3FN, b, E4M3FN, np.float32(0.5), 0, np.float32(0.25), 0, BF16,
                                            rows=rows, bias=_bias_values(bias_bits, BF16))
-    compare.check(gpu[rows], value, sabs, bits, BF16, f"bias slow 256x256 {M}x{N}x{K}")
+    compare.check(gpu[rows], value, sabs, bits, BF16, f"bias slow {M}x{N}x{K}")
 
 
 # M = 33 .. 64 with K <= 4096 runs the skinny kernel with sixteen waves and two K steps each in flight (K = 4096,
@@ -299,7 +336,8 @@ def test_block_scales_small(M, N, K, sb_mode):
 # CU, a ragged M, and a K whose last chunk straddles a 16-byte boundary; with a 128x128 scale_b these run the
 # interleaved main loop (one s_b per wave and step), with a 1x128 scale_b the plain one
 BLOCK_TILE_CASES = [(1024, 4096, 1032, 2), (2048, 4096, 1032, 2), (1000, 4096, 1032, 2),
-                    (1024, 4096, 1032, 1), (2048, 4096, 1032, 1)]
+                    (1024, 4096, 1032, 1), (2048, 4096, 1032, 1),
+                    (4096, 4096, 1024, 2), (4000, 4072, 1000, 2)]  # 256x256 row-chunk tiles (128x128 scale_b)
 
 
 @pytest.mark.parametrize("M,N,K,sb_mode", BLOCK_TILE_CASES)
@@ -899,6 +937,7 @@ def test_bias_block_scaled(sb_mode):
     (2, 2048, 1024, 264, True, BF16, E4M3FN),    # 256x256 tiles
     (3, 70, 200, 136, False, E4M3FN, E4M3FN),    # FP8 out with scale_result
     (8, 2048, 1024, 512, False, BF16, E4M3FN),   # slow, 256x256 tiles (row-chunk loop), padded rows
+    (2, 2048, 14336, 136, False, F16, E4M3FN),   # slow, 256x256 tiles on 12288 columns, 128x128 on the rest
 ])
 def test_batched_per_item_against_oracle(L, M, N, K, fast, d_type, fmt):
     g = np.random.default_rng(L * 1000 + M)
