@@ -650,7 +650,10 @@ mm_status mm_scaled_gemm_grouped_layout(int64_t batch_sum, int64_t N, int64_t K,
     p.grp_sizes = batch_sizes;
     p.kgrp_start = start;
     const int mode = use_fast_accum ? mmfp8::MODE_FAST : mmfp8::MODE_SLOW;
-    const int cfg = choose_cfg(N, K, G, cu_count(), mmfp8::min_cfg(mode, 0));
+    int cfg = choose_cfg(N, K, G, cu_count(), mmfp8::min_cfg(mode, 0));
+    // slow: the 256x256 row-chunk tiles where they cost less for every block (no split plan here)
+    if (mode == mmfp8::MODE_SLOW && cfg == mmfp8::CFG_128x128 && rc_columns(N, K, G, cu_count()) == K)
+        cfg = mmfp8::CFG_256x256;
     p.tiles_m = (int)cdiv(N, mmfp8::kCfgBM[cfg]);
     p.tiles_n = (int)cdiv(K, mmfp8::kCfgBN[cfg]);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * G;

@@ -70,9 +70,10 @@ hipError_t launch_group_pack(bool trans, const uint8_t* src, int64_t R, int64_t 
 // per accumulator; their largest tile is 128x128 at two workgroups per CU,
 // which measured faster than 128x256 at one (eight waves that all meet at
 // every step's barrier, where the older wave of each SIMD pair finishes first
-// and the younger then runs alone). Slow accumulation also has the 256x256
-// tile with its row-chunk loop (only the partials of one fragment row live),
-// which the dense entry points pick by tile count and K (mm_api.cpp); it is
+// and the younger then runs alone). Slow accumulation, and block scaling with
+// a 128x128 scale_b, also have the 256x256 tile with its row-chunk loop (only
+// the partials of one fragment row live), which the dense entry points price
+// against the 128x128 tiles round by round (rc_columns in mm_api.cpp); it is
 // not a starting point of the largest-tile search. FP4 operands on the 64x128
 // wave tile spill over a hundred registers (their scale factors change within
 // a step; on the scaled FP4 MFMA too: 242), so they start at 128x256.

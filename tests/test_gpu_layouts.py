@@ -124,6 +124,7 @@ def test_grouped_nn(G, batch_sum, N, K, empty, fast, d_type):
     (4, 5000, 256, 256, 0, False, BF16),    # groups spanning many 128-element slow chunks
     (6, 777, 40, 300, 2, True, F16),        # thin blocks
     (2, 37, 100, 70, 0, False, E5M2),       # contractions shorter than one step
+    (8, 3000, 1024, 2048, 2, False, BF16),  # slow on 256x256 row-chunk tiles, ragged contractions, empty groups
 ])
 def test_grouped_contraction_split(tb, G, batch_sum, N, K, empty, fast, d_type):
     w = datagen.set_grouped_layout(G, batch_sum, N, K, empty, True, tb, config=80 + G)

@@ -236,15 +236,18 @@ def test_slow_256_matches_128_bitwise(K):
 
 # M = 4096, N = 14336 takes 3.5 rounds of 256x256 tiles: the first 12288 columns run on them (three whole rounds),
 # the last 2048 on 128x128 tiles in a second launch (b, d, bias and scale_b moved to those columns)
-@pytest.mark.parametrize("K,sb_mode,d_type", [(1000, 0, BF16), (520, 2, BF16), (136, 2, F32), (256, 0, E4M3FN)],
-                         ids=["tensor-bf16", "block-bf16", "block-f32", "tensor-e4m3"])
-def test_split_256_and_128_columns(K, sb_mode, d_type):
-    M, N = 4096, 14336
+# (N = 14000: the second launch's 1712 columns end in a partial 128-column tile)
+@pytest.mark.parametrize("N,K,sb_mode,d_type", [(14336, 1000, 0, BF16), (14336, 520, 2, BF16), (14336, 136, 2, F32),
+                                                (14336, 256, 0, E4M3FN), (14000, 264, 2, BF16), (14000, 392, 0, F16)],
+                         ids=["tensor-bf16", "block-bf16", "block-f32", "tensor-e4m3", "block-ragged-n",
+                              "tensor-ragged-n"])
+def test_split_256_and_128_columns(N, K, sb_mode, d_type):
+    M = 4096
     g = np.random.default_rng(K + sb_mode)
     a, b = _nan_padded(g, M, K, E4M3FN, 8), _nan_padded(g, N, K, E4M3FN, 24)
     if sb_mode:
         kb = -(-K // 128)
-        sa, sb, sa_mode = datagen.log_uniform_scales(g, (M, kb)), datagen.log_uniform_scales(g, (N // 128, kb)), 1
+        sa, sb, sa_mode = datagen.log_uniform_scales(g, (M, kb)), datagen.log_uniform_scales(g, (-(-N // 128), kb)), 1
     else:
         sa, sb, sa_mode = np.float32(0.5), np.float32(0.25), 0
     d = dict(a=a, b=b, K=K, a_fmt=E4M3FN, b_fmt=E4M3FN, scale_a=sa, scale_b=sb)
