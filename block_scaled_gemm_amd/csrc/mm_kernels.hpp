@@ -1751,6 +1751,37 @@ __global__ void __launch_bounds__(NW * 64) gemm_ksplit(GemmArgs p) {
         // Fast: one chain into the accumulators. Slow: a fresh fp32 partial per
         // 128-chunk (this step), promoted into the accumulator after.
         constexpr bool chain = MODE == MODE_FAST;
+        if constexpr (!chain && NW == 8) {
+            // Eight waves (two per SIMD): B fragment by B fragment, each 128-chunk partial finished and
+            // promoted before the next (the chunk sums keep their order), so that only MT partials are live
+            // next to the A operands converted once for the whole step
+            i32x4 ar[2][MT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                ar[0][i] = *(const i32x4*)(As + i * 16 * kBK + foff0);
+                ar[1][i] = *(const i32x4*)(As + i * 16 * kBK + foff1);
+            }
+            bf16x8 xa[4][MT];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < MT; ++i) xa[u][i] = to_bf16x8<FA>(ar[u / 2][i], u & 1, 1.0f);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const i32x4 b0 = *(const i32x4*)(Bs + j * 16 * kBK + foff0);
+                const i32x4 b1 = *(const i32x4*)(Bs + j * 16 * kBK + foff1);
+                f32x4 pt[MT];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const bf16x8 xb = to_bf16x8<FB>(u < 2 ? b0 : b1, u & 1, 1.0f);
+#pragma unroll
+                    for (int i = 0; i < MT; ++i) pt[i] = mfma_bf16(xb, xa[u][i], u == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : pt[i]);
+                }
+#pragma unroll
+                for (int i = 0; i < MT; ++i) acc[i][j] += pt[i];
+            }
+            continue;
+        }
 
         f32x4 part[chain ? 1 : MT][chain ? 1 : NT];
         if constexpr (!chain) {

@@ -182,7 +182,8 @@ TILE_CASES = [(4096, 4096, 1032, True),    # fast: 256x256 tile, eight 64x128 wa
               (1536, 4096, 1032, True),    # fast: 128x128, pipelined fragment reads
               (2048, 4096, 1032, False),   # slow: 128x128, two workgroups per CU
               (1000, 4096, 1032, False),   # slow: 128x128, ragged M, one per CU: two K groups
-              (256, 4096, 1032, False),    # K split over the waves, 64x64 tiles
+              (256, 4096, 1032, False),    # K split over the waves, 64x64 tiles (slow: eight waves)
+              (300, 4100, 1000, False),    # the same with ragged M, N and K
               (100, 4096, 1032, True)]     # K split over the waves, 32x64 tiles
 
 
