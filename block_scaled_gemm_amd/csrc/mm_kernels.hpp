@@ -593,11 +593,13 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
     constexpr int NT = NW * KG * 64;  // threads of the workgroup
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
-    // Slow accumulation on 64x128 wave tiles, and block scaling there with a 128x128 scale_b (one s_b per
-    // wave and step): the row-chunk main loop below. A ragged K's last step is loaded like the others
-    // (every offset is per lane there, so the range check covers it) and the chunks at or past K are
-    // zeroed in LDS: the tail load path would not fit its registers.
-    constexpr bool kRc = (MODE == MODE_SLOW || (MODE == MODE_BLOCK && SBM == SB_128x128 && 128 % WTN == 0)) &&
+    // FP8 operands on 64x128 wave tiles run the row-chunk main loop below: slow accumulation, block scaling
+    // with a 128x128 scale_b (one s_b per wave and step), and the chained modes (fast, and MX with fp32
+    // factors; with the page-native factor bytes it spilled 32 VGPRs). A ragged K's last step is loaded like
+    // the others (every offset is per lane there, so the range check covers it) and the chunks at or past K
+    // are zeroed in LDS: the tail load path would not fit its registers.
+    constexpr bool kRc = (MODE == MODE_SLOW || MODE == MODE_FAST || (MODE == MODE_SF32 && SBM == SF_F32) ||
+                          (MODE == MODE_BLOCK && SBM == SB_128x128 && 128 % WTN == 0)) &&
                          !PIPE && KG == 1 && FA != T_E2M1 && FM == 4 && FN == 8;
     constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;  // 1 KB LDS-DMA writes per wave per step
     constexpr int INS = A_INS + B_INS;
@@ -1100,8 +1102,20 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
         // of 2. The next row's B fragment is read and converted between the current row's MFMAs.
         // (block scaling: a row's partials are folded in as acc = fma(part, s_a * s_b, acc), s_a of each A
         // fragment's row read from the stage's scale column and the step's one s_b, as the other loops do)
+        // (the chained modes accumulate each MFMA straight into acc in the same K order as the plain loop,
+        // with the MX factors of the step riding in the conversions)
+        constexpr bool rc_chain = MODE == MODE_FAST || MODE == MODE_SF32;
         auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
             stage_ready(kt, cur);
+            float c_a[FM], c_b[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) c_a[i] = 1.0f;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) c_b[j] = 1.0f;
+            if constexpr (MODE == MODE_SF32) {
+                float s_a[FM], s_b[FN][4];
+                step_scales(kt, cur, s_a, s_b, c_a, c_b);
+            }
             float sab[FM];
             if constexpr (MODE == MODE_BLOCK) {
                 const float sb = sc_cur.b[0];
@@ -1127,8 +1141,8 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
 #pragma unroll
             for (int i = 0; i < FM; ++i) ra[1][i] = *(const i32x4*)(As + i * 16 * kBK + foff1);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) xa[0][i] = to_bf16x8<FA>(ra[0][i], 0, 1.0f);
-            bf16x8 xb = to_bf16x8<FB>(rb0, 0, 1.0f);
+            for (int i = 0; i < FM; ++i) xa[0][i] = to_bf16x8<FA>(ra[0][i], 0, c_a[i]);
+            bf16x8 xb = to_bf16x8<FB>(rb0, 0, c_b[0]);
             f32x4 pt[FM];
             i32x4 nb0 = rb0, nb1 = rb1;
             __builtin_amdgcn_sched_barrier(0);
@@ -1137,18 +1151,22 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
                 constexpr int j = decltype(jc)::value, u = decltype(uc)::value;
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
-                    if constexpr (u == 0 && j > 0) fold(acc[j - 1][i], pt[i], i);
-                    pt[i] = mfma_bf16(xb, xa[u][i], u == 0 ? z : pt[i]);
+                    if constexpr (rc_chain) {
+                        acc[j][i] = mfma_bf16(xb, xa[u][i], acc[j][i]);
+                    } else {
+                        if constexpr (u == 0 && j > 0) fold(acc[j - 1][i], pt[i], i);
+                        pt[i] = mfma_bf16(xb, xa[u][i], u == 0 ? z : pt[i]);
+                    }
                 }
                 if constexpr (j == 0 && u < 3) {  // the A operands of the next sub-step
 #pragma unroll
-                    for (int i = 0; i < FM; ++i) xa[u + 1][i] = to_bf16x8<FA>(ra[(u + 1) / 2][i], (u + 1) & 1, 1.0f);
+                    for (int i = 0; i < FM; ++i) xa[u + 1][i] = to_bf16x8<FA>(ra[(u + 1) / 2][i], (u + 1) & 1, c_a[i]);
                 }
                 // (the next row's halves are read once this row's have been converted for the last time, so
                 // that one half of each is live at a time)
                 if constexpr (u == 1 && j + 1 < FN) nb0 = *(const i32x4*)(Bs + (j + 1) * 16 * kBK + foff0);
-                if constexpr (u < 3) xb = to_bf16x8<FB>(u + 1 < 2 ? rb0 : rb1, (u + 1) & 1, 1.0f);
-                else if constexpr (j + 1 < FN) xb = to_bf16x8<FB>(nb0, 0, 1.0f);
+                if constexpr (u < 3) xb = to_bf16x8<FB>(u + 1 < 2 ? rb0 : rb1, (u + 1) & 1, c_b[j]);
+                else if constexpr (j + 1 < FN) xb = to_bf16x8<FB>(nb0, 0, c_b[j + 1]);
                 if constexpr (u == 2 && j + 1 < FN) nb1 = *(const i32x4*)(Bs + (j + 1) * 16 * kBK + foff1);
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (u == 3) {
@@ -1165,8 +1183,10 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
             static_assert(FN == 8, "eight B fragment rows");
             row(IC<0>{}); row(IC<1>{}); row(IC<2>{}); row(IC<3>{});
             row(IC<4>{}); row(IC<5>{}); row(IC<6>{}); row(IC<7>{});
+            if constexpr (!rc_chain) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) fold(acc[FN - 1][i], pt[i], i);
+                for (int i = 0; i < FM; ++i) fold(acc[FN - 1][i], pt[i], i);
+            }
         };
         issue(0, smem0);
         for (int kt = 0; kt < KT; kt += 2) {
