@@ -570,8 +570,10 @@ __device__ __forceinline__ void ilv_step(const uint8_t* As, const uint8_t* Bs, i
 // k = 32g .. 32g+31 of row r (one MX group), converted to bf16 8 values at a
 // time for the four v_mfma_f32_16x16x32_bf16 of the step.
 //
-// The main loop is one of four. Slow accumulation on the 256x256 tile (64x128
-// wave tiles) runs the row-chunk loop (kRc), which keeps only one fragment
+// The main loop is one of four. FP8 operands on 64x128 wave tiles (the 256x256
+// tile: slow, fast, MX with fp32 factors, block scaling with a 128x128
+// scale_b) run the row-chunk loop (kRc), which converts the step's A fragments
+// once and walks the B fragment rows, so that the promoted modes keep only one
 // row's 128-chunk partials live. FP8 operands on square wave tiles (every
 // per-tensor and MX 128x128 / 64x64 tile, and block scaling with a 128x128
 // scale_b) run ilv_step, which interleaves the next K = 32 sub-step's
