@@ -932,6 +932,23 @@ def test_bias_block_scaled(sb_mode):
     compare.check(gpu[rows], value, sabs, bits, BF16, f"bias block sb={sb_mode}")
 
 
+# block scaling with a 128x128 scale_b and a bias on the 256x256 row-chunk tiles, alone and in the split plan
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 520), (4096, 14336, 264)], ids=["256x256", "split"])
+def test_bias_block_scaled_256(M, N, K):
+    g = np.random.default_rng(M + N + K)
+    a = datagen.gauss_codes(g, (M, K), 64.0)
+    b = datagen.gauss_codes(g, (N, K), 64.0)
+    kb = -(-K // 128)
+    sa = datagen.log_uniform_scales(g, (M, kb))
+    sb = datagen.log_uniform_scales(g, (-(-N // 128), kb))
+    bias_bits = _bias_bits(g, N, F16)
+    gpu = gu.scaled_gemm_bias(a, E4M3FN, b, E4M3FN, K, sa, 1, sb, 2, bias_bits, F16)
+    rows = tile_rows(M, band=256, edge=8)
+    value, sabs, bits = oracle.scaled_gemm(a, E4M3FN, b, E4M3FN, sa, 1, sb, 2, F16, rows=rows,
+                                           bias=_bias_values(bias_bits, F16))
+    compare.check(gpu[rows], value, sabs, bits, F16, f"bias block 128x128 {M}x{N}x{K}")
+
+
 # ------------------------------------------------------------------ batched (TileOPs BmmFP8FwdOp)
 
 @pytest.mark.parametrize("L,M,N,K,fast,d_type,fmt", [
