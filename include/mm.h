@@ -9,9 +9,13 @@
  *    enqueued on it and the call returns without waiting for the GPU, so the
  *    calls can be captured into a HIP graph (the library records no memset
  *    nodes: outputs it must clear are cleared by its own kernels).
- *  - Arguments are validated completely before any HIP call. On any status
- *    other than MM_OK nothing has been enqueued or written, and
- *    mm_last_error() describes the problem. No C++ exception crosses the ABI.
+ *  - Arguments are validated completely before any HIP call. On a status
+ *    other than MM_OK and MM_ERR_DEVICE nothing has been enqueued or written.
+ *    MM_ERR_DEVICE means that a HIP call failed while the call enqueued its
+ *    work; a call may enqueue several kernels (operand packing, or two tile
+ *    shapes over different columns), and those enqueued before the failure
+ *    may still run. mm_last_error() describes the problem. No C++ exception
+ *    crosses the ABI.
  *  - The library uses the calling thread's current HIP device.
  *  - The kernels never fault whatever the byte values of the operands are:
  *    NaN and Inf codes, padding bytes and partial tiles are all handled.
