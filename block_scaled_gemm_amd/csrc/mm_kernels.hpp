@@ -9,7 +9,7 @@
 // frontend: GEMM + Amax (SM100)" (Equations).
 //
 // Hardware facts this file relies on (measured on MI355X with in-bounds
-// probes, see the design notes):
+// probes; tests/mfma_precision.py reproduces the first):
 //  * The FP8 MFMAs of gfx950 (v_mfma_scale_f32_16x16x128_f8f6f4 and the older
 //    fp8 ones) do not sum their products exactly: small products that share an
 //    adder group with large ones lose low bits, up to ~2^-16.5 * sum|t| per
