@@ -1095,17 +1095,19 @@ __global__ void __launch_bounds__(WM * WN * KG * 64, (WM * WN * KG == 4 && !PIPE
 
     if constexpr (kRc) {
         // Each step converts the wave's A fragments for all four K = 32 sub-steps once (the first sub-step's
-        // before the first MFMA, the others between the first row's MFMAs), then walks the B fragment rows
-        // (a 128-chunk's partial sums keep the same order as in the other loops, so the results are the
-        // same bit for bit): row j's partials (one per A fragment) take
-        // their four MFMAs back to back, interleaved over the A fragments, and row j - 1's partials are added
-        // to the accumulators just before row j's first MFMAs overwrite them. Only FM partials are live, so
-        // the 64x128 tile of the chained modes fits the promoted mode too: 1.5 conversions per MFMA instead
-        // of 2. The next row's B fragment is read and converted between the current row's MFMAs.
-        // (block scaling: a row's partials are folded in as acc = fma(part, s_a * s_b, acc), s_a of each A
-        // fragment's row read from the stage's scale column and the step's one s_b, as the other loops do)
-        // (the chained modes accumulate each MFMA straight into acc in the same K order as the plain loop,
-        // with the MX factors of the step riding in the conversions)
+        // before the first MFMA, the others between the first row's MFMAs) and then walks the B fragment rows.
+        // Row j's four accumulation chains (one per A fragment) take their four MFMAs back to back,
+        // interleaved over the A fragments, while the next row's B fragment is read and converted; B is thus
+        // converted once per wave for four A fragments and A once for eight B fragments (1.5 conversions per
+        // MFMA against 2 on 64x64 wave tiles).
+        //  * Promoted modes: each row's 128-chunk partials start from zero and are folded into the
+        //    accumulators just before the next row's first MFMAs overwrite them (acc += part; block scaling
+        //    acc = fma(part, s_a * s_b, acc) with s_a of the A fragment's row from the stage's scale column and
+        //    the step's one s_b). Only FM partials are live, which lets the promoted modes use the 64x128 tile.
+        //  * Chained modes (fast, MX): each MFMA accumulates straight into acc, the MX factors of the step
+        //    riding in the conversions.
+        // Every accumulator sees its K values in the order of the other loops, so the results are the same bit
+        // for bit.
         constexpr bool rc_chain = MODE == MODE_FAST || MODE == MODE_SF32;
         auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
             stage_ready(kt, cur);
