@@ -205,7 +205,8 @@ def test_production_tiles_per_tensor(M, N, K, fast):
                                                 (4096, 4096, 1000, E4M3FN, E4M3FN, F32),
                                                 (4000, 4096, 1032, E5M2, E5M2, BF16),
                                                 (4096, 4096, 40, E4M3FN, E4M3FN, F32),
-                                                (4096, 4096, 0, E4M3FN, E4M3FN, F32)])
+                                                (4096, 4096, 0, E4M3FN, E4M3FN, F32),
+                                                (4001, 4095, 1000, E4M3FN, E5M2, BF16)])
 def test_production_tiles_slow_256(M, N, K, fa, fb, d_type):
     g = np.random.default_rng(M + N + K)
     a, b = _nan_padded(g, M, K, fa, 24), _nan_padded(g, N, K, fb, 8)
